@@ -1,0 +1,163 @@
+"""ctypes wrapper of the plain C oracle (``dsa_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg import this module.  The HIP library and its binding never
+import it.  Arrays are numpy, host memory; bf16 operands are uint16 bit
+patterns as drawn by ``workloads``.
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dsa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
+            os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "dsa_oracle.h"))):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                        "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+                        "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _configure(lib):
+    P = ctypes.c_void_p
+    i64, i32, dbl = ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+    lib.oracle_indexer_scores.argtypes = [P, P, P, i64, i64, i64, i32, i32, P, i64, P, i32]
+    lib.oracle_topk_select.argtypes = [P, i64, i64, P, i32, P, P, i32]
+    lib.oracle_sparse_mla_attn.argtypes = [P, P, P, P, i64, i64, i32, i32, i32, i32, dbl,
+                                           P, i64, P, P, i32]
+    lib.oracle_prefill_chunk.argtypes = [P, P, P, P, P, i64, i64, i64, i32, i32, i32, i32, i32,
+                                         i32, dbl, P, i64, P, P, P, i32]
+    lib.oracle_decode_step.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, dbl,
+                                       P, P, P, i32]
+    for f in (lib.oracle_indexer_scores, lib.oracle_topk_select, lib.oracle_sparse_mla_attn,
+              lib.oracle_prefill_chunk, lib.oracle_decode_step):
+        f.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        _lib = _configure(ctypes.CDLL(build()))
+    return _lib
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Run the wrappers against another build of the oracle (the tests use
+    this to check that deliberately broken copies fail the pins)."""
+    global _lib
+    saved = _lib
+    _lib = _configure(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def default_threads() -> int:
+    return max(1, min(os.cpu_count() or 1, 64))
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _rows(rows, L) -> np.ndarray:
+    return _c(np.arange(L) if rows is None else rows, np.int64)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError("oracle %s failed with code %d" % (what, rc))
+
+
+def indexer_scores(qI, kI, w, q_start: int, rows=None, nthreads: Optional[int] = None) -> np.ndarray:
+    """Scores [len(rows), N] float32 (-inf on masked keys)."""
+    qI, kI, w = _c(qI, np.uint16), _c(kI, np.uint16), _c(w, np.float32)
+    L, Hi, Di = qI.shape
+    N = kI.shape[0]
+    rows = _rows(rows, L)
+    S = np.empty((rows.size, N), dtype=np.float32)
+    _check(_load().oracle_indexer_scores(_p(qI), _p(kI), _p(w), L, N, q_start, Hi, Di, _p(rows),
+                                         rows.size, _p(S), nthreads or default_threads()), "indexer")
+    return S
+
+
+def topk_select(S, pos, top_k: int, nthreads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """(idx [rows, top_k] int32 ascending, -1 padded; count [rows] int32)."""
+    S = _c(S, np.float32)
+    pos = _c(pos, np.int64)
+    nrows, N = S.shape
+    idx = np.empty((nrows, top_k), dtype=np.int32)
+    cnt = np.empty((nrows,), dtype=np.int32)
+    _check(_load().oracle_topk_select(_p(S), nrows, N, _p(pos), top_k, _p(idx), _p(cnt),
+                                      nthreads or default_threads()), "topk")
+    return idx, cnt
+
+
+def sparse_mla_attn(q, kv, idx, count, d_latent: int, scale: float, rows=None,
+                    nthreads: Optional[int] = None, want_lse: bool = False):
+    """Attention output [rows, H, Dl] float64 (and lse [rows, H] if asked)."""
+    q, kv, idx, count = _c(q, np.uint16), _c(kv, np.uint16), _c(idx, np.int32), _c(count, np.int32)
+    L, H, Dqk = q.shape
+    N = kv.shape[0]
+    top_k = idx.shape[1]
+    rows = _rows(rows, L)
+    out = np.empty((rows.size, H, d_latent), dtype=np.float64)
+    lse = np.empty((rows.size, H), dtype=np.float64) if want_lse else None
+    _check(_load().oracle_sparse_mla_attn(_p(q), _p(kv), _p(idx), _p(count), L, N, H, Dqk, d_latent,
+                                          top_k, scale, _p(rows), rows.size, _p(out), _p(lse),
+                                          nthreads or default_threads()), "attention")
+    return (out, lse) if want_lse else out
+
+
+def prefill_chunk(inp: dict, shape, q_start: int, rows=None, nthreads: Optional[int] = None):
+    """(idx [rows, top_k], count [rows], out [rows, H, Dl] float64)."""
+    q, qI, w = _c(inp["q"], np.uint16), _c(inp["qI"], np.uint16), _c(inp["w"], np.float32)
+    kv, kI = _c(inp["kv"], np.uint16), _c(inp["kI"], np.uint16)
+    L, N = q.shape[0], kv.shape[0]
+    rows = _rows(rows, L)
+    idx = np.empty((rows.size, shape.top_k), dtype=np.int32)
+    cnt = np.empty((rows.size,), dtype=np.int32)
+    out = np.empty((rows.size, shape.n_heads, shape.d_latent), dtype=np.float64)
+    _check(_load().oracle_prefill_chunk(
+        _p(q), _p(qI), _p(w), _p(kv), _p(kI), L, N, q_start, shape.n_heads, shape.d_latent,
+        shape.d_rope, shape.n_idx_heads, shape.d_idx, shape.top_k, shape.softmax_scale,
+        _p(rows), rows.size, _p(idx), _p(cnt), _p(out), nthreads or default_threads()), "prefill")
+    return idx, cnt, out
+
+
+def decode_step(inp: dict, shape, nthreads: Optional[int] = None):
+    """(idx [B, top_k] sequence-local key ids, count [B], out [B, H, Dl] float64)."""
+    q, qI, w = _c(inp["q"], np.uint16), _c(inp["qI"], np.uint16), _c(inp["w"], np.float32)
+    kv, kI = _c(inp["kv"], np.uint16), _c(inp["kI"], np.uint16)
+    ctx = _c(inp["ctx"], np.int64)
+    B = ctx.size
+    idx = np.empty((B, shape.top_k), dtype=np.int32)
+    cnt = np.empty((B,), dtype=np.int32)
+    out = np.empty((B, shape.n_heads, shape.d_latent), dtype=np.float64)
+    _check(_load().oracle_decode_step(
+        _p(q), _p(qI), _p(w), _p(kv), _p(kI), B, _p(ctx), shape.n_heads, shape.d_latent,
+        shape.d_rope, shape.n_idx_heads, shape.d_idx, shape.top_k, shape.softmax_scale,
+        _p(idx), _p(cnt), _p(out), nthreads or default_threads()), "decode")
+    return idx, cnt, out

@@ -1,0 +1,372 @@
+/*
+ * dsa_oracle.c - plain, slow, obviously correct CPU oracle for the DSA
+ * prefill/decode path (indexer -> top-k -> absorbed-MLA attention).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no source,
+ * header, table or helper with the HIP library, and neither includes the
+ * other.
+ *
+ * Sources (the pages; section names, no line numbers):
+ *  - exo PR #2539 "GLM-5.2/5.3 (glm_moe_dsa) attention and MoE speed-ups",
+ *    Prefill section: the indexer score (weighted relu of q.k summed over the
+ *    32 indexer heads, float32, causal mask applied), the top-2048 selection,
+ *    the every-earlier-key rule for queries with fewer causal keys than the
+ *    selection size, and the float32 softmax over gathered latent keys;
+ *    Decode section: single-token attention with the heads as rows.
+ *  - "GLM-5.2-Vision: llama.cpp vs vLLM line-by-line pipeline trace",
+ *    section 6 (attention core, absorbed MLA): Q = [q_nope_absorbed | q_pe],
+ *    K = [kv_cmpr | k_pe], V = kv_cmpr; kq = K.q, softmax with kq_scale,
+ *    kqv = V.kq.  The config line gives index_topk 2048 and the head widths.
+ *
+ * Readings where the pages are silent are stated at each function and in
+ * the design notes: key j is visible to the query at position p iff j <= p;
+ * equal scores go to the lower key index; the selection is returned in
+ * ascending key order padded with -1; no extra factor enters the indexer.
+ *
+ * Every step is computed in double precision except where noted.  There is
+ * no blocking, fusion or reordering beyond the definitions.
+ */
+#include "dsa_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- step 1: load and convert ------------------------------------------
+ * bf16 is the upper half of an IEEE binary32; widening is exact. */
+static double bf16_to_double(uint16_t b) {
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double* widen_all(const uint16_t* src, int64_t n) {
+    double* dst = (double*)malloc((size_t)n * sizeof(double));
+    if (!dst) return NULL;
+    for (int64_t k = 0; k < n; ++k) dst[k] = bf16_to_double(src[k]);
+    return dst;
+}
+
+/* ---- a plain parallel-for over rows: row r goes to thread r % T --------- */
+typedef void (*row_fn)(void* ctx, int64_t r, void* scratch);
+
+typedef struct {
+    row_fn fn;
+    void* ctx;
+    int64_t nrows;
+    int32_t tid, nthreads;
+    size_t scratch_bytes;
+    int failed;
+} pf_job;
+
+static void* pf_worker(void* arg) {
+    pf_job* j = (pf_job*)arg;
+    void* scratch = NULL;
+    if (j->scratch_bytes) {
+        scratch = malloc(j->scratch_bytes);
+        if (!scratch) { j->failed = 1; return NULL; }
+    }
+    for (int64_t r = j->tid; r < j->nrows; r += j->nthreads) j->fn(j->ctx, r, scratch);
+    free(scratch);
+    return NULL;
+}
+
+static int parallel_rows(row_fn fn, void* ctx, int64_t nrows, int32_t nthreads, size_t scratch_bytes) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > nrows) nthreads = (int32_t)(nrows > 0 ? nrows : 1);
+    pthread_t th[256];
+    pf_job jobs[256];
+    int started[256];
+    for (int32_t t = 0; t < nthreads; ++t) {
+        jobs[t] = (pf_job){fn, ctx, nrows, t, nthreads, scratch_bytes, 0};
+        started[t] = (t > 0) && pthread_create(&th[t], NULL, pf_worker, &jobs[t]) == 0;
+    }
+    pf_worker(&jobs[0]);
+    int failed = jobs[0].failed;
+    for (int32_t t = 1; t < nthreads; ++t) {
+        if (started[t]) pthread_join(th[t], NULL);
+        else pf_worker(&jobs[t]);          /* could not start a thread: run inline */
+        failed |= jobs[t].failed;
+    }
+    return failed ? -9 : 0;
+}
+
+/* ---- step 2: indexer scores ---------------------------------------------
+ * exo PR #2539, Prefill section, float32 indexer item: the per-key score is
+ * relu(q.k) times each head's weight, summed over the indexer heads, with the
+ * causal mask applied.  One Di-wide indexer key per token is shared by all
+ * heads; w is per query and head; nothing else scales the sum. */
+static void indexer_row(const double* qIrow /* [Hi*Di] */, const double* kId /* [N*Di] */,
+                        const float* wrow /* [Hi] */, int64_t N, int64_t p,
+                        int32_t Hi, int32_t Di, float* Srow) {
+    for (int64_t j = 0; j < N; ++j) {
+        if (j > p) { Srow[j] = -INFINITY; continue; }     /* causal mask */
+        double total = 0.0;
+        for (int32_t h = 0; h < Hi; ++h) {
+            double dot = 0.0;
+            for (int32_t d = 0; d < Di; ++d) dot += qIrow[(int64_t)h * Di + d] * kId[j * Di + d];
+            double relu = dot > 0.0 ? dot : 0.0;
+            total += (double)wrow[h] * relu;
+        }
+        Srow[j] = (float)total;   /* the pages' score is a float32 value */
+    }
+}
+
+typedef struct {
+    const uint16_t* qI; const double* kId; const float* w;
+    int64_t N, q_start; int32_t Hi, Di;
+    const int64_t* rows; float* S_out;
+} indexer_ctx;
+
+static void indexer_task(void* c, int64_t r, void* scratch) {
+    indexer_ctx* x = (indexer_ctx*)c;
+    int64_t i = x->rows[r];
+    double* qrow = (double*)scratch;
+    const uint16_t* src = x->qI + i * (int64_t)x->Hi * x->Di;
+    for (int64_t k = 0; k < (int64_t)x->Hi * x->Di; ++k) qrow[k] = bf16_to_double(src[k]);
+    indexer_row(qrow, x->kId, x->w + i * x->Hi, x->N, x->q_start + i, x->Hi, x->Di,
+                x->S_out + r * x->N);
+}
+
+static int rows_ok(const int64_t* rows, int64_t nrows, int64_t L) {
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= L) return 0;
+    return 1;
+}
+
+int oracle_indexer_scores(const uint16_t* qI, const uint16_t* kI, const float* w,
+                          int64_t L, int64_t N, int64_t q_start, int32_t Hi, int32_t Di,
+                          const int64_t* rows, int64_t nrows, float* S_out, int32_t nthreads) {
+    if (!qI || !kI || !w || !rows || !S_out) return -1;
+    if (L <= 0 || N <= 0 || Hi <= 0 || Di <= 0 || nrows < 0 || q_start < 0) return -1;
+    if (!rows_ok(rows, nrows, L)) return -1;
+    double* kId = widen_all(kI, N * Di);
+    if (!kId) return -8;
+    indexer_ctx x = {qI, kId, w, N, q_start, Hi, Di, rows, S_out};
+    int rc = parallel_rows(indexer_task, &x, nrows, nthreads, (size_t)Hi * Di * sizeof(double));
+    free(kId);
+    return rc;
+}
+
+/* ---- step 3: top-k selection --------------------------------------------
+ * exo PR #2539, Prefill section: each query keeps its index_topk (2048)
+ * highest-scoring causal keys; a query with no more causal keys than that
+ * keeps every earlier key.  Readings: equal scores go to the lower key index;
+ * the kept keys are listed in ascending key order and padded with -1. */
+typedef struct { float s; int32_t j; } cand;
+
+static int by_score_then_key(const void* a, const void* b) {
+    const cand* x = (const cand*)a;
+    const cand* y = (const cand*)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->j < y->j) ? -1 : (x->j > y->j);
+}
+
+static int ascending_int(const void* a, const void* b) {
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x < y) ? -1 : (x > y);
+}
+
+static void topk_row(const float* Srow, int64_t p, int32_t top_k, cand* work,
+                     int32_t* idxrow, int32_t* count) {
+    int64_t n = p + 1;                       /* causal keys 0..p */
+    for (int32_t t = 0; t < top_k; ++t) idxrow[t] = -1;
+    if (n <= top_k) {                        /* every earlier key */
+        for (int64_t j = 0; j < n; ++j) idxrow[j] = (int32_t)j;
+        *count = (int32_t)n;
+        return;
+    }
+    for (int64_t j = 0; j < n; ++j) { work[j].s = Srow[j]; work[j].j = (int32_t)j; }
+    qsort(work, (size_t)n, sizeof(cand), by_score_then_key);
+    for (int32_t t = 0; t < top_k; ++t) idxrow[t] = work[t].j;
+    qsort(idxrow, (size_t)top_k, sizeof(int32_t), ascending_int);
+    *count = top_k;
+}
+
+typedef struct {
+    const float* S; int64_t N; const int64_t* pos; int32_t top_k;
+    int32_t* idx; int32_t* count; int bad;
+} topk_ctx;
+
+static void topk_task(void* c, int64_t r, void* scratch) {
+    topk_ctx* x = (topk_ctx*)c;
+    topk_row(x->S + r * x->N, x->pos[r], x->top_k, (cand*)scratch,
+             x->idx + r * x->top_k, x->count + r);
+}
+
+int oracle_topk_select(const float* S, int64_t nrows, int64_t N, const int64_t* pos,
+                       int32_t top_k, int32_t* idx, int32_t* count, int32_t nthreads) {
+    if (!S || !pos || !idx || !count || nrows < 0 || N <= 0 || top_k <= 0) return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (pos[r] < 0 || pos[r] >= N) return -1;
+    topk_ctx x = {S, N, pos, top_k, idx, count, 0};
+    return parallel_rows(topk_task, &x, nrows, nthreads, (size_t)N * sizeof(cand));
+}
+
+/* ---- step 4: absorbed-MLA attention over the selected latent rows --------
+ * Pipeline trace, section 6: Q = [q_nope_absorbed | q_pe] (Dl + Dr wide),
+ * K = [kv_cmpr | k_pe], V = kv_cmpr (the first Dl columns of the latent row);
+ * scores K.q scaled by kq_scale, softmax, then V weighted by it.
+ * exo PR #2539, Prefill section: the softmax runs over the gathered selected
+ * keys only.  No bias, sink or soft-cap enters the softmax. */
+static void attention_row(const double* qrow /* [H*Dqk] */, const double* kvd /* [N*Dqk] */,
+                          const int32_t* sel, int32_t cnt, int64_t N, int32_t H, int32_t Dqk,
+                          int32_t Dv, double scale, double* s /* [cnt] */,
+                          double* outrow /* [H*Dv] */, double* lserow /* [H] or NULL */) {
+    for (int32_t h = 0; h < H; ++h) {
+        const double* qh = qrow + (int64_t)h * Dqk;
+        double* oh = outrow + (int64_t)h * Dv;
+        for (int32_t d = 0; d < Dv; ++d) oh[d] = 0.0;
+        int32_t used = 0;
+        double m = -INFINITY;
+        for (int32_t t = 0; t < cnt; ++t) {
+            int64_t j = sel[t];
+            if (j < 0 || j >= N) { s[t] = -INFINITY; continue; }   /* not a key */
+            double dot = 0.0;
+            for (int32_t d = 0; d < Dqk; ++d) dot += qh[d] * kvd[j * Dqk + d];
+            s[t] = scale * dot;
+            if (s[t] > m) m = s[t];
+            ++used;
+        }
+        if (used == 0) { if (lserow) lserow[h] = -INFINITY; continue; }
+        double Z = 0.0;
+        for (int32_t t = 0; t < cnt; ++t) Z += (s[t] == -INFINITY) ? 0.0 : exp(s[t] - m);
+        for (int32_t t = 0; t < cnt; ++t) {
+            if (s[t] == -INFINITY) continue;
+            double pt = exp(s[t] - m) / Z;
+            const double* v = kvd + (int64_t)sel[t] * Dqk;          /* V = first Dv columns */
+            for (int32_t d = 0; d < Dv; ++d) oh[d] += pt * v[d];
+        }
+        if (lserow) lserow[h] = m + log(Z);
+    }
+}
+
+typedef struct {
+    const uint16_t* q; const double* kvd; const int32_t* idx; const int32_t* count;
+    int64_t N; int32_t H, Dqk, Dv, top_k; double scale;
+    const int64_t* rows; double* out; double* lse;
+} attn_ctx;
+
+static void attn_task(void* c, int64_t r, void* scratch) {
+    attn_ctx* x = (attn_ctx*)c;
+    int64_t i = x->rows[r];
+    double* qrow = (double*)scratch;
+    double* s = qrow + (int64_t)x->H * x->Dqk;
+    const uint16_t* src = x->q + i * (int64_t)x->H * x->Dqk;
+    for (int64_t k = 0; k < (int64_t)x->H * x->Dqk; ++k) qrow[k] = bf16_to_double(src[k]);
+    int32_t cnt = x->count[i];
+    if (cnt > x->top_k) cnt = x->top_k;
+    attention_row(qrow, x->kvd, x->idx + i * x->top_k, cnt, x->N, x->H, x->Dqk, x->Dv, x->scale,
+                  s, x->out + r * (int64_t)x->H * x->Dv, x->lse ? x->lse + r * x->H : NULL);
+}
+
+int oracle_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                           const int32_t* count, int64_t L, int64_t N, int32_t H, int32_t Dqk,
+                           int32_t Dv, int32_t top_k, double scale,
+                           const int64_t* rows, int64_t nrows, double* out, double* lse,
+                           int32_t nthreads) {
+    if (!q || !kv || !idx || !count || !rows || !out) return -1;
+    if (L <= 0 || N <= 0 || H <= 0 || Dqk <= 0 || Dv <= 0 || Dv > Dqk || top_k <= 0 || nrows < 0)
+        return -1;
+    if (!rows_ok(rows, nrows, L)) return -1;
+    double* kvd = widen_all(kv, N * Dqk);
+    if (!kvd) return -8;
+    attn_ctx x = {q, kvd, idx, count, N, H, Dqk, Dv, top_k, scale, rows, out, lse};
+    int rc = parallel_rows(attn_task, &x, nrows, nthreads,
+                           ((size_t)H * Dqk + (size_t)top_k) * sizeof(double));
+    free(kvd);
+    return rc;
+}
+
+/* ---- step 5: the chunk and the decode step end to end --------------------
+ * exo PR #2539, Prefill section: queries with no more causal keys than the
+ * selection size skip the indexer and take every earlier key; the others are
+ * scored, selected and attended sparsely.  Decode section: a decode step is
+ * one query per sequence at the end of its cache. */
+typedef struct {
+    const uint16_t *q, *qI; const float* w; const double *kvd, *kId;
+    int64_t N, q_start; int32_t H, Dqk, Dv, Hi, Di, top_k; double scale;
+    const int64_t* rows; int32_t* idx_out; int32_t* count_out; double* out;
+} chunk_ctx;
+
+static void chunk_task(void* c, int64_t r, void* scratch) {
+    chunk_ctx* x = (chunk_ctx*)c;
+    int64_t i = x->rows[r];
+    int64_t p = x->q_start + i;
+    /* scratch: S row [N] float | cand [N] | q row doubles | s [top_k] doubles */
+    char* base = (char*)scratch;
+    float* Srow = (float*)base;
+    cand* work = (cand*)(base + (size_t)x->N * sizeof(float));
+    double* qrow = (double*)(base + (size_t)x->N * (sizeof(float) + sizeof(cand)));
+    int64_t qw = (int64_t)x->Hi * x->Di > (int64_t)x->H * x->Dqk ? (int64_t)x->Hi * x->Di
+                                                                 : (int64_t)x->H * x->Dqk;
+    double* s = qrow + qw;
+    int32_t* sel = x->idx_out + r * x->top_k;
+    if (p + 1 > x->top_k) {
+        const uint16_t* src = x->qI + i * (int64_t)x->Hi * x->Di;
+        for (int64_t k = 0; k < (int64_t)x->Hi * x->Di; ++k) qrow[k] = bf16_to_double(src[k]);
+        indexer_row(qrow, x->kId, x->w + i * x->Hi, x->N, p, x->Hi, x->Di, Srow);
+    }
+    topk_row(Srow, p, x->top_k, work, sel, x->count_out + r);
+    const uint16_t* src = x->q + i * (int64_t)x->H * x->Dqk;
+    for (int64_t k = 0; k < (int64_t)x->H * x->Dqk; ++k) qrow[k] = bf16_to_double(src[k]);
+    attention_row(qrow, x->kvd, sel, x->count_out[r], x->N, x->H, x->Dqk, x->Dv, x->scale, s,
+                  x->out + r * (int64_t)x->H * x->Dv, NULL);
+}
+
+static size_t chunk_scratch(int64_t N, int32_t H, int32_t Dqk, int32_t Hi, int32_t Di, int32_t top_k) {
+    int64_t qw = (int64_t)Hi * Di > (int64_t)H * Dqk ? (int64_t)Hi * Di : (int64_t)H * Dqk;
+    return (size_t)N * (sizeof(float) + sizeof(cand)) + ((size_t)qw + (size_t)top_k) * sizeof(double);
+}
+
+int oracle_prefill_chunk(const uint16_t* q, const uint16_t* qI, const float* w,
+                         const uint16_t* kv, const uint16_t* kI,
+                         int64_t L, int64_t N, int64_t q_start,
+                         int32_t H, int32_t Dl, int32_t Dr, int32_t Hi, int32_t Di,
+                         int32_t top_k, double scale,
+                         const int64_t* rows, int64_t nrows,
+                         int32_t* idx_out, int32_t* count_out, double* out, int32_t nthreads) {
+    if (!q || !qI || !w || !kv || !kI || !rows || !idx_out || !count_out || !out) return -1;
+    if (L <= 0 || N <= 0 || q_start < 0 || q_start + L > N || H <= 0 || Dl <= 0 || Dr < 0 ||
+        Hi <= 0 || Di <= 0 || top_k <= 0 || nrows < 0)
+        return -1;
+    if (!rows_ok(rows, nrows, L)) return -1;
+    int32_t Dqk = Dl + Dr;
+    double* kvd = widen_all(kv, N * Dqk);
+    double* kId = widen_all(kI, N * Di);
+    if (!kvd || !kId) { free(kvd); free(kId); return -8; }
+    chunk_ctx x = {q, qI, w, kvd, kId, N, q_start, H, Dqk, Dl, Hi, Di, top_k, scale,
+                   rows, idx_out, count_out, out};
+    int rc = parallel_rows(chunk_task, &x, nrows, nthreads, chunk_scratch(N, H, Dqk, Hi, Di, top_k));
+    free(kvd);
+    free(kId);
+    return rc;
+}
+
+int oracle_decode_step(const uint16_t* q, const uint16_t* qI, const float* w,
+                       const uint16_t* kv, const uint16_t* kI, int32_t B, const int64_t* ctx,
+                       int32_t H, int32_t Dl, int32_t Dr, int32_t Hi, int32_t Di,
+                       int32_t top_k, double scale,
+                       int32_t* idx_out, int32_t* count_out, double* out, int32_t nthreads) {
+    if (!q || !qI || !w || !kv || !kI || !ctx || !idx_out || !count_out || !out || B <= 0) return -1;
+    int32_t Dqk = Dl + Dr;
+    int64_t off = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        if (ctx[b] <= 0) return -1;
+        /* sequence b is a one-query chunk at position ctx-1 over its own cache */
+        int64_t row0 = 0;
+        int rc = oracle_prefill_chunk(q + (int64_t)b * H * Dqk, qI + (int64_t)b * Hi * Di, w + (int64_t)b * Hi,
+                                      kv + off * Dqk, kI + off * Di, 1, ctx[b], ctx[b] - 1,
+                                      H, Dl, Dr, Hi, Di, top_k, scale, &row0, 1,
+                                      idx_out + (int64_t)b * top_k, count_out + b,
+                                      out + (int64_t)b * H * Dl, nthreads);
+        if (rc) return rc;
+        off += ctx[b];
+    }
+    return 0;
+}

@@ -1,0 +1,83 @@
+/*
+ * dsa_oracle.h - plain CPU oracle for the DeepSeek-sparse-attention (DSA)
+ * prefill/decode path.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check
+ * and the benchmark's CPU-baseline leg call it; the HIP library never does,
+ * and it shares no code, header, table or helper with the HIP library.
+ *
+ * Arithmetic: every floating-point step in double precision.  The one place
+ * the pages fix a precision is the indexer score, which exo PR #2539 (Prefill
+ * section, float32 indexer item) sums in float32; the oracle therefore forms
+ * the exact score in double and rounds it once to float, and the top-k
+ * decision compares those float values.
+ *
+ * Storage conventions (all arrays dense, row-major, host memory):
+ *   bf16 operands are passed as uint16_t bit patterns;
+ *   a prefill chunk has L queries at positions q_start + i over keys 0..N-1;
+ *   key j is visible to the query at position p iff j <= p.
+ *
+ * Every function returns 0 on success and a negative value on a bad
+ * argument (null pointer, non-positive size, row out of range).
+ */
+#ifndef DSA_ORACLE_H
+#define DSA_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Indexer scores for selected query rows.
+ *   qI [L, Hi, Di] bf16, kI [N, Di] bf16, w [L, Hi] float.
+ *   rows[r] (r < nrows) names the query row; S_out is [nrows, N] float.
+ * S_out[r, j] = float( sum_h w[i,h] * max(0, sum_d qI[i,h,d] * kI[j,d]) )
+ * for j <= q_start + i, and -infinity for later keys. */
+int oracle_indexer_scores(const uint16_t* qI, const uint16_t* kI, const float* w,
+                          int64_t L, int64_t N, int64_t q_start, int32_t Hi, int32_t Di,
+                          const int64_t* rows, int64_t nrows, float* S_out, int32_t nthreads);
+
+/* Top-k selection for nrows score rows S [nrows, N]; pos[r] is the query's
+ * position (keys 0..pos[r] are candidates, pos[r] < N).
+ *   pos+1 <= top_k : idx = 0..pos (every earlier key, scores unused);
+ *   otherwise      : the top_k keys ordered by (score descending, key
+ *                    ascending), written in ascending key order.
+ * idx [nrows, top_k] is padded with -1; count[r] = min(pos+1, top_k). */
+int oracle_topk_select(const float* S, int64_t nrows, int64_t N, const int64_t* pos,
+                       int32_t top_k, int32_t* idx, int32_t* count, int32_t nthreads);
+
+/* Absorbed-MLA attention over selected latent rows.
+ *   q [L, H, Dqk] bf16; kv [N, Dqk] bf16 (value = first Dv columns);
+ *   idx [L, top_k] key ids (first count[i] used); rows[r] names the query.
+ *   out [nrows, H, Dv] double; lse [nrows, H] double (may be NULL).
+ * s_t = scale * <q[i,h,:], kv[idx_t,:]>;  out = sum_t softmax(s)_t kv[idx_t,:Dv];
+ * lse = log sum_t exp(s_t).  count 0 gives out = 0, lse = -inf. */
+int oracle_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                           const int32_t* count, int64_t L, int64_t N, int32_t H, int32_t Dqk,
+                           int32_t Dv, int32_t top_k, double scale,
+                           const int64_t* rows, int64_t nrows, double* out, double* lse,
+                           int32_t nthreads);
+
+/* One prefill chunk end to end for selected rows: indexer (only for queries
+ * with more causal keys than top_k), top-k, attention.
+ * idx_out [nrows, top_k], count_out [nrows], out [nrows, H, Dv] (double). */
+int oracle_prefill_chunk(const uint16_t* q, const uint16_t* qI, const float* w,
+                         const uint16_t* kv, const uint16_t* kI,
+                         int64_t L, int64_t N, int64_t q_start,
+                         int32_t H, int32_t Dl, int32_t Dr, int32_t Hi, int32_t Di,
+                         int32_t top_k, double scale,
+                         const int64_t* rows, int64_t nrows,
+                         int32_t* idx_out, int32_t* count_out, double* out, int32_t nthreads);
+
+/* One batched decode step: B sequences, one query each at position ctx[b]-1,
+ * caches packed in sequence order (sequence b's rows start at sum(ctx[:b])).
+ *   q [B, H, Dl+Dr], qI [B, Hi, Di], w [B, Hi], kv [sum ctx, Dl+Dr], kI [sum ctx, Di].
+ * idx_out [B, top_k] (key ids local to the sequence), count_out [B], out [B, H, Dl]. */
+int oracle_decode_step(const uint16_t* q, const uint16_t* qI, const float* w,
+                       const uint16_t* kv, const uint16_t* kI, int32_t B, const int64_t* ctx,
+                       int32_t H, int32_t Dl, int32_t Dr, int32_t Hi, int32_t Di,
+                       int32_t top_k, double scale,
+                       int32_t* idx_out, int32_t* count_out, double* out, int32_t nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,389 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+a value that does not come from the oracle itself: a hand-worked example
+(tests/golden/), an exact rational brute force on tiny inputs, a closed
+form, an invariant, or a special case that reduces to a library routine
+(torch's scaled_dot_product_attention, Python's sorted).
+
+The functions are plain so that the mutation test can run them against
+deliberately broken builds of the oracle in a separate process.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            k, v = line.split(":", 1)
+            vals[k.strip()] = [float(x) for x in v.split()]
+    return vals
+
+
+def _bf(x):
+    return W.to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+# --------------------------------------------------------------------------
+# indexer
+# --------------------------------------------------------------------------
+def pin_indexer_worked_example():
+    """tests/golden/indexer_worked_example.txt (exo #2539 Prefill, indexer)."""
+    g = _read_golden("indexer_worked_example.txt")
+    Hi, Di, q0 = int(g["Hi"][0]), int(g["Di"][0]), int(g["q_start"][0])
+    qI = _bf(np.array(g["qI"]).reshape(2, Hi, Di))
+    kI = _bf(np.array(g["kI"]).reshape(3, Di))
+    w = np.array(g["w"], dtype=np.float32).reshape(2, Hi)
+    S = oracle.indexer_scores(qI, kI, w, q0)
+    want = np.array(g["S"], dtype=np.float32).reshape(2, 3)
+    assert np.array_equal(S, want), (S, want)
+    for k in (1, 2, 3):
+        idx, cnt = oracle.topk_select(S, q0 + np.arange(2), k)
+        assert np.array_equal(idx.ravel(), np.array(g["topk%d_idx" % k], dtype=np.int32)), (k, idx)
+        assert np.array_equal(cnt, np.array(g["topk%d_count" % k], dtype=np.int32)), (k, cnt)
+
+
+def pin_indexer_exact_rational():
+    """Brute force in exact rational arithmetic on tiny random integer inputs:
+    the fp32 score must be the exact value rounded once to float32."""
+    rng = np.random.default_rng(7)
+    for trial in range(4):
+        L, N, Hi, Di, q0 = 3, 7, 3, 5, 4
+        qI = rng.integers(-8, 9, size=(L, Hi, Di))
+        kI = rng.integers(-8, 9, size=(N, Di))
+        w = rng.choice([0.5, 1.0, 2.0, -1.0, 0.25], size=(L, Hi)).astype(np.float32)
+        S = oracle.indexer_scores(_bf(qI), _bf(kI), w, q0)
+        for i in range(L):
+            for j in range(N):
+                if j > q0 + i:
+                    assert S[i, j] == -np.inf
+                    continue
+                exact = Fraction(0)
+                for h in range(Hi):
+                    dot = sum(int(qI[i, h, d]) * int(kI[j, d]) for d in range(Di))
+                    exact += Fraction(float(w[i, h])) * max(dot, 0)
+                assert S[i, j] == np.float32(float(exact)), (i, j, S[i, j], exact)
+
+
+def pin_indexer_one_hot_closed_form():
+    """qI[i,h] = c_h * e_{d_h}  =>  S[i,j] = sum_h w_h relu(c_h kI[j,d_h])."""
+    rng = np.random.default_rng(8)
+    L, N, Hi, Di, q0 = 4, 9, 4, 6, 5
+    d_h = rng.integers(0, Di, size=(L, Hi))
+    c_h = rng.choice([-2.0, -1.0, 1.0, 3.0], size=(L, Hi))
+    qI = np.zeros((L, Hi, Di))
+    for i in range(L):
+        for h in range(Hi):
+            qI[i, h, d_h[i, h]] = c_h[i, h]
+    kI = rng.integers(-5, 6, size=(N, Di)).astype(np.float64)
+    w = rng.choice([0.5, 1.0, 2.0], size=(L, Hi)).astype(np.float32)
+    S = oracle.indexer_scores(_bf(qI), _bf(kI), w, q0)
+    for i in range(L):
+        for j in range(q0 + i + 1):
+            want = sum(w[i, h] * max(c_h[i, h] * kI[j, d_h[i, h]], 0.0) for h in range(Hi))
+            assert S[i, j] == np.float32(want), (i, j, S[i, j], want)
+
+
+def pin_indexer_relu_mask_linearity():
+    """relu clips negative dot products to 0; the mask is -inf exactly past the
+    query's position (diagonal included); the score is linear in w and
+    invariant under a joint permutation of the heads."""
+    rng = np.random.default_rng(9)
+    L, N, Hi, Di, q0 = 5, 12, 4, 8, 7
+    kI = np.abs(rng.integers(1, 5, size=(N, Di)))
+    qI_neg = -np.abs(rng.integers(1, 5, size=(L, Hi, Di)))       # every q.k < 0
+    w = rng.choice([0.5, 1.0, 2.0], size=(L, Hi)).astype(np.float32)
+    S = oracle.indexer_scores(_bf(qI_neg), _bf(kI), w, q0)
+    for i in range(L):
+        assert np.all(S[i, : q0 + i + 1] == 0.0), S[i]
+        assert np.all(S[i, q0 + i + 1:] == -np.inf), S[i]
+    qI = rng.integers(-8, 9, size=(L, Hi, Di))
+    S1 = oracle.indexer_scores(_bf(qI), _bf(kI), w, q0)
+    S2 = oracle.indexer_scores(_bf(qI), _bf(kI), 2 * w, q0)
+    S3 = oracle.indexer_scores(_bf(qI), _bf(kI), -w, q0)
+    perm = rng.permutation(Hi)
+    S4 = oracle.indexer_scores(_bf(qI[:, perm]), _bf(kI), np.ascontiguousarray(w[:, perm]), q0)
+    vis = np.isfinite(S1)
+    assert np.array_equal(vis, np.arange(N)[None, :] <= (q0 + np.arange(L))[:, None])
+    assert np.array_equal(S2[vis], 2 * S1[vis])
+    assert np.array_equal(S3[vis], -S1[vis])
+    assert np.array_equal(S4, S1)
+
+
+# --------------------------------------------------------------------------
+# top-k
+# --------------------------------------------------------------------------
+def _brute_topk(srow, p, k):
+    keys = list(range(p + 1))
+    if p + 1 <= k:
+        sel = keys
+    else:
+        sel = sorted(keys, key=lambda j: (-float(srow[j]), j))[:k]
+    sel = sorted(sel)
+    return sel + [-1] * (k - len(sel)), len(sel)
+
+
+def pin_topk_brute_force():
+    """Python's sorted() on (-score, key) over tiny rows, with many ties."""
+    rng = np.random.default_rng(10)
+    for trial in range(30):
+        N = int(rng.integers(1, 40))
+        k = int(rng.integers(1, 12))
+        nrows = 6
+        S = rng.integers(0, 4, size=(nrows, N)).astype(np.float32)     # heavy ties
+        if trial % 3 == 1:
+            S = rng.standard_normal((nrows, N)).astype(np.float32)
+        if trial % 3 == 2:
+            S = -np.abs(S) - 1.0                                      # all negative
+        pos = rng.integers(0, N, size=nrows)
+        idx, cnt = oracle.topk_select(S, pos, k)
+        for r in range(nrows):
+            want, c = _brute_topk(S[r], int(pos[r]), k)
+            assert list(idx[r]) == want, (trial, r, list(idx[r]), want)
+            assert cnt[r] == c
+
+
+def pin_topk_boundary_rule():
+    """p+1 == top_k takes every earlier key regardless of scores; p+1 ==
+    top_k+1 drops exactly the single worst key (ties to the higher index)."""
+    k = 8
+    S = np.zeros((2, 16), dtype=np.float32)
+    S[0, :8] = [-5, -4, -3, -2, -1, -6, -7, -8]
+    S[1, :9] = [3, 3, 3, 3, 3, 3, 3, 3, 3]
+    idx, cnt = oracle.topk_select(S, np.array([7, 8]), k)
+    assert list(idx[0]) == list(range(8)) and cnt[0] == 8
+    assert list(idx[1]) == list(range(8)) and cnt[1] == 8        # key 8 loses the tie
+    S[1, 0] = 2.0                                                # now key 0 is the worst
+    idx, cnt = oracle.topk_select(S, np.array([7, 8]), k)
+    assert list(idx[1]) == list(range(1, 9))
+
+
+def pin_topk_invariants_tiny():
+    """On the tiny workload: ascending, inside the causal range, count =
+    min(p+1, top_k), every kept score >= every dropped score, and among equal
+    scores at the boundary the kept keys have the lower indices."""
+    cfg = W.PREFILL["tiny"]
+    d = W.make_prefill(cfg)
+    S = oracle.indexer_scores(d["qI"], d["kI"], d["w"], cfg.q_start)
+    pos = cfg.q_start + np.arange(cfg.L)
+    idx, cnt = oracle.topk_select(S, pos, cfg.shape.top_k)
+    for r in range(cfg.L):
+        p = int(pos[r])
+        c = int(cnt[r])
+        sel = idx[r, :c]
+        assert c == min(p + 1, cfg.shape.top_k)
+        assert np.all(idx[r, c:] == -1)
+        assert np.all(np.diff(sel) > 0) and sel[0] >= 0 and sel[-1] <= p
+        mask = np.zeros(p + 1, bool)
+        mask[sel] = True
+        kept, dropped = S[r, : p + 1][mask], S[r, : p + 1][~mask]
+        if dropped.size:
+            assert kept.min() >= dropped.max()
+            t = kept.min()
+            if dropped.max() == t:
+                assert np.flatnonzero(mask & (S[r, : p + 1] == t)).max() < \
+                    np.flatnonzero(~mask & (S[r, : p + 1] == t)).min()
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+def pin_attention_worked_example():
+    """tests/golden/attention_worked_example.txt (closed form)."""
+    g = _read_golden("attention_worked_example.txt")
+    q = _bf(np.array(g["q"]).reshape(1, 1, 3))
+    kv = _bf(np.array(g["kv"]).reshape(3, 3))
+    idx = np.array([g["idx"]], dtype=np.int32)
+    cnt = np.array([int(g["count"][0])], dtype=np.int32)
+    out, lse = oracle.sparse_mla_attn(q, kv, idx, cnt, 2, 1.0 / 16, want_lse=True)
+    assert np.allclose(out.ravel(), g["out"], rtol=0, atol=1e-15), out
+    assert abs(lse[0, 0] - g["lse"][0]) < 1e-14, lse
+
+
+def _sdpa(q, kv, mask, Dl, scale):
+    import torch
+    qf = torch.from_numpy(W.bf16_bits_to_f32(q).astype(np.float64))          # [L,H,D]
+    kf = torch.from_numpy(W.bf16_bits_to_f32(kv).astype(np.float64))         # [N,D]
+    vf = kf[:, :Dl]
+    L, H, D = qf.shape
+    qh = qf.permute(1, 0, 2).contiguous()                                      # [H,L,D]
+    kh = kf.unsqueeze(0).expand(H, -1, -1).contiguous()
+    vh = vf.unsqueeze(0).expand(H, -1, -1).contiguous()
+    m = torch.from_numpy(mask).unsqueeze(0).expand(H, -1, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, attn_mask=m, scale=scale)
+    return o.permute(1, 0, 2).numpy()                                          # [L,H,Dl]
+
+
+def pin_attention_dense_equals_sdpa():
+    """When every query keeps every earlier key (top_k >= p+1), the chunk is
+    textbook causal attention: torch's SDPA in float64 with a j <= p mask."""
+    for name in ("tiny_dense", "glm_small_first"):
+        cfg = W.PREFILL[name]
+        d = W.make_prefill(cfg)
+        rows = np.arange(cfg.L) if cfg.L <= 64 else W.sample_rows(cfg.L, 16)
+        idx, cnt, out = oracle.prefill_chunk(d, cfg.shape, cfg.q_start, rows=rows)
+        pos = cfg.q_start + rows
+        assert np.array_equal(cnt, pos + 1)
+        mask = np.arange(cfg.N)[None, :] <= pos[:, None]
+        ref = _sdpa(d["q"][rows], d["kv"], mask, cfg.shape.d_latent, cfg.shape.softmax_scale)
+        err = np.abs(out - ref).max() / np.abs(ref).max()
+        assert err < 1e-12, (name, err)
+
+
+def pin_attention_sparse_equals_masked_sdpa():
+    """Sparse attention over a selection equals dense attention with every
+    unselected key masked out (torch SDPA, float64); selection order is free."""
+    rng = np.random.default_rng(12)
+    cfg = W.PREFILL["tiny"]
+    d = W.make_prefill(cfg)
+    L, N, k = cfg.L, cfg.N, cfg.shape.top_k
+    idx = np.full((L, k), -1, np.int32)
+    cnt = rng.integers(1, k + 1, size=L).astype(np.int32)
+    mask = np.zeros((L, N), bool)
+    for i in range(L):
+        sel = rng.choice(N, size=cnt[i], replace=False)          # unsorted on purpose
+        idx[i, : cnt[i]] = sel
+        mask[i, sel] = True
+    out = oracle.sparse_mla_attn(d["q"], d["kv"], idx, cnt, cfg.shape.d_latent, cfg.shape.softmax_scale)
+    ref = _sdpa(d["q"], d["kv"], mask, cfg.shape.d_latent, cfg.shape.softmax_scale)
+    err = np.abs(out - ref).max() / np.abs(ref).max()
+    assert err < 1e-12, err
+
+
+def pin_attention_closed_forms():
+    """All selected rows equal -> out = that row's value part; q = 0 -> out =
+    mean of the selected value rows and lse = log(count); one key -> its
+    value; the output does not depend on the order of the selection."""
+    rng = np.random.default_rng(13)
+    H, Dl, Dr, N, k = 3, 8, 4, 20, 6
+    D = Dl + Dr
+    kv = _bf(rng.standard_normal((N, D)))
+    q = _bf(rng.standard_normal((2, H, D)) * 3)
+    sel = rng.choice(N, size=k, replace=False).astype(np.int32)
+    idx = np.stack([sel, sel])
+    cnt = np.array([k, 1], np.int32)
+    kvf = W.bf16_bits_to_f32(kv).astype(np.float64)
+    # one key
+    out = oracle.sparse_mla_attn(q, kv, idx, cnt, Dl, 1.0 / 16)
+    assert np.allclose(out[1], kvf[sel[0], :Dl][None, :], rtol=0, atol=0)
+    # equal rows
+    kv_eq = np.tile(kv[sel[0]], (N, 1))
+    out = oracle.sparse_mla_attn(q, kv_eq, idx, cnt, Dl, 1.0 / 16)
+    assert np.allclose(out, kvf[sel[0], :Dl][None, None, :], rtol=0, atol=1e-15)
+    # zero query
+    q0 = np.zeros_like(q)
+    out, lse = oracle.sparse_mla_attn(q0, kv, idx, cnt, Dl, 1.0 / 16, want_lse=True)
+    assert np.allclose(out[0], kvf[sel, :Dl].mean(0)[None, :], rtol=0, atol=1e-15)
+    assert np.allclose(lse[0], math.log(k), rtol=0, atol=1e-15)
+    assert np.allclose(lse[1], 0.0, rtol=0, atol=1e-15)
+    # order of the selection
+    out_a = oracle.sparse_mla_attn(q, kv, idx, cnt, Dl, 1.0 / 16)
+    idx_b = idx.copy()
+    idx_b[0] = sel[rng.permutation(k)]
+    out_b = oracle.sparse_mla_attn(q, kv, idx_b, cnt, Dl, 1.0 / 16)
+    assert np.allclose(out_a, out_b, rtol=0, atol=1e-14)
+
+
+def pin_attention_scale_and_rope_part():
+    """The rope columns enter the score but not the value; the scale divides
+    the dot product: moving a factor 2 from the scale into q is a no-op."""
+    rng = np.random.default_rng(14)
+    H, Dl, Dr, N = 2, 8, 8, 10
+    kv = rng.standard_normal((N, Dl + Dr))
+    kv[:, Dl:] = 0.0
+    q = rng.standard_normal((1, H, Dl + Dr))
+    sel = np.arange(N, dtype=np.int32)[None, :]
+    cnt = np.array([N], np.int32)
+    a = oracle.sparse_mla_attn(_bf(q), _bf(kv), sel, cnt, Dl, 1.0 / 16)
+    q2 = q.copy()
+    q2[..., Dl:] = 100.0                       # rope part of q meets zero keys
+    b = oracle.sparse_mla_attn(_bf(q2), _bf(kv), sel, cnt, Dl, 1.0 / 16)
+    assert np.allclose(a, b, rtol=0, atol=1e-14)
+    c = oracle.sparse_mla_attn(_bf(q * 2), _bf(kv), sel, cnt, Dl, 1.0 / 32)
+    assert np.allclose(a, c, rtol=0, atol=1e-14)
+    # a key whose rope part alone makes it dominant
+    kv3 = np.zeros((3, Dl + Dr))
+    kv3[0, :Dl] = 1.0
+    kv3[1, :Dl] = -1.0
+    kv3[1, Dl:] = 1.0
+    q3 = np.zeros((1, 1, Dl + Dr))
+    q3[..., Dl:] = 64.0                        # s_1 = 8*64/16 = 32, s_0 = 0
+    out = oracle.sparse_mla_attn(_bf(q3), _bf(kv3), np.array([[0, 1]], np.int32),
+                                 np.array([2], np.int32), Dl, 1.0 / 16)
+    p1 = 1.0 / (1.0 + math.exp(-32.0))
+    assert np.allclose(out[0, 0], (1 - p1) * 1.0 + p1 * -1.0, rtol=0, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# chunk and decode compositions
+# --------------------------------------------------------------------------
+def pin_chunk_composition_matches_stages():
+    """The chunk runs the stages in the pages' order: its selection equals
+    brute-force selection over the indexer's scores (dense rule below top_k),
+    and its output equals masked SDPA over that selection."""
+    cfg = W.PREFILL["tiny"]
+    d = W.make_prefill(cfg)
+    idx, cnt, out = oracle.prefill_chunk(d, cfg.shape, cfg.q_start)
+    S = oracle.indexer_scores(d["qI"], d["kI"], d["w"], cfg.q_start)
+    mask = np.zeros((cfg.L, cfg.N), bool)
+    for i in range(cfg.L):
+        want, c = _brute_topk(S[i], cfg.q_start + i, cfg.shape.top_k)
+        assert list(idx[i]) == want and cnt[i] == c
+        mask[i, idx[i, :c]] = True
+    ref = _sdpa(d["q"], d["kv"], mask, cfg.shape.d_latent, cfg.shape.softmax_scale)
+    assert np.abs(out - ref).max() / np.abs(ref).max() < 1e-12
+
+
+def pin_decode_dense_sequences_equal_sdpa():
+    """A decode sequence whose context fits in top_k is plain attention of its
+    last position over its whole cache."""
+    cfg = W.DECODE["tiny_decode"]
+    d = W.make_decode(cfg)
+    idx, cnt, out = oracle.decode_step(d, cfg.shape)
+    off = d["row_off"]
+    for b, c in enumerate(cfg.ctx):
+        assert cnt[b] == min(c, cfg.shape.top_k)
+        if c > cfg.shape.top_k:
+            continue
+        kvb = d["kv"][off[b]: off[b + 1]]
+        ref = _sdpa(d["q"][b: b + 1], kvb, np.ones((1, c), bool), cfg.shape.d_latent,
+                    cfg.shape.softmax_scale)
+        assert np.abs(out[b] - ref[0]).max() / np.abs(ref).max() < 1e-12, b
+
+
+def pin_decode_sparse_sequences_follow_brute_force():
+    """A decode sequence with a context longer than top_k keeps the
+    brute-force top_k of its exact scores over its own cache."""
+    cfg = W.DECODE["tiny_decode"]
+    d = W.make_decode(cfg)
+    idx, cnt, out = oracle.decode_step(d, cfg.shape)
+    off = d["row_off"]
+    for b, c in enumerate(cfg.ctx):
+        if c <= cfg.shape.top_k:
+            continue
+        S = oracle.indexer_scores(d["qI"][b: b + 1], d["kI"][off[b]: off[b + 1]], d["w"][b: b + 1], c - 1)
+        want, n = _brute_topk(S[0], c - 1, cfg.shape.top_k)
+        assert list(idx[b]) == want and cnt[b] == n, b
+        mask = np.zeros((1, c), bool)
+        mask[0, idx[b, :n]] = True
+        ref = _sdpa(d["q"][b: b + 1], d["kv"][off[b]: off[b + 1]], mask, cfg.shape.d_latent,
+                    cfg.shape.softmax_scale)
+        assert np.abs(out[b] - ref[0]).max() / np.abs(ref).max() < 1e-12, b
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,82 @@
+"""CPU tests of the oracle: every pin, plus a mutation check showing that the
+pins catch plausible mistakes planted in copies of the oracle (on the CPU)."""
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+# (description, exact text in dsa_oracle.c, replacement).  Each is a mistake a
+# careful reader could plausibly make; every one must trip at least one pin.
+MUTATIONS = [
+    ("relu dropped", "double relu = dot > 0.0 ? dot : 0.0;", "double relu = dot;"),
+    ("mask excludes the diagonal", "if (j > p) { Srow[j] = -INFINITY; continue; }",
+     "if (j >= p) { Srow[j] = -INFINITY; continue; }"),
+    ("head weight dropped", "total += (double)wrow[h] * relu;", "total += relu;"),
+    ("indexer head stride", "qIrow[(int64_t)h * Di + d]", "qIrow[d]"),
+    ("indexer key transposed", "kId[j * Di + d]", "kId[d * Di + (j % Di)]"),
+    ("ties to the higher key", "return (x->j < y->j) ? -1 : (x->j > y->j);",
+     "return (x->j > y->j) ? -1 : (x->j < y->j);"),
+    ("lowest scores kept", "if (x->s > y->s) return -1;\n    if (x->s < y->s) return 1;",
+     "if (x->s < y->s) return -1;\n    if (x->s > y->s) return 1;"),
+    ("dense rule reports top_k keys", "*count = (int32_t)n;", "*count = top_k;"),
+    ("dense rule skips the diagonal key", "for (int64_t j = 0; j < n; ++j) idxrow[j] = (int32_t)j;",
+     "for (int64_t j = 0; j + 1 < n; ++j) idxrow[j] = (int32_t)j;"),
+    ("selection left in score order",
+     "qsort(idxrow, (size_t)top_k, sizeof(int32_t), ascending_int);", ""),
+    ("softmax scale dropped", "s[t] = scale * dot;", "s[t] = dot;"),
+    ("value taken from the rope end", "const double* v = kvd + (int64_t)sel[t] * Dqk;",
+     "const double* v = kvd + (int64_t)sel[t] * Dqk + (Dqk - Dv);"),
+    ("query head stride", "const double* qh = qrow + (int64_t)h * Dqk;",
+     "const double* qh = qrow;"),
+    ("softmax not normalised", "double pt = exp(s[t] - m) / Z;", "double pt = exp(s[t] - m);"),
+    ("lse without log", "lserow[h] = m + log(Z);", "lserow[h] = m + Z;"),
+    ("score rounded to bf16-ish", "Srow[j] = (float)total;",
+     "Srow[j] = (float)(total + 0.25);"),
+]
+
+_RUNNER = r"""
+import sys
+sys.path.insert(0, {root!r})
+import oracle
+from tests import oracle_pins
+failed = []
+with oracle.using_library({lib!r}):
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except Exception as e:   # AssertionError or an oracle error code
+            failed.append(pin.__name__)
+print("FAILED_PINS", len(failed), failed)
+"""
+
+
+@pytest.mark.parametrize("desc,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(desc, old, new, tmp_path):
+    src = open(os.path.join(ROOT, "oracle", "dsa_oracle.c")).read()
+    assert src.count(old) == 1, "mutation anchor not found exactly once: %r" % old
+    d = tmp_path
+    shutil.copy(os.path.join(ROOT, "oracle", "dsa_oracle.h"), d / "dsa_oracle.h")
+    (d / "dsa_oracle.c").write_text(src.replace(old, new))
+    lib = str(d / "libmutant.so")
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-pthread", "-o", lib,
+                    str(d / "dsa_oracle.c"), "-lm"], check=True)
+    r = subprocess.run([sys.executable, "-c", _RUNNER.format(root=ROOT, lib=lib)],
+                       capture_output=True, text=True, timeout=600)
+    # a crash of the mutant also counts as caught
+    if r.returncode == 0:
+        line = [l for l in r.stdout.splitlines() if l.startswith("FAILED_PINS")][-1]
+        assert int(line.split()[1]) > 0, "planted mistake '%s' passed every pin" % desc

@@ -1,0 +1,168 @@
+"""Seeded synthetic inputs for the DSA prefill/decode path.
+
+This module only draws random numbers and rounds them to bf16 storage.  It
+holds none of the method's arithmetic, so both the CPU oracle's tests and the
+GPU path take their inputs from here without sharing any computation.
+
+Shapes follow the GLM-5.x ``glm_moe_dsa`` configuration printed in the text
+config of "GLM-5.2-Vision: llama.cpp vs vLLM line-by-line pipeline trace"
+(64 heads, kv_lora_rank 512, qk_rope 64, index_topk 2048) and the indexer
+description in exo PR #2539 (Prefill section, float32 indexer item: 32
+indexer heads).  The indexer width 128 is not on the pages; it is the
+DeepSeek-V3.2 indexer head size and is taken as a parameter.
+
+Value recipe (stated once here, repeated in the design doc):
+  draw order  qI, kI, w, q, kv from ``numpy.random.default_rng(seed)``;
+  qI, kI      integers uniform in [-r, r] (r = 4 tiny, 8 GLM), exact in bf16;
+  w           uniform choice of {0.5, 1, 2} (powers of two), fp32;
+  q, kv       standard normal (float32) times a scale, rounded once to bf16
+              (round to nearest even).
+
+With integer indexer operands and power-of-two weights every partial sum of
+the indexer is a multiple of 0.5 below 2**20, so fp32 accumulation in any
+order is exact; selection can then be compared bit for bit.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional
+
+import numpy as np
+
+__all__ = [
+    "Shape", "TINY", "GLM", "Prefill", "Decode", "PREFILL", "DECODE",
+    "to_bf16_bits", "bf16_bits_to_f32", "make_prefill", "make_decode",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Shape:
+    n_heads: int          # H   query heads
+    d_latent: int         # Dl  absorbed no-rope width == value width
+    d_rope: int           # Dr  rope width
+    n_idx_heads: int      # Hi  indexer heads
+    d_idx: int            # Di  indexer head width
+    top_k: int            # keys kept per query
+    softmax_scale: float = 1.0 / 16.0
+
+    @property
+    def d_qk(self) -> int:
+        return self.d_latent + self.d_rope
+
+
+# GLM-5.x glm_moe_dsa layer (pipeline-trace config line; exo #2539 indexer).
+GLM = Shape(n_heads=64, d_latent=512, d_rope=64, n_idx_heads=32, d_idx=128, top_k=2048)
+# Tiny check shape: 4 heads, latent 64 + rope 16, indexer 4 x 32, top_k 32.
+TINY = Shape(n_heads=4, d_latent=64, d_rope=16, n_idx_heads=4, d_idx=32, top_k=32)
+
+
+@dataclasses.dataclass(frozen=True)
+class Prefill:
+    name: str
+    shape: Shape
+    L: int                # queries in the chunk
+    q_start: int          # position of the first query
+    seed: int
+    int_range: int        # indexer integers in [-int_range, int_range]
+    q_scale: float
+    kv_scale: float
+
+    @property
+    def N(self) -> int:   # keys: every position up to the chunk's last query
+        return self.q_start + self.L
+
+
+@dataclasses.dataclass(frozen=True)
+class Decode:
+    name: str
+    shape: Shape
+    ctx: tuple            # context length per sequence; query at ctx-1
+    seed: int
+    int_range: int
+    q_scale: float
+    kv_scale: float
+
+
+PREFILL: Dict[str, Prefill] = {
+    # tiny fp32-generated check: L=64 at 192..255 over 256 keys, top_k 32
+    "tiny": Prefill("tiny", TINY, 64, 192, 0, 4, 1.0, 1.0),
+    # tiny shape with top_k 256: every query takes the every-earlier-key rule
+    "tiny_dense": Prefill("tiny_dense", dataclasses.replace(TINY, top_k=256), 64, 192, 10, 4, 1.0, 1.0),
+    # tiny shape with a peaked softmax (queries scaled by 4)
+    "tiny_sharp": Prefill("tiny_sharp", TINY, 64, 192, 11, 4, 4.0, 1.0),
+    # GLM-shape chunk, 4096 queries at 4096..8191 over 8192 keys
+    "glm_8k": Prefill("glm_8k", GLM, 4096, 4096, 1, 8, 0.05, 0.05),
+    # first chunk: queries 0..4095; those below 2048 take every earlier key
+    "glm_first_4k": Prefill("glm_first_4k", GLM, 4096, 0, 2, 8, 0.05, 0.05),
+    # long-context chunk, 4096 queries at 12288..16383 over 16384 keys
+    "glm_16k": Prefill("glm_16k", GLM, 4096, 12288, 3, 8, 0.05, 0.05),
+    # small GLM-shape chunks the oracle finishes quickly; ragged sizes that
+    # span several tiles and cross the top_k boundary inside the chunk
+    "glm_small_cross": Prefill("glm_small_cross", GLM, 77, 2011, 21, 8, 0.05, 0.05),
+    "glm_small_sparse": Prefill("glm_small_sparse", GLM, 45, 3001, 22, 8, 0.05, 0.05),
+    "glm_small_first": Prefill("glm_small_first", GLM, 33, 0, 23, 8, 0.05, 0.05),
+}
+
+DECODE: Dict[str, Decode] = {
+    # batched decode: 8 sequences, contexts 4k..64k
+    "glm_decode_8": Decode("glm_decode_8", GLM,
+                           (4096, 8192, 16384, 32768, 65536, 65536, 16384, 4096), 4, 8, 0.05, 0.05),
+    # small ragged decode the oracle finishes quickly (one context below top_k)
+    "glm_decode_small": Decode("glm_decode_small", GLM, (3000, 1500, 2049, 2048, 4133), 24, 8, 0.05, 0.05),
+    "tiny_decode": Decode("tiny_decode", TINY, (256, 31, 100, 1, 33), 25, 4, 1.0, 1.0),
+}
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); return uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u.astype(np.uint64) + np.uint64(0x7FFF) + lsb.astype(np.uint64)) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _draw(rng: np.random.Generator, shape: Shape, n_q: int, n_k: int, r: int,
+          q_scale: float, kv_scale: float) -> Dict[str, np.ndarray]:
+    """Draw one set of operands in the fixed order qI, kI, w, q, kv."""
+    qI = rng.integers(-r, r + 1, size=(n_q, shape.n_idx_heads, shape.d_idx)).astype(np.float32)
+    kI = rng.integers(-r, r + 1, size=(n_k, shape.d_idx)).astype(np.float32)
+    w = rng.choice(np.array([0.5, 1.0, 2.0], dtype=np.float32), size=(n_q, shape.n_idx_heads))
+    q = rng.standard_normal(size=(n_q, shape.n_heads, shape.d_qk), dtype=np.float32) * np.float32(q_scale)
+    kv = rng.standard_normal(size=(n_k, shape.d_qk), dtype=np.float32) * np.float32(kv_scale)
+    return {
+        "qI": to_bf16_bits(qI), "kI": to_bf16_bits(kI), "w": np.ascontiguousarray(w, dtype=np.float32),
+        "q": to_bf16_bits(q), "kv": to_bf16_bits(kv),
+    }
+
+
+def make_prefill(cfg: Prefill) -> Dict[str, np.ndarray]:
+    """Inputs of one prefill chunk.  Keys sit at positions 0..N-1."""
+    rng = np.random.default_rng(cfg.seed)
+    return _draw(rng, cfg.shape, cfg.L, cfg.N, cfg.int_range, cfg.q_scale, cfg.kv_scale)
+
+
+def make_decode(cfg: Decode) -> Dict[str, np.ndarray]:
+    """Inputs of one batched decode step: one query per sequence, caches packed
+    in sequence order (rows of sequence b start at sum(ctx[:b]))."""
+    rng = np.random.default_rng(cfg.seed)
+    d = _draw(rng, cfg.shape, len(cfg.ctx), int(sum(cfg.ctx)), cfg.int_range, cfg.q_scale, cfg.kv_scale)
+    d["ctx"] = np.asarray(cfg.ctx, dtype=np.int64)
+    d["row_off"] = np.concatenate([[0], np.cumsum(d["ctx"])]).astype(np.int64)
+    return d
+
+
+def sample_rows(L: int, n: int, seed: int = 1234, must: Optional[List[int]] = None) -> np.ndarray:
+    """A sorted, seeded sample of n query rows out of L, always holding the
+    first and last row and any rows listed in ``must``."""
+    rng = np.random.default_rng(seed)
+    pick = set(int(x) for x in rng.choice(L, size=min(n, L), replace=False))
+    pick.update([0, L - 1])
+    for m in must or []:
+        if 0 <= m < L:
+            pick.add(int(m))
+    return np.array(sorted(pick), dtype=np.int64)
