@@ -1,0 +1,152 @@
+/*
+ * dsa.h - C ABI of the MI355X (gfx950) DeepSeek-sparse-attention core:
+ * indexer scores -> top-k selection -> absorbed-MLA attention over the
+ * selected latent rows, for one prefill chunk or one batched decode step.
+ *
+ * What is computed (the pages define it; section names, no line numbers):
+ *  - exo PR #2539 "GLM-5.2/5.3 (glm_moe_dsa) attention and MoE speed-ups",
+ *    Prefill section: a key's indexer score is the sum over the indexer heads
+ *    of the head's weight times relu(q.k), summed in float32 with the causal
+ *    mask applied; each query keeps its index_topk best causal keys, and a
+ *    query with no more causal keys than that keeps every earlier key; the
+ *    selected latent rows are gathered and attended with a float32 softmax.
+ *    Decode section: single-token attention treats the heads as the rows of
+ *    one product with the shared latent keys.
+ *  - "GLM-5.2-Vision: llama.cpp vs vLLM line-by-line pipeline trace",
+ *    section 6 (absorbed MLA): Q = [q_nope_absorbed | q_pe], K = [kv_cmpr |
+ *    k_pe], V = kv_cmpr; the config line gives 64 heads, kv_lora_rank 512,
+ *    qk_rope 64 and index_topk 2048.
+ *
+ * Readings taken where the pages are silent:
+ *  - key j sits at position j and is visible to the query at position p iff
+ *    j <= p; the indexer key is one Di-wide row per token shared by all
+ *    indexer heads; w is per query and head; no other factor scales it;
+ *  - equal scores go to the lower key index; a selection is listed in
+ *    ascending key order, padded with -1, count = min(p + 1, top_k);
+ *  - the softmax scale is an argument (GLM: 1/16 = 1/sqrt(192 + 64));
+ *  - the output is the latent-space attention output in float32.
+ *
+ * Conventions for every call:
+ *  - Pointers marked [dev] are device pointers owned by the caller, 16-byte
+ *    aligned, dense row-major with the shapes given.  [host] pointers are
+ *    read during the call only.  bf16 data is passed as uint16_t bits.
+ *  - The library allocates nothing and keeps no state beyond a per-device
+ *    architecture check.  Every call is asynchronous on `stream` (a
+ *    hipStream_t; NULL = the default stream); it never synchronises and
+ *    never reads device data on the host.
+ *  - Arguments are validated before anything is enqueued; on any error
+ *    nothing is enqueued and the status says why.  A failed launch returns
+ *    DSA_ERR_HIP.  Non-finite inputs give undefined results.
+ *  - Supported shapes: (n_heads, d_latent, d_rope, n_idx_heads, d_idx) =
+ *    (64, 512, 64, 32, 128) (GLM-5.x) or (4, 64, 16, 4, 32) (tiny check
+ *    shape); 1 <= top_k <= 2048; key counts up to 65536 for selection.
+ *    Others return DSA_ERR_UNSUPPORTED.  The device must be gfx950.
+ *  - The value product runs with fp16 operands (probabilities and the first
+ *    d_latent latent columns) and fp32 accumulation: latent values must lie
+ *    within +-65504.  The score product runs in bf16 with fp32 accumulation.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size or position */
+    DSA_ERR_UNSUPPORTED = -2,   /* shape, size or device this build does not handle */
+    DSA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
+    DSA_ERR_HIP = -4            /* a HIP runtime call or kernel launch failed */
+} dsa_status;
+
+typedef struct {
+    int32_t n_heads;       /* H: query heads (GLM 64) */
+    int32_t d_latent;      /* Dl: absorbed no-rope width = value width (GLM 512) */
+    int32_t d_rope;        /* Dr: rope width (GLM 64); query/key width Dl + Dr */
+    int32_t n_idx_heads;   /* Hi: indexer heads (GLM 32) */
+    int32_t d_idx;         /* Di: indexer head width (128) */
+    int32_t top_k;         /* keys kept per query (GLM index_topk 2048) */
+    float softmax_scale;   /* multiplies q.k before the softmax (GLM 1/16) */
+} dsa_shape;
+
+/* Human-readable name of a status code (static string). */
+const char* dsa_status_string(dsa_status status);
+
+/* Indexer scores of L queries at positions q_start .. q_start+L-1 over keys
+ * 0 .. N-1 (exo #2539, Prefill, float32 indexer):
+ *   S[i, j] = sum_h w[i,h] * max(0, sum_d qI[i,h,d] * kI[j,d])   if j <= q_start+i
+ *   S[i, j] = -infinity                                           otherwise.
+ * qI [dev] [L, Hi, Di] bf16; kI [dev] [N, Di] bf16; w [dev] [L, Hi] fp32;
+ * S [dev] [L, N] fp32 (written entirely).  Requires L >= 1, q_start >= 0,
+ * q_start + L <= N.  Products are exact in fp32; sums accumulate in fp32. */
+dsa_status dsa_indexer_scores(const dsa_shape* shape, const uint16_t* qI, const uint16_t* kI,
+                              const float* w, int32_t L, int32_t N, int64_t q_start, float* S,
+                              void* stream);
+
+/* Top-k selection per query (exo #2539, Prefill: index_topk selection and
+ * the every-earlier-key rule).  For the query at p = q_start + i:
+ *   p + 1 <= top_k : idx[i] = 0, 1, .., p (S is not read);
+ *   otherwise      : the top_k keys j <= p by (S desc, j asc), ascending.
+ * S [dev] [L, N] fp32 (only j <= p read); idx [dev] [L, top_k] int32, padded
+ * with -1; count [dev] [L] int32 = min(p + 1, top_k).  Requires
+ * q_start + L <= N <= 65536. */
+dsa_status dsa_topk_select(const dsa_shape* shape, const float* S, int32_t L, int32_t N,
+                           int64_t q_start, int32_t* idx, int32_t* count, void* stream);
+
+/* Absorbed-MLA attention of L queries over their selected latent rows
+ * (pipeline trace section 6; exo #2539 Prefill sparse attention, Decode):
+ *   s_t = softmax_scale * <q[i,h,:], kv[idx[i,t], :]>   for t < count[i]
+ *   out[i,h,:] = sum_t softmax(s)_t * kv[idx[i,t], 0:Dl];  lse = log sum exp s.
+ * q [dev] [L, H, Dl+Dr] bf16; kv [dev] [N, Dl+Dr] bf16; idx [dev] [L, top_k]
+ * int32 in any order (entries outside [0, N) are skipped); count [dev] [L]
+ * int32 (values above top_k are clamped); out [dev] [L, H, Dl] fp32;
+ * lse [dev] [L, H] fp32 natural log, or NULL.  A row with no usable key
+ * gets out = 0 and lse = -infinity. */
+dsa_status dsa_sparse_mla_attn(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv,
+                               const int32_t* idx, const int32_t* count, int32_t L, int32_t N,
+                               float* out, float* lse, void* stream);
+
+/* Workspace bytes dsa_prefill_chunk needs for this chunk geometry
+ * (0 on invalid or unsupported arguments). */
+size_t dsa_prefill_workspace_bytes(const dsa_shape* shape, int32_t L, int32_t N, int64_t q_start);
+
+/* One prefill chunk end to end: L queries at q_start .. q_start+L-1 over
+ * keys 0 .. N-1 with N = q_start + L (exo #2539, Prefill).  Queries with
+ * p + 1 <= top_k skip the indexer and keep every earlier key; the rest are
+ * scored, selected and attended over their top_k keys.
+ * q [dev] [L,H,Dl+Dr], qI [dev] [L,Hi,Di] bf16; w [dev] [L,Hi] fp32;
+ * kv [dev] [N,Dl+Dr], kI [dev] [N,Di] bf16; out [dev] [L,H,Dl] fp32;
+ * idx_out [dev] [L,top_k] int32 or NULL; count_out [dev] [L] int32 or NULL;
+ * ws [dev] of at least dsa_prefill_workspace_bytes() bytes. */
+dsa_status dsa_prefill_chunk(const dsa_shape* shape, const uint16_t* q, const uint16_t* qI,
+                             const float* w, const uint16_t* kv, const uint16_t* kI, int32_t L,
+                             int32_t N, int64_t q_start, float* out, int32_t* idx_out,
+                             int32_t* count_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Largest batch dsa_decode_step accepts. */
+#define DSA_MAX_DECODE_BATCH 128
+
+/* Workspace bytes dsa_decode_step needs (0 on invalid arguments). */
+size_t dsa_decode_workspace_bytes(const dsa_shape* shape, int32_t B, const int64_t* ctx);
+
+/* One batched decode step (exo #2539, Decode): B sequences, one query each
+ * at position ctx[b] - 1 over that sequence's ctx[b] cached keys.  Caches
+ * are packed in sequence order: sequence b's rows start at sum(ctx[:b]).
+ * ctx [host] [B], 1 <= ctx[b] <= 65536, B <= DSA_MAX_DECODE_BATCH;
+ * q [dev] [B,H,Dl+Dr], qI [dev] [B,Hi,Di] bf16; w [dev] [B,Hi] fp32;
+ * kv [dev] [sum ctx, Dl+Dr], kI [dev] [sum ctx, Di] bf16;
+ * out [dev] [B,H,Dl] fp32; idx_out [dev] [B,top_k] int32 (key ids local to
+ * the sequence) or NULL; count_out [dev] [B] or NULL; ws as above. */
+dsa_status dsa_decode_step(const dsa_shape* shape, int32_t B, const int64_t* ctx,
+                           const uint16_t* q, const uint16_t* qI, const float* w,
+                           const uint16_t* kv, const uint16_t* kI, float* out, int32_t* idx_out,
+                           int32_t* count_out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

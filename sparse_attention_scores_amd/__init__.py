@@ -1,0 +1,179 @@
+"""Python binding of the MI355X DSA core (``libdsa.so``, C ABI in include/dsa.h).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, checks dtype / device / contiguity, and passes their data
+pointers and the current HIP stream to the C function of the same name.
+Every step of the path runs in the library's HIP kernels; there is no
+fallback.  If the library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+from . import build as _build
+
+__all__ = [
+    "DsaError", "Shape", "GLM", "TINY", "lib",
+    "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn",
+    "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
+    "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_status_string",
+    "EXPORTED_SYMBOLS",
+]
+
+EXPORTED_SYMBOLS = (
+    "dsa_status_string", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn",
+    "dsa_prefill_workspace_bytes", "dsa_prefill_chunk", "dsa_decode_workspace_bytes",
+    "dsa_decode_step",
+)
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s: %s" % (fn, msg))
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    """dsa_shape: (n_heads, d_latent, d_rope, n_idx_heads, d_idx, top_k, softmax_scale)."""
+    _fields_ = [("n_heads", ctypes.c_int32), ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("n_idx_heads", ctypes.c_int32), ("d_idx", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+    @classmethod
+    def of(cls, s) -> "Shape":
+        """From any object with the same attribute names (e.g. workloads.Shape)."""
+        if isinstance(s, cls):
+            return s
+        return cls(s.n_heads, s.d_latent, s.d_rope, s.n_idx_heads, s.d_idx, s.top_k, s.softmax_scale)
+
+    @property
+    def d_qk(self) -> int:
+        return self.d_latent + self.d_rope
+
+
+GLM = Shape(64, 512, 64, 32, 128, 2048, 1.0 / 16)
+TINY = Shape(4, 64, 16, 4, 32, 32, 1.0 / 16)
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    L = ctypes.CDLL(_build.LIB)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    SP = ctypes.POINTER(Shape)
+    sig = {
+        "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "dsa_indexer_scores": (ctypes.c_int, [SP, P, P, P, i32, i32, i64, P, P]),
+        "dsa_topk_select": (ctypes.c_int, [SP, P, i32, i32, i64, P, P, P]),
+        "dsa_sparse_mla_attn": (ctypes.c_int, [SP, P, P, P, P, i32, i32, P, P, P]),
+        "dsa_prefill_workspace_bytes": (sz, [SP, i32, i32, i64]),
+        "dsa_prefill_chunk": (ctypes.c_int, [SP, P, P, P, P, P, i32, i32, i64, P, P, P, P, sz, P]),
+        "dsa_decode_workspace_bytes": (sz, [SP, i32, P]),
+        "dsa_decode_step": (ctypes.c_int, [SP, i32, P, P, P, P, P, P, P, P, P, P, sz, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    return L
+
+
+lib = _load()
+
+
+def dsa_status_string(status: int) -> str:
+    return lib.dsa_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise DsaError(fn, status, dsa_status_string(status))
+
+
+def _ptr(t: Optional[torch.Tensor], dtype: torch.dtype, name: str):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype:
+        raise TypeError("%s must be a %s tensor" % (name, dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must live on the GPU" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# bf16 operands travel as their 16-bit patterns: int16/uint16/bfloat16 tensors
+def _bits(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("%s must hold bf16 bit patterns (bfloat16/int16/uint16)" % name)
+    return _ptr(t, t.dtype, name)
+
+
+def dsa_indexer_scores(shape, qI, kI, w, L: int, N: int, q_start: int, S, stream=None) -> None:
+    sh = Shape.of(shape)
+    _check("dsa_indexer_scores", lib.dsa_indexer_scores(
+        ctypes.byref(sh), _bits(qI, "qI"), _bits(kI, "kI"), _ptr(w, torch.float32, "w"),
+        L, N, q_start, _ptr(S, torch.float32, "S"), _stream(stream)))
+
+
+def dsa_topk_select(shape, S, L: int, N: int, q_start: int, idx, count, stream=None) -> None:
+    sh = Shape.of(shape)
+    _check("dsa_topk_select", lib.dsa_topk_select(
+        ctypes.byref(sh), _ptr(S, torch.float32, "S"), L, N, q_start,
+        _ptr(idx, torch.int32, "idx"), _ptr(count, torch.int32, "count"), _stream(stream)))
+
+
+def dsa_sparse_mla_attn(shape, q, kv, idx, count, L: int, N: int, out, lse=None, stream=None) -> None:
+    sh = Shape.of(shape)
+    _check("dsa_sparse_mla_attn", lib.dsa_sparse_mla_attn(
+        ctypes.byref(sh), _bits(q, "q"), _bits(kv, "kv"), _ptr(idx, torch.int32, "idx"),
+        _ptr(count, torch.int32, "count"), L, N, _ptr(out, torch.float32, "out"),
+        _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def dsa_prefill_workspace_bytes(shape, L: int, N: int, q_start: int) -> int:
+    return int(lib.dsa_prefill_workspace_bytes(ctypes.byref(Shape.of(shape)), L, N, q_start))
+
+
+def dsa_prefill_chunk(shape, q, qI, w, kv, kI, L: int, N: int, q_start: int, out, idx_out=None,
+                      count_out=None, ws=None, stream=None) -> None:
+    sh = Shape.of(shape)
+    ws_ptr, ws_bytes = (None, 0) if ws is None else (_ptr(ws, torch.uint8, "ws"), ws.numel())
+    _check("dsa_prefill_chunk", lib.dsa_prefill_chunk(
+        ctypes.byref(sh), _bits(q, "q"), _bits(qI, "qI"), _ptr(w, torch.float32, "w"), _bits(kv, "kv"),
+        _bits(kI, "kI"), L, N, q_start, _ptr(out, torch.float32, "out"),
+        _ptr(idx_out, torch.int32, "idx_out"), _ptr(count_out, torch.int32, "count_out"),
+        ws_ptr, ws_bytes, _stream(stream)))
+
+
+def _ctx_array(ctx: Sequence[int]):
+    arr = (ctypes.c_int64 * len(ctx))(*[int(c) for c in ctx])
+    return arr
+
+
+def dsa_decode_workspace_bytes(shape, ctx: Sequence[int]) -> int:
+    arr = _ctx_array(ctx)
+    return int(lib.dsa_decode_workspace_bytes(ctypes.byref(Shape.of(shape)), len(ctx),
+                                              ctypes.cast(arr, ctypes.c_void_p)))
+
+
+def dsa_decode_step(shape, ctx: Sequence[int], q, qI, w, kv, kI, out, idx_out=None, count_out=None,
+                    ws=None, stream=None) -> None:
+    sh = Shape.of(shape)
+    arr = _ctx_array(ctx)
+    ws_ptr, ws_bytes = (None, 0) if ws is None else (_ptr(ws, torch.uint8, "ws"), ws.numel())
+    _check("dsa_decode_step", lib.dsa_decode_step(
+        ctypes.byref(sh), len(ctx), ctypes.cast(arr, ctypes.c_void_p), _bits(q, "q"), _bits(qI, "qI"),
+        _ptr(w, torch.float32, "w"), _bits(kv, "kv"), _bits(kI, "kI"), _ptr(out, torch.float32, "out"),
+        _ptr(idx_out, torch.int32, "idx_out"), _ptr(count_out, torch.int32, "count_out"),
+        ws_ptr, ws_bytes, _stream(stream)))

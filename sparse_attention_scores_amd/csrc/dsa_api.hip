@@ -1,0 +1,282 @@
+// dsa_api.hip - the C ABI declared in include/dsa.h: argument validation,
+// workspace layout, launch geometry and stream ordering.  All checks run
+// before anything is enqueued; nothing here reads device memory.
+#include "../../include/dsa.h"
+#include "dsa_kernels.h"
+
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+namespace {
+
+using dsa::SeqMeta;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// 0 = GLM-5.x (64, 512, 64, 32, 128); 1 = tiny check shape (4, 64, 16, 4, 32); -1 otherwise
+int shape_id(const dsa_shape* s) {
+    if (!s) return -1;
+    if (s->n_heads == 64 && s->d_latent == 512 && s->d_rope == 64 && s->n_idx_heads == 32 && s->d_idx == 128)
+        return 0;
+    if (s->n_heads == 4 && s->d_latent == 64 && s->d_rope == 16 && s->n_idx_heads == 4 && s->d_idx == 32)
+        return 1;
+    return -1;
+}
+
+dsa_status check_shape(const dsa_shape* s) {
+    if (!s) return DSA_ERR_INVALID_ARG;
+    if (s->n_heads <= 0 || s->d_latent <= 0 || s->d_rope < 0 || s->n_idx_heads <= 0 || s->d_idx <= 0 ||
+        s->top_k <= 0 || !isfinite(s->softmax_scale))
+        return DSA_ERR_INVALID_ARG;
+    if (shape_id(s) < 0 || s->top_k > dsa::kMaxTopK) return DSA_ERR_UNSUPPORTED;
+    return DSA_OK;
+}
+
+// The kernels are built for gfx950 only; refuse any other current device.
+dsa_status check_device() {
+    static std::mutex mu;
+    static int known[64];   // 0 unknown, 1 gfx950, 2 other
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_HIP;
+    if (dev < 0 || dev >= 64) return DSA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(mu);
+    if (known[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DSA_ERR_HIP;
+        known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    return known[dev] == 1 ? DSA_OK : DSA_ERR_UNSUPPORTED;
+}
+
+dsa_status launched(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+float scale_log2(const dsa_shape* s) { return s->softmax_scale * 1.4426950408889634f; }
+
+// first query row of a chunk that is scored (p + 1 > top_k)
+int32_t first_sparse_row(int32_t L, int64_t q_start, int32_t top_k) {
+    int64_t i0 = (int64_t)top_k - q_start;
+    if (i0 < 0) i0 = 0;
+    if (i0 > L) i0 = L;
+    return (int32_t)i0;
+}
+
+int64_t padded_row(int64_t n) { return (n + 63) / 64 * 64; }
+
+struct PrefillLayout {
+    size_t s_off, idx_off, cnt_off, total;
+    int32_t row0;
+    int64_t ldS;
+};
+
+PrefillLayout prefill_layout(const dsa_shape* s, int32_t L, int32_t N, int64_t q_start) {
+    PrefillLayout p;
+    p.row0 = first_sparse_row(L, q_start, s->top_k);
+    p.ldS = padded_row(N);
+    p.s_off = 0;
+    p.idx_off = align_up((size_t)(L - p.row0) * (size_t)p.ldS * sizeof(float));
+    p.cnt_off = p.idx_off + align_up((size_t)L * s->top_k * sizeof(int32_t));
+    p.total = p.cnt_off + align_up((size_t)L * sizeof(int32_t));
+    return p;
+}
+
+struct DecodeLayout {
+    SeqMeta idx_meta;    // blocks of the indexer kernel
+    SeqMeta attn_meta;   // blocks (chunks) of the attention kernel
+    int idx_blocks, attn_items, chunk, n_max;
+    size_t s_off, idx_off, cnt_off, po_off, pml_off, total;
+};
+
+// Chunk of selected keys per attention block: enough blocks to cover the
+// chip, at least one 32-key tile per block.
+int decode_chunk(const dsa_shape* s, int32_t B, const int64_t* ctx) {
+    int64_t sel = 0;
+    for (int b = 0; b < B; ++b) sel += ctx[b] < s->top_k ? ctx[b] : s->top_k;
+    int64_t c = (sel + 255) / 256;
+    c = (c + 31) / 32 * 32;
+    if (c < 32) c = 32;
+    if (c > s->top_k) c = (s->top_k + 31) / 32 * 32;
+    return (int)c;
+}
+
+dsa_status decode_layout(const dsa_shape* s, int32_t B, const int64_t* ctx, DecodeLayout& d) {
+    if (B <= 0 || !ctx) return DSA_ERR_INVALID_ARG;
+    if (B > dsa::kMaxBatch) return DSA_ERR_UNSUPPORTED;
+    memset(&d, 0, sizeof d);
+    d.chunk = decode_chunk(s, B, ctx);
+    const int kpb = dsa::indexer_decode_keys_per_block();
+    int64_t koff = 0, soff = 0;
+    int iblk = 0, items = 0;
+    d.n_max = 1;
+    for (int b = 0; b < B; ++b) {
+        if (ctx[b] <= 0) return DSA_ERR_INVALID_ARG;
+        if (ctx[b] > dsa::kMaxSelectKeys) return DSA_ERR_UNSUPPORTED;
+        const int c = (int)ctx[b];
+        d.idx_meta.key_off[b] = d.attn_meta.key_off[b] = koff;
+        d.idx_meta.s_off[b] = d.attn_meta.s_off[b] = soff;
+        d.idx_meta.ctx[b] = d.attn_meta.ctx[b] = c;
+        d.idx_meta.blk0[b] = iblk;
+        d.attn_meta.blk0[b] = items;
+        // a sequence within top_k keeps every key: no scores needed
+        if (c > s->top_k) iblk += (c + kpb - 1) / kpb;
+        const int cnt = c < s->top_k ? c : s->top_k;
+        items += (cnt + d.chunk - 1) / d.chunk;
+        if (c > d.n_max) d.n_max = c;
+        koff += c;
+        soff += padded_row(c);
+    }
+    d.idx_meta.B = d.attn_meta.B = B;
+    d.idx_meta.key_off[B] = d.attn_meta.key_off[B] = koff;
+    d.idx_meta.s_off[B] = d.attn_meta.s_off[B] = soff;
+    d.idx_meta.blk0[B] = iblk;
+    d.attn_meta.blk0[B] = items;
+    d.idx_blocks = iblk;
+    d.attn_items = items;
+    d.s_off = 0;
+    d.idx_off = align_up((size_t)soff * sizeof(float));
+    d.cnt_off = d.idx_off + align_up((size_t)B * s->top_k * sizeof(int32_t));
+    d.po_off = d.cnt_off + align_up((size_t)B * sizeof(int32_t));
+    d.pml_off = d.po_off + align_up((size_t)items * s->n_heads * s->d_latent * sizeof(float));
+    d.total = d.pml_off + align_up((size_t)items * s->n_heads * 2 * sizeof(float));
+    return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status status) {
+    switch (status) {
+        case DSA_OK: return "DSA_OK";
+        case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG: null or misaligned pointer, or bad size/position";
+        case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: shape, size or device not handled by this build";
+        case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+        case DSA_ERR_HIP: return "DSA_ERR_HIP: a HIP call or kernel launch failed";
+    }
+    return "unknown dsa_status";
+}
+
+dsa_status dsa_indexer_scores(const dsa_shape* shape, const uint16_t* qI, const uint16_t* kI,
+                              const float* w, int32_t L, int32_t N, int64_t q_start, float* S,
+                              void* stream) {
+    dsa_status st = check_shape(shape);
+    if (st) return st;
+    if (!qI || !kI || !w || !S || !aligned16(qI) || !aligned16(kI) || !aligned16(w) || !aligned16(S))
+        return DSA_ERR_INVALID_ARG;
+    if (L <= 0 || N <= 0 || q_start < 0 || q_start + L > N) return DSA_ERR_INVALID_ARG;
+    if ((st = check_device())) return st;
+    dsa::IndexerArgs a{qI, kI, w, S, N, L, N, q_start, 1};
+    return launched(dsa::launch_indexer_prefill(shape_id(shape), a, (hipStream_t)stream));
+}
+
+dsa_status dsa_topk_select(const dsa_shape* shape, const float* S, int32_t L, int32_t N,
+                           int64_t q_start, int32_t* idx, int32_t* count, void* stream) {
+    dsa_status st = check_shape(shape);
+    if (st) return st;
+    if (!S || !idx || !count || !aligned16(S) || !aligned16(idx) || !aligned16(count))
+        return DSA_ERR_INVALID_ARG;
+    if (L <= 0 || N <= 0 || q_start < 0 || q_start + L > N) return DSA_ERR_INVALID_ARG;
+    if (N > dsa::kMaxSelectKeys) return DSA_ERR_UNSUPPORTED;
+    if ((st = check_device())) return st;
+    dsa::TopkArgs a{S, N, 0, L, q_start, shape->top_k, idx, count};
+    return launched(dsa::launch_topk_prefill(a, (int)(q_start + L), (hipStream_t)stream));
+}
+
+dsa_status dsa_sparse_mla_attn(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv,
+                               const int32_t* idx, const int32_t* count, int32_t L, int32_t N,
+                               float* out, float* lse, void* stream) {
+    dsa_status st = check_shape(shape);
+    if (st) return st;
+    if (!q || !kv || !idx || !count || !out || !aligned16(q) || !aligned16(kv) || !aligned16(out) ||
+        (lse && !aligned16(lse)))
+        return DSA_ERR_INVALID_ARG;
+    if (L <= 0 || N <= 0) return DSA_ERR_INVALID_ARG;
+    if ((st = check_device())) return st;
+    dsa::AttnArgs a{q, kv, idx, count, L, N, shape->top_k, scale_log2(shape), out, lse};
+    return launched(dsa::launch_attention(shape_id(shape), a, (hipStream_t)stream));
+}
+
+size_t dsa_prefill_workspace_bytes(const dsa_shape* shape, int32_t L, int32_t N, int64_t q_start) {
+    if (check_shape(shape) != DSA_OK || L <= 0 || q_start < 0 || (int64_t)N != q_start + L) return 0;
+    return prefill_layout(shape, L, N, q_start).total;
+}
+
+dsa_status dsa_prefill_chunk(const dsa_shape* shape, const uint16_t* q, const uint16_t* qI,
+                             const float* w, const uint16_t* kv, const uint16_t* kI, int32_t L,
+                             int32_t N, int64_t q_start, float* out, int32_t* idx_out,
+                             int32_t* count_out, void* ws, size_t ws_bytes, void* stream) {
+    dsa_status st = check_shape(shape);
+    if (st) return st;
+    if (!q || !qI || !w || !kv || !kI || !out)
+        return DSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(qI) || !aligned16(w) || !aligned16(kv) || !aligned16(kI) ||
+        !aligned16(out) || (idx_out && !aligned16(idx_out)) || (count_out && !aligned16(count_out)))
+        return DSA_ERR_INVALID_ARG;
+    if (L <= 0 || q_start < 0 || (int64_t)N != q_start + L) return DSA_ERR_INVALID_ARG;
+    if (N > dsa::kMaxSelectKeys) return DSA_ERR_UNSUPPORTED;
+    const PrefillLayout lay = prefill_layout(shape, L, N, q_start);
+    if (!ws || !aligned16(ws) || ws_bytes < lay.total) return DSA_ERR_WORKSPACE;
+    if ((st = check_device())) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const int sid = shape_id(shape);
+    char* base = static_cast<char*>(ws);
+    float* S = reinterpret_cast<float*>(base + lay.s_off);
+    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + lay.idx_off);
+    int32_t* cnt = count_out ? count_out : reinterpret_cast<int32_t*>(base + lay.cnt_off);
+    const int64_t dq = (int64_t)shape->n_idx_heads * shape->d_idx;
+
+    // 1. indexer scores for the queries with more causal keys than top_k
+    dsa::IndexerArgs ia{qI + lay.row0 * dq, kI, w + (int64_t)lay.row0 * shape->n_idx_heads, S, lay.ldS,
+                        L - lay.row0, N, q_start + lay.row0, 0};
+    if ((st = launched(dsa::launch_indexer_prefill(sid, ia, s)))) return st;
+    // 2. selection (every earlier key below the boundary)
+    dsa::TopkArgs ta{S, lay.ldS, lay.row0, L, q_start, shape->top_k, idx, cnt};
+    if ((st = launched(dsa::launch_topk_prefill(ta, N, s)))) return st;
+    // 3. attention over the gathered rows
+    dsa::AttnArgs aa{q, kv, idx, cnt, L, N, shape->top_k, scale_log2(shape), out, nullptr};
+    return launched(dsa::launch_attention(sid, aa, s));
+}
+
+size_t dsa_decode_workspace_bytes(const dsa_shape* shape, int32_t B, const int64_t* ctx) {
+    if (check_shape(shape) != DSA_OK) return 0;
+    static thread_local DecodeLayout d;
+    if (decode_layout(shape, B, ctx, d) != DSA_OK) return 0;
+    return d.total;
+}
+
+dsa_status dsa_decode_step(const dsa_shape* shape, int32_t B, const int64_t* ctx,
+                           const uint16_t* q, const uint16_t* qI, const float* w,
+                           const uint16_t* kv, const uint16_t* kI, float* out, int32_t* idx_out,
+                           int32_t* count_out, void* ws, size_t ws_bytes, void* stream) {
+    dsa_status st = check_shape(shape);
+    if (st) return st;
+    if (!q || !qI || !w || !kv || !kI || !out)
+        return DSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(qI) || !aligned16(w) || !aligned16(kv) || !aligned16(kI) ||
+        !aligned16(out) || (idx_out && !aligned16(idx_out)) || (count_out && !aligned16(count_out)))
+        return DSA_ERR_INVALID_ARG;
+    static thread_local DecodeLayout d;
+    if ((st = decode_layout(shape, B, ctx, d))) return st;
+    if (!ws || !aligned16(ws) || ws_bytes < d.total) return DSA_ERR_WORKSPACE;
+    if ((st = check_device())) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const int sid = shape_id(shape);
+    char* base = static_cast<char*>(ws);
+    float* S = reinterpret_cast<float*>(base + d.s_off);
+    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + d.idx_off);
+    int32_t* cnt = count_out ? count_out : reinterpret_cast<int32_t*>(base + d.cnt_off);
+
+    if ((st = launched(dsa::launch_indexer_decode(sid, qI, kI, w, S, d.idx_meta, d.idx_blocks, s)))) return st;
+    if ((st = launched(dsa::launch_topk_decode(S, d.idx_meta, shape->top_k, idx, cnt, d.n_max, s)))) return st;
+    dsa::AttnSplitArgs aa{q, kv, idx, shape->top_k, d.chunk, scale_log2(shape),
+                          reinterpret_cast<float*>(base + d.po_off), reinterpret_cast<float*>(base + d.pml_off),
+                          out};
+    return launched(dsa::launch_attention_split(sid, aa, d.attn_meta, d.attn_items, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// dsa_kernels.h - internal to the HIP library: device types, helpers and the
+// launcher entry points the C ABI (dsa_api.hip) calls.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxBatch = 128;      // decode sequences per step
+constexpr int kMaxTopK = 2048;
+constexpr int kMaxSelectKeys = 65536;
+
+// Per-sequence geometry of a decode step, passed by value in kernel
+// arguments so that no host-to-device copy is needed.
+struct SeqMeta {
+    int32_t B;
+    int32_t pad_;
+    int64_t key_off[kMaxBatch + 1];   // first cache row of sequence b
+    int64_t s_off[kMaxBatch + 1];     // first score of sequence b (64-aligned)
+    int32_t ctx[kMaxBatch];           // keys of sequence b; query at ctx-1
+    int32_t blk0[kMaxBatch + 1];      // first block of sequence b (per kernel)
+};
+
+// Which sequence owns block `blk` (blk0 is ascending, B small).
+__device__ inline int seq_of_block(const SeqMeta& m, int blk) {
+    int b = 0;
+    while (b + 1 < m.B && blk >= m.blk0[b + 1]) ++b;
+    return b;
+}
+
+__device__ inline f32x4 mfma16_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ inline f32x4 mfma16_f16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ inline f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ inline u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// ---- launchers (each returns hipGetLastError() of its launches) ----------
+
+struct IndexerArgs {
+    const uint16_t* qI;   // [rows, Hi, Di]  (row r = query row0 + r)
+    const uint16_t* kI;   // [N, Di]
+    const float* w;       // [rows, Hi]
+    float* S;             // [rows, ldS]
+    int64_t ldS;
+    int32_t rows;         // queries scored
+    int32_t N;            // keys
+    int64_t pos0;         // position of the first scored query
+    int32_t write_masked; // also write -inf for keys past each query
+};
+// Shape ids: 0 = GLM (Hi 32, Di 128), 1 = tiny (Hi 4, Di 32)
+hipError_t launch_indexer_prefill(int shape_id, const IndexerArgs& a, hipStream_t s);
+hipError_t launch_indexer_decode(int shape_id, const uint16_t* qI, const uint16_t* kI,
+                                 const float* w, float* S, const SeqMeta& m, int blocks,
+                                 hipStream_t s);
+int indexer_decode_keys_per_block();
+
+struct TopkArgs {
+    const float* S;       // prefill: row r at S + (r - s_row0) * ldS
+    int64_t ldS;
+    int32_t s_row0;       // first row that has scores (earlier rows are dense)
+    int32_t rows;
+    int64_t pos0;         // position of row 0
+    int32_t top_k;
+    int32_t* idx;         // [rows, top_k]
+    int32_t* count;       // [rows] or null
+};
+hipError_t launch_topk_prefill(const TopkArgs& a, int n_max, hipStream_t s);
+hipError_t launch_topk_decode(const float* S, const SeqMeta& m, int top_k, int32_t* idx,
+                              int32_t* count, int n_max, hipStream_t s);
+
+struct AttnArgs {
+    const uint16_t* q;     // [rows, H, Dqk]
+    const uint16_t* kv;    // [N, Dqk] (decode: packed caches)
+    const int32_t* idx;    // [rows, top_k]
+    const int32_t* count;  // [rows]
+    int32_t rows;
+    int32_t N;
+    int32_t top_k;
+    float scale_log2;      // softmax_scale * log2(e)
+    float* out;            // [rows, H, Dl]
+    float* lse;            // [rows, H] or null
+};
+// Split (decode) variant: block -> (sequence, chunk of `chunk` selected keys);
+// writes unnormalised partial outputs, then a combine kernel finishes.
+struct AttnSplitArgs {
+    const uint16_t* q;
+    const uint16_t* kv;
+    const int32_t* idx;
+    int32_t top_k;
+    int32_t chunk;
+    float scale_log2;
+    float* part_o;         // [items, H, Dl]
+    float* part_ml;        // [items, H, 2] (running max in log2 units, sum)
+    float* out;            // [B, H, Dl]
+};
+hipError_t launch_attention(int shape_id, const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_split(int shape_id, const AttnSplitArgs& a, const SeqMeta& m,
+                                  int items, hipStream_t s);
+
+}  // namespace dsa

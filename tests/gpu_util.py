@@ -1,0 +1,52 @@
+"""Helpers shared by the GPU tests (no method arithmetic here)."""
+import sys
+
+import numpy as np
+import pytest
+
+# Attention tolerance: max over (query, head) rows of max_d |o - r| / max_d |r|.
+ATTN_TOL = 2e-3
+
+
+def gpu_available() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+requires_gpu = pytest.mark.skipif(not gpu_available(), reason="needs a GPU")
+
+
+def say(*a):
+    """Name the case before each GPU step (flushed, so a crash still shows it)."""
+    print("[gpu-case]", *a, file=sys.stderr, flush=True)
+
+
+def dev(a: np.ndarray):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t) -> np.ndarray:
+    import torch
+    torch.cuda.synchronize()
+    a = t.cpu().numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
+
+
+def row_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
+    """max over rows (all axes but the last) of max|o-r| / max|r|."""
+    out = out.astype(np.float64).reshape(-1, out.shape[-1])
+    ref = ref.astype(np.float64).reshape(-1, ref.shape[-1])
+    den = np.abs(ref).max(axis=1)
+    num = np.abs(out - ref).max(axis=1)
+    ok = den > 0
+    worst = float((num[ok] / den[ok]).max()) if ok.any() else 0.0
+    if (~ok).any():   # rows whose reference is exactly zero must be exactly zero
+        worst = max(worst, float(num[~ok].max()) * 1e30)
+    return worst

@@ -1,0 +1,103 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/dsa.h declares, and rejects bad arguments before any launch (these
+run without a GPU: validation happens before the first HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+dsa = pytest.importorskip("sparse_attention_scores_amd")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 8, names
+    assert sorted(dsa.EXPORTED_SYMBOLS) == names
+    raw = ctypes.CDLL(dsa._build.LIB)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings():
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR):
+        assert dsa.dsa_status_string(code).startswith("DSA_")
+    assert "unknown" in dsa.dsa_status_string(7)
+
+
+def fake(addr=0x1000):
+    return ctypes.c_void_p(addr)
+
+
+def test_shape_validation():
+    L = dsa.lib
+    bad = dsa.Shape(64, 512, 64, 32, 128, 2048, 1.0 / 16)
+    bad.n_heads = 8                       # not a supported head count
+    assert L.dsa_indexer_scores(ctypes.byref(bad), fake(), fake(), fake(), 4, 8, 0, fake(), None) == UNSUPPORTED
+    big = dsa.Shape(64, 512, 64, 32, 128, 4096, 1.0 / 16)
+    assert L.dsa_topk_select(ctypes.byref(big), fake(), 4, 8, 0, fake(), fake(), None) == UNSUPPORTED
+    neg = dsa.Shape(64, 512, 64, 32, 128, 0, 1.0 / 16)
+    assert L.dsa_topk_select(ctypes.byref(neg), fake(), 4, 8, 0, fake(), fake(), None) == INVALID
+    nan = dsa.Shape(64, 512, 64, 32, 128, 2048, float("nan"))
+    assert L.dsa_sparse_mla_attn(ctypes.byref(nan), fake(), fake(), fake(), fake(), 1, 1, fake(), None, None) == INVALID
+    assert L.dsa_indexer_scores(None, fake(), fake(), fake(), 4, 8, 0, fake(), None) == INVALID
+
+
+def test_pointer_and_size_validation():
+    L, sh = dsa.lib, ctypes.byref(dsa.GLM)
+    assert L.dsa_indexer_scores(sh, None, fake(), fake(), 4, 8, 0, fake(), None) == INVALID
+    assert L.dsa_indexer_scores(sh, fake(0x1008), fake(), fake(), 4, 8, 0, fake(), None) == INVALID  # misaligned
+    assert L.dsa_indexer_scores(sh, fake(), fake(), fake(), 0, 8, 0, fake(), None) == INVALID        # L = 0
+    assert L.dsa_indexer_scores(sh, fake(), fake(), fake(), 4, 8, 5, fake(), None) == INVALID        # q_start+L > N
+    assert L.dsa_indexer_scores(sh, fake(), fake(), fake(), 4, 8, -1, fake(), None) == INVALID
+    assert L.dsa_topk_select(sh, fake(), 4, 70000, 69996, fake(), fake(), None) == UNSUPPORTED      # > 65536 keys
+    assert L.dsa_sparse_mla_attn(sh, fake(), fake(), None, fake(), 1, 1, fake(), None, None) == INVALID
+    assert L.dsa_sparse_mla_attn(sh, fake(), fake(), fake(), fake(), 1, 1, fake(), fake(0x1004), None) == INVALID
+
+
+def test_prefill_workspace_and_validation():
+    L, sh = dsa.lib, ctypes.byref(dsa.GLM)
+    assert dsa.dsa_prefill_workspace_bytes(dsa.GLM, 4096, 16384, 12288) > 4096 * 16384 * 4
+    # the first chunk only scores queries past position 2047
+    small = dsa.dsa_prefill_workspace_bytes(dsa.GLM, 4096, 4096, 0)
+    idx_bytes = 4096 * 2048 * 4
+    assert 2048 * 4096 * 4 + idx_bytes <= small < 4096 * 4096 * 4 + idx_bytes
+    assert dsa.dsa_prefill_workspace_bytes(dsa.GLM, 4096, 16000, 12288) == 0      # N != q_start + L
+    args = [fake()] * 5
+    rc = L.dsa_prefill_chunk(sh, *args, 16, 16, 0, fake(), None, None, fake(), 0, None)
+    assert rc == WORKSPACE
+    rc = L.dsa_prefill_chunk(sh, *args, 16, 17, 0, fake(), None, None, fake(), 1 << 30, None)
+    assert rc == INVALID
+    rc = L.dsa_prefill_chunk(sh, None, *args[1:], 16, 16, 0, fake(), None, None, fake(), 1 << 30, None)
+    assert rc == INVALID
+
+
+def test_decode_workspace_and_validation():
+    L, sh = dsa.lib, ctypes.byref(dsa.GLM)
+    ctx = [4096, 8192, 16384, 32768, 65536, 65536, 16384, 4096]
+    ws = dsa.dsa_decode_workspace_bytes(dsa.GLM, ctx)
+    assert ws >= sum(ctx) * 4
+    assert dsa.dsa_decode_workspace_bytes(dsa.GLM, [0, 5]) == 0
+    assert dsa.dsa_decode_workspace_bytes(dsa.GLM, [70000]) == 0
+    arr = (ctypes.c_int64 * 2)(100, 0)
+    rc = L.dsa_decode_step(sh, 2, ctypes.cast(arr, ctypes.c_void_p), *([fake()] * 6), None, None,
+                           fake(), 1 << 30, None)
+    assert rc == INVALID
+    arr = (ctypes.c_int64 * 1)(100)
+    rc = L.dsa_decode_step(sh, 1, ctypes.cast(arr, ctypes.c_void_p), *([fake()] * 6), None, None,
+                           fake(), 16, None)
+    assert rc == WORKSPACE
+    many = (ctypes.c_int64 * 200)(*([10] * 200))
+    rc = L.dsa_decode_step(sh, 200, ctypes.cast(many, ctypes.c_void_p), *([fake()] * 6), None, None,
+                           fake(), 1 << 30, None)
+    assert rc == UNSUPPORTED

@@ -1,0 +1,287 @@
+"""GPU parity: every HIP entry point against the CPU oracle on the same seeded
+inputs.  Indexer scores and selections must match bit for bit (integer
+indexer data makes every fp32 sum exact); attention must hold a row
+relative error of 2e-3 (max over (query, head) of max|o-r| / max|r|).
+
+Small configs are compared on every row; the full GLM-shape configs run in
+the launch configuration the benchmark times and are compared on a seeded
+sample of rows the oracle computes one by one, plus properties that hold on
+every row."""
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests.gpu_util import ATTN_TOL, dev, host, requires_gpu, row_rel_err, say
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+SMALL = ["tiny", "tiny_dense", "tiny_sharp", "glm_small_cross", "glm_small_sparse", "glm_small_first"]
+FULL = ["glm_first_4k", "glm_8k", "glm_16k"]
+
+
+@functools.lru_cache(maxsize=2)
+def prefill_inputs(name):
+    return W.make_prefill(W.PREFILL[name])
+
+
+def lib():
+    import sparse_attention_scores_amd as dsa
+    return dsa
+
+
+def run_indexer(cfg, d):
+    import torch
+    S = torch.empty((cfg.L, cfg.N), dtype=torch.float32, device="cuda")
+    lib().dsa_indexer_scores(cfg.shape, dev(d["qI"]), dev(d["kI"]), dev(d["w"]), cfg.L, cfg.N, cfg.q_start, S)
+    return S
+
+
+def run_prefill(cfg, d):
+    import torch
+    dsa = lib()
+    out = torch.empty((cfg.L, cfg.shape.n_heads, cfg.shape.d_latent), dtype=torch.float32, device="cuda")
+    idx = torch.empty((cfg.L, cfg.shape.top_k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((cfg.L,), dtype=torch.int32, device="cuda")
+    ws = torch.empty((dsa.dsa_prefill_workspace_bytes(cfg.shape, cfg.L, cfg.N, cfg.q_start),),
+                     dtype=torch.uint8, device="cuda")
+    dsa.dsa_prefill_chunk(cfg.shape, dev(d["q"]), dev(d["qI"]), dev(d["w"]), dev(d["kv"]), dev(d["kI"]),
+                          cfg.L, cfg.N, cfg.q_start, out, idx, cnt, ws)
+    return host(out), host(idx), host(cnt)
+
+
+def check_selection_properties(idx, cnt, pos, top_k):
+    """Every row: count = min(p+1, top_k), ascending ids in [0, p], -1 padding."""
+    want = np.minimum(pos + 1, top_k)
+    assert np.array_equal(cnt, want)
+    for r in range(idx.shape[0]):
+        c = cnt[r]
+        sel = idx[r, :c]
+        assert sel[0] >= 0 and sel[-1] <= pos[r], r
+        assert np.all(np.diff(sel) > 0), r
+        assert np.all(idx[r, c:] == -1), r
+
+
+# ---------------------------------------------------------------- indexer
+@pytest.mark.parametrize("name", SMALL)
+def test_indexer_small_bit_exact(name):
+    cfg = W.PREFILL[name]
+    d = prefill_inputs(name)
+    say("indexer", name, cfg.L, cfg.N, cfg.q_start)
+    S = host(run_indexer(cfg, d))
+    ref = oracle.indexer_scores(d["qI"], d["kI"], d["w"], cfg.q_start)
+    assert np.array_equal(S, ref)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_indexer_full_sampled_bit_exact(name):
+    cfg = W.PREFILL[name]
+    d = prefill_inputs(name)
+    say("indexer-full", name)
+    S = run_indexer(cfg, d)
+    rows = W.sample_rows(cfg.L, 24, seed=5, must=[W.GLM.top_k - cfg.q_start, W.GLM.top_k - cfg.q_start - 1])
+    got = host(S[rows.tolist()])
+    ref = oracle.indexer_scores(d["qI"], d["kI"], d["w"], cfg.q_start, rows=rows)
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------- top-k
+@pytest.mark.parametrize("name", SMALL)
+def test_topk_small_bit_exact(name):
+    import torch
+    cfg = W.PREFILL[name]
+    d = prefill_inputs(name)
+    S = oracle.indexer_scores(d["qI"], d["kI"], d["w"], cfg.q_start)
+    pos = cfg.q_start + np.arange(cfg.L)
+    ref_idx, ref_cnt = oracle.topk_select(S, pos, cfg.shape.top_k)
+    idx = torch.empty((cfg.L, cfg.shape.top_k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((cfg.L,), dtype=torch.int32, device="cuda")
+    say("topk", name)
+    lib().dsa_topk_select(cfg.shape, dev(S), cfg.L, cfg.N, cfg.q_start, idx, cnt)
+    assert np.array_equal(host(cnt), ref_cnt)
+    assert np.array_equal(host(idx), ref_idx)
+
+
+@pytest.mark.parametrize("N,top_k,levels", [(300, 32, 3), (5000, 2048, 5), (16384, 2048, 40),
+                                            (16384, 2048, 2), (65536, 2048, 7), (3000, 1, 4),
+                                            (2049, 2048, 2)])
+def test_topk_ties_and_sizes(N, top_k, levels):
+    """Scores drawn from a few values (many ties at the boundary), negative
+    values and -0.0/+0.0 included; every row at a different length."""
+    import dataclasses
+    import torch
+    rng = np.random.default_rng(N + top_k + levels)
+    L = 6
+    S = (rng.integers(0, levels, size=(L, N)) - levels // 2).astype(np.float32)
+    S[S == 0] = np.where(rng.random((S == 0).sum()) < 0.5, -0.0, 0.0).astype(np.float32)
+    q_start = N - L
+    pos = q_start + np.arange(L)
+    ref_idx, ref_cnt = oracle.topk_select(S, pos, top_k)
+    shape = dataclasses.replace(W.GLM, top_k=top_k)
+    idx = torch.empty((L, top_k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((L,), dtype=torch.int32, device="cuda")
+    say("topk-ties", N, top_k, levels)
+    lib().dsa_topk_select(shape, dev(S), L, N, q_start, idx, cnt)
+    assert np.array_equal(host(cnt), ref_cnt)
+    assert np.array_equal(host(idx), ref_idx)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_topk_full_sampled_bit_exact(name):
+    import torch
+    cfg = W.PREFILL[name]
+    d = prefill_inputs(name)
+    say("topk-full", name)
+    S = run_indexer(cfg, d)
+    idx = torch.empty((cfg.L, cfg.shape.top_k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((cfg.L,), dtype=torch.int32, device="cuda")
+    lib().dsa_topk_select(cfg.shape, S, cfg.L, cfg.N, cfg.q_start, idx, cnt)
+    idx_h, cnt_h = host(idx), host(cnt)
+    pos = cfg.q_start + np.arange(cfg.L)
+    check_selection_properties(idx_h, cnt_h, pos, cfg.shape.top_k)
+    rows = W.sample_rows(cfg.L, 16, seed=6)
+    Sref = oracle.indexer_scores(d["qI"], d["kI"], d["w"], cfg.q_start, rows=rows)
+    ref_idx, ref_cnt = oracle.topk_select(Sref, pos[rows], cfg.shape.top_k)
+    assert np.array_equal(idx_h[rows], ref_idx)
+
+
+# ---------------------------------------------------------------- attention
+@pytest.mark.parametrize("name", SMALL)
+def test_attention_small(name):
+    import torch
+    cfg = W.PREFILL[name]
+    d = prefill_inputs(name)
+    ref_idx, ref_cnt, ref_out = oracle.prefill_chunk(d, cfg.shape, cfg.q_start)
+    _, ref_lse = oracle.sparse_mla_attn(d["q"], d["kv"], ref_idx, ref_cnt, cfg.shape.d_latent,
+                                        cfg.shape.softmax_scale, want_lse=True)
+    out = torch.empty((cfg.L, cfg.shape.n_heads, cfg.shape.d_latent), dtype=torch.float32, device="cuda")
+    lse = torch.empty((cfg.L, cfg.shape.n_heads), dtype=torch.float32, device="cuda")
+    say("attention", name)
+    lib().dsa_sparse_mla_attn(cfg.shape, dev(d["q"]), dev(d["kv"]), dev(ref_idx), dev(ref_cnt), cfg.L, cfg.N,
+                              out, lse)
+    err = row_rel_err(host(out), ref_out)
+    assert err <= ATTN_TOL, err
+    assert np.abs(host(lse) - ref_lse).max() < 1e-4
+
+
+def test_attention_selection_edge_cases():
+    """Unordered selections, -1 and out-of-range ids (skipped), counts above
+    top_k (clamped), a single key, and a row with no usable key."""
+    import torch
+    cfg = W.PREFILL["tiny"]
+    d = prefill_inputs("tiny")
+    rng = np.random.default_rng(3)
+    L, N, k = cfg.L, cfg.N, cfg.shape.top_k
+    idx = np.full((L, k), -1, np.int32)
+    cnt = np.zeros(L, np.int32)
+    for i in range(L):
+        c = int(rng.integers(1, k + 1))
+        idx[i, :c] = rng.choice(N, size=c, replace=False)
+        cnt[i] = c
+    idx[1, 3] = N + 5          # out of range: skipped
+    idx[2, 0] = -7             # negative: skipped
+    cnt[3] = k + 100           # clamped to top_k (padding -1 entries are skipped)
+    cnt[4] = 1
+    idx[5, :] = -1             # no usable key
+    cnt[5] = 4
+    ref_out, ref_lse = oracle.sparse_mla_attn(d["q"], d["kv"], idx, np.minimum(cnt, k), cfg.shape.d_latent,
+                                              cfg.shape.softmax_scale, want_lse=True)
+    out = torch.empty((L, cfg.shape.n_heads, cfg.shape.d_latent), dtype=torch.float32, device="cuda")
+    lse = torch.empty((L, cfg.shape.n_heads), dtype=torch.float32, device="cuda")
+    say("attention-edge")
+    lib().dsa_sparse_mla_attn(cfg.shape, dev(d["q"]), dev(d["kv"]), dev(idx), dev(cnt), L, N, out, lse)
+    o, s = host(out), host(lse)
+    assert np.all(o[5] == 0.0) and np.all(s[5] == -np.inf)
+    keep = np.arange(L) != 5
+    assert row_rel_err(o[keep], ref_out[keep]) <= ATTN_TOL
+    assert np.abs(s[keep] - ref_lse[keep]).max() < 1e-4
+    # the order of a selection does not matter
+    idx2 = idx.copy()
+    for i in range(L):
+        idx2[i, : min(cnt[i], k)] = rng.permutation(idx[i, : min(cnt[i], k)])
+    out2 = torch.empty_like(out)
+    lib().dsa_sparse_mla_attn(cfg.shape, dev(d["q"]), dev(d["kv"]), dev(idx2), dev(cnt), L, N, out2, None)
+    assert row_rel_err(host(out2)[keep], ref_out[keep]) <= ATTN_TOL
+
+
+# ---------------------------------------------------------------- prefill chunk
+@pytest.mark.parametrize("name", SMALL)
+def test_prefill_chunk_small(name):
+    cfg = W.PREFILL[name]
+    d = prefill_inputs(name)
+    say("prefill", name)
+    out, idx, cnt = run_prefill(cfg, d)
+    ref_idx, ref_cnt, ref_out = oracle.prefill_chunk(d, cfg.shape, cfg.q_start)
+    assert np.array_equal(cnt, ref_cnt)
+    assert np.array_equal(idx, ref_idx)
+    err = row_rel_err(out, ref_out)
+    assert err <= ATTN_TOL, err
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_prefill_chunk_full_sampled(name):
+    cfg = W.PREFILL[name]
+    d = prefill_inputs(name)
+    say("prefill-full", name)
+    out, idx, cnt = run_prefill(cfg, d)
+    pos = cfg.q_start + np.arange(cfg.L)
+    check_selection_properties(idx, cnt, pos, cfg.shape.top_k)
+    assert np.all(np.isfinite(out))
+    rows = W.sample_rows(cfg.L, 24, seed=7, must=[W.GLM.top_k - cfg.q_start, W.GLM.top_k - cfg.q_start - 1])
+    ref_idx, ref_cnt, ref_out = oracle.prefill_chunk(d, cfg.shape, cfg.q_start, rows=rows)
+    assert np.array_equal(idx[rows], ref_idx)
+    err = row_rel_err(out[rows], ref_out)
+    assert err <= ATTN_TOL, err
+
+
+def test_prefill_chunk_deterministic():
+    cfg = W.PREFILL["glm_small_cross"]
+    d = prefill_inputs("glm_small_cross")
+    a = run_prefill(cfg, d)
+    b = run_prefill(cfg, d)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+@pytest.mark.parametrize("L,q_start", [(1, 0), (1, 5000), (3, 2046), (129, 1919)])
+def test_prefill_chunk_edges(L, q_start):
+    """One query at position 0 (a single key), one deep query, a chunk that
+    straddles the top_k boundary by one, and a ragged 129-query chunk."""
+    import dataclasses
+    cfg = dataclasses.replace(W.PREFILL["glm_small_cross"], L=L, q_start=q_start, seed=40 + L)
+    d = W.make_prefill(cfg)
+    say("prefill-edge", L, q_start)
+    out, idx, cnt = run_prefill(cfg, d)
+    ref_idx, ref_cnt, ref_out = oracle.prefill_chunk(d, cfg.shape, cfg.q_start)
+    assert np.array_equal(cnt, ref_cnt)
+    assert np.array_equal(idx, ref_idx)
+    assert row_rel_err(out, ref_out) <= ATTN_TOL
+
+
+# ---------------------------------------------------------------- decode
+def run_decode(cfg, d):
+    import torch
+    dsa = lib()
+    B = len(cfg.ctx)
+    out = torch.empty((B, cfg.shape.n_heads, cfg.shape.d_latent), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, cfg.shape.top_k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B,), dtype=torch.int32, device="cuda")
+    ws = torch.empty((dsa.dsa_decode_workspace_bytes(cfg.shape, cfg.ctx),), dtype=torch.uint8, device="cuda")
+    dsa.dsa_decode_step(cfg.shape, cfg.ctx, dev(d["q"]), dev(d["qI"]), dev(d["w"]), dev(d["kv"]), dev(d["kI"]),
+                        out, idx, cnt, ws)
+    return host(out), host(idx), host(cnt)
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "glm_decode_small", "glm_decode_8"])
+def test_decode_step(name):
+    cfg = W.DECODE[name]
+    d = W.make_decode(cfg)
+    say("decode", name, cfg.ctx)
+    out, idx, cnt = run_decode(cfg, d)
+    ref_idx, ref_cnt, ref_out = oracle.decode_step(d, cfg.shape)
+    assert np.array_equal(cnt, ref_cnt)
+    assert np.array_equal(idx, ref_idx)
+    err = row_rel_err(out, ref_out)
+    assert err <= ATTN_TOL, err
