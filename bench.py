@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA prefill/decode core on one MI355X.
+
+Headline: dsa_prefill_chunk on the long-context chunk (4096 queries at
+positions 12288..16383 over 16384 keys, GLM-5.x shapes, top_k 2048) in
+queries/s, with algorithmic TFLOP/s against the bf16 MFMA peak.  Also:
+dsa_decode_step on 8 sequences (contexts 4k..64k) in us/step, each stage's
+roofline from HIP events, and the CPU oracle timed on a bounded sample of
+the same chunk.
+
+Inputs are seeded synthetic data (workloads module), resident in HBM before
+the timed region starts.  One JSON line is printed on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA prefill-chunk queries/s + TFLOP/s (% MFMA peak) at 16k ctx; decode us/step"
+PEAK_MFMA_TFLOPS = 2500.0       # MI355X dense bf16 / fp16 MFMA
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PREFILL = "glm_16k"
+DECODE = "glm_decode_8"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "attention": "sparse_attention_scores_amd/csrc/attention.hip",
+    "indexer": "sparse_attention_scores_amd/csrc/indexer.hip",
+    "topk": "sparse_attention_scores_amd/csrc/topk.hip",
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_sha(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(stage: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or
+    None if they were taken on another version of the kernel's source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)[stage]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha") != source_sha(KERNEL_SOURCES[stage]):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def work_prefill(cfg):
+    """Algorithmic work of one chunk: indexer pairs, selected keys."""
+    top_k = cfg.shape.top_k
+    pos = range(cfg.q_start, cfg.q_start + cfg.L)
+    pairs = sum(p + 1 for p in pos if p + 1 > top_k)           # scored (query, key) pairs
+    selected = sum(min(p + 1, top_k) for p in pos)             # gathered keys
+    sh = cfg.shape
+    idx_flop = 2 * sh.n_idx_heads * sh.d_idx * pairs
+    attn_flop = 2 * sh.n_heads * (sh.d_qk + sh.d_latent) * selected
+    gather_bytes = 2 * sh.d_qk * selected
+    topk_bytes = 4 * pairs + 4 * top_k * cfg.L + 4 * cfg.L
+    return dict(pairs=pairs, selected=selected, idx_flop=idx_flop, attn_flop=attn_flop,
+                gather_bytes=gather_bytes, topk_bytes=topk_bytes)
+
+
+def timed_events(fn, n: int, torch):
+    """Average duration (s) of fn() over n launches, from events recorded on
+    the current stream (the one the binding launches on)."""
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(s)
+        fn()
+        b.record(s)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / n / 1e3
+
+
+def cpu_baseline(cfg, d, rows_n: int):
+    import numpy as np
+    import oracle
+    rows = np.linspace(0, cfg.L - 1, rows_n).round().astype(np.int64)
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.prefill_chunk(d, cfg.shape, cfg.q_start, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": rows.size / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": "%d evenly spaced queries of the same 16k chunk (indexer, top-k and attention per "
+                      "query, fp64), %.1f s wall" % (rows.size, dt)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-rows", type=int, default=512, help="oracle sample size (0 = skip)")
+    ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-stages", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: there is no multi-GPU path (a chunk would shard by "
+              "query with no exchange). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import sparse_attention_scores_amd as dsa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    K, Wm = args.steps, args.warmup
+
+    # ---------------- prefill chunk (headline) ----------------
+    cfg = W.PREFILL[PREFILL]
+    sh = cfg.shape
+    log("generating", PREFILL)
+    d = W.make_prefill(cfg)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else a).cuda()
+    q, qI, w, kv, kI = (to(d[k]) for k in ("q", "qI", "w", "kv", "kI"))
+    out = torch.empty((cfg.L, sh.n_heads, sh.d_latent), dtype=torch.float32, device="cuda")
+    idx = torch.empty((cfg.L, sh.top_k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((cfg.L,), dtype=torch.int32, device="cuda")
+    ws = torch.empty((dsa.dsa_prefill_workspace_bytes(sh, cfg.L, cfg.N, cfg.q_start),), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        dsa.dsa_prefill_chunk(sh, q, qI, w, kv, kI, cfg.L, cfg.N, cfg.q_start, out, idx, cnt, ws)
+
+    log("prefill warmup", Wm)
+    for _ in range(Wm):
+        step()
+    torch.cuda.synchronize()
+    log("prefill timed", K)
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / K
+    wk = work_prefill(cfg)
+    tflops = (wk["idx_flop"] + wk["attn_flop"]) / dt / 1e12
+    result = {
+        "metric": METRIC, "value": cfg.L / dt, "unit": "queries/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": dt * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill chunk, GLM-5.x shapes: L=4096 queries at positions 12288..16383 over "
+                               "N=16384 keys; 64 heads x 576 (512 latent + 64 rope), value 512; indexer 32 x 128; "
+                               "top_k 2048", "L": cfg.L, "q_start": cfg.q_start, "N": cfg.N,
+                   "top_k": sh.top_k},
+        "tflops": tflops, "mfma_peak_frac": tflops / PEAK_MFMA_TFLOPS,
+    }
+
+    # ---------------- per-stage rooflines (same kernels, same inputs) ----------------
+    if not args.skip_stages:
+        S = torch.empty((cfg.L, cfg.N), dtype=torch.float32, device="cuda")
+        idx2 = torch.empty_like(idx)
+        cnt2 = torch.empty_like(cnt)
+        out2 = torch.empty_like(out)
+        n = max(K, 3)
+        f_idx = lambda: dsa.dsa_indexer_scores(sh, qI, kI, w, cfg.L, cfg.N, cfg.q_start, S)
+        f_topk = lambda: dsa.dsa_topk_select(sh, S, cfg.L, cfg.N, cfg.q_start, idx2, cnt2)
+        f_attn = lambda: dsa.dsa_sparse_mla_attn(sh, q, kv, idx, cnt, cfg.L, cfg.N, out2, None)
+        for f in (f_idx, f_topk, f_attn):
+            f()
+        torch.cuda.synchronize()
+        log("stage timing", n)
+        t_idx = timed_events(f_idx, n, torch)
+        t_topk = timed_events(f_topk, n, torch)
+        t_attn = timed_events(f_attn, n, torch)
+        stages = {
+            "indexer": {"kernel": "indexer_prefill_kernel<32,128>", "us": t_idx * 1e6,
+                        "tflops": wk["idx_flop"] / t_idx / 1e12,
+                        "frac": wk["idx_flop"] / t_idx / 1e12 / PEAK_MFMA_TFLOPS,
+                        "note": "standalone call also writes -inf past each query"},
+            "topk": {"kernel": "topk_prefill_kernel<16>", "us": t_topk * 1e6,
+                     "gbps": wk["topk_bytes"] / t_topk / 1e9,
+                     "frac": wk["topk_bytes"] / t_topk / 1e9 / PEAK_HBM_GBPS},
+            "attention": {"kernel": "attention_kernel<64,512,64>", "us": t_attn * 1e6,
+                          "tflops": wk["attn_flop"] / t_attn / 1e12,
+                          "frac": wk["attn_flop"] / t_attn / 1e12 / PEAK_MFMA_TFLOPS,
+                          "gather_gbps": wk["gather_bytes"] / t_attn / 1e9,
+                          "gather_hbm_frac": wk["gather_bytes"] / t_attn / 1e9 / PEAK_HBM_GBPS},
+        }
+        result["stages"] = stages
+        dom = max(("indexer", t_idx), ("topk", t_topk), ("attention", t_attn), key=lambda x: x[1])[0]
+        if dom == "topk":
+            ach, bound, unit, peak = stages["topk"]["gbps"], "hbm", "GB/s", PEAK_HBM_GBPS
+        else:
+            ach, bound, unit, peak = stages[dom]["tflops"], "mfma", "TFLOP/s", PEAK_MFMA_TFLOPS
+        result["roofline"] = {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
+                              "traffic": measured_traffic(dom), "kernel": stages[dom]["kernel"]}
+        del S, idx2, cnt2, out2
+
+    # ---------------- batched decode ----------------
+    if not args.skip_decode:
+        dc = W.DECODE[DECODE]
+        log("generating", DECODE)
+        dd = W.make_decode(dc)
+        B = len(dc.ctx)
+        dq, dqI, dw, dkv, dkI = (to(dd[k]) for k in ("q", "qI", "w", "kv", "kI"))
+        dout = torch.empty((B, sh.n_heads, sh.d_latent), dtype=torch.float32, device="cuda")
+        dws = torch.empty((dsa.dsa_decode_workspace_bytes(sh, dc.ctx),), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        dstep = lambda: dsa.dsa_decode_step(sh, dc.ctx, dq, dqI, dw, dkv, dkI, dout, None, None, dws)
+        for _ in range(Wm):
+            dstep()
+        torch.cuda.synchronize()
+        nd = max(4 * K, 20)
+        t0 = time.perf_counter()
+        for _ in range(nd):
+            dstep()
+        torch.cuda.synchronize()
+        tdec = (time.perf_counter() - t0) / nd
+        sum_ctx = int(sum(dc.ctx))
+        moved = 2 * sh.d_idx * sum_ctx + 2 * sh.d_qk * sum(min(c, sh.top_k) for c in dc.ctx)
+        result["decode"] = {"workload": "batched decode, 8 sequences x 1 query, contexts "
+                                        + ",".join(str(c) for c in dc.ctx), "us_per_step": tdec * 1e6,
+                            "steps": nd, "hbm_floor_us": moved / (PEAK_HBM_GBPS * 1e9) * 1e6}
+
+    # ---------------- CPU oracle on a bounded sample ----------------
+    if args.cpu_rows > 0:
+        log("oracle baseline", args.cpu_rows, "rows")
+        result["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -71,7 +71,12 @@ def using_library(path: str):
 
 
 def default_threads() -> int:
-    return max(1, min(os.cpu_count() or 1, 64))
+    """Host threads for the oracle: the visible cores, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:

@@ -114,11 +114,12 @@ DECODE: Dict[str, Decode] = {
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bf16 (nearest, ties to even); return uint16 bits."""
+    """Round float32 values to bf16 (nearest, ties to even); return uint16 bits.
+    uint32 arithmetic cannot overflow for finite inputs (the largest finite
+    pattern plus 0x8000 stays below 2**32)."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    r = (u.astype(np.uint64) + np.uint64(0x7FFF) + lsb.astype(np.uint64)) >> np.uint64(16)
-    return r.astype(np.uint16)
+    r = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (r >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
