@@ -8,23 +8,38 @@
 // float32 softmax over them; Decode section: the heads are the rows of one
 // product with the shared latent keys.
 //
-// Design (one block = one query, or one chunk of a query's selection):
-//  - 32 selected rows per tile are gathered with 16-byte loads (a row is 1152
-//    bytes at GLM shape) and staged in LDS twice: row-major bf16 for the
-//    score product and transposed fp16 for the value product.  The
-//    transpose happens in registers (8 keys x 8 features per thread), so
-//    both products read their MFMA operands with 16-byte LDS loads.
-//  - wave w owns heads 16w..16w+15.  Scores are S^T = K Q^T on
-//    v_mfma_f32_16x16x32_bf16 with the queries' fragments held in VGPRs; the
-//    output O^T = V^T P^T runs on v_mfma_f32_16x16x32_f16 with the O
-//    accumulators in VGPRs.  The key order inside a 32-key tile is permuted in
-//    the transposed copy so that the score accumulators of a lane are exactly
-//    its probability operand: no shuffles between the two products.
-//  - online softmax in fp32 in base 2; the output rescale is skipped when no
-//    head's running maximum moved.
+// Design (one block = one query, or one chunk of a query's selection; one
+// block per CU, four waves at GLM shape):
+//  - the selection is copied to LDS once; selected rows are then gathered 32
+//    per tile straight into LDS with global_load_lds_dwordx4 (16 bytes per
+//    lane, no registers), three tiles deep, so two tiles are in flight while
+//    one is computed.  The loads are issued from inline assembly and waited
+//    for with explicit vmcnt counts: the compiler's own wait insertion would
+//    drain every outstanding LDS load before each LDS read.
+//  - a tile is stored bf16 in two row-major regions: the Dl latent columns
+//    (one 1 KB row per gather instruction at GLM shape) and the rope columns.
+//    16-byte chunks are XOR-swizzled per row so that the score reads (16
+//    rows, one chunk) and the transposed value reads (4 rows, 2 chunks) hit
+//    distinct banks.
+//  - scores: wave w owns heads 16w..16w+15; S^T = K Q^T on
+//    v_mfma_f32_16x16x32_bf16, query fragments in VGPRs, key fragments from
+//    LDS.  Exact bf16 products, fp32 accumulation.
+//  - softmax in fp32 (base 2) by the wave that owns the head, with a lazy
+//    reference: the running maximum used for the exponentials moves only
+//    when a score exceeds it by more than 8 (probabilities stay <= 256), so
+//    the output rescale almost never runs.  The wave publishes probabilities
+//    (fp16, already in MFMA operand layout) and rescale factors in LDS.
+//  - values: wave w owns output features 128w..128w+127 of all heads, so each
+//    value element is read from LDS once per tile.  O^T = V^T P^T on
+//    v_mfma_f32_16x16x32_f16; the value fragments come from the row-major
+//    tile through ds_read_b64_tr_b16 (gfx950's transposing read: within 16
+//    lanes, lane i receives element i%4 of the rows addressed by lanes
+//    i/4 + 4k) and are converted bf16 -> fp16 in registers.  The key order of
+//    a lane's score accumulators is exactly its probability operand.
 //  - probabilities enter the value product as fp16 (11-bit significand): a
-//    bf16 probability operand would cost about 1.5e-3 relative error on its
-//    own; the latent values are exact in fp16 for |v| <= 65504.
+//    bf16 probability operand alone would cost about 1.5e-3 relative error.
+//    Latent values are exact in fp16 for |v| in [2^-14, 65504]; smaller ones
+//    become fp16 subnormals (error at most 2^-25).
 #include "dsa_kernels.h"
 
 #include <math.h>
@@ -32,219 +47,380 @@
 namespace dsa {
 namespace {
 
-constexpr int kTK = 32;   // keys per tile
+constexpr int kTK = 32;        // keys per tile
+constexpr int kRing = 3;       // tiles resident in LDS (two in flight)
+constexpr float kLazy = 8.f;   // log2 headroom before the reference maximum moves
 
 template <int NH, int DL, int DR>
 struct AttnShape {
-    static_assert(DL % 16 == 0 && DR % 8 == 0, "latent widths must be multiples of 16 / 8");
-    static constexpr int NW = (NH + 15) / 16;            // waves: 16 heads each
+    static_assert(DL % 32 == 0 && DR % 8 == 0, "latent widths must be multiples of 32 / 8");
+    static constexpr int NW = (NH + 15) / 16;            // waves: 16 heads each for the scores
     static constexpr int NT = NW * 64;
     static constexpr int DQK = DL + DR;
     static constexpr int DQKP = (DQK + 31) / 32 * 32;    // score K dim padded to the MFMA step
     static constexpr int KS = DQKP / 32;                 // score K steps
+    static constexpr int KSL = DL / 32;                  // ... of them in the latent region
     static constexpr int FB = DL / 16;                   // value feature blocks
-    static constexpr int KROW = DQKP * 2 + 16;           // LDS bytes per key row (padded)
-    static constexpr int VROW = kTK * 2 + 16;            // LDS bytes per transposed value row
-    static constexpr int LDS_K = kTK * KROW;
-    static constexpr int LDS_V = DL * VROW;
+    static constexpr int FBW = FB / NW;                  // value feature blocks per wave
+    static constexpr int CL = DL / 8;                    // 16-byte chunks of a latent row
+    static constexpr int CR = (DQKP - DL) / 8;           // chunks of a rope row (with padding)
+    static constexpr int CRD = DR / 8;                   // ... holding data
+    static constexpr int LAT_B = kTK * CL * 16;          // latent region bytes
+    static constexpr int TILE_B = LAT_B + kTK * CR * 16;
+    static constexpr int IL = kTK * CL / 64;             // gather instructions, latent region
+    static constexpr int IR = kTK * CR / 64;             // gather instructions, rope region
+    static constexpr int ILW = IL / NW;                  // latent instructions per wave
+    static constexpr int IRW = IR / NW;                  // rope instructions per wave
+    static constexpr int IPW = ILW + IRW;                // ... per wave
+    static_assert((CL & (CL - 1)) == 0 && (CR & (CR - 1)) == 0, "row chunk counts must be powers of two");
+    static_assert(64 % CL == 0 || CL % 64 == 0, "latent rows must pack whole instructions");
+    static_assert(FB % NW == 0 && IL % NW == 0 && IR % NW == 0 && kTK * CR % 64 == 0,
+                  "work must split evenly");
 };
 
-// bf16 element c (0..7) of a 16-byte piece, widened to float
-__device__ inline float bf16_at(const u32x4& d, int c) {
-    const uint32_t w = d[c >> 1];
-    return __uint_as_float((c & 1) ? (w & 0xFFFF0000u) : (w << 16));
-}
+// chunk XOR of tile row r in the latent region (rows 16 apart share it) and
+// in the rope region
+__device__ inline int swz_lat(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
+__device__ inline int swz_rope(int r) { return (r >> 1) & 7; }
 
 __device__ inline uint32_t pack_f16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
 
+// 4 bf16 (two dwords) -> 4 fp16
+__device__ inline u32x2 bf16x4_to_f16x4(const u32x2& d) {
+    u32x2 r;
+    r[0] = pack_f16(__uint_as_float(d[0] << 16), __uint_as_float(d[0] & 0xFFFF0000u));
+    r[1] = pack_f16(__uint_as_float(d[1] << 16), __uint_as_float(d[1] & 0xFFFF0000u));
+    return r;
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lds_bf16x4;
+#define DSA_LDS __attribute__((address_space(3)))
+
+__device__ inline u32x2 lds_read_tr16(const unsigned char* p) {
+    const DSA_LDS lds_bf16x4* a = (const DSA_LDS lds_bf16x4*)(p);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((DSA_LDS lds_bf16x4*)a));
+}
+
+__device__ inline uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const DSA_LDS void*)p;
+}
+
+// 16 bytes per lane from `g` to LDS at m0 + 16 * lane.  M0 is written here
+// and nowhere else in these kernels.
+__device__ inline void gather16_to_lds(const void* g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(g) : "memory");
+}
+
+// max / sum over the four lanes l, l^16, l^32, l^48 (one head's column), in
+// registers: v_permlane16_swap and v_permlane32_swap exchange 16-lane rows
+__device__ inline float max4_rows(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float sum4_rows(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int N>
+__device__ inline void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
 template <int NH, int DL, int DR>
 struct Attend {
     using C = AttnShape<NH, DL, DR>;
 
-    // Attend one query over selected rows sel[t_begin .. t_end) of a cache
-    // holding nkeys rows.  Leaves, per lane, the unnormalised output for head
-    // 16w + (lane & 15) and features 16fb + 4(lane >> 4) + i, the running
-    // maximum m2 (log2 units) and the lane's share of the exponent sum.
+    struct Smem {
+        unsigned char tile[kRing][C::TILE_B];   // gathered rows, bf16, swizzled
+        int32_t sel[kMaxTopK];                  // selection, -1 = not a key
+        u32x4 pfrag[2][C::NW][64];              // probabilities per head block, operand layout
+        float alpha[2][C::NW * 16];             // rescale factor per head, per tile parity
+        float hsum[C::NW * 16];                 // exponent sum per head (end)
+        float hmax[C::NW * 16];                 // reference maximum per head (end)
+        f32x4 rescale[C::NW][C::NW * 64];       // per-wave scratch for the rare output rescale
+    };
+
+    // Attend one query over selected rows sel_g[t_begin .. t_end) of a cache
+    // holding nkeys rows.  Leaves, per lane, the unnormalised output o[f][hb]
+    // for head 16hb + (lane & 15) and features 16(FBW w + f) + 4(lane >> 4) + i,
+    // and sm.hmax / sm.hsum per head (reference max in log2 units, sum).
     __device__ static void run(const uint16_t* __restrict__ qrow, const uint16_t* __restrict__ kv,
-                               const int32_t* __restrict__ sel, int t_begin, int t_end, int nkeys,
-                               float scale_log2, unsigned char* lds_k, unsigned char* lds_v,
-                               uint32_t* lds_mask, f32x4 (&o)[C::FB], float& m2, float& lsum) {
+                               const int32_t* __restrict__ sel_g, int t_begin, int t_end, int nkeys,
+                               float scale_log2, Smem& sm, f32x4 (&o)[C::FBW][C::NW]) {
         const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
         const int head = 16 * w + c16;
-        const u32x4 zero = {0u, 0u, 0u, 0u};
+        const int n = max(t_end - t_begin, 0);
 
+#pragma unroll
+        for (int f = 0; f < C::FBW; ++f)
+#pragma unroll
+            for (int hb = 0; hb < C::NW; ++hb) o[f][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // selection -> LDS (all loads issued before any is used); ids
+        // outside the cache become -1
+        {
+            constexpr int PER = kMaxTopK / C::NT;
+            int jv[PER];
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int t = tid + k * C::NT;
+                jv[k] = sel_g[t_begin + min(t, max(n - 1, 0))];
+            }
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int t = tid + k * C::NT;
+                if (t < n) sm.sel[t] = ((unsigned)jv[k] < (unsigned)nkeys) ? jv[k] : -1;
+            }
+        }
+        // query fragments (bf16) for this lane's head
+        const u32x4 zero = {0u, 0u, 0u, 0u};
         u32x4 qf[C::KS];
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
             const int f = 32 * ks + 8 * g;
             qf[ks] = (head < NH && f < C::DQK) ? ldg16(qrow + (int64_t)head * C::DQK + f) : zero;
         }
+        // Consume the fragments here so that every compiler-tracked load has
+        // completed before the gather loop: its LDS loads are counted by hand.
 #pragma unroll
-        for (int fb = 0; fb < C::FB; ++fb) o[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m2 = -INFINITY;
-        lsum = 0.f;
+        for (int ks = 0; ks < C::KS; ++ks) asm volatile("" :: "v"(qf[ks]));
+        float mref = -INFINITY, lsum = 0.f;   // for head `head` (replicated over g)
+        __syncthreads();
+        const int ntiles = (n + kTK - 1) / kTK;
 
-        if constexpr (C::DQKP > C::DQK) {   // K-dim padding columns stay zero
-            constexpr int PP = (C::DQKP - C::DQK) / 8;
-            for (int e = tid; e < kTK * PP; e += C::NT)
-                *reinterpret_cast<u32x4*>(lds_k + (e / PP) * C::KROW + 2 * C::DQK + 16 * (e % PP)) = zero;
-        }
+        // Gather tile `it`: latent instruction i covers slots i*64 .. i*64+63
+        // of the latent region (row slot / CL, physical chunk slot % CL), rope
+        // instruction i likewise in the rope region.  Masked keys read row 0;
+        // padding chunks read chunk 0 (they meet zero query columns).
+        auto gather = [&](int it) {
+            unsigned char* buf = sm.tile[it % kRing];
+#pragma unroll
+            for (int k = 0; k < C::ILW; ++k) {
+                const int i = C::ILW * w + k;
+                const int slot = i * 64 + l;
+                const int r = slot / C::CL, pc = slot % C::CL;
+                const int c = pc ^ (swz_lat(r) & (C::CL - 1));
+                const int j = max(sm.sel[min(it * kTK + r, n - 1)], 0);
+                gather16_to_lds(kv + (int64_t)j * C::DQK + 8 * c, lds_addr(buf + 1024 * i));
+            }
+#pragma unroll
+            for (int k = 0; k < C::IRW; ++k) {
+                const int i = C::IRW * w + k;
+                const int slot = i * 64 + l;
+                const int r = slot / C::CR, pc = slot % C::CR;
+                const int c = pc ^ (swz_rope(r) & (C::CR - 1));
+                const int j = max(sm.sel[min(it * kTK + r, n - 1)], 0);
+                gather16_to_lds(kv + (int64_t)j * C::DQK + DL + 8 * (c < C::CRD ? c : 0),
+                                lds_addr(buf + C::LAT_B + 1024 * i));
+            }
+        };
 
-        for (int t0 = t_begin; t0 < t_end; t0 += kTK) {
-            // ---- gather the tile: latent part as 8x8 blocks, transposed copy in fp16
-            constexpr int FO = DL / 8;
-            for (int bi = tid; bi < 4 * FO; bi += C::NT) {
-                const int ko = bi & 3, fo = bi >> 2;
-                // key k of the tile sits at 8((k%16)/4) + 4(k/16) + k%4 in a value row:
-                // keys 8ko+0..3 at pa.., keys 8ko+4..7 at pa+8..
-                const int pa = 16 * (ko & 1) + 4 * (ko >> 1);
+        // per-lane LDS offsets.  Score reads: row 16mb + c16 (swizzle depends
+        // on c16 only), logical chunk 4ks + g.
+        const int xl = swz_lat(c16) & (C::CL - 1);
+        int qlat[4];
 #pragma unroll
-                for (int hv = 0; hv < 2; ++hv) {
-                    u32x4 d[4];
+        for (int k = 0; k < 4; ++k) qlat[k] = c16 * C::CL * 16 + 16 * (((4 * k + g) ^ xl) & 15);
+        const int xr = swz_rope(c16) & (C::CR - 1);
+        int qrope[2];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = t0 + 8 * ko + 4 * hv + r;
-                        const int j = sel[min(t, t_end - 1)];
-                        const bool ok = t < t_end && (unsigned)j < (unsigned)nkeys;
-                        d[r] = ldg16(kv + (int64_t)(ok ? j : 0) * C::DQK + 8 * fo);   // row 0 always exists
-                        if (!ok) d[r] = zero;
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        *reinterpret_cast<u32x4*>(lds_k + (8 * ko + 4 * hv + r) * C::KROW + 16 * fo) = d[r];
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        u32x2 v;
-                        v[0] = pack_f16(bf16_at(d[0], c), bf16_at(d[1], c));
-                        v[1] = pack_f16(bf16_at(d[2], c), bf16_at(d[3], c));
-                        *reinterpret_cast<u32x2*>(lds_v + (8 * fo + c) * C::VROW + 2 * (pa + 8 * hv)) = v;
-                    }
-                }
-            }
-            constexpr int RO = DR / 8;
-            for (int ci = tid; ci < kTK * RO; ci += C::NT) {
-                const int key = ci / RO, part = ci % RO;
-                const int t = t0 + key;
-                const int j = sel[min(t, t_end - 1)];
-                const bool ok = t < t_end && (unsigned)j < (unsigned)nkeys;
-                u32x4 d = ldg16(kv + (int64_t)(ok ? j : 0) * C::DQK + DL + 8 * part);
-                if (!ok) d = zero;
-                *reinterpret_cast<u32x4*>(lds_k + key * C::KROW + 2 * DL + 16 * part) = d;
-            }
-            if (tid < 64) {
-                const int t = t0 + tid;
-                const int j = sel[min(t, t_end - 1)];
-                const uint64_t bm = __ballot(tid < kTK && t < t_end && (unsigned)j < (unsigned)nkeys);
-                if (tid == 0) *lds_mask = (uint32_t)bm;
-            }
-            __syncthreads();
+        for (int k = 0; k < 2; ++k) qrope[k] = C::LAT_B + c16 * C::CR * 16 + 16 * ((4 * k + g) ^ xr);
+        // transposed reads: rows 16h + 4g + (c16 >> 2), features
+        // 16fb + 4(c16 & 3): logical chunk 2fb + ((c16 >> 1) & 1), half c16 & 1
+        const int trow = 4 * g + (c16 >> 2);
+        const int vx = (swz_lat(trow) & (C::CL - 1)) ^ ((c16 >> 1) & 1);
+        const int vrow = trow * C::CL * 16 + 8 * (c16 & 1);
 
-            // ---- scores: S^T[key][head] for keys 0-15 (s0) and 16-31 (s1)
-            const uint32_t vmask = *lds_mask;
-            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        auto key_frag = [&](const unsigned char* tile, int ks, u32x4 (&dst)[2]) {
+            int off;
+            if (ks < C::KSL) {
+                // logical chunk 4ks + g: bits 0..3 swizzled, bits 4.. untouched
+                const int lo = (C::CL >= 16) ? qlat[ks & 3] + 256 * (ks >> 2)
+                                             : c16 * C::CL * 16 + 16 * ((4 * ks + g) ^ xl);
+                off = lo;
+            } else {
+                off = qrope[(ks - C::KSL) & 1] + 128 * ((ks - C::KSL) >> 1);
+            }
+            const int rs = (ks < C::KSL) ? C::CL * 16 : C::CR * 16;   // bytes per row
+            dst[0] = *reinterpret_cast<const u32x4*>(tile + off);
+            dst[1] = *reinterpret_cast<const u32x4*>(tile + off + 16 * rs);
+        };
+
+        // Scores of tile `it` for this wave's heads, then the softmax update;
+        // publishes probabilities and rescale factors under parity it & 1.
+        auto score_tile = [&](int it) {
+            const unsigned char* tile = sm.tile[it % kRing];
+            const int t0 = it * kTK;
+            // validity of the tile's 32 keys (every wave computes the same mask)
+            const uint32_t vmask =
+                (uint32_t)__ballot(l < kTK && t0 + l < n && sm.sel[min(t0 + l, n - 1)] >= 0);
+            f32x4 s[2] = {};
+            u32x4 ka[3][2];   // key fragments, two k-steps ahead of their MFMAs
+            key_frag(tile, 0, ka[0]);
+            if (C::KS > 1) key_frag(tile, 1, ka[1]);
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
-                const u32x4 a0 = *reinterpret_cast<const u32x4*>(lds_k + c16 * C::KROW + 64 * ks + 16 * g);
-                const u32x4 a1 = *reinterpret_cast<const u32x4*>(lds_k + (16 + c16) * C::KROW + 64 * ks + 16 * g);
-                s0 = mfma16_bf16(a0, qf[ks], s0);
-                s1 = mfma16_bf16(a1, qf[ks], s1);
+                if (ks + 2 < C::KS) key_frag(tile, ks + 2, ka[(ks + 2) % 3]);
+                s[0] = mfma16_bf16(ka[ks % 3][0], qf[ks], s[0]);
+                s[1] = mfma16_bf16(ka[ks % 3][1], qf[ks], s[1]);
             }
-            // lane (g, c16) holds keys 4g+i (s0) and 16+4g+i (s1) of head c16
             float x[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[i] = ((vmask >> (4 * g + i)) & 1u) ? s0[i] * scale_log2 : -INFINITY;
-                x[4 + i] = ((vmask >> (16 + 4 * g + i)) & 1u) ? s1[i] * scale_log2 : -INFINITY;
-            }
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    x[4 * mb + i] = ((vmask >> (16 * mb + 4 * g + i)) & 1u) ? s[mb][i] * scale_log2 : -INFINITY;
             float mx = x[0];
 #pragma unroll
             for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(m2, mx);
-            // all keys so far masked: keep the state at zero without NaNs
-            const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-            const float alpha = exp2f(m2 - mref);
+            mx = max4_rows(mx);
+            // lazy reference: move it only when a score clears it by kLazy;
+            // alpha 0 (first valid tile) needs no rescale: the output is zero
+            float alpha = 1.f;
+            if (mx > mref + kLazy) {
+                alpha = (mref == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mref - mx);
+                mref = mx;
+            }
+            const float mbase = (mref == -INFINITY) ? 0.f : mref;
             float p[8], ps = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) { p[i] = exp2f(x[i] - mref); ps += p[i]; }
+            // arguments are <= kLazy; v_exp_f32 returns 0 for -inf
+            for (int i = 0; i < 8; ++i) { p[i] = __builtin_amdgcn_exp2f(x[i] - mbase); ps += p[i]; }
             lsum = lsum * alpha + ps;
-            if (__ballot(alpha != 1.f)) {   // wave-uniform: skip when no maximum moved
-#pragma unroll
-                for (int fb = 0; fb < C::FB; ++fb) o[fb] *= alpha;
-            }
-            m2 = mnew;
             u32x4 pb;
             pb[0] = pack_f16(p[0], p[1]);
             pb[1] = pack_f16(p[2], p[3]);
             pb[2] = pack_f16(p[4], p[5]);
             pb[3] = pack_f16(p[6], p[7]);
-            // ---- values: O^T[feature][head] += V^T[feature][keys] P^T[keys][head]
+            sm.pfrag[it & 1][w][l] = pb;
+            if (g == 0) sm.alpha[it & 1][head] = alpha;
+        };
+
+        // Values of tile `it` for this wave's features, all heads.
+        auto value_tile = [&](int it) {
+            const unsigned char* tile = sm.tile[it % kRing];
+            u32x4 pf[C::NW];
+            float al[C::NW];
+            bool moved = false;
 #pragma unroll
-            for (int fb = 0; fb < C::FB; ++fb) {
-                const u32x4 av = *reinterpret_cast<const u32x4*>(lds_v + (16 * fb + c16) * C::VROW + 16 * g);
-                o[fb] = mfma16_f16(av, pb, o[fb]);
+            for (int hb = 0; hb < C::NW; ++hb) {
+                pf[hb] = sm.pfrag[it & 1][hb][l];
+                al[hb] = sm.alpha[it & 1][16 * hb + c16];
+                moved |= al[hb] != 1.f;
             }
+            if (__ballot(moved)) {   // wave-uniform and rare
+                // Rescale through a per-wave LDS scratch: the accumulators are
+                // only stored and reloaded here, never read by VALU, so the
+                // compiler can keep them in AGPRs on the hot path.
+                f32x4* scratch = sm.rescale[w];
+#pragma unroll
+                for (int f = 0; f < C::FBW; ++f) {
+#pragma unroll
+                    for (int hb = 0; hb < C::NW; ++hb) scratch[hb * 64 + l] = o[f][hb];
+                    asm volatile("" ::: "memory");
+#pragma unroll
+                    for (int hb = 0; hb < C::NW; ++hb) o[f][hb] = scratch[hb * 64 + l] * al[hb];
+                    asm volatile("" ::: "memory");
+                }
+            }
+#pragma unroll
+            for (int f = 0; f < C::FBW; ++f) {
+                const int fb = C::FBW * w + f;
+                // logical chunk 2fb + tb, swizzled in its aligned group of 16
+                const int off = vrow + 16 * (((2 * fb) & ~15) + (((2 * fb) & 15) ^ vx));
+                const u32x2 v0 = bf16x4_to_f16x4(lds_read_tr16(tile + off));
+                const u32x2 v1 = bf16x4_to_f16x4(lds_read_tr16(tile + off + 16 * C::CL * 16));
+                const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
+#pragma unroll
+                for (int hb = 0; hb < C::NW; ++hb) o[f][hb] = mfma16_f16(av, pf[hb], o[f][hb]);
+            }
+        };
+
+        // Pipeline: iteration it scores tile it+1 and accumulates the values
+        // of tile it (scored one iteration earlier) while tile it+2 is being
+        // gathered.  One barrier per tile.
+        if (ntiles > 0) {
+            gather(0);
+            if (ntiles > 1) { gather(1); wait_vmcnt<C::IPW>(); }
+            else wait_vmcnt<0>();
             __syncthreads();
+            score_tile(0);
         }
-        lsum += __shfl_xor(lsum, 16);
-        lsum += __shfl_xor(lsum, 32);
+        for (int it = 0; it < ntiles; ++it) {
+            if (it + 1 < ntiles) wait_vmcnt<0>();   // tile it+1 (the only gather in flight)
+            __syncthreads();   // probabilities of tile it and tile it+1 visible; tile it-1 free
+            if (it + 2 < ntiles) gather(it + 2);   // into tile it-1's buffer
+            if (it + 1 < ntiles) score_tile(it + 1);
+            value_tile(it);
+        }
+        lsum = sum4_rows(lsum);
+        if (g == 0) { sm.hsum[head] = lsum; sm.hmax[head] = mref; }
+        __syncthreads();
     }
 };
 
 template <int NH, int DL, int DR>
-__global__ __launch_bounds__((AttnShape<NH, DL, DR>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__((AttnShape<NH, DL, DR>::NT)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attention_kernel(AttnArgs a) {
     using C = AttnShape<NH, DL, DR>;
-    __shared__ __attribute__((aligned(16))) unsigned char lds_k[C::LDS_K];
-    __shared__ __attribute__((aligned(16))) unsigned char lds_v[C::LDS_V];
-    __shared__ uint32_t lds_mask;
+    __shared__ __attribute__((aligned(16))) typename Attend<NH, DL, DR>::Smem sm;
     const int row = blockIdx.x;
     const int cnt = min(max(a.count[row], 0), a.top_k);
-    f32x4 o[C::FB];
-    float m2, lsum;
+    f32x4 o[C::FBW][C::NW];
     Attend<NH, DL, DR>::run(a.q + (int64_t)row * NH * C::DQK, a.kv, a.idx + (int64_t)row * a.top_k, 0, cnt,
-                            a.N, a.scale_log2, lds_k, lds_v, &lds_mask, o, m2, lsum);
-    const int l = threadIdx.x & 63, g = l >> 4;
-    const int head = 16 * (threadIdx.x >> 6) + (l & 15);
-    if (head >= NH) return;
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    float* orow = a.out + ((int64_t)row * NH + head) * DL;
+                            a.N, a.scale_log2, sm, o);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, c16 = l & 15;
 #pragma unroll
-    for (int fb = 0; fb < C::FB; ++fb) *reinterpret_cast<f32x4*>(orow + 16 * fb + 4 * g) = o[fb] * inv;
-    if (a.lse && g == 0)
-        a.lse[(int64_t)row * NH + head] = lsum > 0.f ? (m2 + log2f(lsum)) * 0.69314718055994531f : -INFINITY;
+    for (int hb = 0; hb < C::NW; ++hb) {
+        const int head = 16 * hb + c16;
+        if (head >= NH) continue;
+        const float ls = sm.hsum[head];
+        const float inv = ls > 0.f ? 1.f / ls : 0.f;
+        float* orow = a.out + ((int64_t)row * NH + head) * DL;
+#pragma unroll
+        for (int f = 0; f < C::FBW; ++f)
+            *reinterpret_cast<f32x4*>(orow + 16 * (C::FBW * w + f) + 4 * g) = o[f][hb] * inv;
+    }
+    if (a.lse && threadIdx.x < NH) {
+        const float ls = sm.hsum[threadIdx.x];
+        a.lse[(int64_t)row * NH + threadIdx.x] =
+            ls > 0.f ? (sm.hmax[threadIdx.x] + log2f(ls)) * 0.69314718055994531f : -INFINITY;
+    }
 }
 
 template <int NH, int DL, int DR>
-__global__ __launch_bounds__((AttnShape<NH, DL, DR>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__((AttnShape<NH, DL, DR>::NT)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attention_split_kernel(AttnSplitArgs a, SeqMeta m) {
     using C = AttnShape<NH, DL, DR>;
-    __shared__ __attribute__((aligned(16))) unsigned char lds_k[C::LDS_K];
-    __shared__ __attribute__((aligned(16))) unsigned char lds_v[C::LDS_V];
-    __shared__ uint32_t lds_mask;
+    __shared__ __attribute__((aligned(16))) typename Attend<NH, DL, DR>::Smem sm;
     const int item = blockIdx.x;
     const int b = seq_of_block(m, item);
     const int ctx = m.ctx[b];
     const int cnt = min(ctx, a.top_k);
     const int t_begin = (item - m.blk0[b]) * a.chunk;
     const int t_end = min(t_begin + a.chunk, cnt);
-    f32x4 o[C::FB];
-    float m2, lsum;
+    f32x4 o[C::FBW][C::NW];
     Attend<NH, DL, DR>::run(a.q + (int64_t)b * NH * C::DQK, a.kv + m.key_off[b] * C::DQK,
-                            a.idx + (int64_t)b * a.top_k, t_begin, t_end, ctx, a.scale_log2, lds_k, lds_v,
-                            &lds_mask, o, m2, lsum);
-    const int l = threadIdx.x & 63, g = l >> 4;
-    const int head = 16 * (threadIdx.x >> 6) + (l & 15);
-    if (head >= NH) return;
-    float* orow = a.part_o + ((int64_t)item * NH + head) * DL;
+                            a.idx + (int64_t)b * a.top_k, t_begin, t_end, ctx, a.scale_log2, sm, o);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, c16 = l & 15;
 #pragma unroll
-    for (int fb = 0; fb < C::FB; ++fb) *reinterpret_cast<f32x4*>(orow + 16 * fb + 4 * g) = o[fb];
-    if (g == 0) {
-        a.part_ml[((int64_t)item * NH + head) * 2 + 0] = m2;
-        a.part_ml[((int64_t)item * NH + head) * 2 + 1] = lsum;
+    for (int hb = 0; hb < C::NW; ++hb) {
+        const int head = 16 * hb + c16;
+        if (head >= NH) continue;
+        float* orow = a.part_o + ((int64_t)item * NH + head) * DL;
+#pragma unroll
+        for (int f = 0; f < C::FBW; ++f)
+            *reinterpret_cast<f32x4*>(orow + 16 * (C::FBW * w + f) + 4 * g) = o[f][hb];
+    }
+    if (threadIdx.x < NH) {
+        a.part_ml[((int64_t)item * NH + threadIdx.x) * 2 + 0] = sm.hmax[threadIdx.x];
+        a.part_ml[((int64_t)item * NH + threadIdx.x) * 2 + 1] = sm.hsum[threadIdx.x];
     }
 }
 
