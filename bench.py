@@ -58,6 +58,107 @@ def measured_traffic(stage: str):
     return t.get("bytes_per_launch")
 
 
+PROFILE_STAGES = ("prefill", "indexer", "topk", "attention", "decode", "copy")
+COPY_BYTES = 1 << 30            # plain copy used to scale the HBM byte counters
+STAGE_KERNELS = {
+    "attention": "attention_kernel<",
+    "indexer": "indexer_prefill_kernel<",
+    "topk": "topk_prefill_kernel<",
+}
+
+
+def profile_stage(stage, reps, np, torch, dsa, W) -> int:
+    """Run one stage of the headline chunk reps times and nothing else that
+    matters (inputs are generated first).  `copy` runs a plain device copy of
+    COPY_BYTES, whose counter readings scale FETCH_SIZE / WRITE_SIZE."""
+    if stage == "copy":
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(reps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy done", reps)
+        return 0
+    if stage == "decode":
+        dc = W.DECODE[DECODE]
+        sh = dc.shape
+        dd = W.make_decode(dc)
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else a).cuda()
+        dq, dqI, dw, dkv, dkI = (to(dd[k]) for k in ("q", "qI", "w", "kv", "kI"))
+        dout = torch.empty((len(dc.ctx), sh.n_heads, sh.d_latent), dtype=torch.float32, device="cuda")
+        dws = torch.empty((dsa.dsa_decode_workspace_bytes(sh, dc.ctx),), dtype=torch.uint8, device="cuda")
+        for _ in range(reps):
+            dsa.dsa_decode_step(sh, dc.ctx, dq, dqI, dw, dkv, dkI, dout, None, None, dws)
+        torch.cuda.synchronize()
+        log("decode done", reps)
+        return 0
+    cfg = W.PREFILL[PREFILL]
+    sh = cfg.shape
+    d = W.make_prefill(cfg)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else a).cuda()
+    q, qI, w, kv, kI = (to(d[k]) for k in ("q", "qI", "w", "kv", "kI"))
+    out = torch.empty((cfg.L, sh.n_heads, sh.d_latent), dtype=torch.float32, device="cuda")
+    idx = torch.empty((cfg.L, sh.top_k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((cfg.L,), dtype=torch.int32, device="cuda")
+    if stage == "prefill":
+        ws = torch.empty((dsa.dsa_prefill_workspace_bytes(sh, cfg.L, cfg.N, cfg.q_start),), dtype=torch.uint8,
+                         device="cuda")
+        f = lambda: dsa.dsa_prefill_chunk(sh, q, qI, w, kv, kI, cfg.L, cfg.N, cfg.q_start, out, idx, cnt, ws)
+    else:
+        S = torch.empty((cfg.L, cfg.N), dtype=torch.float32, device="cuda")
+        if stage != "indexer":
+            dsa.dsa_indexer_scores(sh, qI, kI, w, cfg.L, cfg.N, cfg.q_start, S)
+        if stage == "attention":
+            dsa.dsa_topk_select(sh, S, cfg.L, cfg.N, cfg.q_start, idx, cnt)
+        f = {"indexer": lambda: dsa.dsa_indexer_scores(sh, qI, kI, w, cfg.L, cfg.N, cfg.q_start, S),
+             "topk": lambda: dsa.dsa_topk_select(sh, S, cfg.L, cfg.N, cfg.q_start, idx, cnt),
+             "attention": lambda: dsa.dsa_sparse_mla_attn(sh, q, kv, idx, cnt, cfg.L, cfg.N, out, None)}[stage]
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        f()
+    torch.cuda.synchronize()
+    log(stage, "done", reps)
+    return 0
+
+
+def _counter_per_dispatch(path: str, name_part, counter: str):
+    """Median over dispatches of one counter (rocprofv3 counter_collection
+    CSV), for kernels whose name holds name_part (None: every dispatch)."""
+    import csv
+    import statistics
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and (name_part is None or name_part in r["Kernel_Name"])]
+    if not vals:
+        raise SystemExit("no %s rows for %s in %s" % (counter, name_part, path))
+    return statistics.median(vals), len(vals)
+
+
+def write_traffic(d: str) -> int:
+    """profiles/traffic.json from the counter runs in d:
+    {stage}_fetch / {stage}_write and copy_fetch / copy_write, each made by
+    `rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE -o <name> -- python3 bench.py --profile-stage <stage>`.
+    Counters read KiB per dispatch; each is scaled by what it reads for a copy
+    of COPY_BYTES (which reads and writes exactly that much)."""
+    f = lambda n: os.path.join(d, n + "_counter_collection.csv")
+    cf, _ = _counter_per_dispatch(f("copy_fetch"), None, "FETCH_SIZE")
+    cw, _ = _counter_per_dispatch(f("copy_write"), None, "WRITE_SIZE")
+    kf, kw = cf * 1024 / COPY_BYTES, cw * 1024 / COPY_BYTES
+    res = {"copy": {"bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw, "fetch_factor": kf, "write_factor": kw}}
+    for stage, kname in STAGE_KERNELS.items():
+        if not os.path.exists(f(stage + "_fetch")) or not os.path.exists(f(stage + "_write")):
+            continue
+        fk, n1 = _counter_per_dispatch(f(stage + "_fetch"), kname, "FETCH_SIZE")
+        wk, n2 = _counter_per_dispatch(f(stage + "_write"), kname, "WRITE_SIZE")
+        fb, wb = fk * 1024 / kf, wk * 1024 / kw
+        res[stage] = {"source_sha": source_sha(KERNEL_SOURCES[stage]), "fetch_kib": fk, "write_kib": wk,
+                      "dispatches": [n1, n2], "fetch_bytes": fb, "write_bytes": wb,
+                      "bytes_per_launch": fb + wb}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res))
+    return 0
+
+
 def work_prefill(cfg):
     """Algorithmic work of one chunk: indexer pairs, selected keys."""
     top_k = cfg.shape.top_k
@@ -104,7 +205,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-rows", type=int, default=512, help="oracle sample size (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle sample size (0 = skip)")
+    ap.add_argument("--profile-stage", choices=PROFILE_STAGES,
+                    help="only run one stage (or a plain copy) --steps times, for rocprofv3 counter runs")
+    ap.add_argument("--write-traffic", metavar="DIR",
+                    help="turn FETCH_SIZE/WRITE_SIZE counter CSVs in DIR into profiles/traffic.json")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-stages", action="store_true")
     args = ap.parse_args()
@@ -112,6 +217,8 @@ def main() -> int:
         print("bench.py measures one GPU only: there is no multi-GPU path (a chunk would shard by "
               "query with no exchange). Run with --gpus 1.", file=sys.stderr)
         return 2
+    if args.write_traffic:
+        return write_traffic(args.write_traffic)
 
     import numpy as np
     import torch
@@ -122,6 +229,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     K, Wm = args.steps, args.warmup
+    if args.profile_stage:
+        return profile_stage(args.profile_stage, K, np, torch, dsa, W)
 
     # ---------------- prefill chunk (headline) ----------------
     cfg = W.PREFILL[PREFILL]
