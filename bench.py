@@ -294,7 +294,7 @@ def main() -> int:
                         "tflops": wk["idx_flop"] / t_idx / 1e12,
                         "frac": wk["idx_flop"] / t_idx / 1e12 / PEAK_MFMA_TFLOPS,
                         "note": "standalone call also writes -inf past each query"},
-            "topk": {"kernel": "topk_prefill_kernel<16>", "us": t_topk * 1e6,
+            "topk": {"kernel": "topk_prefill_kernel<512,32>", "us": t_topk * 1e6,
                      "gbps": wk["topk_bytes"] / t_topk / 1e9,
                      "frac": wk["topk_bytes"] / t_topk / 1e9 / PEAK_HBM_GBPS},
             "attention": {"kernel": "attention_kernel<64,512,64>", "us": t_attn * 1e6,

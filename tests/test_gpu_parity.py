@@ -128,6 +128,39 @@ def test_topk_ties_and_sizes(N, top_k, levels):
     assert np.array_equal(host(idx), ref_idx)
 
 
+@pytest.mark.parametrize("case", ["inf", "wide", "tiny_range", "denormal"])
+def test_topk_extreme_values(case):
+    """Rows the value-binned levels cannot split (infinities, ranges too wide
+    or too narrow for fp32 bins, denormals): the exact fallback must still
+    match the brute-force oracle bit for bit."""
+    import dataclasses
+    import torch
+    rng = np.random.default_rng({"inf": 1, "wide": 2, "tiny_range": 3, "denormal": 4}[case])
+    L, N, top_k = 5, 12000, 2048
+    if case == "inf":
+        S = rng.integers(-50, 50, size=(L, N)).astype(np.float32)
+        S[:, rng.choice(N, 300, replace=False)] = np.inf
+        S[:, rng.choice(N, 300, replace=False)] = -np.inf
+    elif case == "wide":
+        S = (rng.standard_normal((L, N)) * 10.0 ** rng.integers(-30, 30, size=(L, N))).astype(np.float32)
+        S[:, :3] = [3.0e38, -3.0e38, 1.0e-38]
+    elif case == "tiny_range":
+        base = np.float32(1000.0)
+        S = (base + rng.integers(0, 40, size=(L, N)).astype(np.float32) * np.float32(2.0 ** -13)).astype(np.float32)
+    else:
+        S = (rng.integers(-1000, 1000, size=(L, N)) * np.float32(1e-42)).astype(np.float32)
+    q_start = N - L
+    pos = q_start + np.arange(L)
+    ref_idx, ref_cnt = oracle.topk_select(S, pos, top_k)
+    shape = dataclasses.replace(W.GLM, top_k=top_k)
+    idx = torch.empty((L, top_k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((L,), dtype=torch.int32, device="cuda")
+    say("topk-extreme", case)
+    lib().dsa_topk_select(shape, dev(S), L, N, q_start, idx, cnt)
+    assert np.array_equal(host(cnt), ref_cnt)
+    assert np.array_equal(host(idx), ref_idx)
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_topk_full_sampled_bit_exact(name):
     import torch
