@@ -9,33 +9,36 @@
 // product with the shared latent keys.
 //
 // Design (one block = one query, or one chunk of a query's selection; one
-// block per CU, four waves at GLM shape):
+// block per CU; at GLM shape eight waves, two per SIMD):
+//  - producer waves (the first half) own the scores: wave w holds the query
+//    fragments of heads 16w..16w+15, computes S^T = K Q^T for each tile on
+//    v_mfma_f32_16x16x32_bf16 and runs the softmax; consumer waves (the
+//    second half) own the output: consumer c accumulates features
+//    128c..128c+127 of all heads.  The split keeps each wave under 256
+//    registers, so a SIMD holds one wave of each kind and the matrix pipe
+//    is fed by one while the other waits on LDS or runs its softmax.
 //  - the selection is copied to LDS once; selected rows are then gathered 32
 //    per tile straight into LDS with global_load_lds_dwordx4 (16 bytes per
 //    lane, no registers), three tiles deep, so two tiles are in flight while
 //    one is computed.  The loads are issued from inline assembly and waited
 //    for with explicit vmcnt counts: the compiler's own wait insertion would
-//    drain every outstanding LDS load before each LDS read.
+//    drain every outstanding LDS load before each LDS read.  A 1 KB latent
+//    row is one instruction with a scalar row address.
 //  - a tile is stored bf16 in two row-major regions: the Dl latent columns
-//    (one 1 KB row per gather instruction at GLM shape) and the rope columns.
-//    16-byte chunks are XOR-swizzled per row so that the score reads (16
-//    rows, one chunk) and the transposed value reads (4 rows, 2 chunks) hit
-//    distinct banks.
-//  - scores: wave w owns heads 16w..16w+15; S^T = K Q^T on
-//    v_mfma_f32_16x16x32_bf16, query fragments in VGPRs, key fragments from
-//    LDS.  Exact bf16 products, fp32 accumulation.
-//  - softmax in fp32 (base 2) by the wave that owns the head, with a lazy
-//    reference: the running maximum used for the exponentials moves only
-//    when a score exceeds it by more than 8 (probabilities stay <= 256), so
-//    the output rescale almost never runs.  The wave publishes probabilities
-//    (fp16, already in MFMA operand layout) and rescale factors in LDS.
-//  - values: wave w owns output features 128w..128w+127 of all heads, so each
-//    value element is read from LDS once per tile.  O^T = V^T P^T on
-//    v_mfma_f32_16x16x32_f16; the value fragments come from the row-major
-//    tile through ds_read_b64_tr_b16 (gfx950's transposing read: within 16
-//    lanes, lane i receives element i%4 of the rows addressed by lanes
-//    i/4 + 4k) and are converted bf16 -> fp16 in registers.  The key order of
-//    a lane's score accumulators is exactly its probability operand.
+//    and the rope columns.  16-byte chunks are XOR-swizzled per row so that
+//    the score reads (16 rows, one chunk) and the transposed value reads
+//    (4 rows, 2 chunks) hit distinct banks.
+//  - softmax in fp32 (base 2) with a lazy reference: the running maximum
+//    used for the exponentials moves only when a score exceeds it by more
+//    than 8 (probabilities stay <= 256), so the output rescale almost never
+//    runs.  Producers publish probabilities (fp16, already in MFMA operand
+//    layout) and rescale factors in LDS; one barrier per tile.
+//  - values: O^T = V^T P^T on v_mfma_f32_16x16x32_f16; the value fragments
+//    come from the row-major tile through ds_read_b64_tr_b16 (gfx950's
+//    transposing read: within 16 lanes, lane i receives element i%4 of the
+//    rows addressed by lanes i/4 + 4k) and are converted bf16 -> fp16 in
+//    registers.  The key order of a producer lane's score accumulators is
+//    exactly the consumer's probability operand.
 //  - probabilities enter the value product as fp16 (11-bit significand): a
 //    bf16 probability operand alone would cost about 1.5e-3 relative error.
 //    Latent values are exact in fp16 for |v| in [2^-14, 65504]; smaller ones
@@ -54,14 +57,15 @@ constexpr float kLazy = 8.f;   // log2 headroom before the reference maximum mov
 template <int NH, int DL, int DR>
 struct AttnShape {
     static_assert(DL % 32 == 0 && DR % 8 == 0, "latent widths must be multiples of 32 / 8");
-    static constexpr int NW = (NH + 15) / 16;            // waves: 16 heads each for the scores
-    static constexpr int NT = NW * 64;
+    static constexpr int NHB = (NH + 15) / 16;           // head blocks = producer waves = consumer waves
+    static constexpr int NWAVE = 2 * NHB;
+    static constexpr int NT = NWAVE * 64;
     static constexpr int DQK = DL + DR;
     static constexpr int DQKP = (DQK + 31) / 32 * 32;    // score K dim padded to the MFMA step
     static constexpr int KS = DQKP / 32;                 // score K steps
     static constexpr int KSL = DL / 32;                  // ... of them in the latent region
     static constexpr int FB = DL / 16;                   // value feature blocks
-    static constexpr int FBW = FB / NW;                  // value feature blocks per wave
+    static constexpr int FBW = FB / NHB;                 // value feature blocks per consumer
     static constexpr int CL = DL / 8;                    // 16-byte chunks of a latent row
     static constexpr int CR = (DQKP - DL) / 8;           // chunks of a rope row (with padding)
     static constexpr int CRD = DR / 8;                   // ... holding data
@@ -69,12 +73,10 @@ struct AttnShape {
     static constexpr int TILE_B = LAT_B + kTK * CR * 16;
     static constexpr int IL = kTK * CL / 64;             // gather instructions, latent region
     static constexpr int IR = kTK * CR / 64;             // gather instructions, rope region
-    static constexpr int ILW = IL / NW;                  // latent instructions per wave
-    static constexpr int IRW = IR / NW;                  // rope instructions per wave
-    static constexpr int IPW = ILW + IRW;                // ... per wave
+    static constexpr int ILW = IL / NWAVE;               // latent instructions per wave
     static_assert((CL & (CL - 1)) == 0 && (CR & (CR - 1)) == 0, "row chunk counts must be powers of two");
-    static_assert(64 % CL == 0 || CL % 64 == 0, "latent rows must pack whole instructions");
-    static_assert(FB % NW == 0 && IL % NW == 0 && IR % NW == 0 && kTK * CR % 64 == 0,
+    static_assert(64 % CL == 0 || CL == 64, "latent rows must pack whole instructions");
+    static_assert(FB % NHB == 0 && IL % NWAVE == 0 && IR <= NWAVE && kTK * CR % 64 == 0,
                   "work must split evenly");
 };
 
@@ -107,11 +109,12 @@ __device__ inline uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const DSA_LDS void*)p;
 }
 
-// 16 bytes per lane from `g` to LDS at m0 + 16 * lane.  M0 is written here
-// and nowhere else in these kernels.
-__device__ inline void gather16_to_lds(const void* g, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(g) : "memory");
+// 16 bytes per lane from base + voff (a uniform 64-bit base, a per-lane
+// 32-bit offset) to LDS at m0 + 16 * lane.  M0 is written here and nowhere
+// else in these kernels.
+__device__ inline void gather16_to_lds(const void* base, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(base) : "memory");
 }
 
 // max / sum over the four lanes l, l^16, l^32, l^48 (one head's column), in
@@ -139,46 +142,127 @@ struct Attend {
     struct Smem {
         unsigned char tile[kRing][C::TILE_B];   // gathered rows, bf16, swizzled
         int32_t sel[kMaxTopK];                  // selection, -1 = not a key
-        u32x4 pfrag[2][C::NW][64];              // probabilities per head block, operand layout
-        float alpha[2][C::NW * 16];             // rescale factor per head, per tile parity
-        float hsum[C::NW * 16];                 // exponent sum per head (end)
-        float hmax[C::NW * 16];                 // reference maximum per head (end)
-        f32x4 rescale[C::NW][C::NW * 64];       // per-wave scratch for the rare output rescale
+        u32x4 pfrag[2][C::NHB][64];             // probabilities per head block, operand layout
+        float alpha[2][C::NHB * 16];            // rescale factor per head, per tile parity
+        float hsum[C::NHB * 16];                // exponent sum per head (end)
+        float hmax[C::NHB * 16];                // reference maximum per head (end)
+        f32x4 rescale[C::NHB][C::NHB * 64];     // per-consumer scratch for the rare output rescale
     };
 
-    // Attend one query over selected rows sel_g[t_begin .. t_end) of a cache
-    // holding nkeys rows.  Leaves, per lane, the unnormalised output o[f][hb]
-    // for head 16hb + (lane & 15) and features 16(FBW w + f) + 4(lane >> 4) + i,
-    // and sm.hmax / sm.hsum per head (reference max in log2 units, sum).
-    __device__ static void run(const uint16_t* __restrict__ qrow, const uint16_t* __restrict__ kv,
-                               const int32_t* __restrict__ sel_g, int t_begin, int t_end, int nkeys,
-                               float scale_log2, Smem& sm, f32x4 (&o)[C::FBW][C::NW]) {
-        const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
-        const int head = 16 * w + c16;
-        const int n = max(t_end - t_begin, 0);
+    // Shared state of one block attending selected rows sel_g[t_begin ..
+    // t_end) of a cache holding nkeys rows.
+    struct Ctx {
+        const uint16_t* kv;
+        int n, ntiles;
+        int w, l, g, c16;
+        uint32_t lat_off[C::ILW];
+        Smem* sm;
+    };
 
+    // Selection -> LDS (all loads issued before any is used), padded with -1
+    // to whole tiles; ids outside the cache become -1.  Ends with a barrier;
+    // every wave calls it.
+    __device__ static Ctx setup(const uint16_t* kv, const int32_t* __restrict__ sel_g, int t_begin, int t_end,
+                                int nkeys, Smem& sm) {
+        Ctx c;
+        const int tid = threadIdx.x;
+        c.kv = kv;
+        c.sm = &sm;
+        c.w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        c.l = tid & 63;
+        c.g = c.l >> 4;
+        c.c16 = c.l & 15;
+        c.n = max(t_end - t_begin, 0);
+        c.ntiles = (c.n + kTK - 1) / kTK;
+        const int npad = c.ntiles * kTK;
+        constexpr int PER = kMaxTopK / C::NT;
+        int jv[PER];
 #pragma unroll
-        for (int f = 0; f < C::FBW; ++f)
+        for (int k = 0; k < PER; ++k) {
+            const int t = tid + k * C::NT;
+            jv[k] = sel_g[t_begin + min(t, max(c.n - 1, 0))];
+        }
 #pragma unroll
-            for (int hb = 0; hb < C::NW; ++hb) o[f][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < PER; ++k) {
+            const int t = tid + k * C::NT;
+            if (t < npad) sm.sel[t] = (t < c.n && (unsigned)jv[k] < (unsigned)nkeys) ? jv[k] : -1;
+        }
+#pragma unroll
+        for (int k = 0; k < C::ILW; ++k) {
+            const int i = C::ILW * c.w + k;
+            const int slot = i * 64 + c.l;
+            const int r = slot / C::CL, pc = slot % C::CL;
+            c.lat_off[k] = 16u * (uint32_t)(pc ^ (swz_lat(r) & (C::CL - 1)));
+        }
+        __syncthreads();   // the selection is read by every wave's gathers
+        return c;
+    }
 
-        // selection -> LDS (all loads issued before any is used); ids
-        // outside the cache become -1
-        {
-            constexpr int PER = kMaxTopK / C::NT;
-            int jv[PER];
+    // Gather tile `it` (this wave's share): latent instruction i covers slots
+    // i*64 .. i*64+63 of the latent region (row slot / CL, physical chunk
+    // slot % CL), rope instruction i likewise in the rope region.  Masked
+    // keys read row 0; padding chunks read chunk 0 (they meet zero query
+    // columns).  With 64 chunks per latent row an instruction moves one
+    // whole row: its address is wave-uniform (scalar).
+    __device__ static void gather(const Ctx& c, int it) {
+        Smem& sm = *c.sm;
+        unsigned char* buf = sm.tile[it % kRing];
+        const int t0 = it * kTK;
+        constexpr uint32_t kRowBytes = 2u * C::DQK;
 #pragma unroll
-            for (int k = 0; k < PER; ++k) {
-                const int t = tid + k * C::NT;
-                jv[k] = sel_g[t_begin + min(t, max(n - 1, 0))];
-            }
-#pragma unroll
-            for (int k = 0; k < PER; ++k) {
-                const int t = tid + k * C::NT;
-                if (t < n) sm.sel[t] = ((unsigned)jv[k] < (unsigned)nkeys) ? jv[k] : -1;
+        for (int k = 0; k < C::ILW; ++k) {
+            const int i = C::ILW * c.w + k;
+            if constexpr (C::CL == 64) {
+                const int j = max(__builtin_amdgcn_readfirstlane(sm.sel[t0 + i]), 0);
+                gather16_to_lds(c.kv + (int64_t)j * C::DQK, c.lat_off[k], lds_addr(buf + 1024 * i));
+            } else {
+                const int r = (i * 64 + c.l) / C::CL;
+                const int j = max(sm.sel[t0 + r], 0);
+                gather16_to_lds(c.kv, (uint32_t)j * kRowBytes + c.lat_off[k], lds_addr(buf + 1024 * i));
             }
         }
-        // query fragments (bf16) for this lane's head
+        if (c.w < C::IR) {
+            const int i = c.w;
+            const int slot = i * 64 + c.l;
+            const int r = slot / C::CR, pc = slot % C::CR;
+            const int ch = pc ^ (swz_rope(r) & (C::CR - 1));
+            const int j = max(sm.sel[t0 + r], 0);
+            gather16_to_lds(c.kv, (uint32_t)j * kRowBytes + 2u * DL + 16u * (ch < C::CRD ? ch : 0),
+                            lds_addr(buf + C::LAT_B + 1024 * i));
+        }
+    }
+
+    // Wait until at most one tile of this wave's gathers is outstanding.
+    __device__ static void wait_one_tile(const Ctx& c) {
+        if (c.w < C::IR) wait_vmcnt<C::ILW + 1>();
+        else wait_vmcnt<C::ILW>();
+    }
+
+    // Prologue shared by both roles: tiles 0 and 1 in flight, tile 0 landed.
+    __device__ static void prologue(const Ctx& c) {
+        if (c.ntiles > 0) {
+            gather(c, 0);
+            if (c.ntiles > 1) { gather(c, 1); wait_one_tile(c); }
+            else wait_vmcnt<0>();
+        }
+        __syncthreads();
+    }
+
+    // Top of iteration it, both roles: tile it+1 landed for every wave,
+    // probabilities of tile it visible, tile it-1 free; then tile it+2 is
+    // gathered into tile it-1's buffer.
+    __device__ static void step(const Ctx& c, int it) {
+        if (it + 1 < c.ntiles) wait_vmcnt<0>();
+        __syncthreads();
+        if (it + 2 < c.ntiles) gather(c, it + 2);
+    }
+
+    // Producer wave hb = w: scores and softmax of heads 16hb .. 16hb+15.
+    // Leaves sm.hmax / sm.hsum per head (reference max in log2 units, sum).
+    __device__ static void produce(const Ctx& c, const uint16_t* __restrict__ qrow, float scale_log2) {
+        Smem& sm = *c.sm;
+        const int w = c.w, l = c.l, g = c.g, c16 = c.c16;
+        const int head = 16 * w + c16;
         const u32x4 zero = {0u, 0u, 0u, 0u};
         u32x4 qf[C::KS];
 #pragma unroll
@@ -191,38 +275,9 @@ struct Attend {
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) asm volatile("" :: "v"(qf[ks]));
         float mref = -INFINITY, lsum = 0.f;   // for head `head` (replicated over g)
-        __syncthreads();
-        const int ntiles = (n + kTK - 1) / kTK;
 
-        // Gather tile `it`: latent instruction i covers slots i*64 .. i*64+63
-        // of the latent region (row slot / CL, physical chunk slot % CL), rope
-        // instruction i likewise in the rope region.  Masked keys read row 0;
-        // padding chunks read chunk 0 (they meet zero query columns).
-        auto gather = [&](int it) {
-            unsigned char* buf = sm.tile[it % kRing];
-#pragma unroll
-            for (int k = 0; k < C::ILW; ++k) {
-                const int i = C::ILW * w + k;
-                const int slot = i * 64 + l;
-                const int r = slot / C::CL, pc = slot % C::CL;
-                const int c = pc ^ (swz_lat(r) & (C::CL - 1));
-                const int j = max(sm.sel[min(it * kTK + r, n - 1)], 0);
-                gather16_to_lds(kv + (int64_t)j * C::DQK + 8 * c, lds_addr(buf + 1024 * i));
-            }
-#pragma unroll
-            for (int k = 0; k < C::IRW; ++k) {
-                const int i = C::IRW * w + k;
-                const int slot = i * 64 + l;
-                const int r = slot / C::CR, pc = slot % C::CR;
-                const int c = pc ^ (swz_rope(r) & (C::CR - 1));
-                const int j = max(sm.sel[min(it * kTK + r, n - 1)], 0);
-                gather16_to_lds(kv + (int64_t)j * C::DQK + DL + 8 * (c < C::CRD ? c : 0),
-                                lds_addr(buf + C::LAT_B + 1024 * i));
-            }
-        };
-
-        // per-lane LDS offsets.  Score reads: row 16mb + c16 (swizzle depends
-        // on c16 only), logical chunk 4ks + g.
+        // Score reads: row 16mb + c16 (swizzle depends on c16 only), logical
+        // chunk 4ks + g.
         const int xl = swz_lat(c16) & (C::CL - 1);
         int qlat[4];
 #pragma unroll
@@ -231,19 +286,12 @@ struct Attend {
         int qrope[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) qrope[k] = C::LAT_B + c16 * C::CR * 16 + 16 * ((4 * k + g) ^ xr);
-        // transposed reads: rows 16h + 4g + (c16 >> 2), features
-        // 16fb + 4(c16 & 3): logical chunk 2fb + ((c16 >> 1) & 1), half c16 & 1
-        const int trow = 4 * g + (c16 >> 2);
-        const int vx = (swz_lat(trow) & (C::CL - 1)) ^ ((c16 >> 1) & 1);
-        const int vrow = trow * C::CL * 16 + 8 * (c16 & 1);
 
         auto key_frag = [&](const unsigned char* tile, int ks, u32x4 (&dst)[2]) {
             int off;
             if (ks < C::KSL) {
-                // logical chunk 4ks + g: bits 0..3 swizzled, bits 4.. untouched
-                const int lo = (C::CL >= 16) ? qlat[ks & 3] + 256 * (ks >> 2)
-                                             : c16 * C::CL * 16 + 16 * ((4 * ks + g) ^ xl);
-                off = lo;
+                off = (C::CL >= 16) ? qlat[ks & 3] + 256 * (ks >> 2)
+                                    : c16 * C::CL * 16 + 16 * ((4 * ks + g) ^ xl);
             } else {
                 off = qrope[(ks - C::KSL) & 1] + 128 * ((ks - C::KSL) >> 1);
             }
@@ -251,15 +299,11 @@ struct Attend {
             dst[0] = *reinterpret_cast<const u32x4*>(tile + off);
             dst[1] = *reinterpret_cast<const u32x4*>(tile + off + 16 * rs);
         };
-
-        // Scores of tile `it` for this wave's heads, then the softmax update;
-        // publishes probabilities and rescale factors under parity it & 1.
-        auto score_tile = [&](int it) {
+        auto score = [&](int it) {
             const unsigned char* tile = sm.tile[it % kRing];
             const int t0 = it * kTK;
-            // validity of the tile's 32 keys (every wave computes the same mask)
-            const uint32_t vmask =
-                (uint32_t)__ballot(l < kTK && t0 + l < n && sm.sel[min(t0 + l, n - 1)] >= 0);
+            // validity of the tile's 32 keys (every producer computes the same mask)
+            const uint32_t vmask = (uint32_t)__ballot(l < kTK && sm.sel[t0 + (l & (kTK - 1))] >= 0);
             f32x4 s[2] = {};
             u32x4 ka[3][2];   // key fragments, two k-steps ahead of their MFMAs
             key_frag(tile, 0, ka[0]);
@@ -281,16 +325,14 @@ struct Attend {
             for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
             mx = max4_rows(mx);
             // lazy reference: move it only when a score clears it by kLazy;
-            // alpha 0 (first valid tile) needs no rescale: the output is zero
-            float alpha = 1.f;
-            if (mx > mref + kLazy) {
-                alpha = (mref == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mref - mx);
-                mref = mx;
-            }
+            // the first valid tile needs no rescale (the output is zero)
+            const bool up = mx > mref + kLazy;
+            const float alpha = (up && mref != -INFINITY) ? __builtin_amdgcn_exp2f(mref - mx) : 1.f;
+            mref = up ? mx : mref;
             const float mbase = (mref == -INFINITY) ? 0.f : mref;
             float p[8], ps = 0.f;
-#pragma unroll
             // arguments are <= kLazy; v_exp_f32 returns 0 for -inf
+#pragma unroll
             for (int i = 0; i < 8; ++i) { p[i] = __builtin_amdgcn_exp2f(x[i] - mbase); ps += p[i]; }
             lsum = lsum * alpha + ps;
             u32x4 pb;
@@ -299,17 +341,43 @@ struct Attend {
             pb[2] = pack_f16(p[4], p[5]);
             pb[3] = pack_f16(p[6], p[7]);
             sm.pfrag[it & 1][w][l] = pb;
-            if (g == 0) sm.alpha[it & 1][head] = alpha;
+            sm.alpha[it & 1][head] = alpha;   // the four lanes of a head store the same value
         };
 
-        // Values of tile `it` for this wave's features, all heads.
-        auto value_tile = [&](int it) {
-            const unsigned char* tile = sm.tile[it % kRing];
-            u32x4 pf[C::NW];
-            float al[C::NW];
+        prologue(c);
+        if (c.ntiles > 0) score(0);
+        for (int it = 0; it < c.ntiles; ++it) {
+            step(c, it);
+            if (it + 1 < c.ntiles) score(it + 1);
+        }
+        lsum = sum4_rows(lsum);
+        if (g == 0) { sm.hsum[head] = lsum; sm.hmax[head] = mref; }
+        __syncthreads();
+    }
+
+    // Consumer wave cw = w - NHB: accumulates o[f][hb], the unnormalised
+    // output of head 16hb + (lane & 15) and features
+    // 16(FBW cw + f) + 4(lane >> 4) + i.
+    __device__ static void consume(const Ctx& c, f32x4 (&o)[C::FBW][C::NHB]) {
+        Smem& sm = *c.sm;
+        const int l = c.l, g = c.g, c16 = c.c16;
+        const int cw = c.w - C::NHB;
+#pragma unroll
+        for (int f = 0; f < C::FBW; ++f)
+#pragma unroll
+            for (int hb = 0; hb < C::NHB; ++hb) o[f][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // transposed reads: rows 16h + 4g + (c16 >> 2), features
+        // 16fb + 4(c16 & 3): logical chunk 2fb + ((c16 >> 1) & 1), half c16 & 1
+        const int trow = 4 * g + (c16 >> 2);
+        const int vx = (swz_lat(trow) & (C::CL - 1)) ^ ((c16 >> 1) & 1);
+        const int vrow = trow * C::CL * 16 + 8 * (c16 & 1);
+
+        auto values = [&](int it) {
+            u32x4 pf[C::NHB];
+            float al[C::NHB];
             bool moved = false;
 #pragma unroll
-            for (int hb = 0; hb < C::NW; ++hb) {
+            for (int hb = 0; hb < C::NHB; ++hb) {
                 pf[hb] = sm.pfrag[it & 1][hb][l];
                 al[hb] = sm.alpha[it & 1][16 * hb + c16];
                 moved |= al[hb] != 1.f;
@@ -318,109 +386,109 @@ struct Attend {
                 // Rescale through a per-wave LDS scratch: the accumulators are
                 // only stored and reloaded here, never read by VALU, so the
                 // compiler can keep them in AGPRs on the hot path.
-                f32x4* scratch = sm.rescale[w];
+                f32x4* scratch = sm.rescale[cw];
 #pragma unroll
                 for (int f = 0; f < C::FBW; ++f) {
 #pragma unroll
-                    for (int hb = 0; hb < C::NW; ++hb) scratch[hb * 64 + l] = o[f][hb];
+                    for (int hb = 0; hb < C::NHB; ++hb) scratch[hb * 64 + l] = o[f][hb];
                     asm volatile("" ::: "memory");
 #pragma unroll
-                    for (int hb = 0; hb < C::NW; ++hb) o[f][hb] = scratch[hb * 64 + l] * al[hb];
+                    for (int hb = 0; hb < C::NHB; ++hb) o[f][hb] = scratch[hb * 64 + l] * al[hb];
                     asm volatile("" ::: "memory");
                 }
             }
+            const unsigned char* tile = sm.tile[it % kRing];
 #pragma unroll
             for (int f = 0; f < C::FBW; ++f) {
-                const int fb = C::FBW * w + f;
+                const int fb = C::FBW * cw + f;
                 // logical chunk 2fb + tb, swizzled in its aligned group of 16
                 const int off = vrow + 16 * (((2 * fb) & ~15) + (((2 * fb) & 15) ^ vx));
                 const u32x2 v0 = bf16x4_to_f16x4(lds_read_tr16(tile + off));
                 const u32x2 v1 = bf16x4_to_f16x4(lds_read_tr16(tile + off + 16 * C::CL * 16));
                 const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
 #pragma unroll
-                for (int hb = 0; hb < C::NW; ++hb) o[f][hb] = mfma16_f16(av, pf[hb], o[f][hb]);
+                for (int hb = 0; hb < C::NHB; ++hb) o[f][hb] = mfma16_f16(av, pf[hb], o[f][hb]);
             }
         };
 
-        // Pipeline: iteration it scores tile it+1 and accumulates the values
-        // of tile it (scored one iteration earlier) while tile it+2 is being
-        // gathered.  One barrier per tile.
-        if (ntiles > 0) {
-            gather(0);
-            if (ntiles > 1) { gather(1); wait_vmcnt<C::IPW>(); }
-            else wait_vmcnt<0>();
-            __syncthreads();
-            score_tile(0);
+        prologue(c);
+        for (int it = 0; it < c.ntiles; ++it) {
+            step(c, it);
+            values(it);
         }
-        for (int it = 0; it < ntiles; ++it) {
-            if (it + 1 < ntiles) wait_vmcnt<0>();   // tile it+1 (the only gather in flight)
-            __syncthreads();   // probabilities of tile it and tile it+1 visible; tile it-1 free
-            if (it + 2 < ntiles) gather(it + 2);   // into tile it-1's buffer
-            if (it + 1 < ntiles) score_tile(it + 1);
-            value_tile(it);
-        }
-        lsum = sum4_rows(lsum);
-        if (g == 0) { sm.hsum[head] = lsum; sm.hmax[head] = mref; }
         __syncthreads();
     }
 };
 
 template <int NH, int DL, int DR>
-__global__ __launch_bounds__((AttnShape<NH, DL, DR>::NT)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__((AttnShape<NH, DL, DR>::NT)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_kernel(AttnArgs a) {
     using C = AttnShape<NH, DL, DR>;
-    __shared__ __attribute__((aligned(16))) typename Attend<NH, DL, DR>::Smem sm;
+    using A = Attend<NH, DL, DR>;
+    __shared__ __attribute__((aligned(16))) typename A::Smem sm;
     const int row = blockIdx.x;
     const int cnt = min(max(a.count[row], 0), a.top_k);
-    f32x4 o[C::FBW][C::NW];
-    Attend<NH, DL, DR>::run(a.q + (int64_t)row * NH * C::DQK, a.kv, a.idx + (int64_t)row * a.top_k, 0, cnt,
-                            a.N, a.scale_log2, sm, o);
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, c16 = l & 15;
+    const auto c = A::setup(a.kv, a.idx + (int64_t)row * a.top_k, 0, cnt, a.N, sm);
+    if (c.w < C::NHB) {
+        A::produce(c, a.q + (int64_t)row * NH * C::DQK, a.scale_log2);
+        if (a.lse && c.w == 0 && c.l < 16) {
+            for (int h = c.l; h < NH; h += 16) {
+                const float ls = sm.hsum[h];
+                a.lse[(int64_t)row * NH + h] = ls > 0.f ? (sm.hmax[h] + log2f(ls)) * 0.69314718055994531f : -INFINITY;
+            }
+        }
+    } else {
+        f32x4 o[C::FBW][C::NHB];
+        A::consume(c, o);
+        const int cw = c.w - C::NHB;
 #pragma unroll
-    for (int hb = 0; hb < C::NW; ++hb) {
-        const int head = 16 * hb + c16;
-        if (head >= NH) continue;
-        const float ls = sm.hsum[head];
-        const float inv = ls > 0.f ? 1.f / ls : 0.f;
-        float* orow = a.out + ((int64_t)row * NH + head) * DL;
+        for (int hb = 0; hb < C::NHB; ++hb) {
+            const int head = 16 * hb + c.c16;
+            if (head >= NH) continue;
+            const float ls = sm.hsum[head];
+            const float inv = ls > 0.f ? 1.f / ls : 0.f;
+            float* orow = a.out + ((int64_t)row * NH + head) * DL;
 #pragma unroll
-        for (int f = 0; f < C::FBW; ++f)
-            *reinterpret_cast<f32x4*>(orow + 16 * (C::FBW * w + f) + 4 * g) = o[f][hb] * inv;
-    }
-    if (a.lse && threadIdx.x < NH) {
-        const float ls = sm.hsum[threadIdx.x];
-        a.lse[(int64_t)row * NH + threadIdx.x] =
-            ls > 0.f ? (sm.hmax[threadIdx.x] + log2f(ls)) * 0.69314718055994531f : -INFINITY;
+            for (int f = 0; f < C::FBW; ++f)
+                *reinterpret_cast<f32x4*>(orow + 16 * (C::FBW * cw + f) + 4 * c.g) = o[f][hb] * inv;
+        }
     }
 }
 
 template <int NH, int DL, int DR>
-__global__ __launch_bounds__((AttnShape<NH, DL, DR>::NT)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__((AttnShape<NH, DL, DR>::NT)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_split_kernel(AttnSplitArgs a, SeqMeta m) {
     using C = AttnShape<NH, DL, DR>;
-    __shared__ __attribute__((aligned(16))) typename Attend<NH, DL, DR>::Smem sm;
+    using A = Attend<NH, DL, DR>;
+    __shared__ __attribute__((aligned(16))) typename A::Smem sm;
     const int item = blockIdx.x;
     const int b = seq_of_block(m, item);
     const int ctx = m.ctx[b];
     const int cnt = min(ctx, a.top_k);
     const int t_begin = (item - m.blk0[b]) * a.chunk;
     const int t_end = min(t_begin + a.chunk, cnt);
-    f32x4 o[C::FBW][C::NW];
-    Attend<NH, DL, DR>::run(a.q + (int64_t)b * NH * C::DQK, a.kv + m.key_off[b] * C::DQK,
-                            a.idx + (int64_t)b * a.top_k, t_begin, t_end, ctx, a.scale_log2, sm, o);
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, c16 = l & 15;
+    const auto c = A::setup(a.kv + m.key_off[b] * C::DQK, a.idx + (int64_t)b * a.top_k, t_begin, t_end, ctx, sm);
+    if (c.w < C::NHB) {
+        A::produce(c, a.q + (int64_t)b * NH * C::DQK, a.scale_log2);
+        if (c.w == 0 && c.l < 16) {
+            for (int h = c.l; h < NH; h += 16) {
+                a.part_ml[((int64_t)item * NH + h) * 2 + 0] = sm.hmax[h];
+                a.part_ml[((int64_t)item * NH + h) * 2 + 1] = sm.hsum[h];
+            }
+        }
+    } else {
+        f32x4 o[C::FBW][C::NHB];
+        A::consume(c, o);
+        const int cw = c.w - C::NHB;
 #pragma unroll
-    for (int hb = 0; hb < C::NW; ++hb) {
-        const int head = 16 * hb + c16;
-        if (head >= NH) continue;
-        float* orow = a.part_o + ((int64_t)item * NH + head) * DL;
+        for (int hb = 0; hb < C::NHB; ++hb) {
+            const int head = 16 * hb + c.c16;
+            if (head >= NH) continue;
+            float* orow = a.part_o + ((int64_t)item * NH + head) * DL;
 #pragma unroll
-        for (int f = 0; f < C::FBW; ++f)
-            *reinterpret_cast<f32x4*>(orow + 16 * (C::FBW * w + f) + 4 * g) = o[f][hb];
-    }
-    if (threadIdx.x < NH) {
-        a.part_ml[((int64_t)item * NH + threadIdx.x) * 2 + 0] = sm.hmax[threadIdx.x];
-        a.part_ml[((int64_t)item * NH + threadIdx.x) * 2 + 1] = sm.hsum[threadIdx.x];
+            for (int f = 0; f < C::FBW; ++f)
+                *reinterpret_cast<f32x4*>(orow + 16 * (C::FBW * cw + f) + 4 * c.g) = o[f][hb];
+        }
     }
 }
 
