@@ -108,11 +108,13 @@ def profile_stage(stage, reps, np, torch, dsa, W) -> int:
         S = torch.empty((cfg.L, cfg.N), dtype=torch.float32, device="cuda")
         if stage != "indexer":
             dsa.dsa_indexer_scores(sh, qI, kI, w, cfg.L, cfg.N, cfg.q_start, S)
+        kv16 = torch.empty_like(kv)
         if stage == "attention":
             dsa.dsa_topk_select(sh, S, cfg.L, cfg.N, cfg.q_start, idx, cnt)
+            dsa.dsa_latent_to_f16(sh, kv, cfg.N, kv16)
         f = {"indexer": lambda: dsa.dsa_indexer_scores(sh, qI, kI, w, cfg.L, cfg.N, cfg.q_start, S),
              "topk": lambda: dsa.dsa_topk_select(sh, S, cfg.L, cfg.N, cfg.q_start, idx, cnt),
-             "attention": lambda: dsa.dsa_sparse_mla_attn(sh, q, kv, idx, cnt, cfg.L, cfg.N, out, None)}[stage]
+             "attention": lambda: dsa.dsa_sparse_mla_attn_f16(sh, q, kv16, idx, cnt, cfg.L, cfg.N, out, None)}[stage]
     torch.cuda.synchronize()
     for _ in range(reps):
         f()
@@ -279,16 +281,21 @@ def main() -> int:
         cnt2 = torch.empty_like(cnt)
         out2 = torch.empty_like(out)
         n = max(K, 3)
+        kv16 = torch.empty_like(kv)
         f_idx = lambda: dsa.dsa_indexer_scores(sh, qI, kI, w, cfg.L, cfg.N, cfg.q_start, S)
         f_topk = lambda: dsa.dsa_topk_select(sh, S, cfg.L, cfg.N, cfg.q_start, idx2, cnt2)
-        f_attn = lambda: dsa.dsa_sparse_mla_attn(sh, q, kv, idx, cnt, cfg.L, cfg.N, out2, None)
-        for f in (f_idx, f_topk, f_attn):
+        f_conv = lambda: dsa.dsa_latent_to_f16(sh, kv, cfg.N, kv16)
+        # the attention kernel the chunk runs: fp16-latent cache
+        f_attn = lambda: dsa.dsa_sparse_mla_attn_f16(sh, q, kv16, idx, cnt, cfg.L, cfg.N, out2, None)
+        for f in (f_idx, f_topk, f_conv, f_attn):
             f()
         torch.cuda.synchronize()
         log("stage timing", n)
         t_idx = timed_events(f_idx, n, torch)
         t_topk = timed_events(f_topk, n, torch)
+        t_conv = timed_events(f_conv, n, torch)
         t_attn = timed_events(f_attn, n, torch)
+        conv_bytes = 2 * 2 * sh.d_qk * cfg.N
         stages = {
             "indexer": {"kernel": "indexer_prefill_kernel<32,128>", "us": t_idx * 1e6,
                         "tflops": wk["idx_flop"] / t_idx / 1e12,
@@ -297,7 +304,10 @@ def main() -> int:
             "topk": {"kernel": "topk_prefill_kernel<512,32>", "us": t_topk * 1e6,
                      "gbps": wk["topk_bytes"] / t_topk / 1e9,
                      "frac": wk["topk_bytes"] / t_topk / 1e9 / PEAK_HBM_GBPS},
-            "attention": {"kernel": "attention_kernel<64,512,64>", "us": t_attn * 1e6,
+            "latent_to_f16": {"kernel": "latent_to_f16_kernel<512,64>", "us": t_conv * 1e6,
+                              "gbps": conv_bytes / t_conv / 1e9,
+                              "frac": conv_bytes / t_conv / 1e9 / PEAK_HBM_GBPS},
+            "attention": {"kernel": "attention_kernel<64,512,64,true>", "us": t_attn * 1e6,
                           "tflops": wk["attn_flop"] / t_attn / 1e12,
                           "frac": wk["attn_flop"] / t_attn / 1e12 / PEAK_MFMA_TFLOPS,
                           "gather_gbps": wk["gather_bytes"] / t_attn / 1e9,

@@ -105,10 +105,34 @@ dsa_status dsa_topk_select(const dsa_shape* shape, const float* S, int32_t L, in
  * int32 in any order (entries outside [0, N) are skipped); count [dev] [L]
  * int32 (values above top_k are clamped); out [dev] [L, H, Dl] fp32;
  * lse [dev] [L, H] fp32 natural log, or NULL.  A row with no usable key
- * gets out = 0 and lse = -infinity. */
+ * gets out = 0 and lse = -infinity.  Probabilities and latent values enter
+ * the value product as fp16: requires |kv latent| <= 65504.  Rows are
+ * addressed with 32-bit byte offsets: N * 2 * (Dl+Dr) must stay below 2^32
+ * (DSA_ERR_UNSUPPORTED otherwise; 3.7 M rows at GLM shape). */
 dsa_status dsa_sparse_mla_attn(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv,
                                const int32_t* idx, const int32_t* count, int32_t L, int32_t N,
                                float* out, float* lse, void* stream);
+
+/* Latent cache in the fp16-latent layout: kv16 has kv's shape [N, Dl+Dr];
+ * its Dl latent columns hold kv's values converted bf16 -> fp16 (round to
+ * nearest even) and its Dr rope columns are copied unchanged.  kv [dev],
+ * kv16 [dev], caller-owned, 16-byte aligned, not overlapping.  The
+ * conversion is exact for |v| in [2^-14, 65504]; smaller magnitudes become
+ * fp16 subnormals (absolute error <= 2^-25), larger ones infinities, so the
+ * fp16-latent path requires |v| <= 65504 (the value product already does,
+ * see dsa_sparse_mla_attn). */
+dsa_status dsa_latent_to_f16(const dsa_shape* shape, const uint16_t* kv, int32_t N, uint16_t* kv16,
+                             void* stream);
+
+/* dsa_sparse_mla_attn over an fp16-latent cache (dsa_latent_to_f16): the
+ * same operation, arguments and errors, with kv16 in place of kv.  The
+ * latent part of q is converted to fp16 inside the kernel (same range
+ * condition as the cache), so the latent score products run on fp16
+ * operands; the rope part stays bf16.  This is the kernel dsa_prefill_chunk
+ * runs. */
+dsa_status dsa_sparse_mla_attn_f16(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv16,
+                                   const int32_t* idx, const int32_t* count, int32_t L, int32_t N,
+                                   float* out, float* lse, void* stream);
 
 /* Workspace bytes dsa_prefill_chunk needs for this chunk geometry
  * (0 on invalid or unsupported arguments). */
@@ -121,7 +145,9 @@ size_t dsa_prefill_workspace_bytes(const dsa_shape* shape, int32_t L, int32_t N,
  * q [dev] [L,H,Dl+Dr], qI [dev] [L,Hi,Di] bf16; w [dev] [L,Hi] fp32;
  * kv [dev] [N,Dl+Dr], kI [dev] [N,Di] bf16; out [dev] [L,H,Dl] fp32;
  * idx_out [dev] [L,top_k] int32 or NULL; count_out [dev] [L] int32 or NULL;
- * ws [dev] of at least dsa_prefill_workspace_bytes() bytes. */
+ * ws [dev] of at least dsa_prefill_workspace_bytes() bytes.  The attention
+ * runs on an fp16-latent copy of kv held in the workspace (see
+ * dsa_latent_to_f16 for the range condition). */
 dsa_status dsa_prefill_chunk(const dsa_shape* shape, const uint16_t* q, const uint16_t* qI,
                              const float* w, const uint16_t* kv, const uint16_t* kI, int32_t L,
                              int32_t N, int64_t q_start, float* out, int32_t* idx_out,

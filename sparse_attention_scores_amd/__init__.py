@@ -18,16 +18,16 @@ from . import build as _build
 
 __all__ = [
     "DsaError", "Shape", "GLM", "TINY", "lib",
-    "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn",
-    "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
+    "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn", "dsa_latent_to_f16",
+    "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
     "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_status_string",
     "EXPORTED_SYMBOLS",
 ]
 
 EXPORTED_SYMBOLS = (
     "dsa_status_string", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn",
-    "dsa_prefill_workspace_bytes", "dsa_prefill_chunk", "dsa_decode_workspace_bytes",
-    "dsa_decode_step",
+    "dsa_latent_to_f16", "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
+    "dsa_decode_workspace_bytes", "dsa_decode_step",
 )
 
 
@@ -70,6 +70,8 @@ def _load() -> ctypes.CDLL:
         "dsa_indexer_scores": (ctypes.c_int, [SP, P, P, P, i32, i32, i64, P, P]),
         "dsa_topk_select": (ctypes.c_int, [SP, P, i32, i32, i64, P, P, P]),
         "dsa_sparse_mla_attn": (ctypes.c_int, [SP, P, P, P, P, i32, i32, P, P, P]),
+        "dsa_latent_to_f16": (ctypes.c_int, [SP, P, i32, P, P]),
+        "dsa_sparse_mla_attn_f16": (ctypes.c_int, [SP, P, P, P, P, i32, i32, P, P, P]),
         "dsa_prefill_workspace_bytes": (sz, [SP, i32, i32, i64]),
         "dsa_prefill_chunk": (ctypes.c_int, [SP, P, P, P, P, P, i32, i32, i64, P, P, P, P, sz, P]),
         "dsa_decode_workspace_bytes": (sz, [SP, i32, P]),
@@ -114,8 +116,8 @@ def _stream(stream) -> ctypes.c_void_p:
 def _bits(t: Optional[torch.Tensor], name: str):
     if t is None:
         return None
-    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-        raise TypeError("%s must hold bf16 bit patterns (bfloat16/int16/uint16)" % name)
+    if t.dtype not in (torch.bfloat16, torch.float16, torch.int16, torch.uint16):
+        raise TypeError("%s must hold 16-bit patterns (bfloat16/float16/int16/uint16)" % name)
     return _ptr(t, t.dtype, name)
 
 
@@ -137,6 +139,20 @@ def dsa_sparse_mla_attn(shape, q, kv, idx, count, L: int, N: int, out, lse=None,
     sh = Shape.of(shape)
     _check("dsa_sparse_mla_attn", lib.dsa_sparse_mla_attn(
         ctypes.byref(sh), _bits(q, "q"), _bits(kv, "kv"), _ptr(idx, torch.int32, "idx"),
+        _ptr(count, torch.int32, "count"), L, N, _ptr(out, torch.float32, "out"),
+        _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def dsa_latent_to_f16(shape, kv, N: int, kv16, stream=None) -> None:
+    sh = Shape.of(shape)
+    _check("dsa_latent_to_f16", lib.dsa_latent_to_f16(ctypes.byref(sh), _bits(kv, "kv"), N, _bits(kv16, "kv16"),
+                                                      _stream(stream)))
+
+
+def dsa_sparse_mla_attn_f16(shape, q, kv16, idx, count, L: int, N: int, out, lse=None, stream=None) -> None:
+    sh = Shape.of(shape)
+    _check("dsa_sparse_mla_attn_f16", lib.dsa_sparse_mla_attn_f16(
+        ctypes.byref(sh), _bits(q, "q"), _bits(kv16, "kv16"), _ptr(idx, torch.int32, "idx"),
         _ptr(count, torch.int32, "count"), L, N, _ptr(out, torch.float32, "out"),
         _ptr(lse, torch.float32, "lse"), _stream(stream)))
 

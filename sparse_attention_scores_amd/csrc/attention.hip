@@ -17,15 +17,19 @@
 //    128c..128c+127 of all heads.  The split keeps each wave under 256
 //    registers, so a SIMD holds one wave of each kind and the matrix pipe
 //    is fed by one while the other waits on LDS or runs its softmax.
-//  - the selection is copied to LDS once; selected rows are then gathered 32
-//    per tile straight into LDS with global_load_lds_dwordx4 (16 bytes per
-//    lane, no registers), three tiles deep, so two tiles are in flight while
-//    one is computed.  The loads are issued from inline assembly and waited
-//    for with explicit vmcnt counts: the compiler's own wait insertion would
-//    drain every outstanding LDS load before each LDS read.  A 1 KB latent
-//    row is one instruction with a scalar row address.
-//  - a tile is stored bf16 in two row-major regions: the Dl latent columns
-//    and the rope columns.  16-byte chunks are XOR-swizzled per row so that
+//  - the selection is copied to LDS once (row ids plus a validity bitmap);
+//    selected rows are then gathered 32 per tile straight into LDS with
+//    global_load_lds_dwordx4 (16 bytes per lane, no registers) into a ring
+//    of three tiles: while consumers read tile it and producers score tile
+//    it+1, tile it+2 is in flight.  The loads are issued from inline
+//    assembly and waited for with explicit vmcnt counts: the compiler's own
+//    wait insertion would drain every outstanding LDS load before each LDS
+//    read.  A 1 KB latent row is one instruction with a scalar row address.
+//    (A fourth tile in flight measured no faster.)
+//  - a tile is stored in two row-major regions: the Dl latent columns (bf16,
+//    or fp16 when the cache was converted once by latent_to_f16_kernel, which
+//    removes the per-query conversion from the value path) and the bf16 rope
+//    columns.  16-byte chunks are XOR-swizzled per row so that
 //    the score reads (16 rows, one chunk) and the transposed value reads
 //    (4 rows, 2 chunks) hit distinct banks.
 //  - softmax in fp32 (base 2) with a lazy reference: the running maximum
@@ -51,7 +55,7 @@ namespace dsa {
 namespace {
 
 constexpr int kTK = 32;        // keys per tile
-constexpr int kRing = 3;       // tiles resident in LDS (two in flight)
+constexpr int kRing = 3;       // tiles resident in LDS: the ring keeps kRing - 2 gathers in flight
 constexpr float kLazy = 8.f;   // log2 headroom before the reference maximum moves
 
 template <int NH, int DL, int DR>
@@ -74,6 +78,7 @@ struct AttnShape {
     static constexpr int IL = kTK * CL / 64;             // gather instructions, latent region
     static constexpr int IR = kTK * CR / 64;             // gather instructions, rope region
     static constexpr int ILW = IL / NWAVE;               // latent instructions per wave
+    static constexpr int LR = 64 / CL > 0 ? 64 / CL : 1; // rows per latent instruction
     static_assert((CL & (CL - 1)) == 0 && (CR & (CR - 1)) == 0, "row chunk counts must be powers of two");
     static_assert(64 % CL == 0 || CL == 64, "latent rows must pack whole instructions");
     static_assert(FB % NHB == 0 && IL % NWAVE == 0 && IR <= NWAVE && kTK * CR % 64 == 0,
@@ -95,6 +100,18 @@ __device__ inline u32x2 bf16x4_to_f16x4(const u32x2& d) {
     r[0] = pack_f16(__uint_as_float(d[0] << 16), __uint_as_float(d[0] & 0xFFFF0000u));
     r[1] = pack_f16(__uint_as_float(d[1] << 16), __uint_as_float(d[1] & 0xFFFF0000u));
     return r;
+}
+
+// bf16 bits -> fp16 bits, round to nearest even (exact for |v| in
+// [2^-14, 65504]; larger magnitudes become infinities)
+__device__ inline uint32_t bf16x2_to_f16x2_rne(uint32_t d) {
+    const _Float16 lo = (_Float16)__uint_as_float(d << 16);
+    const _Float16 hi = (_Float16)__uint_as_float(d & 0xFFFF0000u);
+    return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+__device__ inline u32x4 bf16x8_to_f16x8_rne(const u32x4& d) {
+    return u32x4{bf16x2_to_f16x2_rne(d[0]), bf16x2_to_f16x2_rne(d[1]), bf16x2_to_f16x2_rne(d[2]),
+                 bf16x2_to_f16x2_rne(d[3])};
 }
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lds_bf16x4;
@@ -135,18 +152,20 @@ __device__ inline float sum4_rows(float x) {
 template <int N>
 __device__ inline void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
-template <int NH, int DL, int DR>
+// F16: the cache's latent columns hold fp16 (see latent_to_f16_kernel) rather
+// than bf16; the rope columns are bf16 either way.
+template <int NH, int DL, int DR, bool F16>
 struct Attend {
     using C = AttnShape<NH, DL, DR>;
 
     struct Smem {
-        unsigned char tile[kRing][C::TILE_B];   // gathered rows, bf16, swizzled
-        int32_t sel[kMaxTopK];                  // selection, -1 = not a key
+        unsigned char tile[kRing][C::TILE_B];   // gathered rows, bf16 / fp16, swizzled
+        int32_t sel[kMaxTopK];                  // row id per selection slot (0 where unusable)
+        uint32_t valid[kMaxTopK / 32];          // selection slot t holds a usable key: bit t
         u32x4 pfrag[2][C::NHB][64];             // probabilities per head block, operand layout
         float alpha[2][C::NHB * 16];            // rescale factor per head, per tile parity
         float hsum[C::NHB * 16];                // exponent sum per head (end)
         float hmax[C::NHB * 16];                // reference maximum per head (end)
-        f32x4 rescale[C::NHB][C::NHB * 64];     // per-consumer scratch for the rare output rescale
     };
 
     // Shared state of one block attending selected rows sel_g[t_begin ..
@@ -159,10 +178,10 @@ struct Attend {
         Smem* sm;
     };
 
-    // Selection -> LDS (all loads issued before any is used), padded with -1
-    // to whole tiles; ids outside the cache become -1.  Ends with a barrier;
-    // every wave calls it.
-    __device__ static Ctx setup(const uint16_t* kv, const int32_t* __restrict__ sel_g, int t_begin, int t_end,
+    // Selection -> LDS as row ids (row 0 where a slot is unusable: past the
+    // count or outside the cache) plus a validity bitmap, padded to whole
+    // tiles.  Every wave calls it; ends with a barrier.
+    __device__ __forceinline__ static Ctx setup(const uint16_t* kv, const int32_t* __restrict__ sel_g, int t_begin, int t_end,
                                 int nkeys, Smem& sm) {
         Ctx c;
         const int tid = threadIdx.x;
@@ -178,14 +197,21 @@ struct Attend {
         constexpr int PER = kMaxTopK / C::NT;
         int jv[PER];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int t = tid + k * C::NT;
+        for (int k = 0; k < PER; ++k) {   // slot t = k*NT + tid: a wave covers 64 consecutive slots
+            const int t = k * C::NT + tid;
             jv[k] = sel_g[t_begin + min(t, max(c.n - 1, 0))];
         }
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
-            const int t = tid + k * C::NT;
-            if (t < npad) sm.sel[t] = (t < c.n && (unsigned)jv[k] < (unsigned)nkeys) ? jv[k] : -1;
+            const int t = k * C::NT + tid;
+            const bool ok = t < c.n && (unsigned)jv[k] < (unsigned)nkeys;
+            if (t < npad) sm.sel[t] = ok ? jv[k] : 0;
+            const uint64_t m = __ballot(ok);
+            if (c.l == 0) {
+                const int word = (k * C::NT + 64 * c.w) / 32;
+                sm.valid[word] = (uint32_t)m;
+                sm.valid[word + 1] = (uint32_t)(m >> 32);
+            }
         }
 #pragma unroll
         for (int k = 0; k < C::ILW; ++k) {
@@ -194,17 +220,17 @@ struct Attend {
             const int r = slot / C::CL, pc = slot % C::CL;
             c.lat_off[k] = 16u * (uint32_t)(pc ^ (swz_lat(r) & (C::CL - 1)));
         }
-        __syncthreads();   // the selection is read by every wave's gathers
+        __syncthreads();
         return c;
     }
 
     // Gather tile `it` (this wave's share): latent instruction i covers slots
     // i*64 .. i*64+63 of the latent region (row slot / CL, physical chunk
-    // slot % CL), rope instruction i likewise in the rope region.  Masked
-    // keys read row 0; padding chunks read chunk 0 (they meet zero query
-    // columns).  With 64 chunks per latent row an instruction moves one
-    // whole row: its address is wave-uniform (scalar).
-    __device__ static void gather(const Ctx& c, int it) {
+    // slot % CL), rope instruction i likewise in the rope region.  Padding
+    // chunks read chunk 0 (they meet zero query columns).  With 64 chunks
+    // per latent row an instruction moves one whole row: its address is
+    // wave-uniform (scalar).
+    __device__ __forceinline__ static void gather(const Ctx& c, int it) {
         Smem& sm = *c.sm;
         unsigned char* buf = sm.tile[it % kRing];
         const int t0 = it * kTK;
@@ -212,12 +238,11 @@ struct Attend {
 #pragma unroll
         for (int k = 0; k < C::ILW; ++k) {
             const int i = C::ILW * c.w + k;
-            if constexpr (C::CL == 64) {
-                const int j = max(__builtin_amdgcn_readfirstlane(sm.sel[t0 + i]), 0);
+            if constexpr (C::LR == 1) {
+                const int j = __builtin_amdgcn_readfirstlane(sm.sel[t0 + i]);
                 gather16_to_lds(c.kv + (int64_t)j * C::DQK, c.lat_off[k], lds_addr(buf + 1024 * i));
             } else {
-                const int r = (i * 64 + c.l) / C::CL;
-                const int j = max(sm.sel[t0 + r], 0);
+                const int j = sm.sel[t0 + (i * 64 + c.l) / C::CL];
                 gather16_to_lds(c.kv, (uint32_t)j * kRowBytes + c.lat_off[k], lds_addr(buf + 1024 * i));
             }
         }
@@ -226,40 +251,51 @@ struct Attend {
             const int slot = i * 64 + c.l;
             const int r = slot / C::CR, pc = slot % C::CR;
             const int ch = pc ^ (swz_rope(r) & (C::CR - 1));
-            const int j = max(sm.sel[t0 + r], 0);
+            const int j = sm.sel[t0 + r];
             gather16_to_lds(c.kv, (uint32_t)j * kRowBytes + 2u * DL + 16u * (ch < C::CRD ? ch : 0),
                             lds_addr(buf + C::LAT_B + 1024 * i));
         }
     }
 
-    // Wait until at most one tile of this wave's gathers is outstanding.
-    __device__ static void wait_one_tile(const Ctx& c) {
-        if (c.w < C::IR) wait_vmcnt<C::ILW + 1>();
-        else wait_vmcnt<C::ILW>();
+    // Wait until at most K tiles of this wave's gathers are outstanding.
+    template <int K>
+    __device__ __forceinline__ static void wait_tiles(const Ctx& c) {
+        if (c.w < C::IR) wait_vmcnt<K * (C::ILW + 1)>();
+        else wait_vmcnt<K * C::ILW>();
+    }
+    __device__ __forceinline__ static void wait_tiles_rt(const Ctx& c, int k) {   // k uniform, < kRing
+        static_assert(kRing <= 5, "extend the switch");
+        switch (k) {
+            case 0: wait_tiles<0>(c); break;
+            case 1: wait_tiles<1>(c); break;
+            case 2: wait_tiles<2>(c); break;
+            default: wait_tiles<3>(c); break;
+        }
     }
 
-    // Prologue shared by both roles: tiles 0 and 1 in flight, tile 0 landed.
-    __device__ static void prologue(const Ctx& c) {
-        if (c.ntiles > 0) {
-            gather(c, 0);
-            if (c.ntiles > 1) { gather(c, 1); wait_one_tile(c); }
-            else wait_vmcnt<0>();
-        }
+    // Prologue shared by both roles: tiles 0 .. kRing-2 in flight, tile 0
+    // landed.
+    __device__ __forceinline__ static void prologue(const Ctx& c) {
+#pragma unroll
+        for (int t = 0; t < kRing - 1; ++t)
+            if (t < c.ntiles) gather(c, t);
+        if (c.ntiles > 0) wait_tiles_rt(c, min(kRing - 2, c.ntiles - 1));
         __syncthreads();
     }
 
     // Top of iteration it, both roles: tile it+1 landed for every wave,
-    // probabilities of tile it visible, tile it-1 free; then tile it+2 is
-    // gathered into tile it-1's buffer.
-    __device__ static void step(const Ctx& c, int it) {
-        if (it + 1 < c.ntiles) wait_vmcnt<0>();
+    // probabilities of tile it visible, tile it-1 free; then tile
+    // it+kRing-1 is gathered into tile it-1's buffer.
+    __device__ __forceinline__ static void step(const Ctx& c, int it) {
+        // tiles it+1 .. min(it+kRing-2, ntiles-1) are in flight; keep all but it+1
+        if (it + 1 < c.ntiles) wait_tiles_rt(c, min(kRing - 3, c.ntiles - 2 - it));
         __syncthreads();
-        if (it + 2 < c.ntiles) gather(c, it + 2);
+        if (it + kRing - 1 < c.ntiles) gather(c, it + kRing - 1);
     }
 
     // Producer wave hb = w: scores and softmax of heads 16hb .. 16hb+15.
     // Leaves sm.hmax / sm.hsum per head (reference max in log2 units, sum).
-    __device__ static void produce(const Ctx& c, const uint16_t* __restrict__ qrow, float scale_log2) {
+    __device__ __forceinline__ static void produce(const Ctx& c, const uint16_t* __restrict__ qrow, float scale_log2) {
         Smem& sm = *c.sm;
         const int w = c.w, l = c.l, g = c.g, c16 = c.c16;
         const int head = 16 * w + c16;
@@ -270,11 +306,19 @@ struct Attend {
             const int f = 32 * ks + 8 * g;
             qf[ks] = (head < NH && f < C::DQK) ? ldg16(qrow + (int64_t)head * C::DQK + f) : zero;
         }
+        if constexpr (F16) {
+            // the latent part meets fp16 keys: convert (exact for |q| in
+            // [2^-14, 65504], round to nearest even below)
+#pragma unroll
+            for (int ks = 0; ks < C::KSL; ++ks) qf[ks] = bf16x8_to_f16x8_rne(qf[ks]);
+        }
         // Consume the fragments here so that every compiler-tracked load has
         // completed before the gather loop: its LDS loads are counted by hand.
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) asm volatile("" :: "v"(qf[ks]));
         float mref = -INFINITY, lsum = 0.f;   // for head `head` (replicated over g)
+        const bool neg_scale = scale_log2 < 0.f;
+        const float cabs = fabsf(scale_log2);
 
         // Score reads: row 16mb + c16 (swizzle depends on c16 only), logical
         // chunk 4ks + g.
@@ -301,9 +345,8 @@ struct Attend {
         };
         auto score = [&](int it) {
             const unsigned char* tile = sm.tile[it % kRing];
-            const int t0 = it * kTK;
-            // validity of the tile's 32 keys (every producer computes the same mask)
-            const uint32_t vmask = (uint32_t)__ballot(l < kTK && sm.sel[t0 + (l & (kTK - 1))] >= 0);
+            // validity of the tile's 32 keys: bit k is key t0 + k
+            const uint32_t vmask = sm.valid[it];
             f32x4 s[2] = {};
             u32x4 ka[3][2];   // key fragments, two k-steps ahead of their MFMAs
             key_frag(tile, 0, ka[0]);
@@ -311,19 +354,31 @@ struct Attend {
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
                 if (ks + 2 < C::KS) key_frag(tile, ks + 2, ka[(ks + 2) % 3]);
-                s[0] = mfma16_bf16(ka[ks % 3][0], qf[ks], s[0]);
-                s[1] = mfma16_bf16(ka[ks % 3][1], qf[ks], s[1]);
+                if (F16 && ks < C::KSL) {
+                    s[0] = mfma16_f16(ka[ks % 3][0], qf[ks], s[0]);
+                    s[1] = mfma16_f16(ka[ks % 3][1], qf[ks], s[1]);
+                } else {
+                    s[0] = mfma16_bf16(ka[ks % 3][0], qf[ks], s[0]);
+                    s[1] = mfma16_bf16(ka[ks % 3][1], qf[ks], s[1]);
+                }
             }
-            float x[8];
+            // x = s * scale (log2 units) = sv * cabs; unusable keys -> -inf
+            float sv[8];
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    x[4 * mb + i] = ((vmask >> (16 * mb + 4 * g + i)) & 1u) ? s[mb][i] * scale_log2 : -INFINITY;
-            float mx = x[0];
+                for (int i = 0; i < 4; ++i) sv[4 * mb + i] = neg_scale ? -s[mb][i] : s[mb][i];
+            if (vmask != 0xFFFFFFFFu) {
 #pragma unroll
-            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-            mx = max4_rows(mx);
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!((vmask >> (16 * mb + 4 * g + i)) & 1u)) sv[4 * mb + i] = -INFINITY;
+            }
+            float mx = sv[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+            mx = max4_rows(mx) * cabs;
             // lazy reference: move it only when a score clears it by kLazy;
             // the first valid tile needs no rescale (the output is zero)
             const bool up = mx > mref + kLazy;
@@ -333,7 +388,7 @@ struct Attend {
             float p[8], ps = 0.f;
             // arguments are <= kLazy; v_exp_f32 returns 0 for -inf
 #pragma unroll
-            for (int i = 0; i < 8; ++i) { p[i] = __builtin_amdgcn_exp2f(x[i] - mbase); ps += p[i]; }
+            for (int i = 0; i < 8; ++i) { p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], cabs, -mbase)); ps += p[i]; }
             lsum = lsum * alpha + ps;
             u32x4 pb;
             pb[0] = pack_f16(p[0], p[1]);
@@ -358,7 +413,7 @@ struct Attend {
     // Consumer wave cw = w - NHB: accumulates o[f][hb], the unnormalised
     // output of head 16hb + (lane & 15) and features
     // 16(FBW cw + f) + 4(lane >> 4) + i.
-    __device__ static void consume(const Ctx& c, f32x4 (&o)[C::FBW][C::NHB]) {
+    __device__ __forceinline__ static void consume(const Ctx& c, f32x4 (&o)[C::FBW][C::NHB]) {
         Smem& sm = *c.sm;
         const int l = c.l, g = c.g, c16 = c.c16;
         const int cw = c.w - C::NHB;
@@ -383,19 +438,10 @@ struct Attend {
                 moved |= al[hb] != 1.f;
             }
             if (__ballot(moved)) {   // wave-uniform and rare
-                // Rescale through a per-wave LDS scratch: the accumulators are
-                // only stored and reloaded here, never read by VALU, so the
-                // compiler can keep them in AGPRs on the hot path.
-                f32x4* scratch = sm.rescale[cw];
 #pragma unroll
-                for (int f = 0; f < C::FBW; ++f) {
+                for (int f = 0; f < C::FBW; ++f)
 #pragma unroll
-                    for (int hb = 0; hb < C::NHB; ++hb) scratch[hb * 64 + l] = o[f][hb];
-                    asm volatile("" ::: "memory");
-#pragma unroll
-                    for (int hb = 0; hb < C::NHB; ++hb) o[f][hb] = scratch[hb * 64 + l] * al[hb];
-                    asm volatile("" ::: "memory");
-                }
+                    for (int hb = 0; hb < C::NHB; ++hb) o[f][hb] *= al[hb];
             }
             const unsigned char* tile = sm.tile[it % kRing];
 #pragma unroll
@@ -403,8 +449,12 @@ struct Attend {
                 const int fb = C::FBW * cw + f;
                 // logical chunk 2fb + tb, swizzled in its aligned group of 16
                 const int off = vrow + 16 * (((2 * fb) & ~15) + (((2 * fb) & 15) ^ vx));
-                const u32x2 v0 = bf16x4_to_f16x4(lds_read_tr16(tile + off));
-                const u32x2 v1 = bf16x4_to_f16x4(lds_read_tr16(tile + off + 16 * C::CL * 16));
+                u32x2 v0 = lds_read_tr16(tile + off);
+                u32x2 v1 = lds_read_tr16(tile + off + 16 * C::CL * 16);
+                if constexpr (!F16) {
+                    v0 = bf16x4_to_f16x4(v0);
+                    v1 = bf16x4_to_f16x4(v1);
+                }
                 const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
 #pragma unroll
                 for (int hb = 0; hb < C::NHB; ++hb) o[f][hb] = mfma16_f16(av, pf[hb], o[f][hb]);
@@ -420,11 +470,11 @@ struct Attend {
     }
 };
 
-template <int NH, int DL, int DR>
+template <int NH, int DL, int DR, bool F16>
 __global__ __launch_bounds__((AttnShape<NH, DL, DR>::NT)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_kernel(AttnArgs a) {
     using C = AttnShape<NH, DL, DR>;
-    using A = Attend<NH, DL, DR>;
+    using A = Attend<NH, DL, DR, F16>;
     __shared__ __attribute__((aligned(16))) typename A::Smem sm;
     const int row = blockIdx.x;
     const int cnt = min(max(a.count[row], 0), a.top_k);
@@ -459,7 +509,7 @@ template <int NH, int DL, int DR>
 __global__ __launch_bounds__((AttnShape<NH, DL, DR>::NT)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_split_kernel(AttnSplitArgs a, SeqMeta m) {
     using C = AttnShape<NH, DL, DR>;
-    using A = Attend<NH, DL, DR>;
+    using A = Attend<NH, DL, DR, false>;
     __shared__ __attribute__((aligned(16))) typename A::Smem sm;
     const int item = blockIdx.x;
     const int b = seq_of_block(m, item);
@@ -492,6 +542,21 @@ void attention_split_kernel(AttnSplitArgs a, SeqMeta m) {
     }
 }
 
+// kv16 = kv with the Dl latent columns of every row converted bf16 -> fp16
+// (round to nearest even; exact for |v| in [2^-14, 65504]) and the rope
+// columns copied.  One thread per 16-byte chunk.
+template <int DL, int DR>
+__global__ __launch_bounds__(256) void latent_to_f16_kernel(const uint16_t* __restrict__ kv,
+                                                            uint16_t* __restrict__ kv16, int64_t nchunks) {
+    constexpr int CPR = (DL + DR) / 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= nchunks) return;
+    const int ch = (int)(gid % CPR);
+    u32x4 v = ldg16(kv + gid * 8);
+    if (ch < DL / 8) v = bf16x8_to_f16x8_rne(v);
+    *reinterpret_cast<u32x4*>(kv16 + gid * 8) = v;
+}
+
 // out[b,h,:] = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the chunks of b
 template <int NH, int DL>
 __global__ __launch_bounds__(128) void combine_kernel(AttnSplitArgs a, SeqMeta m) {
@@ -518,12 +583,26 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnSplitArgs a, SeqMeta m
 
 }  // namespace
 
-hipError_t launch_attention(int shape_id, const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attention(int shape_id, const AttnArgs& a, bool kv_f16, hipStream_t s) {
     if (a.rows <= 0) return hipSuccess;
-    if (shape_id == 0)
-        hipLaunchKernelGGL((attention_kernel<64, 512, 64>), dim3(a.rows), dim3(AttnShape<64, 512, 64>::NT), 0, s, a);
-    else
-        hipLaunchKernelGGL((attention_kernel<4, 64, 16>), dim3(a.rows), dim3(AttnShape<4, 64, 16>::NT), 0, s, a);
+    const dim3 grid(a.rows);
+    if (shape_id == 0) {
+        if (kv_f16) hipLaunchKernelGGL((attention_kernel<64, 512, 64, true>), grid, dim3(AttnShape<64, 512, 64>::NT), 0, s, a);
+        else hipLaunchKernelGGL((attention_kernel<64, 512, 64, false>), grid, dim3(AttnShape<64, 512, 64>::NT), 0, s, a);
+    } else {
+        if (kv_f16) hipLaunchKernelGGL((attention_kernel<4, 64, 16, true>), grid, dim3(AttnShape<4, 64, 16>::NT), 0, s, a);
+        else hipLaunchKernelGGL((attention_kernel<4, 64, 16, false>), grid, dim3(AttnShape<4, 64, 16>::NT), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_latent_to_f16(int shape_id, const uint16_t* kv, uint16_t* kv16, int64_t rows, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    const int cpr = shape_id == 0 ? (512 + 64) / 8 : (64 + 16) / 8;
+    const int64_t nchunks = rows * cpr;
+    const dim3 grid((unsigned)((nchunks + 255) / 256));
+    if (shape_id == 0) hipLaunchKernelGGL((latent_to_f16_kernel<512, 64>), grid, dim3(256), 0, s, kv, kv16, nchunks);
+    else hipLaunchKernelGGL((latent_to_f16_kernel<64, 16>), grid, dim3(256), 0, s, kv, kv16, nchunks);
     return hipGetLastError();
 }
 

@@ -67,9 +67,13 @@ int32_t first_sparse_row(int32_t L, int64_t q_start, int32_t top_k) {
 }
 
 int64_t padded_row(int64_t n) { return (n + 63) / 64 * 64; }
+// The attention gathers address a row through a 32-bit byte offset.
+bool attn_keys_ok(const dsa_shape* s, int64_t N) {
+    return N * 2 * (int64_t)(s->d_latent + s->d_rope) + 2 * (int64_t)(s->d_latent + s->d_rope) <= 0xFFFFFFFFll;
+}
 
 struct PrefillLayout {
-    size_t s_off, idx_off, cnt_off, total;
+    size_t s_off, idx_off, cnt_off, kv16_off, total;
     int32_t row0;
     int64_t ldS;
 };
@@ -81,7 +85,8 @@ PrefillLayout prefill_layout(const dsa_shape* s, int32_t L, int32_t N, int64_t q
     p.s_off = 0;
     p.idx_off = align_up((size_t)(L - p.row0) * (size_t)p.ldS * sizeof(float));
     p.cnt_off = p.idx_off + align_up((size_t)L * s->top_k * sizeof(int32_t));
-    p.total = p.cnt_off + align_up((size_t)L * sizeof(int32_t));
+    p.kv16_off = p.cnt_off + align_up((size_t)L * sizeof(int32_t));
+    p.total = p.kv16_off + align_up((size_t)N * (s->d_latent + s->d_rope) * sizeof(uint16_t));
     return p;
 }
 
@@ -196,9 +201,34 @@ dsa_status dsa_sparse_mla_attn(const dsa_shape* shape, const uint16_t* q, const 
         (lse && !aligned16(lse)))
         return DSA_ERR_INVALID_ARG;
     if (L <= 0 || N <= 0) return DSA_ERR_INVALID_ARG;
+    if (!attn_keys_ok(shape, N)) return DSA_ERR_UNSUPPORTED;
     if ((st = check_device())) return st;
     dsa::AttnArgs a{q, kv, idx, count, L, N, shape->top_k, scale_log2(shape), out, lse};
-    return launched(dsa::launch_attention(shape_id(shape), a, (hipStream_t)stream));
+    return launched(dsa::launch_attention(shape_id(shape), a, false, (hipStream_t)stream));
+}
+
+dsa_status dsa_latent_to_f16(const dsa_shape* shape, const uint16_t* kv, int32_t N, uint16_t* kv16,
+                             void* stream) {
+    dsa_status st = check_shape(shape);
+    if (st) return st;
+    if (!kv || !kv16 || !aligned16(kv) || !aligned16(kv16) || N <= 0) return DSA_ERR_INVALID_ARG;
+    if ((st = check_device())) return st;
+    return launched(dsa::launch_latent_to_f16(shape_id(shape), kv, kv16, N, (hipStream_t)stream));
+}
+
+dsa_status dsa_sparse_mla_attn_f16(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv16,
+                                   const int32_t* idx, const int32_t* count, int32_t L, int32_t N,
+                                   float* out, float* lse, void* stream) {
+    dsa_status st = check_shape(shape);
+    if (st) return st;
+    if (!q || !kv16 || !idx || !count || !out || !aligned16(q) || !aligned16(kv16) || !aligned16(out) ||
+        (lse && !aligned16(lse)))
+        return DSA_ERR_INVALID_ARG;
+    if (L <= 0 || N <= 0) return DSA_ERR_INVALID_ARG;
+    if (!attn_keys_ok(shape, N)) return DSA_ERR_UNSUPPORTED;
+    if ((st = check_device())) return st;
+    dsa::AttnArgs a{q, kv16, idx, count, L, N, shape->top_k, scale_log2(shape), out, lse};
+    return launched(dsa::launch_attention(shape_id(shape), a, true, (hipStream_t)stream));
 }
 
 size_t dsa_prefill_workspace_bytes(const dsa_shape* shape, int32_t L, int32_t N, int64_t q_start) {
@@ -237,9 +267,12 @@ dsa_status dsa_prefill_chunk(const dsa_shape* shape, const uint16_t* q, const ui
     // 2. selection (every earlier key below the boundary)
     dsa::TopkArgs ta{S, lay.ldS, lay.row0, L, q_start, shape->top_k, idx, cnt};
     if ((st = launched(dsa::launch_topk_prefill(ta, N, s)))) return st;
-    // 3. attention over the gathered rows
-    dsa::AttnArgs aa{q, kv, idx, cnt, L, N, shape->top_k, scale_log2(shape), out, nullptr};
-    return launched(dsa::launch_attention(sid, aa, s));
+    // 3. attention over the gathered rows, on an fp16-latent copy of the
+    //    cache (converted once per chunk, read by every query)
+    uint16_t* kv16 = reinterpret_cast<uint16_t*>(base + lay.kv16_off);
+    if ((st = launched(dsa::launch_latent_to_f16(sid, kv, kv16, N, s)))) return st;
+    dsa::AttnArgs aa{q, kv16, idx, cnt, L, N, shape->top_k, scale_log2(shape), out, nullptr};
+    return launched(dsa::launch_attention(sid, aa, true, s));
 }
 
 size_t dsa_decode_workspace_bytes(const dsa_shape* shape, int32_t B, const int64_t* ctx) {

@@ -111,7 +111,9 @@ struct AttnSplitArgs {
     float* part_ml;        // [items, H, 2] (running max in log2 units, sum)
     float* out;            // [B, H, Dl]
 };
-hipError_t launch_attention(int shape_id, const AttnArgs& a, hipStream_t s);
+// kv_f16: the cache's latent columns are fp16 (launch_latent_to_f16 output)
+hipError_t launch_attention(int shape_id, const AttnArgs& a, bool kv_f16, hipStream_t s);
+hipError_t launch_latent_to_f16(int shape_id, const uint16_t* kv, uint16_t* kv16, int64_t rows, hipStream_t s);
 hipError_t launch_attention_split(int shape_id, const AttnSplitArgs& a, const SeqMeta& m,
                                   int items, hipStream_t s);
 

@@ -52,6 +52,19 @@ def run_prefill(cfg, d):
     return host(out), host(idx), host(cnt)
 
 
+def run_attention(shape, q, kv, idx, cnt, L, N, out, lse, variant):
+    """dsa_sparse_mla_attn on a bf16 cache, or dsa_sparse_mla_attn_f16 on the
+    fp16-latent copy dsa_latent_to_f16 makes of it (all device tensors)."""
+    import torch
+    dsa = lib()
+    if variant == "bf16":
+        dsa.dsa_sparse_mla_attn(shape, q, kv, idx, cnt, L, N, out, lse)
+    else:
+        kv16 = torch.empty_like(kv)
+        dsa.dsa_latent_to_f16(shape, kv, N, kv16)
+        dsa.dsa_sparse_mla_attn_f16(shape, q, kv16, idx, cnt, L, N, out, lse)
+
+
 def check_selection_properties(idx, cnt, pos, top_k):
     """Every row: count = min(p+1, top_k), ascending ids in [0, p], -1 padding."""
     want = np.minimum(pos + 1, top_k)
@@ -181,6 +194,45 @@ def test_topk_full_sampled_bit_exact(name):
 
 
 # ---------------------------------------------------------------- attention
+@pytest.mark.parametrize("shape_name", ["TINY", "GLM"])
+def test_latent_to_f16_bit_exact(shape_name):
+    """Latent columns converted bf16 -> fp16 with round to nearest even
+    (numpy's float32 -> float16 is that rounding), rope columns copied; values
+    span normal, fp16-subnormal, overflowing and signed-zero cases."""
+    import torch
+    shape = getattr(W, shape_name)
+    rng = np.random.default_rng(7)
+    N = 1000
+    x = (rng.standard_normal((N, shape.d_qk)) * 10.0 ** rng.integers(-9, 6, size=(N, shape.d_qk))).astype(np.float32)
+    x[0, :4] = [0.0, -0.0, 70000.0, -1.0e-30]
+    kv = W.to_bf16_bits(x)
+    want = kv.copy()
+    lat = W.bf16_bits_to_f32(kv[:, :shape.d_latent]).astype(np.float16)
+    want[:, :shape.d_latent] = lat.view(np.uint16)
+    kv16 = torch.empty((N, shape.d_qk), dtype=torch.int16, device="cuda")
+    say("latent-to-f16", shape_name)
+    lib().dsa_latent_to_f16(shape, dev(kv), N, kv16)
+    assert np.array_equal(host(kv16), want)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_attention_f16_small(name):
+    """The fp16-latent kernel (the one the prefill chunk runs) on its own."""
+    import torch
+    cfg = W.PREFILL[name]
+    d = prefill_inputs(name)
+    ref_idx, ref_cnt, ref_out = oracle.prefill_chunk(d, cfg.shape, cfg.q_start)
+    _, ref_lse = oracle.sparse_mla_attn(d["q"], d["kv"], ref_idx, ref_cnt, cfg.shape.d_latent,
+                                        cfg.shape.softmax_scale, want_lse=True)
+    out = torch.empty((cfg.L, cfg.shape.n_heads, cfg.shape.d_latent), dtype=torch.float32, device="cuda")
+    lse = torch.empty((cfg.L, cfg.shape.n_heads), dtype=torch.float32, device="cuda")
+    say("attention-f16", name)
+    run_attention(cfg.shape, dev(d["q"]), dev(d["kv"]), dev(ref_idx), dev(ref_cnt), cfg.L, cfg.N, out, lse, "f16")
+    err = row_rel_err(host(out), ref_out)
+    assert err <= ATTN_TOL, err
+    assert np.abs(host(lse) - ref_lse).max() < 1e-4
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_attention_small(name):
     import torch
@@ -199,7 +251,8 @@ def test_attention_small(name):
     assert np.abs(host(lse) - ref_lse).max() < 1e-4
 
 
-def test_attention_selection_edge_cases():
+@pytest.mark.parametrize("variant", ["bf16", "f16"])
+def test_attention_selection_edge_cases(variant):
     """Unordered selections, -1 and out-of-range ids (skipped), counts above
     top_k (clamped), a single key, and a row with no usable key."""
     import torch
@@ -223,8 +276,8 @@ def test_attention_selection_edge_cases():
                                               cfg.shape.softmax_scale, want_lse=True)
     out = torch.empty((L, cfg.shape.n_heads, cfg.shape.d_latent), dtype=torch.float32, device="cuda")
     lse = torch.empty((L, cfg.shape.n_heads), dtype=torch.float32, device="cuda")
-    say("attention-edge")
-    lib().dsa_sparse_mla_attn(cfg.shape, dev(d["q"]), dev(d["kv"]), dev(idx), dev(cnt), L, N, out, lse)
+    say("attention-edge", variant)
+    run_attention(cfg.shape, dev(d["q"]), dev(d["kv"]), dev(idx), dev(cnt), L, N, out, lse, variant)
     o, s = host(out), host(lse)
     assert np.all(o[5] == 0.0) and np.all(s[5] == -np.inf)
     keep = np.arange(L) != 5
@@ -235,7 +288,7 @@ def test_attention_selection_edge_cases():
     for i in range(L):
         idx2[i, : min(cnt[i], k)] = rng.permutation(idx[i, : min(cnt[i], k)])
     out2 = torch.empty_like(out)
-    lib().dsa_sparse_mla_attn(cfg.shape, dev(d["q"]), dev(d["kv"]), dev(idx2), dev(cnt), L, N, out2, None)
+    run_attention(cfg.shape, dev(d["q"]), dev(d["kv"]), dev(idx2), dev(cnt), L, N, out2, None, variant)
     assert row_rel_err(host(out2)[keep], ref_out[keep]) <= ATTN_TOL
 
 
