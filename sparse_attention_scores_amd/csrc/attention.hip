@@ -57,6 +57,13 @@ namespace {
 constexpr int kTK = 32;        // keys per tile
 constexpr int kRing = 3;       // tiles resident in LDS: the ring keeps kRing - 2 gathers in flight
 constexpr float kLazy = 8.f;   // log2 headroom before the reference maximum moves
+// LDS fragments are read this many k-steps (scores) or feature blocks
+// (values) ahead of the MFMAs that use them.  Each read is pinned in
+// program order by a compiler memory fence: left alone, the scheduler sinks
+// the reads next to their MFMAs to save registers and every MFMA then waits
+// out a full LDS latency.
+constexpr int kKeyAhead = 2;
+constexpr int kValAhead = 2;
 
 template <int NH, int DL, int DR>
 struct AttnShape {
@@ -299,6 +306,8 @@ struct Attend {
         Smem& sm = *c.sm;
         const int w = c.w, l = c.l, g = c.g, c16 = c.c16;
         const int head = 16 * w + c16;
+        // producers are the critical path: let them issue first on their SIMD
+        __builtin_amdgcn_s_setprio(2);
         const u32x4 zero = {0u, 0u, 0u, 0u};
         u32x4 qf[C::KS];
 #pragma unroll
@@ -348,18 +357,20 @@ struct Attend {
             // validity of the tile's 32 keys: bit k is key t0 + k
             const uint32_t vmask = sm.valid[it];
             f32x4 s[2] = {};
-            u32x4 ka[3][2];   // key fragments, two k-steps ahead of their MFMAs
-            key_frag(tile, 0, ka[0]);
-            if (C::KS > 1) key_frag(tile, 1, ka[1]);
+            constexpr int KR = kKeyAhead + 1;
+            u32x4 ka[KR][2];   // key fragments, kKeyAhead k-steps ahead of their MFMAs
+#pragma unroll
+            for (int ks = 0; ks < kKeyAhead && ks < C::KS; ++ks) key_frag(tile, ks, ka[ks]);
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
-                if (ks + 2 < C::KS) key_frag(tile, ks + 2, ka[(ks + 2) % 3]);
+                if (ks + kKeyAhead < C::KS) key_frag(tile, ks + kKeyAhead, ka[(ks + kKeyAhead) % KR]);
+                asm volatile("" ::: "memory");
                 if (F16 && ks < C::KSL) {
-                    s[0] = mfma16_f16(ka[ks % 3][0], qf[ks], s[0]);
-                    s[1] = mfma16_f16(ka[ks % 3][1], qf[ks], s[1]);
+                    s[0] = mfma16_f16(ka[ks % KR][0], qf[ks], s[0]);
+                    s[1] = mfma16_f16(ka[ks % KR][1], qf[ks], s[1]);
                 } else {
-                    s[0] = mfma16_bf16(ka[ks % 3][0], qf[ks], s[0]);
-                    s[1] = mfma16_bf16(ka[ks % 3][1], qf[ks], s[1]);
+                    s[0] = mfma16_bf16(ka[ks % KR][0], qf[ks], s[0]);
+                    s[1] = mfma16_bf16(ka[ks % KR][1], qf[ks], s[1]);
                 }
             }
             // x = s * scale (log2 units) = sv * cabs; unusable keys -> -inf
@@ -444,13 +455,22 @@ struct Attend {
                     for (int hb = 0; hb < C::NHB; ++hb) o[f][hb] *= al[hb];
             }
             const unsigned char* tile = sm.tile[it % kRing];
-#pragma unroll
-            for (int f = 0; f < C::FBW; ++f) {
+            constexpr int VR = kValAhead + 1;
+            u32x2 vr[VR][2];   // raw value fragments, kValAhead feature blocks ahead
+            auto vread = [&](int f, u32x2 (&dst)[2]) {
                 const int fb = C::FBW * cw + f;
                 // logical chunk 2fb + tb, swizzled in its aligned group of 16
                 const int off = vrow + 16 * (((2 * fb) & ~15) + (((2 * fb) & 15) ^ vx));
-                u32x2 v0 = lds_read_tr16(tile + off);
-                u32x2 v1 = lds_read_tr16(tile + off + 16 * C::CL * 16);
+                dst[0] = lds_read_tr16(tile + off);
+                dst[1] = lds_read_tr16(tile + off + 16 * C::CL * 16);
+            };
+#pragma unroll
+            for (int f = 0; f < kValAhead && f < C::FBW; ++f) vread(f, vr[f]);
+#pragma unroll
+            for (int f = 0; f < C::FBW; ++f) {
+                if (f + kValAhead < C::FBW) vread(f + kValAhead, vr[(f + kValAhead) % VR]);
+                asm volatile("" ::: "memory");
+                u32x2 v0 = vr[f % VR][0], v1 = vr[f % VR][1];
                 if constexpr (!F16) {
                     v0 = bf16x4_to_f16x4(v0);
                     v1 = bf16x4_to_f16x4(v1);

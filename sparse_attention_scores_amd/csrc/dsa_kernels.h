@@ -50,6 +50,11 @@ __device__ inline f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+__device__ inline f32x16 mfma32_f16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 __device__ inline u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // ---- launchers (each returns hipGetLastError() of its launches) ----------
