@@ -122,24 +122,12 @@ __device__ inline u32x4 bf16x8_to_f16x8_rne(const u32x4& d) {
 }
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lds_bf16x4;
-#define DSA_LDS __attribute__((address_space(3)))
 
 __device__ inline u32x2 lds_read_tr16(const unsigned char* p) {
     const DSA_LDS lds_bf16x4* a = (const DSA_LDS lds_bf16x4*)(p);
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((DSA_LDS lds_bf16x4*)a));
 }
 
-__device__ inline uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const DSA_LDS void*)p;
-}
-
-// 16 bytes per lane from base + voff (a uniform 64-bit base, a per-lane
-// 32-bit offset) to LDS at m0 + 16 * lane.  M0 is written here and nowhere
-// else in these kernels.
-__device__ inline void gather16_to_lds(const void* base, uint32_t voff, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(base) : "memory");
-}
 
 // max / sum over the four lanes l, l^16, l^32, l^48 (one head's column), in
 // registers: v_permlane16_swap and v_permlane32_swap exchange 16-lane rows
@@ -156,8 +144,6 @@ __device__ inline float sum4_rows(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int N>
-__device__ inline void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
 // F16: the cache's latent columns hold fp16 (see latent_to_f16_kernel) rather
 // than bf16; the rope columns are bf16 either way.

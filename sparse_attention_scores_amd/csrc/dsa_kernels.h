@@ -57,6 +57,25 @@ __device__ inline f32x16 mfma32_f16(u32x4 a, u32x4 b, f32x16 c) {
 
 __device__ inline u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+#define DSA_LDS __attribute__((address_space(3)))
+
+__device__ inline uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const DSA_LDS void*)p;
+}
+
+// 16 bytes per lane from base + voff (a uniform 64-bit base, a per-lane
+// 32-bit offset) to LDS at m0 + 16 * lane, without passing through VGPRs.
+// Completion is counted by vmcnt only: the compiler does not see these
+// loads, so the kernel waits for them itself (wait_vmcnt) before a barrier.
+// M0 is written here and nowhere else in these kernels.
+__device__ inline void gather16_to_lds(const void* base, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(base) : "memory");
+}
+
+template <int N>
+__device__ inline void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
 // ---- launchers (each returns hipGetLastError() of its launches) ----------
 
 struct IndexerArgs {
@@ -69,6 +88,7 @@ struct IndexerArgs {
     int32_t N;            // keys
     int64_t pos0;         // position of the first scored query
     int32_t write_masked; // also write -inf for keys past each query
+    int32_t key_tile;     // keys per block (set by the launcher)
 };
 // Shape ids: 0 = GLM (Hi 32, Di 128), 1 = tiny (Hi 4, Di 32)
 hipError_t launch_indexer_prefill(int shape_id, const IndexerArgs& a, hipStream_t s);

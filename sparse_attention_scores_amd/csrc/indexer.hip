@@ -15,9 +15,12 @@
 // fp32 sum is exact while it stays below 2^24.
 //
 // Prefill: a block holds 16 queries (2 per wave, their Q fragments and
-// weights stay in VGPRs) and streams a 1024-key tile through LDS in 64-key
-// double-buffered sub-tiles, so each key row is read from L2 once per 16
-// queries.  Tiles past the block's last causal key are not computed.
+// weights stay in VGPRs) and streams a key tile through LDS in 128-key
+// double-buffered stages, so each key row is read from L2 once per 16
+// queries.  The tile is all keys when there are enough query blocks to fill
+// the chip (each query block's fragments are then loaded once), else the
+// keys are split so that the grid covers every compute unit.  Tiles past the
+// block's last causal key are not computed.
 // Decode: one query per sequence, so no reuse across queries: each wave reads
 // its keys straight from memory into MFMA operands (the step is HBM bound).
 #include "dsa_kernels.h"
@@ -39,8 +42,9 @@ struct IdxShape {
 constexpr int kIdxWaves = 8;
 constexpr int kIdxThreads = kIdxWaves * 64;
 constexpr int kIdxQPB = kIdxWaves * 2;   // queries per block
-constexpr int kIdxSub = 64;              // keys per LDS sub-tile
-constexpr int kIdxTile = 1024;           // keys per block
+constexpr int kIdxSub = 128;             // keys per LDS stage
+constexpr int kIdxChunks = kIdxSub / 32; // 32-key MFMA chunks per stage
+constexpr int kIdxCUs = 256;              // compute units the grid should cover
 
 constexpr int kIdxdWaves = 4;
 constexpr int kIdxdKeysPerWave = 128;
@@ -49,50 +53,73 @@ constexpr int kIdxdKeysPerBlock = kIdxdWaves * kIdxdKeysPerWave;
 // Head held by accumulator register r of lane-half `half` in the 32x32 layout.
 __device__ inline int acc_head(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
+// Query q's MFMA A fragments (rows = heads) and the weights of the 16 heads
+// this lane's accumulator holds.  Loads are unconditional (q must be a valid
+// row); rows past HI read as zero.
 template <int HI, int DI>
-__device__ inline void load_query(const uint16_t* qI, const float* w, int64_t q, bool valid,
-                                  int col, int half, u32x4 (&qf)[IdxShape<HI, DI>::KS],
-                                  float (&wr)[16]) {
+__device__ __forceinline__ void load_query(const uint16_t* qI, const float* w, int64_t q, int col,
+                                           int half, u32x4 (&qf)[IdxShape<HI, DI>::KS],
+                                           float (&wr)[16]) {
     using C = IdxShape<HI, DI>;
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    const int hc = col < HI ? col : HI - 1;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-        qf[ks] = (valid && col < HI) ? ldg16(qI + (q * HI + col) * DI + ks * 16 + half * 8) : zero;
+    for (int ks = 0; ks < C::KS; ++ks) {
+        const u32x4 v = ldg16(qI + (q * HI + hc) * DI + ks * 16 + half * 8);
+        qf[ks] = col < HI ? v : zero;
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int h = acc_head(r, half);
-        wr[r] = (valid && h < HI) ? w[q * HI + h] : 0.f;
+        const float v = w[q * HI + (h < HI ? h : HI - 1)];
+        wr[r] = h < HI ? v : 0.f;
     }
 }
 
+// relu as one integer max: a float's bit pattern read as int32 is negative
+// exactly when its sign bit is set, so max(bits, 0) maps every negative
+// value (and -0) to +0 and keeps the rest.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // sum over this lane's 16 heads of w * relu(score)
-__device__ inline float weighted_relu(const f32x16& acc, const float (&wr)[16]) {
+__device__ __forceinline__ float weighted_relu(const f32x16& acc, const float (&wr)[16]) {
     float s = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s = fmaf(wr[r], fmaxf(acc[r], 0.f), s);
+    for (int r = 0; r < 16; ++r) s = fmaf(wr[r], relu(acc[r]), s);
     return s;
 }
 
 // lanes 0-31 get x summed over both halves, lanes 32-63 get y summed likewise
-__device__ inline float combine_halves(float x, float y) {
+__device__ __forceinline__ float combine_halves(float x, float y) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Prefill: block = 16 queries (two per wave: lanes 0-31 report the first,
+// lanes 32-63 the second) x a key tile, streamed through LDS in 128-key
+// stages (double-buffered, filled by direct global-to-LDS loads).  The loop
+// is software-pipelined by one 32-key chunk: the MFMAs of chunk g are
+// interleaved with the relu-weighted head sum of chunk g-1, so the vector
+// ALU work runs under the matrix unit.  Results are stored once per stage,
+// right after the wait for the stage's loads (which also covers stores), so
+// the stores have a whole stage to drain before the next wait.
 template <int HI, int DI>
-__global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void indexer_prefill_kernel(IndexerArgs a) {
     using C = IdxShape<HI, DI>;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2][kIdxSub * C::ROWB];
+    constexpr int STAGE_B = kIdxSub * C::ROWB;            // LDS bytes per stage
+    static_assert(STAGE_B % 1024 == 0, "a stage must be whole 64-slot runs");
+    constexpr int NRUN = STAGE_B / 1024;                  // 64-slot DMA runs per stage
+    constexpr int RUNS = (NRUN + kIdxWaves - 1) / kIdxWaves;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2][STAGE_B];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int half = lane >> 5, col = lane & 31;
     const int q_base = blockIdx.y * kIdxQPB;
-    if (q_base >= a.rows) return;
     const int q_last = min(q_base + kIdxQPB, a.rows) - 1;
     const int64_t p_last = a.pos0 + q_last;
-    const int key_beg = blockIdx.x * kIdxTile;
-    const int key_tile_end = min(key_beg + kIdxTile, a.N);
+    const int key_beg = blockIdx.x * a.key_tile;
+    const int key_tile_end = min(key_beg + a.key_tile, a.N);
     const int kend = (int)min<int64_t>((int64_t)key_tile_end, p_last + 1);
 
     if (a.write_masked) {   // keys every query of the block masks
@@ -106,75 +133,88 @@ void indexer_prefill_kernel(IndexerArgs a) {
     }
     if (kend <= key_beg) return;
 
-    const int qa = q_base + 2 * wave, qb = qa + 1;
-    const bool va = qa < a.rows, vb = qb < a.rows;
-    const int64_t pa = a.pos0 + qa, pb = a.pos0 + qb;
-    const int64_t pmax = vb ? pb : pa;
+    // this lane's query (waves past the last row compute a copy and store nothing)
+    const int qa = min(q_base + 2 * wave, q_last), qb = min(q_base + 2 * wave + 1, q_last);
+    const int myq = q_base + 2 * wave + half;
+    const bool vq = myq <= q_last;
+    const int64_t myp = a.pos0 + myq;
+    float* srow = a.S + (int64_t)myq * a.ldS;
 
     u32x4 qfa[C::KS], qfb[C::KS];
     float wa[16], wb[16];
-    load_query<HI, DI>(a.qI, a.w, qa, va, col, half, qfa, wa);
-    load_query<HI, DI>(a.qI, a.w, qb, vb, col, half, qfb, wb);
+    load_query<HI, DI>(a.qI, a.w, qa, col, half, qfa, wa);
+    load_query<HI, DI>(a.qI, a.w, qb, col, half, qfb, wb);
 
-    constexpr int CH = kIdxSub * C::CPR;
-    constexpr int CPT = (CH + kIdxThreads - 1) / kIdxThreads;
-    u32x4 stage[CPT];
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    auto gload = [&](int s) {
+    // A stage is kIdxSub padded rows of ROWB bytes, i.e. SLOTS 16-byte slots
+    // in LDS order; row r's slot p < CPR holds piece p of key row
+    // (stage base + r), its padding slot a copy of piece 0.  Wave w fills
+    // the 64-slot runs w, w + 8, ... by DMA, each lane one slot.  Rows past
+    // the last key read the last key (never stored).
+    const uint32_t lds0 = lds_addr(&lds[0][0]);
+    const uint32_t kI_bytes_max = (uint32_t)(a.N - 1) * (uint32_t)(DI * 2);
+    auto dma = [&](int s, int buf) {
+        const int row0 = key_beg + s * kIdxSub;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int ci = tid + c * kIdxThreads;
-            const int j = key_beg + s * kIdxSub + ci / C::CPR;
-            stage[c] = (ci < CH && j < a.N) ? ldg16(a.kI + (int64_t)j * DI + (ci % C::CPR) * 8) : zero;
+        for (int c = 0; c < RUNS; ++c) {
+            const int run = wave + c * kIdxWaves;
+            if (RUNS * kIdxWaves == NRUN || run < NRUN) {
+                const int slot = run * 64 + lane;
+                const int r = slot / (C::CPR + 1), p = slot - r * (C::CPR + 1);
+                const uint32_t off = min((uint32_t)(row0 + r) * (uint32_t)(DI * 2), kI_bytes_max) +
+                                     (uint32_t)(p < C::CPR ? p : 0) * 16u;
+                gather16_to_lds(a.kI, off, lds0 + buf * STAGE_B + run * 1024);
+            }
         }
     };
-    auto swrite = [&](int buf) {
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int ci = tid + c * kIdxThreads;
-            if (ci < CH)
-                *reinterpret_cast<u32x4*>(&lds[buf][(ci / C::CPR) * C::ROWB + (ci % C::CPR) * 16]) = stage[c];
+    // store the head sum of flat chunk g (lanes: this lane's query, key g*32+col)
+    auto put = [&](int g, float v) {
+        const int key = key_beg + g * 32 + col;
+        if (g >= 0 && vq && key < kend) {
+            if (key <= myp) srow[key] = v;
+            else if (a.write_masked) srow[key] = -INFINITY;
         }
     };
 
     const int nsub = (kend - key_beg + kIdxSub - 1) / kIdxSub;
-    gload(0);
-    swrite(0);
+    dma(0, 0);
+    if (nsub > 1) dma(1, 1);
+    wait_vmcnt<0>();
     __syncthreads();
+
+    f32x16 pa = {}, pb = {};   // accumulators of the previous chunk
+    constexpr int NSTEP = kIdxChunks * C::KS;   // (chunk, k-step) pairs per stage
     for (int s = 0; s < nsub; ++s) {
-        if (s + 1 < nsub) gload(s + 1);
-        const unsigned char* buf = lds[s & 1];
+        const unsigned char* buf = lds[s & 1] + col * C::ROWB + half * 16;
+        auto bread = [&](int i) {
+            return *reinterpret_cast<const u32x4*>(buf + 32 * (i / C::KS) * C::ROWB + (i % C::KS) * 32);
+        };
+        float res[kIdxChunks];
+        u32x4 br[3];   // key fragments, read two k-steps ahead
+        br[0] = bread(0);
+        br[1] = bread(1);
+        f32x16 ca = {}, cb = {};
 #pragma unroll
-        for (int c = 0; c < kIdxSub / 32; ++c) {
-            const int jc = key_beg + s * kIdxSub + 32 * c;
-            if (!va || jc >= kend) continue;
-            const int key = jc + col;
-            const int q = half ? qb : qa;
-            const bool vq = half ? vb : va;
-            const int64_t p = half ? pb : pa;
-            if (jc > pmax) {   // every key of the chunk is past both queries
-                if (a.write_masked && vq && key < kend) a.S[(int64_t)q * a.ldS + key] = -INFINITY;
-                continue;
-            }
-            u32x4 bf[C::KS];
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks)
-                bf[ks] = *reinterpret_cast<const u32x4*>(buf + (32 * c + col) * C::ROWB + ks * 32 + half * 16);
-            f32x16 acca = {}, accb = {};
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                acca = mfma32_bf16(qfa[ks], bf[ks], acca);
-                accb = mfma32_bf16(qfb[ks], bf[ks], accb);
-            }
-            const float tot = combine_halves(weighted_relu(acca, wa), weighted_relu(accb, wb));
-            if (vq && key < kend) {
-                if (key <= p) a.S[(int64_t)q * a.ldS + key] = tot;
-                else if (a.write_masked) a.S[(int64_t)q * a.ldS + key] = -INFINITY;
+        for (int i = 0; i < NSTEP; ++i) {
+            const int ks = i % C::KS;
+            if (i + 2 < NSTEP) br[(i + 2) % 3] = bread(i + 2);
+            if (ks == 0) ca = cb = f32x16{};
+            ca = mfma32_bf16(qfa[ks], br[i % 3], ca);
+            cb = mfma32_bf16(qfb[ks], br[i % 3], cb);
+            if (ks == C::KS - 1) {
+                res[i / C::KS] = combine_halves(weighted_relu(pa, wa), weighted_relu(pb, wb));
+                pa = ca;
+                pb = cb;
             }
         }
-        if (s + 1 < nsub) swrite((s + 1) & 1);
+        // stage s+1 has landed and every wave is done with stage s, whose
+        // buffer then takes stage s+2; the stores drain during stage s+1
+        wait_vmcnt<0>();
         __syncthreads();
+        if (s + 2 < nsub) dma(s + 2, s & 1);
+#pragma unroll
+        for (int t = 0; t < kIdxChunks; ++t) put(s * kIdxChunks + t - 1, res[t]);
     }
+    put(nsub * kIdxChunks - 1, combine_halves(weighted_relu(pa, wa), weighted_relu(pb, wb)));
 }
 
 template <int HI, int DI>
@@ -191,7 +231,7 @@ void indexer_decode_kernel(const uint16_t* __restrict__ qI, const uint16_t* __re
 
     u32x4 qf[C::KS];
     float wr[16];
-    load_query<HI, DI>(qI, w, b, true, col, half, qf, wr);
+    load_query<HI, DI>(qI, w, b, col, half, qf, wr);
     const uint16_t* kbase = kI + m.key_off[b] * DI;
     float* srow = S + m.s_off[b];
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -223,11 +263,18 @@ int indexer_decode_keys_per_block() { return kIdxdKeysPerBlock; }
 
 hipError_t launch_indexer_prefill(int shape_id, const IndexerArgs& a, hipStream_t s) {
     if (a.rows <= 0) return hipSuccess;
-    dim3 grid((a.N + kIdxTile - 1) / kIdxTile, (a.rows + kIdxQPB - 1) / kIdxQPB);
+    // key rows are addressed with 32-bit byte offsets (one stage past N included)
+    const int64_t row_bytes = shape_id == 0 ? 256 : 64;
+    if (((int64_t)a.N + kIdxSub) * row_bytes > 0xFFFFFFFFll) return hipErrorInvalidValue;
+    const int qblocks = (a.rows + kIdxQPB - 1) / kIdxQPB;
+    const int ntiles = max(1, min((kIdxCUs + qblocks - 1) / qblocks, (a.N + kIdxSub - 1) / kIdxSub));
+    IndexerArgs b = a;
+    b.key_tile = ((a.N + ntiles - 1) / ntiles + kIdxSub - 1) / kIdxSub * kIdxSub;
+    dim3 grid((a.N + b.key_tile - 1) / b.key_tile, qblocks);
     if (shape_id == 0)
-        hipLaunchKernelGGL((indexer_prefill_kernel<32, 128>), grid, dim3(kIdxThreads), 0, s, a);
+        hipLaunchKernelGGL((indexer_prefill_kernel<32, 128>), grid, dim3(kIdxThreads), 0, s, b);
     else
-        hipLaunchKernelGGL((indexer_prefill_kernel<4, 32>), grid, dim3(kIdxThreads), 0, s, a);
+        hipLaunchKernelGGL((indexer_prefill_kernel<4, 32>), grid, dim3(kIdxThreads), 0, s, b);
     return hipGetLastError();
 }
 
