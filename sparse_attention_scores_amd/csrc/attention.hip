@@ -21,7 +21,9 @@
 //    selected rows are then gathered 32 per tile straight into LDS with
 //    global_load_lds_dwordx4 (16 bytes per lane, no registers) into a ring
 //    of three tiles: while consumers read tile it and producers score tile
-//    it+1, tile it+2 is in flight.  The loads are issued from inline
+//    it+1, tile it+2 is in flight.  The consumers issue the whole gather:
+//    handing a tile's loads to the CU's address unit holds the issuing wave
+//    for hundreds of cycles, which the producers cannot spare.  The loads are issued from inline
 //    assembly and waited for with explicit vmcnt counts: the compiler's own
 //    wait insertion would drain every outstanding LDS load before each LDS
 //    read.  A 1 KB latent row is one instruction with a scalar row address.
@@ -84,11 +86,14 @@ struct AttnShape {
     static constexpr int TILE_B = LAT_B + kTK * CR * 16;
     static constexpr int IL = kTK * CL / 64;             // gather instructions, latent region
     static constexpr int IR = kTK * CR / 64;             // gather instructions, rope region
-    static constexpr int ILW = IL / NWAVE;               // latent instructions per wave
+    static constexpr int NG = NHB;                       // gather waves (the consumers)
+    static constexpr int ILW = IL / NG;                  // latent instructions per gather wave
+    static constexpr int IRW = IR / NG;                  // rope instructions per gather wave
     static constexpr int LR = 64 / CL > 0 ? 64 / CL : 1; // rows per latent instruction
     static_assert((CL & (CL - 1)) == 0 && (CR & (CR - 1)) == 0, "row chunk counts must be powers of two");
     static_assert(64 % CL == 0 || CL == 64, "latent rows must pack whole instructions");
-    static_assert(FB % NHB == 0 && IL % NWAVE == 0 && IR <= NWAVE && kTK * CR % 64 == 0,
+    static_assert(64 % CR == 0, "rope rows must pack whole instructions");
+    static_assert(FB % NHB == 0 && IL % NG == 0 && IR % NG == 0 && kTK * CR % 64 == 0,
                   "work must split evenly");
 };
 
@@ -206,9 +211,10 @@ struct Attend {
                 sm.valid[word + 1] = (uint32_t)(m >> 32);
             }
         }
+        const int gw = max(c.w - C::NHB, 0);   // gather wave index (consumers)
 #pragma unroll
         for (int k = 0; k < C::ILW; ++k) {
-            const int i = C::ILW * c.w + k;
+            const int i = C::ILW * gw + k;
             const int slot = i * 64 + c.l;
             const int r = slot / C::CL, pc = slot % C::CL;
             c.lat_off[k] = 16u * (uint32_t)(pc ^ (swz_lat(r) & (C::CL - 1)));
@@ -217,44 +223,71 @@ struct Attend {
         return c;
     }
 
-    // Gather tile `it` (this wave's share): latent instruction i covers slots
-    // i*64 .. i*64+63 of the latent region (row slot / CL, physical chunk
-    // slot % CL), rope instruction i likewise in the rope region.  Padding
-    // chunks read chunk 0 (they meet zero query columns).  With 64 chunks
-    // per latent row an instruction moves one whole row: its address is
-    // wave-uniform (scalar).
-    __device__ __forceinline__ static void gather(const Ctx& c, int it) {
-        Smem& sm = *c.sm;
-        unsigned char* buf = sm.tile[it % kRing];
+    // The gather is issued by the consumer waves only.  Issuing a tile's
+    // loads occupies the wave until the CU's address unit has taken them
+    // (about 64 bytes per clock for the whole CU), and the consumers have
+    // the slack for it; the producers, whose scores are the critical path,
+    // start their product right after the barrier.
+    //
+    // Cache rows one gather of a consumer wave reads: one per latent
+    // instruction (wave-uniform when an instruction moves a whole row) and
+    // this lane's row per rope instruction.  They are read from LDS one
+    // iteration before the gather that uses them, so the gather issues
+    // without waiting on LDS.
+    struct Rows {
+        int lat[C::ILW];
+        int rope[C::IRW];
+    };
+    __device__ __forceinline__ static void load_rows(const Ctx& c, int it, Rows& r) {
+        const Smem& sm = *c.sm;
         const int t0 = it * kTK;
-        constexpr uint32_t kRowBytes = 2u * C::DQK;
+        const int gw = c.w - C::NHB;
 #pragma unroll
         for (int k = 0; k < C::ILW; ++k) {
-            const int i = C::ILW * c.w + k;
+            const int i = C::ILW * gw + k;
+            r.lat[k] = (C::LR == 1) ? sm.sel[t0 + i] : sm.sel[t0 + (i * 64 + c.l) / C::CL];
+        }
+#pragma unroll
+        for (int k = 0; k < C::IRW; ++k) r.rope[k] = sm.sel[t0 + ((gw + C::NG * k) * 64 + c.l) / C::CR];
+    }
+
+    // Gather tile `it` (this consumer's share) from the rows of that tile:
+    // latent instruction i covers slots i*64 .. i*64+63 of the latent region
+    // (row slot / CL, physical chunk slot % CL), rope instruction i likewise
+    // in the rope region.  Padding chunks read chunk 0 (they meet zero query
+    // columns).  With 64 chunks per latent row an instruction moves one
+    // whole row: its address is wave-uniform (scalar).
+    __device__ __forceinline__ static void gather(const Ctx& c, int it, const Rows& rows) {
+        Smem& sm = *c.sm;
+        unsigned char* buf = sm.tile[it % kRing];
+        constexpr uint32_t kRowBytes = 2u * C::DQK;
+        const int gw = c.w - C::NHB;
+#pragma unroll
+        for (int k = 0; k < C::ILW; ++k) {
+            const int i = C::ILW * gw + k;
             if constexpr (C::LR == 1) {
-                const int j = __builtin_amdgcn_readfirstlane(sm.sel[t0 + i]);
+                const int j = __builtin_amdgcn_readfirstlane(rows.lat[k]);
                 gather16_to_lds(c.kv + (int64_t)j * C::DQK, c.lat_off[k], lds_addr(buf + 1024 * i));
             } else {
-                const int j = sm.sel[t0 + (i * 64 + c.l) / C::CL];
-                gather16_to_lds(c.kv, (uint32_t)j * kRowBytes + c.lat_off[k], lds_addr(buf + 1024 * i));
+                gather16_to_lds(c.kv, (uint32_t)rows.lat[k] * kRowBytes + c.lat_off[k], lds_addr(buf + 1024 * i));
             }
         }
-        if (c.w < C::IR) {
-            const int i = c.w;
+#pragma unroll
+        for (int k = 0; k < C::IRW; ++k) {
+            const int i = gw + C::NG * k;
             const int slot = i * 64 + c.l;
             const int r = slot / C::CR, pc = slot % C::CR;
             const int ch = pc ^ (swz_rope(r) & (C::CR - 1));
-            const int j = sm.sel[t0 + r];
-            gather16_to_lds(c.kv, (uint32_t)j * kRowBytes + 2u * DL + 16u * (ch < C::CRD ? ch : 0),
+            gather16_to_lds(c.kv, (uint32_t)rows.rope[k] * kRowBytes + 2u * DL + 16u * (ch < C::CRD ? ch : 0),
                             lds_addr(buf + C::LAT_B + 1024 * i));
         }
     }
 
-    // Wait until at most K tiles of this wave's gathers are outstanding.
+    // Consumer: wait until at most K tiles of this wave's gathers are
+    // outstanding.
     template <int K>
     __device__ __forceinline__ static void wait_tiles(const Ctx& c) {
-        if (c.w < C::IR) wait_vmcnt<K * (C::ILW + 1)>();
-        else wait_vmcnt<K * C::ILW>();
+        wait_vmcnt<K * (C::ILW + C::IRW)>();
     }
     __device__ __forceinline__ static void wait_tiles_rt(const Ctx& c, int k) {   // k uniform, < kRing
         static_assert(kRing <= 5, "extend the switch");
@@ -268,22 +301,34 @@ struct Attend {
 
     // Prologue shared by both roles: tiles 0 .. kRing-2 in flight, tile 0
     // landed.
-    __device__ __forceinline__ static void prologue(const Ctx& c) {
+    __device__ __forceinline__ static void prologue(const Ctx& c, Rows& rows) {
+        if (c.w >= C::NHB) {
 #pragma unroll
-        for (int t = 0; t < kRing - 1; ++t)
-            if (t < c.ntiles) gather(c, t);
-        if (c.ntiles > 0) wait_tiles_rt(c, min(kRing - 2, c.ntiles - 1));
+            for (int t = 0; t < kRing - 1; ++t) {
+                if (t < c.ntiles) {
+                    load_rows(c, t, rows);
+                    gather(c, t, rows);
+                }
+            }
+            if (kRing - 1 < c.ntiles) load_rows(c, kRing - 1, rows);
+            if (c.ntiles > 0) wait_tiles_rt(c, min(kRing - 2, c.ntiles - 1));
+        }
         __syncthreads();
     }
 
     // Top of iteration it, both roles: tile it+1 landed for every wave,
     // probabilities of tile it visible, tile it-1 free; then tile
-    // it+kRing-1 is gathered into tile it-1's buffer.
-    __device__ __forceinline__ static void step(const Ctx& c, int it) {
+    // it+kRing-1 is gathered into tile it-1's buffer (its rows were read in
+    // the previous iteration) and the rows of the next gather are read.
+    __device__ __forceinline__ static void step(const Ctx& c, int it, Rows& rows) {
+        const bool gatherer = c.w >= C::NHB;
         // tiles it+1 .. min(it+kRing-2, ntiles-1) are in flight; keep all but it+1
-        if (it + 1 < c.ntiles) wait_tiles_rt(c, min(kRing - 3, c.ntiles - 2 - it));
+        if (gatherer && it + 1 < c.ntiles) wait_tiles_rt(c, min(kRing - 3, c.ntiles - 2 - it));
         __syncthreads();
-        if (it + kRing - 1 < c.ntiles) gather(c, it + kRing - 1);
+        if (gatherer && it + kRing - 1 < c.ntiles) {
+            gather(c, it + kRing - 1, rows);
+            if (it + kRing < c.ntiles) load_rows(c, it + kRing, rows);
+        }
     }
 
     // Producer wave hb = w: scores and softmax of heads 16hb .. 16hb+15.
@@ -307,10 +352,6 @@ struct Attend {
 #pragma unroll
             for (int ks = 0; ks < C::KSL; ++ks) qf[ks] = bf16x8_to_f16x8_rne(qf[ks]);
         }
-        // Consume the fragments here so that every compiler-tracked load has
-        // completed before the gather loop: its LDS loads are counted by hand.
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) asm volatile("" :: "v"(qf[ks]));
         float mref = -INFINITY, lsum = 0.f;   // for head `head` (replicated over g)
         const bool neg_scale = scale_log2 < 0.f;
         const float cabs = fabsf(scale_log2);
@@ -396,10 +437,11 @@ struct Attend {
             sm.alpha[it & 1][head] = alpha;   // the four lanes of a head store the same value
         };
 
-        prologue(c);
+        Rows rows;
+        prologue(c, rows);
         if (c.ntiles > 0) score(0);
         for (int it = 0; it < c.ntiles; ++it) {
-            step(c, it);
+            step(c, it, rows);
             if (it + 1 < c.ntiles) score(it + 1);
         }
         lsum = sum4_rows(lsum);
@@ -467,9 +509,10 @@ struct Attend {
             }
         };
 
-        prologue(c);
+        Rows rows;
+        prologue(c, rows);
         for (int it = 0; it < c.ntiles; ++it) {
-            step(c, it);
+            step(c, it, rows);
             values(it);
         }
         __syncthreads();
