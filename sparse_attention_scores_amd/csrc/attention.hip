@@ -606,27 +606,51 @@ __global__ __launch_bounds__(256) void latent_to_f16_kernel(const uint16_t* __re
     *reinterpret_cast<u32x4*>(kv16 + gid * 8) = v;
 }
 
-// out[b,h,:] = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the chunks of b
+// out[b,h,:] = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the chunks
+// c of sequence b.  Wave 0 turns the chunks' (m, l) into one weight per chunk
+// (lane c holds chunk c; M and the denominator are wave reductions); then
+// every thread owns four features and issues the loads of all chunks back to
+// back.  Chunks without a usable key have m = -inf and weight 0 (their
+// partial output is zero).
 template <int NH, int DL>
 __global__ __launch_bounds__(128) void combine_kernel(AttnSplitArgs a, SeqMeta m) {
+    constexpr int kMaxChunks = kMaxTopK / kTK;   // chunks hold at least one tile
+    static_assert(kMaxChunks <= 64, "one lane per chunk");
+    __shared__ float wgt[kMaxChunks];
     const int b = blockIdx.x / NH, h = blockIdx.x % NH;
-    const int it0 = m.blk0[b], it1 = m.blk0[b + 1];
-    float M = -INFINITY;
-    for (int it = it0; it < it1; ++it) M = fmaxf(M, a.part_ml[((int64_t)it * NH + h) * 2]);
-    float den = 0.f;
-    for (int it = it0; it < it1; ++it) {
-        const float mi = a.part_ml[((int64_t)it * NH + h) * 2];
-        if (mi != -INFINITY) den += exp2f(mi - M) * a.part_ml[((int64_t)it * NH + h) * 2 + 1];
-    }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    for (int f = 4 * threadIdx.x; f < DL; f += 4 * 128) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int it = it0; it < it1; ++it) {
-            const float mi = a.part_ml[((int64_t)it * NH + h) * 2];
-            if (mi == -INFINITY) continue;
-            acc += exp2f(mi - M) * *reinterpret_cast<const f32x4*>(a.part_o + ((int64_t)it * NH + h) * DL + f);
+    const int it0 = m.blk0[b];
+    const int n = min(m.blk0[b + 1] - it0, kMaxChunks);
+    const int tid = threadIdx.x;
+    if (tid < 64) {
+        float mi = -INFINITY, li = 0.f;
+        if (tid < n) {
+            mi = a.part_ml[((int64_t)(it0 + tid) * NH + h) * 2];
+            li = a.part_ml[((int64_t)(it0 + tid) * NH + h) * 2 + 1];
         }
-        *reinterpret_cast<f32x4*>(a.out + ((int64_t)b * NH + h) * DL + f) = acc * inv;
+        float M = mi;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        const float e = (mi == -INFINITY) ? 0.f : exp2f(mi - M);
+        float den = e * li;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        if (tid < kMaxChunks) wgt[tid] = tid < n ? e * inv : 0.f;
+    }
+    __syncthreads();
+    for (int f = 4 * tid; f < DL; f += 4 * 128) {
+        const float* po = a.part_o + ((int64_t)it0 * NH + h) * DL + f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        int c = 0;
+        for (; c + 8 <= n; c += 8) {
+            f32x4 v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const f32x4*>(po + (int64_t)(c + k) * NH * DL);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc += wgt[c + k] * v[k];
+        }
+        for (; c < n; ++c) acc += wgt[c] * *reinterpret_cast<const f32x4*>(po + (int64_t)c * NH * DL);
+        *reinterpret_cast<f32x4*>(a.out + ((int64_t)b * NH + h) * DL + f) = acc;
     }
 }
 

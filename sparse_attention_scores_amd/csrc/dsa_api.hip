@@ -93,8 +93,9 @@ PrefillLayout prefill_layout(const dsa_shape* s, int32_t L, int32_t N, int64_t q
 struct DecodeLayout {
     SeqMeta idx_meta;    // blocks of the indexer kernel
     SeqMeta attn_meta;   // blocks (chunks) of the attention kernel
+    SeqMeta topk_meta;   // segment blocks of the top-k
     int idx_blocks, attn_items, chunk, n_max;
-    size_t s_off, idx_off, cnt_off, po_off, pml_off, total;
+    size_t s_off, idx_off, cnt_off, po_off, pml_off, cand_off, total;
 };
 
 // Chunk of selected keys per attention block: enough blocks to cover the
@@ -116,7 +117,7 @@ dsa_status decode_layout(const dsa_shape* s, int32_t B, const int64_t* ctx, Deco
     d.chunk = decode_chunk(s, B, ctx);
     const int kpb = dsa::indexer_decode_keys_per_block();
     int64_t koff = 0, soff = 0;
-    int iblk = 0, items = 0;
+    int iblk = 0, items = 0, tblk = 0;
     d.n_max = 1;
     for (int b = 0; b < B; ++b) {
         if (ctx[b] <= 0) return DSA_ERR_INVALID_ARG;
@@ -127,6 +128,11 @@ dsa_status decode_layout(const dsa_shape* s, int32_t B, const int64_t* ctx, Deco
         d.idx_meta.ctx[b] = d.attn_meta.ctx[b] = c;
         d.idx_meta.blk0[b] = iblk;
         d.attn_meta.blk0[b] = items;
+        d.topk_meta.key_off[b] = koff;
+        d.topk_meta.s_off[b] = soff;
+        d.topk_meta.ctx[b] = c;
+        d.topk_meta.blk0[b] = tblk;
+        tblk += dsa::topk_decode_segments(c);
         // a sequence within top_k keeps every key: no scores needed
         if (c > s->top_k) iblk += (c + kpb - 1) / kpb;
         const int cnt = c < s->top_k ? c : s->top_k;
@@ -140,6 +146,10 @@ dsa_status decode_layout(const dsa_shape* s, int32_t B, const int64_t* ctx, Deco
     d.idx_meta.s_off[B] = d.attn_meta.s_off[B] = soff;
     d.idx_meta.blk0[B] = iblk;
     d.attn_meta.blk0[B] = items;
+    d.topk_meta.B = B;
+    d.topk_meta.key_off[B] = koff;
+    d.topk_meta.s_off[B] = soff;
+    d.topk_meta.blk0[B] = tblk;
     d.idx_blocks = iblk;
     d.attn_items = items;
     d.s_off = 0;
@@ -147,7 +157,8 @@ dsa_status decode_layout(const dsa_shape* s, int32_t B, const int64_t* ctx, Deco
     d.cnt_off = d.idx_off + align_up((size_t)B * s->top_k * sizeof(int32_t));
     d.po_off = d.cnt_off + align_up((size_t)B * sizeof(int32_t));
     d.pml_off = d.po_off + align_up((size_t)items * s->n_heads * s->d_latent * sizeof(float));
-    d.total = d.pml_off + align_up((size_t)items * s->n_heads * 2 * sizeof(float));
+    d.cand_off = d.pml_off + align_up((size_t)items * s->n_heads * 2 * sizeof(float));
+    d.total = d.cand_off + align_up((size_t)tblk * s->top_k * sizeof(int32_t));
     return DSA_OK;
 }
 
@@ -305,7 +316,9 @@ dsa_status dsa_decode_step(const dsa_shape* shape, int32_t B, const int64_t* ctx
     int32_t* cnt = count_out ? count_out : reinterpret_cast<int32_t*>(base + d.cnt_off);
 
     if ((st = launched(dsa::launch_indexer_decode(sid, qI, kI, w, S, d.idx_meta, d.idx_blocks, s)))) return st;
-    if ((st = launched(dsa::launch_topk_decode(S, d.idx_meta, shape->top_k, idx, cnt, d.n_max, s)))) return st;
+    if ((st = launched(dsa::launch_topk_decode(S, d.topk_meta, shape->top_k, idx, cnt,
+                                               reinterpret_cast<int32_t*>(base + d.cand_off), d.n_max, s))))
+        return st;
     dsa::AttnSplitArgs aa{q, kv, idx, shape->top_k, d.chunk, scale_log2(shape),
                           reinterpret_cast<float*>(base + d.po_off), reinterpret_cast<float*>(base + d.pml_off),
                           out};

@@ -108,8 +108,12 @@ struct TopkArgs {
     int32_t* count;       // [rows] or null
 };
 hipError_t launch_topk_prefill(const TopkArgs& a, int n_max, hipStream_t s);
+// Decode top-k: m.blk0 numbers the segment blocks of each sequence
+// (topk_decode_segments(ctx) each); cand holds top_k int32 per segment block
+// and is used only when a sequence has more than one segment.
+int topk_decode_segments(int ctx);
 hipError_t launch_topk_decode(const float* S, const SeqMeta& m, int top_k, int32_t* idx,
-                              int32_t* count, int n_max, hipStream_t s);
+                              int32_t* count, int32_t* cand, int n_max, hipStream_t s);
 
 struct AttnArgs {
     const uint16_t* q;     // [rows, H, Dqk]

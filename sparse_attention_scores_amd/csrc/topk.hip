@@ -34,6 +34,7 @@ namespace {
 
 constexpr int kBins = 256;
 constexpr int kMaxLevels = 4;
+constexpr int kDecodeSeg = 8192;    // keys per decode segment block
 
 // Larger float -> larger key; -0 ranks equal to +0 (the floats compare equal).
 __device__ inline uint32_t order_key(float f) {
@@ -119,8 +120,36 @@ __device__ inline int value_bin(float v, float lo, float scale) {
     return min(max(b, 0), kBins - 1);
 }
 
-template <int NT, int EPT>
-__device__ __forceinline__ void topk_row(const float* __restrict__ srow, int n, int top_k,
+// Element k of a row: its score, and the key index written for it.
+struct DirectRow {   // element k is key k
+    static constexpr bool kRemap = false;
+    const float* __restrict__ s;
+    __device__ __forceinline__ float load(int k) const { return s[k]; }
+    __device__ __forceinline__ int32_t index(int k) const { return k; }
+};
+// The candidates of a segmented row: the concatenated selections of its
+// segments (seg keys each, top_k entries per segment, each in ascending
+// order and padded with -1), so element order is key order.  An entry holds
+// a key index local to its segment.  Padding entries score -inf; they are
+// never kept, because every full segment brings top_k finite scores.
+struct CandRow {
+    static constexpr bool kRemap = true;   // outputs are element positions until remapped
+    const float* __restrict__ s;       // the sequence's scores
+    const int32_t* __restrict__ cand;
+    int top_k, seg;
+    __device__ __forceinline__ int32_t key(int k) const {
+        const int c = cand[k];
+        return c < 0 ? -1 : (k / top_k) * seg + c;
+    }
+    __device__ __forceinline__ float load(int k) const {
+        const int j = key(k);
+        return j < 0 ? -INFINITY : s[j];
+    }
+    __device__ __forceinline__ int32_t index(int k) const { return key(k); }
+};
+
+template <int NT, int EPT, typename Row>
+__device__ __forceinline__ void topk_row(const Row& row, int n, int top_k,
                                          int32_t* __restrict__ out, int32_t* count, TopkSmem<NT, EPT>& sm) {
     static_assert(NT >= kBins && NT % 64 == 0 && EPT >= 1 && EPT <= 64, "topk geometry");
     static_assert(EPT * (NT / 64) <= NT, "one scan slot per thread");
@@ -137,10 +166,8 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ srow, int n, 
     float f[EPT];
     const int nfull = n / NT;     // elements every lane of the block holds
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {   // every load in bounds; no waits between them
-        const float* p = srow + e * NT;
-        f[e] = e < nfull ? p[tid] : srow[min(e * NT + tid, n - 1)];
-    }
+    for (int e = 0; e < EPT; ++e)   // every load in bounds; no waits between them
+        f[e] = row.load(e < nfull ? e * NT + tid : min(e * NT + tid, n - 1));
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
         const float x = f[e] == f[e] ? f[e] : -INFINITY;
@@ -327,6 +354,12 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ srow, int n, 
             if (((sel >> lane) & 1) && slot >= 0 && slot < top_k) out[slot] = e * NT + t_;
         }
     }
+    if constexpr (Row::kRemap) {
+        // element positions -> key indices, in one coalesced pass (a lookup
+        // per kept element inside the loop above would serialise its loads)
+        __syncthreads();
+        for (int t = tid; t < top_k; t += NT) out[t] = row.index(out[t]);
+    }
     if (tid == 0 && count) *count = top_k;
 }
 
@@ -337,16 +370,40 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     const int64_t p = a.pos0 + r;
     const int n = (int)(p + 1);
     const float* srow = (n > a.top_k) ? a.S + (int64_t)(r - a.s_row0) * a.ldS : nullptr;
-    topk_row<NT, EPT>(srow, n, a.top_k, a.idx + (int64_t)r * a.top_k, a.count ? a.count + r : nullptr, sm);
+    topk_row<NT, EPT>(DirectRow{srow}, n, a.top_k, a.idx + (int64_t)r * a.top_k, a.count ? a.count + r : nullptr,
+                      sm);
 }
 
+// Decode, phase 1: block -> (sequence b, segment g) of kDecodeSeg keys.  A
+// sequence of one segment is finished here; otherwise the segment's
+// selection goes to the candidate list (top_k entries per segment block).
 template <int NT, int EPT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_decode_kernel(const float* S, SeqMeta m, int top_k, int32_t* idx,
-                                                         int32_t* count) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_decode_kernel(
+        const float* S, SeqMeta m, int top_k, int32_t* idx, int32_t* count, int32_t* cand) {
+    __shared__ TopkSmem<NT, EPT> sm;
+    const int b = seq_of_block(m, blockIdx.x);
+    const int g = blockIdx.x - m.blk0[b];
+    const int ctx = m.ctx[b];
+    const int k0 = g * kDecodeSeg;
+    const int n = min(ctx - k0, kDecodeSeg);
+    const float* srow = S + m.s_off[b] + k0;
+    if (ctx <= kDecodeSeg)
+        topk_row<NT, EPT>(DirectRow{srow}, n, top_k, idx + (int64_t)b * top_k, count ? count + b : nullptr, sm);
+    else
+        topk_row<NT, EPT>(DirectRow{srow}, n, top_k, cand + (int64_t)blockIdx.x * top_k, nullptr, sm);
+}
+
+// Decode, phase 2: block b selects sequence b's top_k among the candidates
+// of its segments (sequences of one segment have nothing to do).
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_merge_kernel(
+        const float* S, SeqMeta m, int top_k, int32_t* idx, int32_t* count, const int32_t* cand) {
     __shared__ TopkSmem<NT, EPT> sm;
     const int b = blockIdx.x;
-    topk_row<NT, EPT>(S + m.s_off[b], m.ctx[b], top_k, idx + (int64_t)b * top_k, count ? count + b : nullptr,
-                      sm);
+    const int nseg = m.blk0[b + 1] - m.blk0[b];
+    if (nseg < 2) return;
+    const CandRow row{S + m.s_off[b], cand + (int64_t)m.blk0[b] * top_k, top_k, kDecodeSeg};
+    topk_row<NT, EPT>(row, nseg * top_k, top_k, idx + (int64_t)b * top_k, count ? count + b : nullptr, sm);
 }
 
 // Block shape by row length: up to 32 keys per thread in 256-, then 512-,
@@ -367,6 +424,21 @@ hipError_t dispatch_shape(int n_max, Launch&& launch) {
     return hipErrorInvalidValue;
 }
 
+// Decode: one row per sequence, so latency rather than throughput counts:
+// always 1024 threads, as few elements per thread as the row allows.
+template <typename Launch>
+hipError_t dispatch_wide(int n_max, Launch&& launch) {
+    using std::integral_constant;
+    if (n_max <= 1024) return launch(integral_constant<int, 1024>{}, integral_constant<int, 1>{});
+    if (n_max <= 2048) return launch(integral_constant<int, 1024>{}, integral_constant<int, 2>{});
+    if (n_max <= 4096) return launch(integral_constant<int, 1024>{}, integral_constant<int, 4>{});
+    if (n_max <= 8192) return launch(integral_constant<int, 1024>{}, integral_constant<int, 8>{});
+    // segments of kDecodeSeg keys, and at most 8 * kMaxTopK candidates
+    static_assert(kDecodeSeg <= 16384 && (kMaxSelectKeys / kDecodeSeg) * kMaxTopK <= 16384, "decode shapes");
+    if (n_max <= 16384) return launch(integral_constant<int, 1024>{}, integral_constant<int, 16>{});
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_topk_prefill(const TopkArgs& a, int n_max, hipStream_t s) {
@@ -378,12 +450,21 @@ hipError_t launch_topk_prefill(const TopkArgs& a, int n_max, hipStream_t s) {
     });
 }
 
+int topk_decode_segments(int ctx) { return (ctx + kDecodeSeg - 1) / kDecodeSeg; }
+
 hipError_t launch_topk_decode(const float* S, const SeqMeta& m, int top_k, int32_t* idx, int32_t* count,
-                              int n_max, hipStream_t s) {
+                              int32_t* cand, int n_max, hipStream_t s) {
     if (m.B <= 0) return hipSuccess;
-    return dispatch_shape(n_max, [&](auto nt, auto ept) {
+    const int blocks = m.blk0[m.B];
+    hipError_t e = dispatch_wide(min(n_max, kDecodeSeg), [&](auto nt, auto ept) {
         constexpr int NT = decltype(nt)::value, EPT = decltype(ept)::value;
-        hipLaunchKernelGGL((topk_decode_kernel<NT, EPT>), dim3(m.B), dim3(NT), 0, s, S, m, top_k, idx, count);
+        hipLaunchKernelGGL((topk_decode_kernel<NT, EPT>), dim3(blocks), dim3(NT), 0, s, S, m, top_k, idx, count, cand);
+        return hipGetLastError();
+    });
+    if (e != hipSuccess || n_max <= kDecodeSeg) return e;
+    return dispatch_wide(topk_decode_segments(n_max) * top_k, [&](auto nt, auto ept) {
+        constexpr int NT = decltype(nt)::value, EPT = decltype(ept)::value;
+        hipLaunchKernelGGL((topk_merge_kernel<NT, EPT>), dim3(m.B), dim3(NT), 0, s, S, m, top_k, idx, count, cand);
         return hipGetLastError();
     });
 }
