@@ -59,13 +59,11 @@ namespace {
 constexpr int kTK = 32;        // keys per tile
 constexpr int kRing = 3;       // tiles resident in LDS: the ring keeps kRing - 2 gathers in flight
 constexpr float kLazy = 8.f;   // log2 headroom before the reference maximum moves
-// LDS fragments are read this many k-steps (scores) or feature blocks
-// (values) ahead of the MFMAs that use them.  Each read is pinned in
-// program order by a compiler memory fence: left alone, the scheduler sinks
-// the reads next to their MFMAs to save registers and every MFMA then waits
-// out a full LDS latency.
+// Key fragments are read this many k-steps ahead of the MFMAs that use
+// them.  Each read is pinned in program order by a compiler memory fence:
+// left alone, the scheduler sinks the reads next to their MFMAs to save
+// registers and every MFMA then waits out a full LDS latency.
 constexpr int kKeyAhead = 2;
-constexpr int kValAhead = 2;
 
 template <int NH, int DL, int DR>
 struct AttnShape {
@@ -483,22 +481,23 @@ struct Attend {
                     for (int hb = 0; hb < C::NHB; ++hb) o[f][hb] *= al[hb];
             }
             const unsigned char* tile = sm.tile[it % kRing];
-            constexpr int VR = kValAhead + 1;
-            u32x2 vr[VR][2];   // raw value fragments, kValAhead feature blocks ahead
-            auto vread = [&](int f, u32x2 (&dst)[2]) {
+            // Every value fragment of the tile is read up front and pinned
+            // there: left alone, the scheduler sinks each transposing read
+            // next to its MFMAs (a compiler memory fence does not hold these
+            // read intrinsics), and every MFMA waits out an LDS latency.
+            u32x2 vr[C::FBW][2];
+#pragma unroll
+            for (int f = 0; f < C::FBW; ++f) {
                 const int fb = C::FBW * cw + f;
                 // logical chunk 2fb + tb, swizzled in its aligned group of 16
                 const int off = vrow + 16 * (((2 * fb) & ~15) + (((2 * fb) & 15) ^ vx));
-                dst[0] = lds_read_tr16(tile + off);
-                dst[1] = lds_read_tr16(tile + off + 16 * C::CL * 16);
-            };
-#pragma unroll
-            for (int f = 0; f < kValAhead && f < C::FBW; ++f) vread(f, vr[f]);
+                vr[f][0] = lds_read_tr16(tile + off);
+                vr[f][1] = lds_read_tr16(tile + off + 16 * C::CL * 16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int f = 0; f < C::FBW; ++f) {
-                if (f + kValAhead < C::FBW) vread(f + kValAhead, vr[(f + kValAhead) % VR]);
-                asm volatile("" ::: "memory");
-                u32x2 v0 = vr[f % VR][0], v1 = vr[f % VR][1];
+                u32x2 v0 = vr[f][0], v1 = vr[f][1];
                 if constexpr (!F16) {
                     v0 = bf16x4_to_f16x4(v0);
                     v1 = bf16x4_to_f16x4(v1);
