@@ -98,12 +98,13 @@ struct DecodeLayout {
     size_t s_off, idx_off, cnt_off, po_off, pml_off, cand_off, total;
 };
 
-// Chunk of selected keys per attention block: enough blocks to cover the
-// chip, at least one 32-key tile per block.
+// Chunk of selected keys per attention block: about 128 blocks per step (a
+// block's fixed cost, its query fragments and partial output, outweighs
+// filling every CU with shorter chunks), at least one 32-key tile each.
 int decode_chunk(const dsa_shape* s, int32_t B, const int64_t* ctx) {
     int64_t sel = 0;
     for (int b = 0; b < B; ++b) sel += ctx[b] < s->top_k ? ctx[b] : s->top_k;
-    int64_t c = (sel + 255) / 256;
+    int64_t c = (sel + 127) / 128;
     c = (c + 31) / 32 * 32;
     if (c < 32) c = 32;
     if (c > s->top_k) c = (s->top_k + 31) / 32 * 32;

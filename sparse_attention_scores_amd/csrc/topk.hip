@@ -241,17 +241,27 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k,
                 }
             }
             __syncthreads();
-            if (tid < inbin) {
-                const float v = sm.cand[tid];
-                int gt = 0, ge = 0;
+            // each key of the bin is ranked by P lanes (a power of two, up to
+            // 16), which split the comparisons and combine them by shuffles
+            int lg = 0;
+            while (lg < 4 && (inbin << (lg + 1)) <= NT) ++lg;
+            const int P = 1 << lg;
+            const int c = tid >> lg, part = tid & (P - 1);
+            int gt = 0, ge = 0;
+            const float v = sm.cand[min(c, max(inbin - 1, 0))];
+            if (c < inbin) {
 #pragma unroll 4
-                for (int i = 0; i < inbin; ++i) {
+                for (int i = part; i < inbin; i += P) {
                     const float x = sm.cand[i];
                     gt += x > v;
                     ge += x >= v;
                 }
-                if (gt < krem && krem <= ge) { sm.T = v; sm.keep = krem - gt; }
             }
+            for (int d = 1; d < P; d <<= 1) {
+                gt += __shfl_xor(gt, d);
+                ge += __shfl_xor(ge, d);
+            }
+            if (c < inbin && part == 0 && gt < krem && krem <= ge) { sm.T = v; sm.keep = krem - gt; }
             __syncthreads();
             T = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sm.T)));
             krem = __builtin_amdgcn_readfirstlane(sm.keep);

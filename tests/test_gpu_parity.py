@@ -371,3 +371,30 @@ def test_decode_step(name):
     assert np.array_equal(idx, ref_idx)
     err = row_rel_err(out, ref_out)
     assert err <= ATTN_TOL, err
+
+
+@pytest.mark.parametrize("case", ["all_ties", "one_segment"])
+def test_decode_segmented_topk(case):
+    """Decode selection over sequences longer than one top-k segment (8192
+    keys): ties spanning every segment (all scores equal: the first top_k
+    keys win), and a selection held entirely by one segment (the others'
+    candidates must all lose)."""
+    cfg = W.Decode("seg_" + case, W.GLM, (20000, 8193, 9000), 31, 8, 0.05, 0.05)
+    d = W.make_decode(cfg)
+    top_k = cfg.shape.top_k
+    if case == "all_ties":
+        d["qI"][:] = 0
+        want0 = np.arange(top_k)
+    else:
+        one, eight = W.to_bf16_bits(np.float32(1.0)), W.to_bf16_bits(np.float32(8.0))
+        d["qI"][0] = one                  # sequence 0: every q.k is the sum of k
+        lo = 9000                         # keys 9000..11047 sit in the second segment
+        d["kI"][lo:lo + top_k] = eight    # the only keys reaching 128 * 8 per head
+        want0 = np.arange(lo, lo + top_k)
+    say("decode-seg", case, cfg.ctx)
+    out, idx, cnt = run_decode(cfg, d)
+    ref_idx, ref_cnt, ref_out = oracle.decode_step(d, cfg.shape)
+    assert np.array_equal(ref_idx[0], want0)
+    assert np.array_equal(cnt, ref_cnt)
+    assert np.array_equal(idx, ref_idx)
+    assert row_rel_err(out, ref_out) <= ATTN_TOL
