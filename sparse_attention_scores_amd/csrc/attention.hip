@@ -31,9 +31,9 @@
 //  - a tile is stored in two row-major regions: the Dl latent columns (bf16,
 //    or fp16 when the cache was converted once by latent_to_f16_kernel, which
 //    removes the per-query conversion from the value path) and the bf16 rope
-//    columns.  16-byte chunks are XOR-swizzled per row so that
-//    the score reads (16 rows, one chunk) and the transposed value reads
-//    (4 rows, 2 chunks) hit distinct banks.
+//    columns.  16-byte chunks are XOR-swizzled per row so that the score
+//    reads (16 rows, one chunk) and the transposed value reads (4 rows,
+//    2 chunks) run without bank conflicts (the map is at swz_lat).
 //  - softmax in fp32 (base 2) with a lazy reference: the running maximum
 //    used for the exponentials moves only when a score exceeds it by more
 //    than 8 (probabilities stay <= 256), so the output rescale almost never
@@ -95,9 +95,20 @@ struct AttnShape {
                   "work must split evenly");
 };
 
-// chunk XOR of tile row r in the latent region (rows 16 apart share it) and
-// in the rope region
-__device__ inline int swz_lat(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
+// Chunk XOR of tile row r in the latent region (rows 16 apart share it) and
+// in the rope region.  The latent XOR is linear in the bits of r (bit 0 -> 3,
+// bit 1 -> 4, bit 2 -> 8, bit 3 -> 10), chosen by measurement: a 16-byte LDS
+// read serves the wave 16 lanes at a time, and the lanes grouped together are
+// not simply 16 consecutive ones, so the score read (lane l: row l & 15,
+// chunk 4k + l / 16) needs chunks that differ across those groups.  With this
+// map the score read runs at the conflict-free rate (182 B per clock per CU
+// against 128 for the plain 2(r & 7) + (r >> 3 & 1) interleave), and the
+// transposed value read (rows 4g..4g+3, two chunks) still hits 16 distinct
+// chunks within each half wave (x >> 1 differs between rows 0-7 and between
+// rows 8-15).
+__device__ inline int swz_lat(int r) {
+    return ((r & 1) ? 3 : 0) ^ ((r & 2) ? 4 : 0) ^ ((r & 4) ? 8 : 0) ^ ((r & 8) ? 10 : 0);
+}
 __device__ inline int swz_rope(int r) { return (r >> 1) & 7; }
 
 __device__ inline uint32_t pack_f16(float a, float b) {
@@ -315,18 +326,13 @@ struct Attend {
     }
 
     // Top of iteration it, both roles: tile it+1 landed for every wave,
-    // probabilities of tile it visible, tile it-1 free; then tile
-    // it+kRing-1 is gathered into tile it-1's buffer (its rows were read in
-    // the previous iteration) and the rows of the next gather are read.
-    __device__ __forceinline__ static void step(const Ctx& c, int it, Rows& rows) {
-        const bool gatherer = c.w >= C::NHB;
+    // probabilities of tile it visible, tile it-1 free.  The consumers then
+    // gather tile it+kRing-1 into tile it-1's buffer from inside their
+    // value step (see consume).
+    __device__ __forceinline__ static void step(const Ctx& c, int it) {
         // tiles it+1 .. min(it+kRing-2, ntiles-1) are in flight; keep all but it+1
-        if (gatherer && it + 1 < c.ntiles) wait_tiles_rt(c, min(kRing - 3, c.ntiles - 2 - it));
+        if (c.w >= C::NHB && it + 1 < c.ntiles) wait_tiles_rt(c, min(kRing - 3, c.ntiles - 2 - it));
         __syncthreads();
-        if (gatherer && it + kRing - 1 < c.ntiles) {
-            gather(c, it + kRing - 1, rows);
-            if (it + kRing < c.ntiles) load_rows(c, it + kRing, rows);
-        }
     }
 
     // Producer wave hb = w: scores and softmax of heads 16hb .. 16hb+15.
@@ -439,7 +445,7 @@ struct Attend {
         prologue(c, rows);
         if (c.ntiles > 0) score(0);
         for (int it = 0; it < c.ntiles; ++it) {
-            step(c, it, rows);
+            step(c, it);
             if (it + 1 < c.ntiles) score(it + 1);
         }
         lsum = sum4_rows(lsum);
@@ -464,7 +470,15 @@ struct Attend {
         const int vx = (swz_lat(trow) & (C::CL - 1)) ^ ((c16 >> 1) & 1);
         const int vrow = trow * C::CL * 16 + 8 * (c16 & 1);
 
+        Rows rows;
         auto values = [&](int it) {
+            // The row ids (read an iteration ago) are taken before this
+            // tile's LDS reads go out; otherwise the first gather
+            // instruction waits for those reads too.
+#pragma unroll
+            for (int k = 0; k < C::ILW; ++k) asm volatile("" :: "v"(rows.lat[k]));
+#pragma unroll
+            for (int k = 0; k < C::IRW; ++k) asm volatile("" :: "v"(rows.rope[k]));
             u32x4 pf[C::NHB];
             float al[C::NHB];
             bool moved = false;
@@ -473,12 +487,6 @@ struct Attend {
                 pf[hb] = sm.pfrag[it & 1][hb][l];
                 al[hb] = sm.alpha[it & 1][16 * hb + c16];
                 moved |= al[hb] != 1.f;
-            }
-            if (__ballot(moved)) {   // wave-uniform and rare
-#pragma unroll
-                for (int f = 0; f < C::FBW; ++f)
-#pragma unroll
-                    for (int hb = 0; hb < C::NHB; ++hb) o[f][hb] *= al[hb];
             }
             const unsigned char* tile = sm.tile[it % kRing];
             // Every value fragment of the tile is read up front and pinned
@@ -495,6 +503,18 @@ struct Attend {
                 vr[f][1] = lds_read_tr16(tile + off + 16 * C::CL * 16);
             }
             __builtin_amdgcn_sched_barrier(0);
+            // The next gather goes out behind this wave's LDS reads, never
+            // ahead of them: an LDS read issued after LDS-DMA loads waits
+            // until the address unit has taken those loads.  Its rows were
+            // read in the previous iteration.
+            if (it + kRing - 1 < c.ntiles) gather(c, it + kRing - 1, rows);
+            __builtin_amdgcn_sched_barrier(0);
+            if (__ballot(moved)) {   // wave-uniform and rare
+#pragma unroll
+                for (int f = 0; f < C::FBW; ++f)
+#pragma unroll
+                    for (int hb = 0; hb < C::NHB; ++hb) o[f][hb] *= al[hb];
+            }
 #pragma unroll
             for (int f = 0; f < C::FBW; ++f) {
                 u32x2 v0 = vr[f][0], v1 = vr[f][1];
@@ -506,12 +526,14 @@ struct Attend {
 #pragma unroll
                 for (int hb = 0; hb < C::NHB; ++hb) o[f][hb] = mfma16_f16(av, pf[hb], o[f][hb]);
             }
+            // rows of the following gather, after the MFMAs have issued
+            __builtin_amdgcn_sched_barrier(0);
+            if (it + kRing < c.ntiles) load_rows(c, it + kRing, rows);
         };
 
-        Rows rows;
         prologue(c, rows);
         for (int it = 0; it < c.ntiles; ++it) {
-            step(c, it, rows);
+            step(c, it);
             values(it);
         }
         __syncthreads();
