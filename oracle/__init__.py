@@ -44,8 +44,10 @@ def _configure(lib):
                                          i32, dbl, P, i64, P, P, P, i32]
     lib.oracle_decode_step.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, dbl,
                                        P, P, P, i32]
+    lib.oracle_cache_write.argtypes = [P, P, dbl, P, i64, i64, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                       i32, dbl]
     for f in (lib.oracle_indexer_scores, lib.oracle_topk_select, lib.oracle_sparse_mla_attn,
-              lib.oracle_prefill_chunk, lib.oracle_decode_step):
+              lib.oracle_prefill_chunk, lib.oracle_decode_step, lib.oracle_cache_write):
         f.restype = ctypes.c_int
     return lib
 
@@ -166,3 +168,22 @@ def decode_step(inp: dict, shape, nthreads: Optional[int] = None):
         shape.d_rope, shape.n_idx_heads, shape.d_idx, shape.top_k, shape.softmax_scale,
         _p(idx), _p(cnt), _p(out), nthreads or default_threads()), "decode")
     return idx, cnt, out
+
+
+def cache_write(kv_a, norm_w, eps: float, pos, kv_cache, kI_new=None, kI_cache=None, q=None, qI=None,
+                *, shape, d_idx_rope: int, theta: float):
+    """Upstream cache write; returns new arrays (kv_cache, kI_cache, q, qI),
+    the inputs left unchanged (None where not given)."""
+    kv_a, norm_w = _c(kv_a, np.uint16), _c(norm_w, np.float32)
+    pos = _c(pos, np.int64)
+    kv_out = np.array(kv_cache, dtype=np.uint16, copy=True, order="C")
+    kI_out = None if kI_cache is None else np.array(kI_cache, dtype=np.uint16, copy=True, order="C")
+    kI_new = None if kI_new is None else _c(kI_new, np.uint16)
+    q_out = None if q is None else np.array(q, dtype=np.uint16, copy=True, order="C")
+    qI_out = None if qI is None else np.array(qI, dtype=np.uint16, copy=True, order="C")
+    T, N = pos.size, kv_out.shape[0]
+    _check(_load().oracle_cache_write(
+        _p(kv_a), _p(norm_w), float(eps), _p(pos), T, N, _p(kv_out), _p(kI_new), _p(kI_out),
+        _p(q_out), _p(qI_out), shape.n_heads, shape.d_latent, shape.d_rope, shape.n_idx_heads,
+        shape.d_idx, d_idx_rope, float(theta)), "cache write")
+    return kv_out, kI_out, q_out, qI_out

@@ -18,6 +18,8 @@
  *    section 6 (attention core, absorbed MLA): Q = [q_nope_absorbed | q_pe],
  *    K = [kv_cmpr | k_pe], V = kv_cmpr; kq = K.q, softmax with kq_scale,
  *    kqv = V.kq.  The config line gives index_topk 2048 and the head widths.
+ *    Sections 4 and 5 (KV compression path, RoPE convention) define the
+ *    upstream cache write at the end of this file.
  *
  * Readings where the pages are silent are stated at each function and in
  * the design notes: key j is visible to the query at position p iff j <= p;
@@ -368,5 +370,105 @@ int oracle_decode_step(const uint16_t* q, const uint16_t* qI, const float* w,
         if (rc) return rc;
         off += ctx[b];
     }
+    return 0;
+}
+
+/* ==========================================================================
+ * Upstream cache write ("GLM-5.2-Vision: llama.cpp vs vLLM" pipeline trace,
+ * section 4, KV compression path, and section 5, RoPE convention): the kv_a
+ * projection output of a token is split into kv_cmpr (the first Dl columns)
+ * and k_pe (the last Dr); k_pe and the query's q_pe are rotated by RoPE of
+ * the NORM flavour (adjacent pairs x[2i], x[2i+1]); kv_cmpr is RMS-normalised
+ * and scaled by the kv_a norm weight after the split; the indexer's query
+ * and key are rotated the same way (the trace's note that the indexer rope
+ * is NORM too).  Readings: the rotation angle of pair i over a rope width d
+ * at position p is p * theta^(-2i/d) (theta is not on the pages and is an
+ * argument); the indexer rope covers the first d_idx_rope columns of each
+ * indexer head; RMSNorm is x / sqrt(mean(x^2) + eps) * weight.
+ * ======================================================================== */
+
+/* double -> bf16 bits, round to nearest with ties to even, for zero and
+ * values in the normal bf16 range: keep 8 significant bits. */
+static uint16_t double_to_bf16(double v) {
+    if (v == 0.0) return signbit(v) ? 0x8000u : 0u;
+    int e;
+    double m = frexp(fabs(v), &e);          /* |v| = m * 2^e, m in [0.5, 1) */
+    double r = nearbyint(ldexp(m, 8));      /* default rounding: ties to even */
+    float f = (float)ldexp(signbit(v) ? -r : r, e - 8);   /* exact: 8 bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* RoPE, NORM flavour, in place on x[0..d): pair (x[2i], x[2i+1]) turns by
+ * the angle p * theta^(-2i/d). */
+static void rope_norm(double* x, int32_t d, double p, double theta) {
+    for (int32_t i = 0; i < d / 2; ++i) {
+        double ang = p * pow(theta, -2.0 * i / d);
+        double c = cos(ang), s = sin(ang);
+        double a = x[2 * i], b = x[2 * i + 1];
+        x[2 * i] = a * c - b * s;
+        x[2 * i + 1] = a * s + b * c;
+    }
+}
+
+/* RMSNorm in place on x[0..n): x / sqrt(mean(x^2) + eps) * w. */
+static void rms_norm(double* x, int32_t n, const float* w, double eps) {
+    double ss = 0.0;
+    for (int32_t k = 0; k < n; ++k) ss += x[k] * x[k];
+    double r = 1.0 / sqrt(ss / n + eps);
+    for (int32_t k = 0; k < n; ++k) x[k] = x[k] * r * (double)w[k];
+}
+
+/* Rope the first `d` of the `width` columns of each of `nheads` bf16 rows
+ * (in place, rounded once to bf16). */
+static void rope_rows_bf16(uint16_t* rows, int32_t nheads, int32_t width, int32_t col0, int32_t d,
+                           double p, double theta, double* tmp) {
+    for (int32_t h = 0; h < nheads; ++h) {
+        uint16_t* r = rows + (int64_t)h * width + col0;
+        for (int32_t k = 0; k < d; ++k) tmp[k] = bf16_to_double(r[k]);
+        rope_norm(tmp, d, p, theta);
+        for (int32_t k = 0; k < d; ++k) r[k] = double_to_bf16(tmp[k]);
+    }
+}
+
+int oracle_cache_write(const uint16_t* kv_a, const float* norm_w, double eps,
+                       const int64_t* pos, int64_t T, int64_t N,
+                       uint16_t* kv_cache, const uint16_t* kI_new, uint16_t* kI_cache,
+                       uint16_t* q, uint16_t* qI,
+                       int32_t H, int32_t Dl, int32_t Dr, int32_t Hi, int32_t Di,
+                       int32_t d_idx_rope, double theta) {
+    if (!kv_a || !norm_w || !pos || !kv_cache || T < 0 || N <= 0 || H <= 0 || Dl <= 0 ||
+        Dr < 0 || (Dr & 1) || Hi <= 0 || Di <= 0 || d_idx_rope < 0 || (d_idx_rope & 1) ||
+        d_idx_rope > Di || !(theta > 0.0) || !(eps >= 0.0) || (!kI_new) != (!kI_cache))
+        return -1;
+    int32_t Dqk = Dl + Dr;
+    int32_t wmax = Dqk > Di ? Dqk : Di;
+    double* tmp = (double*)malloc((size_t)wmax * sizeof(double));
+    if (!tmp) return -8;
+    for (int64_t t = 0; t < T; ++t) {
+        double p = (double)pos[t];
+        if (pos[t] >= 0 && pos[t] < N) {
+            /* latent cache row: [rmsnorm(kv_cmpr) * w | rope(k_pe)] */
+            const uint16_t* src = kv_a + t * Dqk;
+            uint16_t* dst = kv_cache + pos[t] * Dqk;
+            for (int32_t k = 0; k < Dqk; ++k) tmp[k] = bf16_to_double(src[k]);
+            rms_norm(tmp, Dl, norm_w, eps);
+            rope_norm(tmp + Dl, Dr, p, theta);
+            for (int32_t k = 0; k < Dqk; ++k) dst[k] = double_to_bf16(tmp[k]);
+            /* indexer cache row: the new key with its leading columns roped */
+            if (kI_new) {
+                const uint16_t* ks = kI_new + t * Di;
+                uint16_t* kd = kI_cache + pos[t] * Di;
+                for (int32_t k = 0; k < Di; ++k) tmp[k] = bf16_to_double(ks[k]);
+                rope_norm(tmp, d_idx_rope, p, theta);
+                for (int32_t k = 0; k < Di; ++k) kd[k] = double_to_bf16(tmp[k]);
+            }
+        }
+        /* the query's rope part of every head, and the indexer query */
+        if (q) rope_rows_bf16(q + t * H * Dqk, H, Dqk, Dl, Dr, p, theta, tmp);
+        if (qI) rope_rows_bf16(qI + t * Hi * Di, Hi, Di, 0, d_idx_rope, p, theta, tmp);
+    }
+    free(tmp);
     return 0;
 }

@@ -77,6 +77,26 @@ int oracle_decode_step(const uint16_t* q, const uint16_t* qI, const float* w,
                        int32_t top_k, double scale,
                        int32_t* idx_out, int32_t* count_out, double* out, int32_t nthreads);
 
+/* Upstream cache write for T new tokens (pipeline trace sections 4 and 5).
+ *   kv_a [T, Dl+Dr] bf16: per token [kv_cmpr | k_pe] from the kv_a projection;
+ *   norm_w [Dl] float, eps: the RMSNorm weight and epsilon;
+ *   pos [T]: token positions; a token with 0 <= pos < N writes cache rows pos:
+ *     kv_cache [N, Dl+Dr] bf16: [rmsnorm(kv_cmpr) * norm_w | rope(k_pe, pos)];
+ *     kI_cache [N, Di] bf16: kI_new[t] with its first d_idx_rope columns
+ *       roped (kI_new, kI_cache both NULL: skipped);
+ *   q [T, H, Dl+Dr] bf16 or NULL: columns Dl.. of every head roped in place;
+ *   qI [T, Hi, Di] bf16 or NULL: the first d_idx_rope columns of every head
+ *     roped in place.
+ * rope over a width d turns pair (x[2i], x[2i+1]) by pos * theta^(-2i/d).
+ * Every value is computed in double and rounded once to bf16 (nearest,
+ * ties to even).  Cache rows not named by pos are untouched. */
+int oracle_cache_write(const uint16_t* kv_a, const float* norm_w, double eps,
+                       const int64_t* pos, int64_t T, int64_t N,
+                       uint16_t* kv_cache, const uint16_t* kI_new, uint16_t* kI_cache,
+                       uint16_t* q, uint16_t* qI,
+                       int32_t H, int32_t Dl, int32_t Dr, int32_t Hi, int32_t Di,
+                       int32_t d_idx_rope, double theta);
+
 #ifdef __cplusplus
 }
 #endif

@@ -386,4 +386,174 @@ def pin_decode_sparse_sequences_follow_brute_force():
         assert np.abs(out[b] - ref[0]).max() / np.abs(ref).max() < 1e-12, b
 
 
+# --------------------------------------------------------------------------
+# upstream cache write (pipeline trace sections 4 and 5)
+# --------------------------------------------------------------------------
+def _f(bits):
+    return W.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _half_ulp_bf16(x):
+    """Half a bf16 unit in the last place at |x| (normal range)."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(x, 1e-30)))
+    return np.ldexp(1.0, (e - 8).astype(int))
+
+
+def _cw(shape, T, N, pos, kv_a=None, norm_w=None, eps=0.0, q=None, qI=None, kI_new=None,
+        d_idx_rope=None, theta=10000.0):
+    """Run the oracle's cache write on zero caches; missing operands are zeros."""
+    Dqk = shape.d_qk
+    kv_a = np.zeros((T, Dqk), np.uint16) if kv_a is None else kv_a
+    norm_w = np.ones(shape.d_latent, np.float32) if norm_w is None else norm_w
+    kI_new = np.zeros((T, shape.d_idx), np.uint16) if kI_new is None else kI_new
+    return oracle.cache_write(kv_a, norm_w, eps, np.asarray(pos, np.int64),
+                              np.zeros((N, Dqk), np.uint16), kI_new,
+                              np.zeros((N, shape.d_idx), np.uint16), q, qI, shape=shape,
+                              d_idx_rope=shape.d_rope if d_idx_rope is None else d_idx_rope,
+                              theta=theta)
+
+
+def pin_rope_position_zero_is_identity():
+    """At position 0 every rotation angle is 0: q, qI and the key rows keep
+    their bits."""
+    cfg = W.CACHE_WRITE["tiny"]
+    d = W.make_cache_write(cfg)
+    sh = cfg.shape
+    kv, kI, q, qI = oracle.cache_write(d["kv_a"][:3], d["norm_w"], cfg.eps, np.zeros(3, np.int64),
+                                      d["kv_cache"], d["kI_new"][:3], d["kI_cache"], d["q"][:3],
+                                      d["qI"][:3], shape=sh, d_idx_rope=cfg.d_idx_rope, theta=cfg.theta)
+    assert np.array_equal(q, d["q"][:3]) and np.array_equal(qI, d["qI"][:3])
+    assert np.array_equal(kv[0, sh.d_latent:], d["kv_a"][2, sh.d_latent:])   # last write wins
+    assert np.array_equal(kI[0], d["kI_new"][2])
+
+
+def pin_rope_interleaved_pair_closed_form():
+    """NORM flavour (pipeline trace section 5): a one-hot x[2i] = 1 at
+    position p comes out as (cos a, sin a) in columns 2i, 2i+1 and zero
+    elsewhere, a = p * theta^(-2i/d); each value is the exact one rounded
+    once to bf16."""
+    sh = W.TINY
+    d, theta = sh.d_rope, 10000.0
+    for i, p in ((0, 5), (1, 7), (3, 11), (d // 2 - 1, 40000)):
+        q = np.zeros((1, sh.n_heads, sh.d_qk), np.uint16)
+        q[0, 2, sh.d_latent + 2 * i] = np.uint16(0x3F80)   # 1.0
+        _, _, qo, _ = _cw(sh, 1, 4, [p], q=q, theta=theta)
+        got = _f(qo[0, 2, sh.d_latent:])
+        a = p * theta ** (-2.0 * i / d)
+        want = np.zeros(d)
+        want[2 * i], want[2 * i + 1] = math.cos(a), math.sin(a)
+        assert np.all(np.abs(got - want) <= _half_ulp_bf16(want) * 1.0000001), (i, p, got, want)
+        assert np.count_nonzero(got[np.arange(d) // 2 != i]) == 0
+        assert not np.any(_f(qo[0, [0, 1, 3]])) and not np.any(_f(qo[0, 2, :sh.d_latent]))
+
+
+def pin_rope_frequency_ladder():
+    """Recovered from one-hot inputs at p = 1, pair i turns by theta^(-2i/d):
+    pair 0 by exactly 1 radian and each next pair by theta^(-2/d) times the
+    previous angle (the indexer rope over d_idx_rope = 2 * d_rope included)."""
+    sh = W.TINY
+    theta = 500.0
+    for width, which in ((sh.d_rope, "q"), (2 * sh.d_rope, "qI")):
+        ang = []
+        for i in range(width // 2):
+            if which == "q":
+                x = np.zeros((1, sh.n_heads, sh.d_qk), np.uint16)
+                x[0, 0, sh.d_latent + 2 * i] = np.uint16(0x3F80)   # 1.0
+                _, _, out, _ = _cw(sh, 1, 2, [1], q=x, theta=theta)
+                o = _f(out[0, 0, sh.d_latent + 2 * i: sh.d_latent + 2 * i + 2])
+            else:
+                x = np.zeros((1, sh.n_idx_heads, sh.d_idx), np.uint16)
+                x[0, 1, 2 * i] = np.uint16(0x3F80)   # 1.0
+                _, _, _, out = _cw(sh, 1, 2, [1], qI=x, theta=theta, d_idx_rope=width)
+                o = _f(out[0, 1, 2 * i: 2 * i + 2])
+            ang.append(math.atan2(o[1], o[0]))
+        ang = np.array(ang)
+        assert abs(ang[0] - 1.0) < 4e-3, ang[0]
+        ratio = ang[1:] / ang[:-1]
+        assert np.all(np.abs(ratio - theta ** (-2.0 / width)) < 0.01), (which, ratio)
+
+
+def pin_rope_rotation_invariants():
+    """A rotation keeps each pair's length and composes additively in the
+    position: rope(rope(x, a), b) = rope(x, a + b) (up to the two extra bf16
+    roundings)."""
+    cfg = W.CACHE_WRITE["tiny"]
+    d = W.make_cache_write(cfg)
+    sh = cfg.shape
+    q0 = d["q"][:4]
+    pa, pb = np.array([3, 100, 2047, 12345]), np.array([9, 1, 4000, 7])
+    _, _, qa, _ = _cw(sh, 4, 1, pa, q=q0)
+    _, _, qab, _ = _cw(sh, 4, 1, pb, q=qa)
+    _, _, qs, _ = _cw(sh, 4, 1, pa + pb, q=q0)
+    x0 = _f(q0[..., sh.d_latent:]).reshape(4, sh.n_heads, -1, 2)
+    xa = _f(qa[..., sh.d_latent:]).reshape(4, sh.n_heads, -1, 2)
+    n0, na = np.hypot(x0[..., 0], x0[..., 1]), np.hypot(xa[..., 0], xa[..., 1])
+    assert np.all(np.abs(na - n0) <= 2.0 ** -7 * n0 + 1e-30)
+    # three bf16 roundings of at most 2^-8 of the pair's length each
+    tol = 2.0 ** -6 * np.repeat(n0, 2, axis=-1)
+    diff = np.abs(_f(qab[..., sh.d_latent:]) - _f(qs[..., sh.d_latent:]))
+    assert np.all(diff <= tol + 1e-30), float((diff - tol).max())
+
+
+def pin_rmsnorm_closed_forms():
+    """RMSNorm (x / sqrt(mean(x^2) + eps) * weight, after the split, section
+    4): constant rows, alternating rows, an eps that doubles the RMS, and
+    invariance under a power-of-two scaling of x."""
+    sh = W.TINY
+    Dl, Dqk = sh.d_latent, sh.d_qk
+    wv = _f(_bf(np.linspace(-2.0, 2.0, Dl, dtype=np.float32))).astype(np.float32)
+    x = np.zeros((4, Dqk), np.float32)
+    x[0, :Dl] = 3.0                                   # mean(x^2) = 9: y = w
+    x[1, :Dl] = np.where(np.arange(Dl) % 2, -0.5, 0.5)  # y = +-w
+    x[2, :Dl] = 1.0                                   # with eps = 3: y = w / 2
+    x[3, :Dl] = 0.375 * np.arange(1, Dl + 1)
+    kv_a = _bf(x)
+    kv0, _, _, _ = _cw(sh, 4, 4, [0, 1, 2, 3], kv_a=kv_a, norm_w=wv, eps=0.0)
+    kv3, _, _, _ = _cw(sh, 4, 4, [0, 1, 2, 3], kv_a=kv_a, norm_w=wv, eps=3.0)
+    assert np.array_equal(kv0[0, :Dl], _bf(wv))
+    assert np.array_equal(kv0[1, :Dl], _bf(np.where(np.arange(Dl) % 2, -wv, wv)))
+    assert np.array_equal(kv3[2, :Dl], _bf(wv / 2))
+    kv_a4 = kv_a.copy()
+    kv_a4[3, :Dl] = _bf(4.0 * _f(kv_a[3, :Dl]))
+    kv4, _, _, _ = _cw(sh, 4, 4, [0, 1, 2, 3], kv_a=kv_a4, norm_w=wv, eps=0.0)
+    assert np.array_equal(kv4[3, :Dl], kv0[3, :Dl])
+    # the exact value, rounded once
+    r = _f(kv_a[3, :Dl])
+    want = r / math.sqrt(np.mean(r * r)) * wv
+    got = _f(kv0[3, :Dl])
+    assert np.all(np.abs(got - want) <= _half_ulp_bf16(want) * 1.0000001)
+
+
+def pin_cache_write_rows_and_layout():
+    """Only rows named by in-range positions change; a row holds
+    [normed kv_cmpr | roped k_pe]; the indexer row ropes its leading
+    d_idx_rope columns and copies the rest; the query's latent columns stay."""
+    cfg = W.CACHE_WRITE["tiny"]
+    d = W.make_cache_write(cfg)
+    sh = cfg.shape
+    kv, kI, q, qI = oracle.cache_write(d["kv_a"], d["norm_w"], cfg.eps, d["pos"], d["kv_cache"],
+                                      d["kI_new"], d["kI_cache"], d["q"], d["qI"], shape=sh,
+                                      d_idx_rope=cfg.d_idx_rope, theta=cfg.theta)
+    good = (d["pos"] >= 0) & (d["pos"] < cfg.N)
+    assert (~good).sum() == 2
+    hit = np.zeros(cfg.N, bool)
+    hit[d["pos"][good]] = True
+    assert np.array_equal(kv[~hit], d["kv_cache"][~hit]) and np.array_equal(kI[~hit], d["kI_cache"][~hit])
+    assert np.array_equal(q[..., :sh.d_latent], d["q"][..., :sh.d_latent])
+    assert np.array_equal(kI[d["pos"][good], cfg.d_idx_rope:], d["kI_new"][good, cfg.d_idx_rope:])
+    assert np.array_equal(qI[..., cfg.d_idx_rope:], d["qI"][..., cfg.d_idx_rope:])
+    # the rope part of row pos[t] equals q's rotation of the same vector at pos[t]
+    t = int(np.flatnonzero(good)[0])
+    qq = np.zeros((1, sh.n_heads, sh.d_qk), np.uint16)
+    qq[0, 1, sh.d_latent:] = d["kv_a"][t, sh.d_latent:]
+    _, _, qo, _ = _cw(sh, 1, 1, [d["pos"][t]], q=qq, theta=cfg.theta)
+    assert np.array_equal(kv[d["pos"][t], sh.d_latent:], qo[0, 1, sh.d_latent:])
+    # and the latent part does not depend on the position
+    kv2, _, _, _ = oracle.cache_write(d["kv_a"][t:t + 1], d["norm_w"], cfg.eps, np.array([5]),
+                                      d["kv_cache"], None, None, None, None, shape=sh,
+                                      d_idx_rope=cfg.d_idx_rope, theta=cfg.theta)
+    assert np.array_equal(kv2[5, :sh.d_latent], kv[d["pos"][t], :sh.d_latent])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -46,6 +46,22 @@ MUTATIONS = [
     ("lse without log", "lserow[h] = m + log(Z);", "lserow[h] = m + Z;"),
     ("score rounded to bf16-ish", "Srow[j] = (float)total;",
      "Srow[j] = (float)(total + 0.25);"),
+    ("rope turns the other way", "x[2 * i] = a * c - b * s;\n        x[2 * i + 1] = a * s + b * c;",
+     "x[2 * i] = a * c + b * s;\n        x[2 * i + 1] = -a * s + b * c;"),
+    ("rope pairs half a width apart", "double a = x[2 * i], b = x[2 * i + 1];\n        x[2 * i] = a * c - b * s;\n        x[2 * i + 1] = a * s + b * c;",
+     "double a = x[i], b = x[i + d / 2];\n        x[i] = a * c - b * s;\n        x[i + d / 2] = a * s + b * c;"),
+    ("rope exponent i/d", "double ang = p * pow(theta, -2.0 * i / d);", "double ang = p * pow(theta, -1.0 * i / d);"),
+    ("rope position off by one", "double p = (double)pos[t];", "double p = (double)pos[t] + 1.0;"),
+    ("rms over the sum", "double r = 1.0 / sqrt(ss / n + eps);", "double r = 1.0 / sqrt(ss + eps);"),
+    ("eps outside the root", "double r = 1.0 / sqrt(ss / n + eps);", "double r = 1.0 / (sqrt(ss / n) + eps);"),
+    ("norm weight dropped", "x[k] = x[k] * r * (double)w[k];", "x[k] = x[k] * r;"),
+    ("indexer rope over the whole head", "rope_norm(tmp, d_idx_rope, p, theta);", "rope_norm(tmp, Di, p, theta);"),
+    ("k_pe not roped", "rope_norm(tmp + Dl, Dr, p, theta);", ""),
+    ("q rope at column 0", "rope_rows_bf16(q + t * H * Dqk, H, Dqk, Dl, Dr, p, theta, tmp);",
+     "rope_rows_bf16(q + t * H * Dqk, H, Dqk, 0, Dr, p, theta, tmp);"),
+    ("bf16 rounding truncates", "double r = nearbyint(ldexp(m, 8));", "double r = floor(ldexp(m, 8));"),
+    ("positions taken as 1-based rows", "uint16_t* dst = kv_cache + pos[t] * Dqk;",
+     "uint16_t* dst = kv_cache + (pos[t] > 0 ? pos[t] - 1 : 0) * Dqk;"),
 ]
 
 _RUNNER = r"""

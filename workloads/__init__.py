@@ -32,6 +32,7 @@ import numpy as np
 __all__ = [
     "Shape", "TINY", "GLM", "Prefill", "Decode", "PREFILL", "DECODE",
     "to_bf16_bits", "bf16_bits_to_f32", "make_prefill", "make_decode",
+    "CacheWrite", "CACHE_WRITE", "make_cache_write",
 ]
 
 
@@ -167,3 +168,60 @@ def sample_rows(L: int, n: int, seed: int = 1234, must: Optional[List[int]] = No
         if 0 <= m < L:
             pick.add(int(m))
     return np.array(sorted(pick), dtype=np.int64)
+
+
+@dataclasses.dataclass(frozen=True)
+class CacheWrite:
+    """T new tokens written into caches of N rows (the upstream cache write).
+    ``positions``: "chunk" = p0 .. p0+T-1; "scatter" = T distinct seeded
+    positions in [0, N) that include 0 and N-1, plus (if ``bad``) one
+    position -1 and one position N, whose cache rows must not be written."""
+    name: str
+    shape: Shape
+    T: int
+    N: int
+    p0: int
+    positions: str
+    seed: int
+    bad: bool = False
+    d_idx_rope: int = 64
+    theta: float = 10000.0
+    eps: float = 1e-6
+
+
+CACHE_WRITE: Dict[str, CacheWrite] = {
+    # the 16k chunk's 4096 new tokens at positions 12288..16383
+    "glm_16k_chunk": CacheWrite("glm_16k_chunk", GLM, 4096, 16384, 12288, "chunk", 31),
+    # eight decode tokens scattered over a 64k-row cache
+    "glm_decode_8": CacheWrite("glm_decode_8", GLM, 8, 65536, 0, "scatter", 32),
+    # small ragged cases the oracle finishes at once
+    "glm_small": CacheWrite("glm_small", GLM, 37, 300, 0, "scatter", 33, bad=True),
+    "tiny": CacheWrite("tiny", TINY, 29, 64, 0, "scatter", 34, bad=True, d_idx_rope=16),
+}
+
+
+def make_cache_write(cfg: CacheWrite) -> Dict[str, np.ndarray]:
+    """Inputs of one cache write, drawn in the order positions, kv_a, norm_w,
+    kI_new, q, qI, kv_cache, kI_cache.  kv_a, q and the indexer rows are
+    standard normal rounded to bf16; the norm weight is 1 + 0.1 N(0,1) in
+    fp32; the caches start as standard normal rows (so rows that must stay
+    untouched are visible)."""
+    sh = cfg.shape
+    rng = np.random.default_rng(cfg.seed)
+    if cfg.positions == "chunk":
+        pos = np.arange(cfg.p0, cfg.p0 + cfg.T, dtype=np.int64)
+    else:
+        n_good = cfg.T - (2 if cfg.bad else 0)
+        pick = rng.choice(np.arange(1, cfg.N - 1), size=n_good - 2, replace=False)
+        pos = np.concatenate([[0, cfg.N - 1], pick] + ([[-1, cfg.N]] if cfg.bad else []))
+        pos = rng.permutation(pos).astype(np.int64)
+    nrm = lambda *shp: rng.standard_normal(size=shp, dtype=np.float32)
+    kv_a = to_bf16_bits(nrm(cfg.T, sh.d_qk))
+    norm_w = (np.float32(1.0) + np.float32(0.1) * nrm(sh.d_latent)).astype(np.float32)
+    kI_new = to_bf16_bits(nrm(cfg.T, sh.d_idx))
+    q = to_bf16_bits(nrm(cfg.T, sh.n_heads, sh.d_qk))
+    qI = to_bf16_bits(nrm(cfg.T, sh.n_idx_heads, sh.d_idx))
+    kv_cache = to_bf16_bits(nrm(cfg.N, sh.d_qk))
+    kI_cache = to_bf16_bits(nrm(cfg.N, sh.d_idx))
+    return {"pos": pos, "kv_a": kv_a, "norm_w": norm_w, "kI_new": kI_new, "q": q, "qI": qI,
+            "kv_cache": kv_cache, "kI_cache": kI_cache}
