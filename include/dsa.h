@@ -172,6 +172,36 @@ dsa_status dsa_decode_step(const dsa_shape* shape, int32_t B, const int64_t* ctx
                            const uint16_t* kv, const uint16_t* kI, float* out, int32_t* idx_out,
                            int32_t* count_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Upstream cache write of T new tokens ("GLM-5.2-Vision: llama.cpp vs vLLM
+ * line-by-line pipeline trace", section 4, KV compression path: kv_cmpr and
+ * k_pe are split from the kv_a projection output, q_pe and k_pe are roped,
+ * kv_cmpr is RMS-normalised after the split; section 5: the rope is the NORM
+ * flavour, adjacent pairs, and the indexer rope is NORM too).  For token t
+ * at position p = pos[t]:
+ *   kv[p, 0:Dl]     = kv_a[t, 0:Dl] / sqrt(mean(kv_a[t, 0:Dl]^2) + eps) * norm_w
+ *   kv[p, Dl:Dl+Dr] = rope(kv_a[t, Dl:Dl+Dr], p)
+ *   kI[p, :]        = kI_new[t, :] with columns 0 .. d_idx_rope-1 roped
+ *   q[t, h, Dl:Dl+Dr] and qI[t, hi, 0:d_idx_rope] roped in place
+ * where rope over a width d turns the pair (x[2i], x[2i+1]) by the angle
+ * p * rope_theta^(-2i/d).  rope_theta, eps and d_idx_rope are not on the
+ * pages; they are arguments.
+ * kv_a [dev] [T, Dl+Dr] bf16; norm_w [dev] [Dl] fp32; pos [dev] [T] int32;
+ * kv [dev] [N, Dl+Dr] bf16 cache; kI_new [dev] [T, Di] and kI [dev] [N, Di]
+ * bf16 (both NULL: no indexer key is written); q [dev] [T, H, Dl+Dr] bf16 or
+ * NULL; qI [dev] [T, Hi, Di] bf16 or NULL.  Cache rows are written only for
+ * tokens with 0 <= pos < N (the query rope uses pos as given); positions
+ * must be distinct (two tokens writing one row race), and kv_a / kI_new must
+ * not overlap the rows written.  Results are computed in double precision
+ * and rounded once to bf16 (nearest, ties to even), for values in the normal
+ * bf16 range.  Requires T >= 0 (0: nothing is enqueued), N >= 1,
+ * rope_theta > 0, eps >= 0, 0 <= d_idx_rope <= Di; d_idx_rope must be a
+ * multiple of 8 (DSA_ERR_UNSUPPORTED otherwise).  kv_a, kv, kI_new, kI, q,
+ * qI 16-byte aligned; norm_w and pos 4-byte aligned. */
+dsa_status dsa_cache_write(const dsa_shape* shape, const uint16_t* kv_a, const float* norm_w, float eps,
+                           const int32_t* pos, int32_t T, int32_t N, uint16_t* kv, const uint16_t* kI_new,
+                           uint16_t* kI, uint16_t* q, uint16_t* qI, int32_t d_idx_rope, float rope_theta,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

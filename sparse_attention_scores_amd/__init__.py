@@ -20,14 +20,14 @@ __all__ = [
     "DsaError", "Shape", "GLM", "TINY", "lib",
     "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn", "dsa_latent_to_f16",
     "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
-    "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_status_string",
+    "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write", "dsa_status_string",
     "EXPORTED_SYMBOLS",
 ]
 
 EXPORTED_SYMBOLS = (
     "dsa_status_string", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn",
     "dsa_latent_to_f16", "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
-    "dsa_decode_workspace_bytes", "dsa_decode_step",
+    "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write",
 )
 
 
@@ -76,6 +76,8 @@ def _load() -> ctypes.CDLL:
         "dsa_prefill_chunk": (ctypes.c_int, [SP, P, P, P, P, P, i32, i32, i64, P, P, P, P, sz, P]),
         "dsa_decode_workspace_bytes": (sz, [SP, i32, P]),
         "dsa_decode_step": (ctypes.c_int, [SP, i32, P, P, P, P, P, P, P, P, P, P, sz, P]),
+        "dsa_cache_write": (ctypes.c_int, [SP, P, P, ctypes.c_float, P, i32, i32, P, P, P, P, P, i32,
+                                           ctypes.c_float, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -193,3 +195,13 @@ def dsa_decode_step(shape, ctx: Sequence[int], q, qI, w, kv, kI, out, idx_out=No
         _ptr(w, torch.float32, "w"), _bits(kv, "kv"), _bits(kI, "kI"), _ptr(out, torch.float32, "out"),
         _ptr(idx_out, torch.int32, "idx_out"), _ptr(count_out, torch.int32, "count_out"),
         ws_ptr, ws_bytes, _stream(stream)))
+
+
+def dsa_cache_write(shape, kv_a, norm_w, eps: float, pos, T: int, N: int, kv, kI_new=None, kI=None,
+                    q=None, qI=None, d_idx_rope: int = 64, rope_theta: float = 10000.0,
+                    stream=None) -> None:
+    sh = Shape.of(shape)
+    _check("dsa_cache_write", lib.dsa_cache_write(
+        ctypes.byref(sh), _bits(kv_a, "kv_a"), _ptr(norm_w, torch.float32, "norm_w"), float(eps),
+        _ptr(pos, torch.int32, "pos"), T, N, _bits(kv, "kv"), _bits(kI_new, "kI_new"), _bits(kI, "kI"),
+        _bits(q, "q"), _bits(qI, "qI"), d_idx_rope, float(rope_theta), _stream(stream)))

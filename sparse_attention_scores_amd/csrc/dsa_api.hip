@@ -228,6 +228,28 @@ dsa_status dsa_latent_to_f16(const dsa_shape* shape, const uint16_t* kv, int32_t
     return launched(dsa::launch_latent_to_f16(shape_id(shape), kv, kv16, N, (hipStream_t)stream));
 }
 
+dsa_status dsa_cache_write(const dsa_shape* shape, const uint16_t* kv_a, const float* norm_w, float eps,
+                           const int32_t* pos, int32_t T, int32_t N, uint16_t* kv, const uint16_t* kI_new,
+                           uint16_t* kI, uint16_t* q, uint16_t* qI, int32_t d_idx_rope, float rope_theta,
+                           void* stream) {
+    dsa_status st = check_shape(shape);
+    if (st) return st;
+    if (!kv_a || !norm_w || !pos || !kv || !aligned16(kv_a) || !aligned16(kv) ||
+        (reinterpret_cast<uintptr_t>(norm_w) & 3u) || (reinterpret_cast<uintptr_t>(pos) & 3u))
+        return DSA_ERR_INVALID_ARG;
+    if ((!kI_new) != (!kI) || (kI_new && (!aligned16(kI_new) || !aligned16(kI))) || (q && !aligned16(q)) ||
+        (qI && !aligned16(qI)))
+        return DSA_ERR_INVALID_ARG;
+    if (T < 0 || N <= 0 || d_idx_rope < 0 || d_idx_rope > shape->d_idx || !(rope_theta > 0.f) ||
+        !isfinite(rope_theta) || !(eps >= 0.f) || !isfinite(eps))
+        return DSA_ERR_INVALID_ARG;
+    if (d_idx_rope % 8 != 0) return DSA_ERR_UNSUPPORTED;
+    if (T == 0) return DSA_OK;
+    if ((st = check_device())) return st;
+    dsa::CacheWriteArgs a{kv_a, norm_w, pos, kI_new, kv, kI, q, qI, T, N, d_idx_rope, eps, rope_theta};
+    return launched(dsa::launch_cache_write(shape_id(shape), a, (hipStream_t)stream));
+}
+
 dsa_status dsa_sparse_mla_attn_f16(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv16,
                                    const int32_t* idx, const int32_t* count, int32_t L, int32_t N,
                                    float* out, float* lse, void* stream) {

@@ -146,4 +146,18 @@ hipError_t launch_latent_to_f16(int shape_id, const uint16_t* kv, uint16_t* kv16
 hipError_t launch_attention_split(int shape_id, const AttnSplitArgs& a, const SeqMeta& m,
                                   int items, hipStream_t s);
 
+struct CacheWriteArgs {
+    const uint16_t* kv_a;    // [T, Dl+Dr] new rows [kv_cmpr | k_pe]
+    const float* norm_w;     // [Dl]
+    const int32_t* pos;      // [T]
+    const uint16_t* kI_new;  // [T, Di] or null
+    uint16_t* kv;            // [N, Dl+Dr] latent cache
+    uint16_t* kI;            // [N, Di] indexer cache or null
+    uint16_t* q;             // [T, H, Dl+Dr] or null (rope columns rotated in place)
+    uint16_t* qI;            // [T, Hi, Di] or null (leading d_idx_rope columns rotated)
+    int32_t T, N, d_idx_rope;
+    float eps, theta;
+};
+hipError_t launch_cache_write(int shape_id, const CacheWriteArgs& a, hipStream_t s);
+
 }  // namespace dsa

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     assert sorted(dsa.EXPORTED_SYMBOLS) == names
     raw = ctypes.CDLL(dsa._build.LIB)
     for n in names:
@@ -101,3 +101,24 @@ def test_decode_workspace_and_validation():
     rc = L.dsa_decode_step(sh, 200, ctypes.cast(many, ctypes.c_void_p), *([fake()] * 6), None, None,
                            fake(), 1 << 30, None)
     assert rc == UNSUPPORTED
+
+
+def test_cache_write_validation():
+    L, sh = dsa.lib, ctypes.byref(dsa.GLM)
+    f = ctypes.c_float
+    def cw(kv_a=None, norm_w=None, pos=None, kv=None, kI_new=None, kI=None, q=None, qI=None, T=4, N=8,
+           d_idx_rope=64, theta=10000.0, eps=1e-6):
+        return L.dsa_cache_write(sh, kv_a or fake(), norm_w or fake(), f(eps), pos or fake(), T, N,
+                                 kv or fake(), kI_new, kI, q, qI, d_idx_rope, f(theta), None)
+    assert cw(kv_a=fake(0x1008)) == INVALID                     # misaligned
+    assert cw(norm_w=fake(0x1002)) == INVALID                   # norm weight not 4-byte aligned
+    assert cw(kI_new=fake()) == INVALID                         # key without its cache
+    assert cw(T=-1) == INVALID
+    assert cw(N=0) == INVALID
+    assert cw(theta=0.0) == INVALID and cw(theta=float("inf")) == INVALID
+    assert cw(eps=-1.0) == INVALID and cw(eps=float("nan")) == INVALID
+    assert cw(d_idx_rope=130) == INVALID and cw(d_idx_rope=-2) == INVALID
+    assert cw(d_idx_rope=6) == UNSUPPORTED                      # not a multiple of 8
+    assert cw(T=0) == OK                                        # nothing to do, nothing enqueued
+    assert L.dsa_cache_write(None, fake(), fake(), f(0), fake(), 1, 1, fake(), None, None, None, None,
+                             64, f(1e4), None) == INVALID
