@@ -33,7 +33,9 @@ KERNEL_SOURCES = {
     "attention": "sparse_attention_scores_amd/csrc/attention.hip",
     "indexer": "sparse_attention_scores_amd/csrc/indexer.hip",
     "topk": "sparse_attention_scores_amd/csrc/topk.hip",
+    "cache_write": "sparse_attention_scores_amd/csrc/cache_write.hip",
 }
+CACHE_WRITE = "glm_16k_chunk"
 
 
 def log(*a):
@@ -58,13 +60,31 @@ def measured_traffic(stage: str):
     return t.get("bytes_per_launch")
 
 
-PROFILE_STAGES = ("prefill", "indexer", "topk", "attention", "decode", "copy")
+PROFILE_STAGES = ("prefill", "indexer", "topk", "attention", "decode", "cache_write", "copy")
 COPY_BYTES = 1 << 30            # plain copy used to scale the HBM byte counters
 STAGE_KERNELS = {
     "attention": "attention_kernel<",
     "indexer": "indexer_prefill_kernel<",
     "topk": "topk_prefill_kernel<",
+    "cache_write": "cache_write_kernel<",
 }
+
+
+def cache_write_setup(np, torch, dsa, W):
+    """Device inputs of the 16k chunk's cache write and a call that runs it;
+    also the algorithmic bytes one call moves."""
+    cw = W.CACHE_WRITE[CACHE_WRITE]
+    sh = cw.shape
+    d = W.make_cache_write(cw)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else a).cuda()
+    t = {k: to(d[k]) for k in ("kv_a", "norm_w", "kI_new", "q", "qI", "kv_cache", "kI_cache")}
+    pos = torch.from_numpy(d["pos"].astype(np.int32)).cuda()
+    f = lambda: dsa.dsa_cache_write(sh, t["kv_a"], t["norm_w"], cw.eps, pos, cw.T, cw.N, t["kv_cache"],
+                                    t["kI_new"], t["kI_cache"], t["q"], t["qI"], d_idx_rope=cw.d_idx_rope,
+                                    rope_theta=cw.theta)
+    per_token = (2 * 2 * sh.d_qk + 2 * 2 * sh.d_idx + 4 + 2 * 2 * sh.n_heads * sh.d_rope
+                 + 2 * 2 * sh.n_idx_heads * cw.d_idx_rope)
+    return cw, f, per_token * cw.T + 4 * sh.d_latent
 
 
 def profile_stage(stage, reps, np, torch, dsa, W) -> int:
@@ -78,6 +98,14 @@ def profile_stage(stage, reps, np, torch, dsa, W) -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         log("copy done", reps)
+        return 0
+    if stage == "cache_write":
+        _, f, _ = cache_write_setup(np, torch, dsa, W)
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            f()
+        torch.cuda.synchronize()
+        log("cache_write done", reps)
         return 0
     if stage == "decode":
         dc = W.DECODE[DECODE]
@@ -313,6 +341,15 @@ def main() -> int:
                           "gather_gbps": wk["gather_bytes"] / t_attn / 1e9,
                           "gather_hbm_frac": wk["gather_bytes"] / t_attn / 1e9 / PEAK_HBM_GBPS},
         }
+        log("cache write stage")
+        cw, f_cw, cw_bytes = cache_write_setup(np, torch, dsa, W)
+        f_cw()
+        torch.cuda.synchronize()
+        t_cw = timed_events(f_cw, max(n, 10), torch)
+        stages["cache_write"] = {"kernel": "cache_write_kernel<64,512,64,32,128>", "us": t_cw * 1e6,
+                                 "gbps": cw_bytes / t_cw / 1e9, "frac": cw_bytes / t_cw / 1e9 / PEAK_HBM_GBPS,
+                                 "workload": "%d new tokens at positions %d..%d into a %d-row cache; "
+                                             "q and indexer q roped in place" % (cw.T, cw.p0, cw.p0 + cw.T - 1, cw.N)}
         result["stages"] = stages
         dom = max(("indexer", t_idx), ("topk", t_topk), ("attention", t_attn), key=lambda x: x[1])[0]
         if dom == "topk":

@@ -12,11 +12,12 @@
 //
 // One 256-thread block per token.  The work is a few kilobytes of HBM traffic
 // per token (the query's rope columns dominate), so the kernel is bound by
-// HBM and every element is moved once, as 16-byte vectors:
-//  - wave 0 normalises the latent part and writes it to cache row pos;
-//  - wave 1 rotates k_pe into the same row and writes the indexer key row;
-//  - all threads rotate the query's rope columns of every head and the
-//    indexer query's leading columns, in place.
+// HBM and every element is moved once, as 16-byte vectors.  Every load of
+// the token is issued first; while they are in flight waves 2 and 3 build
+// the (cos, sin) tables and wave 0 normalises the latent part into cache row
+// pos; after one barrier wave 1 rotates k_pe into the same row and writes
+// the indexer key row, and all threads rotate the query's rope columns of
+// every head and the indexer query's leading columns, in place.
 // The arithmetic (angles, sines and cosines, the rotation, the sum of squares
 // and the scaling) runs in double precision and each result is rounded once
 // to bf16 (nearest, ties to even): the rounding of a double result to 8
@@ -34,23 +35,21 @@ constexpr int kCwThreads = 256;
 
 __device__ inline double bf16_to_f64(uint32_t b) { return (double)__uint_as_float(b << 16); }
 
-// double -> bf16 bits, round to nearest with ties to even on the 53-bit
-// significand.  Zero and the normal bf16 range are exact; values below the
-// normal range flush to a signed zero, values above it become infinities.
+// double -> bf16 bits, round to nearest with ties to even.  Rounding to
+// float first (nearest-even) and then to bf16 gives the correctly rounded
+// result except when the float lands exactly on a bf16 midpoint (its low 16
+// bits are 0x8000) without the double being there: then the second rounding
+// would see a false tie.  In that case the float is moved one ulp toward the
+// double before the bf16 rounding.  Exact for results in the normal bf16
+// range.
 __device__ inline uint32_t f64_to_bf16(double v) {
-    const uint64_t u = (uint64_t)__double_as_longlong(v);
-    const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
-    const int e = (int)((u >> 52) & 0x7FF);
-    if (e == 0) return sign;
-    const uint64_t m = (u & 0xFFFFFFFFFFFFFull) | (1ull << 52);
-    uint64_t keep = m >> 45;                                  // 8 significant bits
-    const uint64_t rem = m & ((1ull << 45) - 1), half = 1ull << 44;
-    if (rem > half || (rem == half && (keep & 1))) ++keep;
-    int eb = e - 1023 + 127;
-    if (keep == 256) { keep = 128; ++eb; }
-    if (eb <= 0) return sign;
-    if (eb >= 255) return sign | 0x7F80u;
-    return sign | ((uint32_t)eb << 7) | (uint32_t)(keep & 127);
+    const float r = (float)v;
+    uint32_t u = __float_as_uint(r);
+    if ((u & 0xFFFFu) == 0x8000u) {
+        const double back = (double)r;
+        if (back != v) u = (fabs(back) > fabs(v)) ? u - 1u : u + 1u;
+    }
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
 // Rotate the four adjacent pairs of one 16-byte vector (8 bf16); pair k
@@ -71,37 +70,60 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(CacheWriteArgs 
     static_assert(DL % 8 == 0 && DR % 8 == 0 && DI % 8 == 0, "16-byte vectors");
     static_assert(DL / 8 <= 64 && DR / 8 + DI / 8 <= 64, "one wave per part");
     constexpr int DQK = DL + DR;
+    constexpr int VR = DR / 8;                                              // vectors per rope row
+    constexpr int QV = (H * VR + kCwThreads - 1) / kCwThreads;              // query vectors per thread
+    constexpr int IV = (HI * (DI / 8) + kCwThreads - 1) / kCwThreads;       // indexer-query vectors (max)
     __shared__ double2 cs_r[DR / 2 > 0 ? DR / 2 : 1];    // (cos, sin) over the Dr-wide rope
     __shared__ double2 cs_i[DI / 2];                     // ... over the indexer rope width
     const int t = blockIdx.x;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int p = a.pos[t];
-    const double pd = (double)p;
-    const int dir = a.d_idx_rope;
-    const double lth = log2((double)a.theta);
-    if (w == 0 && l < DR / 2) {
-        double s, c;
-        sincos(pd * exp2(lth * (-2.0 * l / DR)), &s, &c);
-        cs_r[l] = make_double2(c, s);
-    } else if (w == 1 && l < dir / 2) {
-        double s, c;
-        sincos(pd * exp2(lth * (-2.0 * l / dir)), &s, &c);
-        cs_i[l] = make_double2(c, s);
-    }
-    __syncthreads();
+    const int dir = a.d_idx_rope, VI = dir / 8;
     const bool write_row = p >= 0 && p < a.N;
-    if (write_row && w == 0) {
-        // latent part: x / sqrt(mean(x^2) + eps) * weight
-        const uint16_t* src = a.kv_a + (int64_t)t * DQK;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        double ss = 0.0;
-        if (l < DL / 8) {
-            x = ldg16(src + 8 * l);
+
+    // 1. every load of the token first, so that they are in flight while
+    //    the rotation tables are built
+    u32x4 qv[QV], iv[IV], rv = {0u, 0u, 0u, 0u};
+    uint16_t* qrow = a.q ? a.q + (int64_t)t * H * DQK + DL : nullptr;
+    uint16_t* irow = a.qI ? a.qI + (int64_t)t * HI * DI : nullptr;
+    if (a.q) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const double lo = bf16_to_f64(x[k] & 0xFFFFu), hi = bf16_to_f64(x[k] >> 16);
-                ss += lo * lo + hi * hi;
-            }
+        for (int j = 0; j < QV; ++j) {
+            const int i = tid + j * kCwThreads;
+            if (i < H * VR) qv[j] = ldg16(qrow + (int64_t)(i / VR) * DQK + 8 * (i % VR));
+        }
+    }
+    if (a.qI) {
+#pragma unroll
+        for (int j = 0; j < IV; ++j) {
+            const int i = tid + j * kCwThreads;
+            if (i < HI * VI) iv[j] = ldg16(irow + (int64_t)(i / VI) * DI + 8 * (i % VI));
+        }
+    }
+    if (write_row) {
+        if (w == 0 && l < DL / 8) rv = ldg16(a.kv_a + (int64_t)t * DQK + 8 * l);                 // kv_cmpr
+        else if (w == 1 && l < VR) rv = ldg16(a.kv_a + (int64_t)t * DQK + DL + 8 * l);          // k_pe
+        else if (w == 1 && a.kI && l < VR + DI / 8) rv = ldg16(a.kI_new + (int64_t)t * DI + 8 * (l - VR));
+    }
+
+    // 2. rotation tables in double: pair i turns by p * theta^(-2i/d)
+    const double pd = (double)p, lth = log2((double)a.theta);
+    if (w == 2 && l < DR / 2) {
+        double sn, cn;
+        sincos(pd * exp2(lth * (-2.0 * l / DR)), &sn, &cn);
+        cs_r[l] = make_double2(cn, sn);
+    } else if (w == 3 && l < dir / 2) {
+        double sn, cn;
+        sincos(pd * exp2(lth * (-2.0 * l / dir)), &sn, &cn);
+        cs_i[l] = make_double2(cn, sn);
+    }
+    // 3. latent part: x / sqrt(mean(x^2) + eps) * weight (no table needed)
+    if (write_row && w == 0) {
+        double ss = 0.0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const double lo = bf16_to_f64(rv[k] & 0xFFFFu), hi = bf16_to_f64(rv[k] >> 16);
+            ss += lo * lo + hi * hi;
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
@@ -110,39 +132,40 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(CacheWriteArgs 
             u32x4 y;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const double lo = bf16_to_f64(x[k] & 0xFFFFu) * r * (double)a.norm_w[8 * l + 2 * k];
-                const double hi = bf16_to_f64(x[k] >> 16) * r * (double)a.norm_w[8 * l + 2 * k + 1];
+                const double lo = bf16_to_f64(rv[k] & 0xFFFFu) * r * (double)a.norm_w[8 * l + 2 * k];
+                const double hi = bf16_to_f64(rv[k] >> 16) * r * (double)a.norm_w[8 * l + 2 * k + 1];
                 y[k] = f64_to_bf16(lo) | (f64_to_bf16(hi) << 16);
             }
             *reinterpret_cast<u32x4*>(a.kv + (int64_t)p * DQK + 8 * l) = y;
         }
-    } else if (write_row && w == 1) {
-        if (l < DR / 8) {            // k_pe -> rope -> cache row
-            const u32x4 x = ldg16(a.kv_a + (int64_t)t * DQK + DL + 8 * l);
-            *reinterpret_cast<u32x4*>(a.kv + (int64_t)p * DQK + DL + 8 * l) = rope_vec(x, cs_r, 4 * l);
-        } else if (a.kI && l < DR / 8 + DI / 8) {   // indexer key: leading columns roped
-            const int v = l - DR / 8;
-            const u32x4 x = ldg16(a.kI_new + (int64_t)t * DI + 8 * v);
-            *reinterpret_cast<u32x4*>(a.kI + (int64_t)p * DI + 8 * v) = (8 * v < dir) ? rope_vec(x, cs_i, 4 * v) : x;
+    }
+    __syncthreads();
+
+    // 4. rotations and stores
+    if (write_row && w == 1) {
+        if (l < VR) {                                   // k_pe -> cache row
+            *reinterpret_cast<u32x4*>(a.kv + (int64_t)p * DQK + DL + 8 * l) = rope_vec(rv, cs_r, 4 * l);
+        } else if (a.kI && l < VR + DI / 8) {           // indexer key: leading columns roped
+            const int v = l - VR;
+            *reinterpret_cast<u32x4*>(a.kI + (int64_t)p * DI + 8 * v) = (8 * v < dir) ? rope_vec(rv, cs_i, 4 * v) : rv;
         }
     }
-    // the query's rope columns of every head, and the indexer query
     if (a.q) {
-        constexpr int VR = DR / 8;
-        uint16_t* qt = a.q + (int64_t)t * H * DQK + DL;
-        for (int i = tid; i < H * VR; i += kCwThreads) {
-            const int h = i / VR, v = i % VR;
-            uint16_t* ptr = qt + (int64_t)h * DQK + 8 * v;
-            *reinterpret_cast<u32x4*>(ptr) = rope_vec(ldg16(ptr), cs_r, 4 * v);
+#pragma unroll
+        for (int j = 0; j < QV; ++j) {
+            const int i = tid + j * kCwThreads;
+            if (i < H * VR)
+                *reinterpret_cast<u32x4*>(qrow + (int64_t)(i / VR) * DQK + 8 * (i % VR)) =
+                    rope_vec(qv[j], cs_r, 4 * (i % VR));
         }
     }
-    if (a.qI && dir > 0) {
-        const int VI = dir / 8;
-        uint16_t* qt = a.qI + (int64_t)t * HI * DI;
-        for (int i = tid; i < HI * VI; i += kCwThreads) {
-            const int h = i / VI, v = i % VI;
-            uint16_t* ptr = qt + (int64_t)h * DI + 8 * v;
-            *reinterpret_cast<u32x4*>(ptr) = rope_vec(ldg16(ptr), cs_i, 4 * v);
+    if (a.qI) {
+#pragma unroll
+        for (int j = 0; j < IV; ++j) {
+            const int i = tid + j * kCwThreads;
+            if (i < HI * VI)
+                *reinterpret_cast<u32x4*>(irow + (int64_t)(i / VI) * DI + 8 * (i % VI)) =
+                    rope_vec(iv[j], cs_i, 4 * (i % VI));
         }
     }
 }
