@@ -46,8 +46,10 @@ def _configure(lib):
                                        P, P, P, i32]
     lib.oracle_cache_write.argtypes = [P, P, dbl, P, i64, i64, P, P, P, P, P, i32, i32, i32, i32, i32,
                                        i32, dbl]
+    lib.oracle_router_topk.argtypes = [P, P, i64, i32, i32, dbl, dbl, P, P]
     for f in (lib.oracle_indexer_scores, lib.oracle_topk_select, lib.oracle_sparse_mla_attn,
-              lib.oracle_prefill_chunk, lib.oracle_decode_step, lib.oracle_cache_write):
+              lib.oracle_prefill_chunk, lib.oracle_decode_step, lib.oracle_cache_write,
+              lib.oracle_router_topk):
         f.restype = ctypes.c_int
     return lib
 
@@ -187,3 +189,17 @@ def cache_write(kv_a, norm_w, eps: float, pos, kv_cache, kI_new=None, kI_cache=N
         _p(q_out), _p(qI_out), shape.n_heads, shape.d_latent, shape.d_rope, shape.n_idx_heads,
         shape.d_idx, d_idx_rope, float(theta)), "cache write")
     return kv_out, kI_out, q_out, qI_out
+
+
+ROUTER_MIN_SUM = 6.1e-5   # the clamp on the weight sum (pipeline trace section 8a)
+
+
+def router_topk(logits, bias, k: int, scale: float, min_sum: float = ROUTER_MIN_SUM):
+    """(ids [T, k] int32 by descending selection score, weights [T, k] float64)."""
+    logits, bias = _c(logits, np.float32), _c(bias, np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    wts = np.empty((T, k), dtype=np.float64)
+    _check(_load().oracle_router_topk(_p(logits), _p(bias), T, E, k, float(scale), float(min_sum),
+                                      _p(ids), _p(wts)), "router")
+    return ids, wts

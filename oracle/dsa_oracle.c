@@ -472,3 +472,53 @@ int oracle_cache_write(const uint16_t* kv_a, const float* norm_w, double eps,
     free(tmp);
     return 0;
 }
+
+/* ==========================================================================
+ * Router selection ("GLM-5.2-Vision: llama.cpp vs vLLM" pipeline trace,
+ * section 8a, Gating; exo PR #2539, router selection in one kernel): per
+ * token the expert probabilities are the sigmoid of the float32 router
+ * logits; the selection score adds the per-expert bias, which is used for
+ * the choice only; the k best experts by selection score are kept; their
+ * weights are the unbiased probabilities divided by their sum (clamped
+ * below at 6.1e-5) and multiplied by the routed scaling factor (GLM: 256
+ * experts, 8 per token, factor 2.5, one expert group).  Readings: a float32
+ * probability is the exact sigmoid rounded once to float; the selection
+ * score is that float plus the bias in float arithmetic; equal selection
+ * scores go to the lower expert index; experts are listed by descending
+ * selection score.
+ * ======================================================================== */
+typedef struct { float s; int32_t e; } expert_key;
+
+static int by_score_then_index(const void* a, const void* b) {
+    const expert_key* x = (const expert_key*)a;
+    const expert_key* y = (const expert_key*)b;
+    if (x->s != y->s) return x->s > y->s ? -1 : 1;   /* higher selection score first */
+    return (x->e < y->e) ? -1 : (x->e > y->e);
+}
+
+int oracle_router_topk(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
+                       double scale, double min_sum, int32_t* ids, double* weights) {
+    if (!logits || !bias || !ids || !weights || T < 0 || E <= 0 || k <= 0 || k > E) return -1;
+    float* p = (float*)malloc((size_t)E * sizeof(float));
+    expert_key* key = (expert_key*)malloc((size_t)E * sizeof(expert_key));
+    if (!p || !key) { free(p); free(key); return -8; }
+    for (int64_t t = 0; t < T; ++t) {
+        const float* lg = logits + t * E;
+        for (int32_t e = 0; e < E; ++e) {
+            p[e] = (float)(1.0 / (1.0 + exp(-(double)lg[e])));
+            key[e].s = p[e] + bias[e];            /* float + float, rounded to float */
+            key[e].e = e;
+        }
+        qsort(key, (size_t)E, sizeof(expert_key), by_score_then_index);
+        double sum = 0.0;
+        for (int32_t j = 0; j < k; ++j) sum += (double)p[key[j].e];
+        double den = sum > min_sum ? sum : min_sum;
+        for (int32_t j = 0; j < k; ++j) {
+            ids[t * k + j] = key[j].e;
+            weights[t * k + j] = (double)p[key[j].e] / den * scale;
+        }
+    }
+    free(p);
+    free(key);
+    return 0;
+}

@@ -97,6 +97,14 @@ int oracle_cache_write(const uint16_t* kv_a, const float* norm_w, double eps,
                        int32_t H, int32_t Dl, int32_t Dr, int32_t Hi, int32_t Di,
                        int32_t d_idx_rope, double theta);
 
+/* Router selection per token (pipeline trace section 8a).
+ *   logits [T, E] float, bias [E] float;
+ *   p_e = sigmoid(logit_e) rounded once to float; s_e = p_e + bias_e (float);
+ *   ids [T, k]: the k experts by (s desc, e asc), in that order;
+ *   weights [T, k] double: p_e / max(sum of the k p_e, min_sum) * scale. */
+int oracle_router_topk(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
+                       double scale, double min_sum, int32_t* ids, double* weights);
+
 #ifdef __cplusplus
 }
 #endif

@@ -556,4 +556,80 @@ def pin_cache_write_rows_and_layout():
     assert np.array_equal(kv2[5, :sh.d_latent], kv[d["pos"][t], :sh.d_latent])
 
 
+# --------------------------------------------------------------------------
+# router selection (pipeline trace section 8a)
+# --------------------------------------------------------------------------
+def _router_brute(logits, bias, k, scale):
+    """Independent ranking with Python's sort on (score desc, expert asc);
+    the float32 probability is the exact sigmoid rounded once (math.exp in
+    double, then numpy's float32 rounding) and the score a float32 sum."""
+    T, E = logits.shape
+    ids = np.empty((T, k), np.int64)
+    wts = np.empty((T, k))
+    for t in range(T):
+        p = np.array([1.0 / (1.0 + math.exp(-float(x))) for x in logits[t]]).astype(np.float32)
+        sc = p + bias                                     # float32 + float32
+        order = sorted(range(E), key=lambda e: (-float(sc[e]), e))[:k]
+        ids[t] = order
+        tot = sum(float(p[e]) for e in order)
+        wts[t] = [float(p[e]) / max(tot, oracle.ROUTER_MIN_SUM) * scale for e in order]
+    return ids, wts
+
+
+def pin_router_brute_force():
+    """Selections on random and on heavily tied inputs equal a plain sort."""
+    for name in ("small", "small_ties", "glm_ties"):
+        cfg = W.ROUTER[name]
+        d = W.make_router(cfg)
+        ids, wts = oracle.router_topk(d["logits"], d["bias"], cfg.k, cfg.scale)
+        bi, bw = _router_brute(d["logits"], d["bias"], cfg.k, cfg.scale)
+        assert np.array_equal(ids, bi), name
+        assert np.allclose(wts, bw, rtol=1e-12, atol=0), name
+
+
+def pin_router_closed_forms():
+    """Equal logits: experts 0..k-1 (ties to the lower index), each weighted
+    scale/k.  A large bias selects an expert first without entering its
+    weight.  Weights of a normalised selection sum to the scale."""
+    E, k, sc = 16, 4, 2.5
+    ids, wts = oracle.router_topk(np.zeros((1, E), np.float32), np.zeros(E, np.float32), k, sc)
+    assert list(ids[0]) == [0, 1, 2, 3] and np.allclose(wts, sc / k, rtol=1e-15)
+    lg = np.zeros((1, E), np.float32)
+    lg[0, E - 1] = -4.0
+    b = np.zeros(E, np.float32)
+    b[E - 1] = 10.0
+    ids, wts = oracle.router_topk(lg, b, k, sc)
+    assert list(ids[0]) == [E - 1, 0, 1, 2]
+    p = float(np.float32(1.0 / (1.0 + math.exp(4.0))))
+    assert abs(wts[0, 0] - p / (p + 1.5) * sc) < 1e-12 and abs(wts[0, 1] - 0.5 / (p + 1.5) * sc) < 1e-12
+    cfg = W.ROUTER["small"]
+    d = W.make_router(cfg)
+    _, wts = oracle.router_topk(d["logits"], d["bias"], cfg.k, cfg.scale)
+    assert np.allclose(wts.sum(axis=1), cfg.scale, rtol=1e-12)
+
+
+def pin_router_weight_clamp():
+    """Probabilities far below the clamp: the weight sum is held at 6.1e-5,
+    so the weights are p / 6.1e-5 * scale rather than summing to the scale."""
+    E, k, sc = 32, 8, 2.5
+    lg = np.full((1, E), -30.0, np.float32)
+    ids, wts = oracle.router_topk(lg, np.zeros(E, np.float32), k, sc)
+    p = float(np.float32(1.0 / (1.0 + math.exp(30.0))))
+    assert list(ids[0]) == list(range(k))
+    assert np.allclose(wts, p / 6.1e-5 * sc, rtol=1e-12)
+
+
+def pin_router_sigmoid_symmetry():
+    """sigmoid(x) + sigmoid(-x) = 1 (each rounded once to float): with equal
+    bias, expert 0 at +x and expert 1 at -x, k = 2, the weights are the two
+    probabilities over their sum of 1 (to float rounding)."""
+    for x in (0.25, 1.0, 3.0, 7.5):
+        lg = np.array([[x, -x]], np.float32)
+        ids, wts = oracle.router_topk(lg, np.zeros(2, np.float32), 2, 1.0)
+        assert list(ids[0]) == [0, 1]
+        assert abs(wts[0].sum() - 1.0) < 1e-15 and abs(wts[0, 0] + wts[0, 1] - 1.0) < 1e-15
+        pp = 1.0 / (1.0 + math.exp(-x))
+        assert abs(wts[0, 0] - pp) < 2.0 ** -24 * 2 and abs(wts[0, 1] - (1 - pp)) < 2.0 ** -24 * 2
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -60,6 +60,18 @@ MUTATIONS = [
     ("q rope at column 0", "rope_rows_bf16(q + t * H * Dqk, H, Dqk, Dl, Dr, p, theta, tmp);",
      "rope_rows_bf16(q + t * H * Dqk, H, Dqk, 0, Dr, p, theta, tmp);"),
     ("bf16 rounding truncates", "double r = nearbyint(ldexp(m, 8));", "double r = floor(ldexp(m, 8));"),
+    ("router weights take the biased score", "weights[t * k + j] = (double)p[key[j].e] / den * scale;",
+     "weights[t * k + j] = (double)key[j].s / den * scale;"),
+    ("router weights not normalised", "weights[t * k + j] = (double)p[key[j].e] / den * scale;",
+     "weights[t * k + j] = (double)p[key[j].e] * scale;"),
+    ("router clamp ignored", "double den = sum > min_sum ? sum : min_sum;", "double den = sum;"),
+    ("router ties to the higher expert", "return (x->e < y->e) ? -1 : (x->e > y->e);",
+     "return (x->e > y->e) ? -1 : (x->e < y->e);"),
+    ("router keeps the lowest scores", "if (x->s != y->s) return x->s > y->s ? -1 : 1;",
+     "if (x->s != y->s) return x->s < y->s ? -1 : 1;"),
+    ("router sigmoid sign", "p[e] = (float)(1.0 / (1.0 + exp(-(double)lg[e])));",
+     "p[e] = (float)(1.0 / (1.0 + exp((double)lg[e])));"),
+    ("router bias ignored", "key[e].s = p[e] + bias[e];", "key[e].s = p[e];"),
     ("positions taken as 1-based rows", "uint16_t* dst = kv_cache + pos[t] * Dqk;",
      "uint16_t* dst = kv_cache + (pos[t] > 0 ? pos[t] - 1 : 0) * Dqk;"),
 ]

@@ -32,7 +32,7 @@ import numpy as np
 __all__ = [
     "Shape", "TINY", "GLM", "Prefill", "Decode", "PREFILL", "DECODE",
     "to_bf16_bits", "bf16_bits_to_f32", "make_prefill", "make_decode",
-    "CacheWrite", "CACHE_WRITE", "make_cache_write",
+    "CacheWrite", "CACHE_WRITE", "make_cache_write", "Router", "ROUTER", "make_router",
 ]
 
 
@@ -225,3 +225,45 @@ def make_cache_write(cfg: CacheWrite) -> Dict[str, np.ndarray]:
     kI_cache = to_bf16_bits(nrm(cfg.N, sh.d_idx))
     return {"pos": pos, "kv_a": kv_a, "norm_w": norm_w, "kI_new": kI_new, "q": q, "qI": qI,
             "kv_cache": kv_cache, "kI_cache": kI_cache}
+
+
+@dataclasses.dataclass(frozen=True)
+class Router:
+    """Router selection over T tokens: E experts, k kept per token, scaled by
+    ``scale`` (GLM: 256 experts, 8 per token, routed_scaling_factor 2.5).
+    ``kind``: "normal" = logits N(0,1)*2 and bias N(0,1)*0.1; "ties" =
+    integer logits in [-1, 1] and a bias of 0 or +-2^-10 (many exactly equal
+    selection scores); "tiny_p" = logits near -30 (probabilities far below
+    the weight-sum clamp)."""
+    name: str
+    T: int
+    E: int
+    k: int
+    seed: int
+    kind: str = "normal"
+    scale: float = 2.5
+
+
+ROUTER: Dict[str, Router] = {
+    "glm_16k_chunk": Router("glm_16k_chunk", 4096, 256, 8, 41),
+    "glm_decode_8": Router("glm_decode_8", 8, 256, 8, 42),
+    "glm_ties": Router("glm_ties", 64, 256, 8, 43, "ties"),
+    "glm_tiny_p": Router("glm_tiny_p", 16, 256, 8, 44, "tiny_p"),
+    "small": Router("small", 33, 64, 4, 45),
+    "small_ties": Router("small_ties", 40, 128, 6, 46, "ties"),
+}
+
+
+def make_router(cfg: Router) -> Dict[str, np.ndarray]:
+    """Router logits [T, E] and bias [E], float32, drawn in that order."""
+    rng = np.random.default_rng(cfg.seed)
+    if cfg.kind == "ties":
+        logits = rng.integers(-1, 2, size=(cfg.T, cfg.E)).astype(np.float32)
+        bias = (rng.integers(-1, 2, size=cfg.E) * 2.0 ** -10).astype(np.float32)
+    elif cfg.kind == "tiny_p":
+        logits = (-30.0 + rng.standard_normal(size=(cfg.T, cfg.E))).astype(np.float32)
+        bias = (rng.standard_normal(size=cfg.E) * 0.1).astype(np.float32)
+    else:
+        logits = (rng.standard_normal(size=(cfg.T, cfg.E)) * 2.0).astype(np.float32)
+        bias = (rng.standard_normal(size=cfg.E) * 0.1).astype(np.float32)
+    return {"logits": np.ascontiguousarray(logits), "bias": np.ascontiguousarray(bias)}
