@@ -350,6 +350,20 @@ def main() -> int:
                                  "gbps": cw_bytes / t_cw / 1e9, "frac": cw_bytes / t_cw / 1e9 / PEAK_HBM_GBPS,
                                  "workload": "%d new tokens at positions %d..%d into a %d-row cache; "
                                              "q and indexer q roped in place" % (cw.T, cw.p0, cw.p0 + cw.T - 1, cw.N)}
+        log("router stage")
+        rc = W.ROUTER["glm_16k_chunk"]
+        rd = W.make_router(rc)
+        r_lg, r_b = to(rd["logits"]), to(rd["bias"])
+        r_ids = torch.empty((rc.T, rc.k), dtype=torch.int32, device="cuda")
+        r_w = torch.empty((rc.T, rc.k), dtype=torch.float32, device="cuda")
+        f_rt = lambda: dsa.dsa_router_topk(r_lg, r_b, rc.T, rc.E, rc.k, rc.scale, r_ids, r_w)
+        f_rt()
+        torch.cuda.synchronize()
+        t_rt = timed_events(f_rt, max(n, 20), torch)
+        rt_bytes = 4 * rc.T * rc.E + 4 * rc.E + 8 * rc.T * rc.k
+        stages["router"] = {"kernel": "router_topk_kernel<4>", "us": t_rt * 1e6,
+                            "gbps": rt_bytes / t_rt / 1e9, "frac": rt_bytes / t_rt / 1e9 / PEAK_HBM_GBPS,
+                            "workload": "%d tokens x %d experts, top %d, scale %.1f" % (rc.T, rc.E, rc.k, rc.scale)}
         result["stages"] = stages
         dom = max(("indexer", t_idx), ("topk", t_topk), ("attention", t_attn), key=lambda x: x[1])[0]
         if dom == "topk":

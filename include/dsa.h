@@ -202,6 +202,25 @@ dsa_status dsa_cache_write(const dsa_shape* shape, const uint16_t* kv_a, const f
                            uint16_t* kI, uint16_t* q, uint16_t* qI, int32_t d_idx_rope, float rope_theta,
                            void* stream);
 
+/* MoE router selection for T tokens ("GLM-5.2-Vision: llama.cpp vs vLLM
+ * line-by-line pipeline trace", section 8a, Gating; exo PR #2539, router
+ * selection in one kernel).  Per token, with p_e = sigmoid(logits[t, e]):
+ *   s_e = p_e + bias[e]                        (the bias serves the choice only)
+ *   ids[t, :] = the k experts by (s desc, e asc), in that order
+ *   weights[t, j] = p_ids[j] / max(sum_j p_ids[j], 6.1e-5) * routed_scale
+ * (GLM: 256 experts, k = 8, routed_scale 2.5, one expert group).  Readings:
+ * p_e is the exact sigmoid rounded once to float; s_e is a float sum; equal
+ * scores go to the lower expert index.  Weights are formed in double and
+ * rounded to float.
+ * logits [dev] [T, n_experts] fp32 (16-byte aligned); bias [dev]
+ * [n_experts] fp32; ids [dev] [T, k] int32; weights [dev] [T, k] fp32.
+ * Requires T >= 0 (0: nothing is enqueued), 1 <= k <= n_experts, a finite
+ * routed_scale; n_experts in {64, 128, 256, 512, 1024} and k <= 32
+ * (DSA_ERR_UNSUPPORTED otherwise).  Non-finite logits or biases give
+ * undefined results. */
+dsa_status dsa_router_topk(const float* logits, const float* bias, int32_t T, int32_t n_experts, int32_t k,
+                           float routed_scale, int32_t* ids, float* weights, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

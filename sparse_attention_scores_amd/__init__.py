@@ -20,14 +20,15 @@ __all__ = [
     "DsaError", "Shape", "GLM", "TINY", "lib",
     "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn", "dsa_latent_to_f16",
     "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
-    "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write", "dsa_status_string",
+    "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write", "dsa_router_topk",
+    "dsa_status_string",
     "EXPORTED_SYMBOLS",
 ]
 
 EXPORTED_SYMBOLS = (
     "dsa_status_string", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn",
     "dsa_latent_to_f16", "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
-    "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write",
+    "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write", "dsa_router_topk",
 )
 
 
@@ -78,6 +79,7 @@ def _load() -> ctypes.CDLL:
         "dsa_decode_step": (ctypes.c_int, [SP, i32, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "dsa_cache_write": (ctypes.c_int, [SP, P, P, ctypes.c_float, P, i32, i32, P, P, P, P, P, i32,
                                            ctypes.c_float, P]),
+        "dsa_router_topk": (ctypes.c_int, [P, P, i32, i32, i32, ctypes.c_float, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -205,3 +207,11 @@ def dsa_cache_write(shape, kv_a, norm_w, eps: float, pos, T: int, N: int, kv, kI
         ctypes.byref(sh), _bits(kv_a, "kv_a"), _ptr(norm_w, torch.float32, "norm_w"), float(eps),
         _ptr(pos, torch.int32, "pos"), T, N, _bits(kv, "kv"), _bits(kI_new, "kI_new"), _bits(kI, "kI"),
         _bits(q, "q"), _bits(qI, "qI"), d_idx_rope, float(rope_theta), _stream(stream)))
+
+
+def dsa_router_topk(logits, bias, T: int, n_experts: int, k: int, routed_scale: float, ids, weights,
+                    stream=None) -> None:
+    _check("dsa_router_topk", lib.dsa_router_topk(
+        _ptr(logits, torch.float32, "logits"), _ptr(bias, torch.float32, "bias"), T, n_experts, k,
+        float(routed_scale), _ptr(ids, torch.int32, "ids"), _ptr(weights, torch.float32, "weights"),
+        _stream(stream)))

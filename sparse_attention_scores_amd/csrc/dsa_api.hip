@@ -250,6 +250,22 @@ dsa_status dsa_cache_write(const dsa_shape* shape, const uint16_t* kv_a, const f
     return launched(dsa::launch_cache_write(shape_id(shape), a, (hipStream_t)stream));
 }
 
+dsa_status dsa_router_topk(const float* logits, const float* bias, int32_t T, int32_t n_experts, int32_t k,
+                           float routed_scale, int32_t* ids, float* weights, void* stream) {
+    if (!logits || !bias || !ids || !weights || !aligned16(logits) || (reinterpret_cast<uintptr_t>(bias) & 3u) ||
+        (reinterpret_cast<uintptr_t>(ids) & 3u) || (reinterpret_cast<uintptr_t>(weights) & 3u))
+        return DSA_ERR_INVALID_ARG;
+    if (T < 0 || n_experts <= 0 || k <= 0 || k > n_experts || !isfinite(routed_scale)) return DSA_ERR_INVALID_ARG;
+    if ((n_experts != 64 && n_experts != 128 && n_experts != 256 && n_experts != 512 && n_experts != 1024) ||
+        k > 32)
+        return DSA_ERR_UNSUPPORTED;
+    if (T == 0) return DSA_OK;
+    dsa_status st = check_device();
+    if (st) return st;
+    dsa::RouterArgs a{logits, bias, ids, weights, T, n_experts, k, routed_scale};
+    return launched(dsa::launch_router_topk(a, (hipStream_t)stream));
+}
+
 dsa_status dsa_sparse_mla_attn_f16(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv16,
                                    const int32_t* idx, const int32_t* count, int32_t L, int32_t N,
                                    float* out, float* lse, void* stream) {

@@ -160,4 +160,15 @@ struct CacheWriteArgs {
 };
 hipError_t launch_cache_write(int shape_id, const CacheWriteArgs& a, hipStream_t s);
 
+struct RouterArgs {
+    const float* logits;     // [T, E]
+    const float* bias;       // [E]
+    int32_t* ids;            // [T, k]
+    float* weights;          // [T, k]
+    int32_t T, E, k;
+    float scale;
+};
+// E in {64, 128, 256, 512, 1024}, 1 <= k <= min(32, E)
+hipError_t launch_router_topk(const RouterArgs& a, hipStream_t s);
+
 }  // namespace dsa

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert sorted(dsa.EXPORTED_SYMBOLS) == names
     raw = ctypes.CDLL(dsa._build.LIB)
     for n in names:
@@ -122,3 +122,18 @@ def test_cache_write_validation():
     assert cw(T=0) == OK                                        # nothing to do, nothing enqueued
     assert L.dsa_cache_write(None, fake(), fake(), f(0), fake(), 1, 1, fake(), None, None, None, None,
                              64, f(1e4), None) == INVALID
+
+
+def test_router_validation():
+    L = dsa.lib
+    f = ctypes.c_float
+    def rt(logits=None, bias=None, ids=None, w=None, T=4, E=256, k=8, scale=2.5):
+        return L.dsa_router_topk(logits or fake(), bias or fake(), T, E, k, f(scale), ids or fake(),
+                                 w or fake(), None)
+    assert rt(logits=fake(0x1004)) == INVALID          # logits not 16-byte aligned
+    assert rt(bias=fake(0x1002)) == INVALID
+    assert rt(T=-1) == INVALID and rt(k=0) == INVALID and rt(k=300) == INVALID
+    assert rt(scale=float("nan")) == INVALID
+    assert rt(E=96, k=8) == UNSUPPORTED and rt(E=256, k=33) == UNSUPPORTED
+    assert rt(T=0) == OK
+    assert L.dsa_router_topk(None, fake(), 1, 256, 8, f(2.5), fake(), fake(), None) == INVALID
