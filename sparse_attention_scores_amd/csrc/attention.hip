@@ -357,7 +357,12 @@ struct Attend {
             for (int ks = 0; ks < C::KSL; ++ks) qf[ks] = bf16x8_to_f16x8_rne(qf[ks]);
         }
         float mref = -INFINITY, lsum = 0.f;   // for head `head` (replicated over g)
-        const bool neg_scale = scale_log2 < 0.f;
+        // a negative scale is folded into the query (flip the sign of every
+        // 16-bit element): the scores then carry its sign and x = s * |scale|
+        if (scale_log2 < 0.f) {
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) qf[ks] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+        }
         const float cabs = fabsf(scale_log2);
 
         // Score reads: row 16mb + c16 (swizzle depends on c16 only), logical
@@ -409,7 +414,7 @@ struct Attend {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sv[4 * mb + i] = neg_scale ? -s[mb][i] : s[mb][i];
+                for (int i = 0; i < 4; ++i) sv[4 * mb + i] = s[mb][i];
             if (vmask != 0xFFFFFFFFu) {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
@@ -417,21 +422,30 @@ struct Attend {
                     for (int i = 0; i < 4; ++i)
                         if (!((vmask >> (16 * mb + 4 * g + i)) & 1u)) sv[4 * mb + i] = -INFINITY;
             }
+            // The exponentials go against the current reference while the
+            // tile maximum is formed alongside.  The lazy reference moves
+            // only when a score clears it by kLazy (always on the first tile
+            // with a usable key; the output is then still zero and needs no
+            // rescale), and only then are the exponentials redone, so the
+            // maximum stays off the critical path.  Arguments are <= kLazy;
+            // v_exp_f32 returns 0 for -inf.
+            float mbase = (mref == -INFINITY) ? 0.f : mref;
+            float p[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], cabs, -mbase));
             float mx = sv[0];
 #pragma unroll
             for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
             mx = max4_rows(mx) * cabs;
-            // lazy reference: move it only when a score clears it by kLazy;
-            // the first valid tile needs no rescale (the output is zero)
             const bool up = mx > mref + kLazy;
-            const float alpha = (up && mref != -INFINITY) ? __builtin_amdgcn_exp2f(mref - mx) : 1.f;
-            mref = up ? mx : mref;
-            const float mbase = (mref == -INFINITY) ? 0.f : mref;
-            float p[8], ps = 0.f;
-            // arguments are <= kLazy; v_exp_f32 returns 0 for -inf
+            float alpha = 1.f;
+            if (__ballot(up)) {   // wave-uniform and rare
+                alpha = (up && mref != -INFINITY) ? __builtin_amdgcn_exp2f(mref - mx) : 1.f;
+                mref = up ? mx : mref;
+                mbase = (mref == -INFINITY) ? 0.f : mref;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) { p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], cabs, -mbase)); ps += p[i]; }
-            lsum = lsum * alpha + ps;
+                for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], cabs, -mbase));
+            }
             u32x4 pb;
             pb[0] = pack_f16(p[0], p[1]);
             pb[1] = pack_f16(p[2], p[3]);
@@ -439,6 +453,10 @@ struct Attend {
             pb[3] = pack_f16(p[6], p[7]);
             sm.pfrag[it & 1][w][l] = pb;
             sm.alpha[it & 1][head] = alpha;   // the four lanes of a head store the same value
+            float ps = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ps += p[i];
+            lsum = lsum * alpha + ps;
         };
 
         Rows rows;
