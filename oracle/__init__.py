@@ -47,9 +47,11 @@ def _configure(lib):
     lib.oracle_cache_write.argtypes = [P, P, dbl, P, i64, i64, P, P, P, P, P, i32, i32, i32, i32, i32,
                                        i32, dbl]
     lib.oracle_router_topk.argtypes = [P, P, i64, i32, i32, dbl, dbl, P, P]
+    lib.oracle_value_up_proj.argtypes = [P, P, i64, i32, i32, i32, P]
+    lib.oracle_o_proj.argtypes = [P, P, i64, i32, i32, P, i64, P]
     for f in (lib.oracle_indexer_scores, lib.oracle_topk_select, lib.oracle_sparse_mla_attn,
               lib.oracle_prefill_chunk, lib.oracle_decode_step, lib.oracle_cache_write,
-              lib.oracle_router_topk):
+              lib.oracle_router_topk, lib.oracle_value_up_proj, lib.oracle_o_proj):
         f.restype = ctypes.c_int
     return lib
 
@@ -203,3 +205,24 @@ def router_topk(logits, bias, k: int, scale: float, min_sum: float = ROUTER_MIN_
     _check(_load().oracle_router_topk(_p(logits), _p(bias), T, E, k, float(scale), float(min_sum),
                                       _p(ids), _p(wts)), "router")
     return ids, wts
+
+
+def value_up_proj(o, wv) -> np.ndarray:
+    """out_v [T, H, Dv] bf16 bits from o [T, H, Dl] float32 and wv [H, Dv, Dl] bf16."""
+    o, wv = _c(o, np.float32), _c(wv, np.uint16)
+    T, H, Dl = o.shape
+    Dv = wv.shape[1]
+    out = np.empty((T, H, Dv), dtype=np.uint16)
+    _check(_load().oracle_value_up_proj(_p(o), _p(wv), T, H, Dl, Dv, _p(out)), "value up-projection")
+    return out
+
+
+def o_proj(x, wo, rows=None) -> np.ndarray:
+    """y [len(rows), Nout] float64 from x [T, Kin] bf16 and wo [Nout, Kin] bf16."""
+    x, wo = _c(x, np.uint16), _c(wo, np.uint16)
+    T, Kin = x.shape
+    Nout = wo.shape[0]
+    rows = _rows(rows, T)
+    y = np.empty((rows.size, Nout), dtype=np.float64)
+    _check(_load().oracle_o_proj(_p(x), _p(wo), T, Kin, Nout, _p(rows), rows.size, _p(y)), "o_proj")
+    return y

@@ -522,3 +522,60 @@ int oracle_router_topk(const float* logits, const float* bias, int64_t T, int32_
     free(key);
     return 0;
 }
+
+/* ==========================================================================
+ * Downstream projections ("GLM-5.2-Vision: llama.cpp vs vLLM" pipeline
+ * trace, section 6, build_attn: the attention output in the latent space is
+ * decompressed per head with wv_b, kqv = v_mla . kqv, then flattened over the
+ * heads and multiplied by the output projection wo; the config line gives
+ * v_head_dim 256 and hidden 6144).  Readings: weights are stored as
+ * [out, in] (bf16, in-dimension contiguous); the products take bf16
+ * operands, so the float32 attention output is rounded once to bf16 and the
+ * up-projected values are rounded once to bf16 before the output
+ * projection; sums are exact here (double).
+ * ======================================================================== */
+
+/* out_v[t, h, j] = bf16( sum_c bf16(o[t, h, c]) * wv[h, j, c] ),
+ *   o [T, H, Dl] float, wv [H, Dv, Dl] bf16, out_v [T, H, Dv] bf16. */
+int oracle_value_up_proj(const float* o, const uint16_t* wv, int64_t T, int32_t H, int32_t Dl,
+                         int32_t Dv, uint16_t* out_v) {
+    if (!o || !wv || !out_v || T < 0 || H <= 0 || Dl <= 0 || Dv <= 0) return -1;
+    double* x = (double*)malloc((size_t)Dl * sizeof(double));
+    if (!x) return -8;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < H; ++h) {
+            const float* orow = o + (t * H + h) * Dl;
+            for (int32_t c = 0; c < Dl; ++c) x[c] = bf16_to_double(double_to_bf16((double)orow[c]));
+            for (int32_t j = 0; j < Dv; ++j) {
+                const uint16_t* wrow = wv + ((int64_t)h * Dv + j) * Dl;
+                double acc = 0.0;
+                for (int32_t c = 0; c < Dl; ++c) acc += x[c] * bf16_to_double(wrow[c]);
+                out_v[(t * H + h) * Dv + j] = double_to_bf16(acc);
+            }
+        }
+    }
+    free(x);
+    return 0;
+}
+
+/* y[t, n] = sum_k x[t, k] * wo[n, k],  x [T, Kin] bf16, wo [Nout, Kin] bf16,
+ * y [T, Nout] double. */
+int oracle_o_proj(const uint16_t* x, const uint16_t* wo, int64_t T, int32_t Kin, int32_t Nout,
+                  const int64_t* rows, int64_t nrows, double* y) {
+    if (!x || !wo || !y || T < 0 || Kin <= 0 || Nout <= 0 || nrows < 0) return -1;
+    double* xr = (double*)malloc((size_t)Kin * sizeof(double));
+    if (!xr) return -8;
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t t = rows ? rows[r] : r;
+        if (t < 0 || t >= T) { free(xr); return -1; }
+        for (int32_t k = 0; k < Kin; ++k) xr[k] = bf16_to_double(x[t * Kin + k]);
+        for (int32_t n = 0; n < Nout; ++n) {
+            const uint16_t* wrow = wo + (int64_t)n * Kin;
+            double acc = 0.0;
+            for (int32_t k = 0; k < Kin; ++k) acc += xr[k] * bf16_to_double(wrow[k]);
+            y[r * Nout + n] = acc;
+        }
+    }
+    free(xr);
+    return 0;
+}

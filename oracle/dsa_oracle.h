@@ -105,6 +105,18 @@ int oracle_cache_write(const uint16_t* kv_a, const float* norm_w, double eps,
 int oracle_router_topk(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
                        double scale, double min_sum, int32_t* ids, double* weights);
 
+/* Value up-projection per head (pipeline trace section 6, kqv = v_mla . kqv):
+ *   out_v[t, h, j] = bf16( sum_c bf16(o[t, h, c]) * wv[h, j, c] )
+ *   o [T, H, Dl] float; wv [H, Dv, Dl] bf16; out_v [T, H, Dv] bf16. */
+int oracle_value_up_proj(const float* o, const uint16_t* wv, int64_t T, int32_t H, int32_t Dl,
+                         int32_t Dv, uint16_t* out_v);
+
+/* Output projection for selected rows (rows == NULL: rows 0..nrows-1):
+ *   y[r, n] = sum_k x[rows[r], k] * wo[n, k];  x [T, Kin], wo [Nout, Kin] bf16;
+ *   y [nrows, Nout] double. */
+int oracle_o_proj(const uint16_t* x, const uint16_t* wo, int64_t T, int32_t Kin, int32_t Nout,
+                  const int64_t* rows, int64_t nrows, double* y);
+
 #ifdef __cplusplus
 }
 #endif

@@ -632,4 +632,64 @@ def pin_router_sigmoid_symmetry():
         assert abs(wts[0, 0] - pp) < 2.0 ** -24 * 2 and abs(wts[0, 1] - (1 - pp)) < 2.0 ** -24 * 2
 
 
+# --------------------------------------------------------------------------
+# downstream projections (pipeline trace section 6, build_attn)
+# --------------------------------------------------------------------------
+def pin_up_proj_identity_and_single_rounding():
+    """An identity up-projection returns the attention output rounded once to
+    bf16; a row of two ones adds the two bf16-rounded inputs and rounds the
+    sum once (1 + 2^-8 + 2^-10 rounds to 1 + 2^-7; plus 2^-8 the sum is a
+    bf16 midpoint that goes to the even 1 + 2^-6, where the unrounded sum
+    would give 1 + 2^-7)."""
+    T, H, Dl, Dv = 3, 2, 64, 32
+    rng = np.random.default_rng(7)
+    o = rng.standard_normal((T, H, Dl)).astype(np.float32)
+    wv = np.zeros((H, Dv, Dl), np.uint16)
+    for h in range(H):
+        for j in range(Dv):
+            wv[h, j, j] = 0x3F80
+    out = oracle.value_up_proj(o, wv)
+    assert np.array_equal(out, W.to_bf16_bits(o[..., :Dv]))
+    o2 = np.zeros((1, 1, Dl), np.float32)
+    o2[0, 0, 0] = 1 + 2.0 ** -8 + 2.0 ** -10
+    o2[0, 0, 1] = 2.0 ** -8
+    w2 = np.zeros((1, 1, Dl), np.uint16)
+    w2[0, 0, 0] = w2[0, 0, 1] = 0x3F80
+    got = float(W.bf16_bits_to_f32(oracle.value_up_proj(o2, w2))[0, 0, 0])
+    assert got == 1 + 2.0 ** -6, got
+
+
+def pin_projections_match_numpy():
+    """Both projections on random bf16 data equal numpy's float64 matmul of
+    the decoded operands (the up-projection within its final rounding)."""
+    rng = np.random.default_rng(8)
+    T, H, Dl, Dv, hid = 5, 3, 64, 32, 48
+    o = rng.standard_normal((T, H, Dl)).astype(np.float32)
+    wv = W.to_bf16_bits(rng.standard_normal((H, Dv, Dl)).astype(np.float32))
+    out = oracle.value_up_proj(o, wv)
+    ob = _f(W.to_bf16_bits(o))
+    ref = np.einsum("thc,hjc->thj", ob, _f(wv))
+    got = _f(out)
+    assert np.all(np.abs(got - ref) <= _half_ulp_bf16(ref) * 1.0000001 + 1e-30)
+    x = W.to_bf16_bits(rng.standard_normal((T, H * Dv)).astype(np.float32))
+    wo = W.to_bf16_bits(rng.standard_normal((hid, H * Dv)).astype(np.float32))
+    y = oracle.o_proj(x, wo)
+    ref = _f(x) @ _f(wo).T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+    rows = np.array([4, 0, 2])
+    assert np.array_equal(oracle.o_proj(x, wo, rows), y[rows])
+
+
+def pin_o_proj_one_hot_rows():
+    """Output row n of a one-hot weight picks input column n's value."""
+    rng = np.random.default_rng(9)
+    T, K, N = 4, 64, 16
+    x = W.to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    wo = np.zeros((N, K), np.uint16)
+    cols = rng.choice(K, size=N, replace=False)
+    wo[np.arange(N), cols] = 0x3F80
+    y = oracle.o_proj(x, wo)
+    assert np.array_equal(y, _f(x)[:, cols])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -72,6 +72,14 @@ MUTATIONS = [
     ("router sigmoid sign", "p[e] = (float)(1.0 / (1.0 + exp(-(double)lg[e])));",
      "p[e] = (float)(1.0 / (1.0 + exp((double)lg[e])));"),
     ("router bias ignored", "key[e].s = p[e] + bias[e];", "key[e].s = p[e];"),
+    ("up-projection weight read transposed", "const uint16_t* wrow = wv + ((int64_t)h * Dv + j) * Dl;\n                double acc = 0.0;\n                for (int32_t c = 0; c < Dl; ++c) acc += x[c] * bf16_to_double(wrow[c]);",
+     "const uint16_t* wrow = wv + (int64_t)h * Dv * Dl;\n                double acc = 0.0;\n                for (int32_t c = 0; c < Dl; ++c) acc += x[c] * bf16_to_double(wrow[((int64_t)c * Dv + j) % ((int64_t)Dv * Dl)]);"),
+    ("up-projection head ignored", "const uint16_t* wrow = wv + ((int64_t)h * Dv + j) * Dl;",
+     "const uint16_t* wrow = wv + ((int64_t)j) * Dl;"),
+    ("attention output not rounded to bf16", "x[c] = bf16_to_double(double_to_bf16((double)orow[c]));",
+     "x[c] = (double)orow[c];"),
+    ("o_proj weight read transposed", "const uint16_t* wrow = wo + (int64_t)n * Kin;\n            double acc = 0.0;\n            for (int32_t k = 0; k < Kin; ++k) acc += xr[k] * bf16_to_double(wrow[k]);",
+     "double acc = 0.0;\n            for (int32_t k = 0; k < Kin; ++k) acc += xr[k] * bf16_to_double(wo[((int64_t)k * Nout + n) % ((int64_t)Nout * Kin)]);"),
     ("positions taken as 1-based rows", "uint16_t* dst = kv_cache + pos[t] * Dqk;",
      "uint16_t* dst = kv_cache + (pos[t] > 0 ? pos[t] - 1 : 0) * Dqk;"),
 ]

@@ -33,6 +33,7 @@ __all__ = [
     "Shape", "TINY", "GLM", "Prefill", "Decode", "PREFILL", "DECODE",
     "to_bf16_bits", "bf16_bits_to_f32", "make_prefill", "make_decode",
     "CacheWrite", "CACHE_WRITE", "make_cache_write", "Router", "ROUTER", "make_router",
+    "Proj", "PROJ", "make_proj",
 ]
 
 
@@ -267,3 +268,38 @@ def make_router(cfg: Router) -> Dict[str, np.ndarray]:
         logits = (rng.standard_normal(size=(cfg.T, cfg.E)) * 2.0).astype(np.float32)
         bias = (rng.standard_normal(size=cfg.E) * 0.1).astype(np.float32)
     return {"logits": np.ascontiguousarray(logits), "bias": np.ascontiguousarray(bias)}
+
+
+@dataclasses.dataclass(frozen=True)
+class Proj:
+    """Downstream projections of T tokens: the attention output o [T, H, Dl]
+    (float32) goes through the per-head value up-projection wv [H, Dv, Dl]
+    and the output projection wo [hidden, H*Dv] (GLM: 64 heads, Dl 512,
+    v_head_dim 256, hidden 6144 from the pipeline trace's config line)."""
+    name: str
+    T: int
+    seed: int
+    H: int = 64
+    Dl: int = 512
+    Dv: int = 256
+    hidden: int = 6144
+
+
+PROJ: Dict[str, Proj] = {
+    "glm_16k_chunk": Proj("glm_16k_chunk", 4096, 51),
+    "glm_decode_8": Proj("glm_decode_8", 8, 52),
+    "glm_small": Proj("glm_small", 37, 53),
+}
+
+
+def make_proj(cfg: Proj) -> Dict[str, np.ndarray]:
+    """o ~ N(0,1)*0.02 in float32; wv ~ N(0,1)/sqrt(Dl) and wo ~ N(0,1)/sqrt(H*Dv)
+    rounded to bf16; x (an output-projection input of its own) ~ N(0,1)*0.1
+    rounded to bf16.  Drawn in the order o, wv, wo, x."""
+    rng = np.random.default_rng(cfg.seed)
+    nrm = lambda *shp: rng.standard_normal(size=shp, dtype=np.float32)
+    o = nrm(cfg.T, cfg.H, cfg.Dl) * np.float32(0.02)
+    wv = to_bf16_bits(nrm(cfg.H, cfg.Dv, cfg.Dl) * np.float32(1.0 / np.sqrt(cfg.Dl)))
+    wo = to_bf16_bits(nrm(cfg.hidden, cfg.H * cfg.Dv) * np.float32(1.0 / np.sqrt(cfg.H * cfg.Dv)))
+    x = to_bf16_bits(nrm(cfg.T, cfg.H * cfg.Dv) * np.float32(0.1))
+    return {"o": np.ascontiguousarray(o), "wv": wv, "wo": wo, "x": x}
