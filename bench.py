@@ -364,6 +364,29 @@ def main() -> int:
         stages["router"] = {"kernel": "router_topk_kernel<4>", "us": t_rt * 1e6,
                             "gbps": rt_bytes / t_rt / 1e9, "frac": rt_bytes / t_rt / 1e9 / PEAK_HBM_GBPS,
                             "workload": "%d tokens x %d experts, top %d, scale %.1f" % (rc.T, rc.E, rc.k, rc.scale)}
+        log("projection stages")
+        pc = W.PROJ["glm_16k_chunk"]
+        pd = W.make_proj(pc)
+        p_o, p_wv, p_wo, p_x = (to(pd[k]) for k in ("o", "wv", "wo", "x"))
+        p_out = torch.empty((pc.T, pc.H, pc.Dv), dtype=torch.int16, device="cuda")
+        p_y = torch.empty((pc.T, pc.hidden), dtype=torch.float32, device="cuda")
+        f_up = lambda: dsa.dsa_value_up_proj(sh, p_o, p_wv, pc.T, pc.Dv, p_out)
+        f_op = lambda: dsa.dsa_o_proj(p_x, p_wo, pc.T, pc.H * pc.Dv, pc.hidden, p_y)
+        f_up()
+        f_op()
+        torch.cuda.synchronize()
+        t_up = timed_events(f_up, max(n, 10), torch)
+        t_op = timed_events(f_op, max(n, 10), torch)
+        up_bytes = 4 * pc.T * pc.H * pc.Dl + 2 * pc.H * pc.Dv * pc.Dl + 2 * pc.T * pc.H * pc.Dv
+        op_flop = 2.0 * pc.T * pc.H * pc.Dv * pc.hidden
+        stages["value_up_proj"] = {"kernel": "gemm_nt_kernel<true,false,256>", "us": t_up * 1e6,
+                                   "gbps": up_bytes / t_up / 1e9, "frac": up_bytes / t_up / 1e9 / PEAK_HBM_GBPS,
+                                   "tflops": 2.0 * pc.T * pc.H * pc.Dl * pc.Dv / t_up / 1e12,
+                                   "workload": "%d tokens x %d heads: [%d] fp32 -> [%d] bf16 per head" % (pc.T, pc.H, pc.Dl, pc.Dv)}
+        stages["o_proj"] = {"kernel": "gemm_nt_kernel<false,true,192>", "us": t_op * 1e6,
+                            "tflops": op_flop / t_op / 1e12, "frac": op_flop / t_op / 1e12 / PEAK_MFMA_TFLOPS,
+                            "workload": "[%d x %d] bf16 x [%d x %d]^T bf16 -> fp32" % (pc.T, pc.H * pc.Dv, pc.hidden, pc.H * pc.Dv)}
+        del p_o, p_wv, p_wo, p_x, p_out, p_y
         result["stages"] = stages
         dom = max(("indexer", t_idx), ("topk", t_topk), ("attention", t_attn), key=lambda x: x[1])[0]
         if dom == "topk":

@@ -221,6 +221,31 @@ dsa_status dsa_cache_write(const dsa_shape* shape, const uint16_t* kv_a, const f
 dsa_status dsa_router_topk(const float* logits, const float* bias, int32_t T, int32_t n_experts, int32_t k,
                            float routed_scale, int32_t* ids, float* weights, void* stream);
 
+/* Value up-projection per head ("GLM-5.2-Vision: llama.cpp vs vLLM
+ * line-by-line pipeline trace", section 6, build_attn: the latent-space
+ * attention output is decompressed per head with wv_b, kqv = v_mla . kqv;
+ * the config line gives v_head_dim 256):
+ *   out_v[t, h, j] = bf16( sum_c bf16(o[t, h, c]) * wv[h, j, c] )
+ * o [dev] [T, H, Dl] fp32 (the attention output); wv [dev] [H, d_v, Dl]
+ * bf16 (stored [out, in]); out_v [dev] [T, H, d_v] bf16.  The products take
+ * bf16 operands (o is rounded to nearest-even once) and accumulate in fp32;
+ * the result is rounded once to bf16.  Requires T >= 0 (0: nothing is
+ * enqueued); d_v must be 256 and Dl a multiple of 64 (DSA_ERR_UNSUPPORTED
+ * otherwise); all pointers 16-byte aligned. */
+dsa_status dsa_value_up_proj(const dsa_shape* shape, const float* o, const uint16_t* wv, int32_t T, int32_t d_v,
+                             uint16_t* out_v, void* stream);
+
+/* Output projection (pipeline trace section 6: the up-projected heads,
+ * flattened, times wo; config line: hidden 6144):
+ *   y[t, n] = sum_k x[t, k] * wo[n, k]
+ * x [dev] [T, k_in] bf16 (e.g. out_v viewed as [T, H * d_v]); wo [dev]
+ * [n_out, k_in] bf16 (stored [out, in]); y [dev] [T, n_out] fp32.  bf16
+ * operands, fp32 accumulation.  Requires T >= 0 (0: nothing is enqueued);
+ * k_in a multiple of 64 and n_out a multiple of 192 (DSA_ERR_UNSUPPORTED
+ * otherwise); all pointers 16-byte aligned. */
+dsa_status dsa_o_proj(const uint16_t* x, const uint16_t* wo, int32_t T, int32_t k_in, int32_t n_out, float* y,
+                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,7 @@ __all__ = [
     "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn", "dsa_latent_to_f16",
     "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
     "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write", "dsa_router_topk",
-    "dsa_status_string",
+    "dsa_value_up_proj", "dsa_o_proj", "dsa_status_string",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -29,6 +29,7 @@ EXPORTED_SYMBOLS = (
     "dsa_status_string", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn",
     "dsa_latent_to_f16", "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
     "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write", "dsa_router_topk",
+    "dsa_value_up_proj", "dsa_o_proj",
 )
 
 
@@ -80,6 +81,8 @@ def _load() -> ctypes.CDLL:
         "dsa_cache_write": (ctypes.c_int, [SP, P, P, ctypes.c_float, P, i32, i32, P, P, P, P, P, i32,
                                            ctypes.c_float, P]),
         "dsa_router_topk": (ctypes.c_int, [P, P, i32, i32, i32, ctypes.c_float, P, P, P]),
+        "dsa_value_up_proj": (ctypes.c_int, [SP, P, P, i32, i32, P, P]),
+        "dsa_o_proj": (ctypes.c_int, [P, P, i32, i32, i32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -215,3 +218,15 @@ def dsa_router_topk(logits, bias, T: int, n_experts: int, k: int, routed_scale: 
         _ptr(logits, torch.float32, "logits"), _ptr(bias, torch.float32, "bias"), T, n_experts, k,
         float(routed_scale), _ptr(ids, torch.int32, "ids"), _ptr(weights, torch.float32, "weights"),
         _stream(stream)))
+
+
+def dsa_value_up_proj(shape, o, wv, T: int, d_v: int, out_v, stream=None) -> None:
+    sh = Shape.of(shape)
+    _check("dsa_value_up_proj", lib.dsa_value_up_proj(
+        ctypes.byref(sh), _ptr(o, torch.float32, "o"), _bits(wv, "wv"), T, d_v, _bits(out_v, "out_v"),
+        _stream(stream)))
+
+
+def dsa_o_proj(x, wo, T: int, k_in: int, n_out: int, y, stream=None) -> None:
+    _check("dsa_o_proj", lib.dsa_o_proj(_bits(x, "x"), _bits(wo, "wo"), T, k_in, n_out,
+                                        _ptr(y, torch.float32, "y"), _stream(stream)))

@@ -266,6 +266,32 @@ dsa_status dsa_router_topk(const float* logits, const float* bias, int32_t T, in
     return launched(dsa::launch_router_topk(a, (hipStream_t)stream));
 }
 
+dsa_status dsa_value_up_proj(const dsa_shape* shape, const float* o, const uint16_t* wv, int32_t T, int32_t d_v,
+                             uint16_t* out_v, void* stream) {
+    dsa_status st = check_shape(shape);
+    if (st) return st;
+    if (!o || !wv || !out_v || !aligned16(o) || !aligned16(wv) || !aligned16(out_v) || T < 0 || d_v <= 0)
+        return DSA_ERR_INVALID_ARG;
+    if (d_v != 256 || shape->d_latent % 64 != 0) return DSA_ERR_UNSUPPORTED;
+    if (T == 0) return DSA_OK;
+    if ((st = check_device())) return st;
+    const int64_t H = shape->n_heads, Dl = shape->d_latent;
+    dsa::GemmArgs g{o, H * Dl, Dl, wv, Dl, (int64_t)d_v * Dl, out_v, H * d_v, d_v, T, d_v, (int32_t)Dl};
+    return launched(dsa::launch_value_up_proj(g, (int)H, (hipStream_t)stream));
+}
+
+dsa_status dsa_o_proj(const uint16_t* x, const uint16_t* wo, int32_t T, int32_t k_in, int32_t n_out, float* y,
+                      void* stream) {
+    if (!x || !wo || !y || !aligned16(x) || !aligned16(wo) || !aligned16(y) || T < 0 || k_in <= 0 || n_out <= 0)
+        return DSA_ERR_INVALID_ARG;
+    if (k_in % 64 != 0 || n_out % 192 != 0) return DSA_ERR_UNSUPPORTED;
+    if (T == 0) return DSA_OK;
+    dsa_status st = check_device();
+    if (st) return st;
+    dsa::GemmArgs g{x, k_in, 0, wo, k_in, 0, y, n_out, 0, T, n_out, k_in};
+    return launched(dsa::launch_o_proj(g, (hipStream_t)stream));
+}
+
 dsa_status dsa_sparse_mla_attn_f16(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv16,
                                    const int32_t* idx, const int32_t* count, int32_t L, int32_t N,
                                    float* out, float* lse, void* stream) {

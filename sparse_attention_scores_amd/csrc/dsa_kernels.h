@@ -171,4 +171,18 @@ struct RouterArgs {
 // E in {64, 128, 256, 512, 1024}, 1 <= k <= min(32, E)
 hipError_t launch_router_topk(const RouterArgs& a, hipStream_t s);
 
+struct GemmArgs {            // C[m, n] = sum_k A[m, k] B[n, k], per batch z
+    const void* A;           // element (z, m, k) at z*a_batch + m*lda + k (float32 or bf16)
+    int64_t lda, a_batch;
+    const uint16_t* B;       // bf16, element (z, n, k) at z*b_batch + n*ldb + k
+    int64_t ldb, b_batch;
+    void* C;                 // element (z, m, n) at z*c_batch + m*ldc + n (bf16 or float32)
+    int64_t ldc, c_batch;
+    int32_t M, N, K;
+};
+// value up-projection: A float32, C bf16, N == 256, K % 64 == 0
+hipError_t launch_value_up_proj(const GemmArgs& g, int batch, hipStream_t s);
+// output projection: A bf16, C float32, N % 192 == 0, K % 64 == 0
+hipError_t launch_o_proj(const GemmArgs& g, hipStream_t s);
+
 }  // namespace dsa

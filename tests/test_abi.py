@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     assert sorted(dsa.EXPORTED_SYMBOLS) == names
     raw = ctypes.CDLL(dsa._build.LIB)
     for n in names:
@@ -137,3 +137,15 @@ def test_router_validation():
     assert rt(E=96, k=8) == UNSUPPORTED and rt(E=256, k=33) == UNSUPPORTED
     assert rt(T=0) == OK
     assert L.dsa_router_topk(None, fake(), 1, 256, 8, f(2.5), fake(), fake(), None) == INVALID
+
+
+def test_projection_validation():
+    L, sh = dsa.lib, ctypes.byref(dsa.GLM)
+    assert L.dsa_value_up_proj(sh, fake(0x1004), fake(), 4, 256, fake(), None) == INVALID
+    assert L.dsa_value_up_proj(sh, fake(), fake(), -1, 256, fake(), None) == INVALID
+    assert L.dsa_value_up_proj(sh, fake(), fake(), 4, 128, fake(), None) == UNSUPPORTED
+    assert L.dsa_value_up_proj(sh, fake(), fake(), 0, 256, fake(), None) == OK
+    assert L.dsa_o_proj(fake(), fake(), 4, 16384, 6144, None, None) == INVALID
+    assert L.dsa_o_proj(fake(), fake(), 4, 100, 6144, fake(), None) == UNSUPPORTED
+    assert L.dsa_o_proj(fake(), fake(), 4, 16384, 6000, fake(), None) == UNSUPPORTED
+    assert L.dsa_o_proj(fake(), fake(), 0, 16384, 6144, fake(), None) == OK
