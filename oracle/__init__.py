@@ -49,9 +49,13 @@ def _configure(lib):
     lib.oracle_router_topk.argtypes = [P, P, i64, i32, i32, dbl, dbl, P, P]
     lib.oracle_value_up_proj.argtypes = [P, P, i64, i32, i32, i32, P]
     lib.oracle_o_proj.argtypes = [P, P, i64, i32, i32, P, i64, P]
+    lib.oracle_selection_mask.argtypes = [P, P, i64, i32, i64, i64, i64, P]
+    lib.oracle_dense_masked_attn.argtypes = [P, P, P, P, i64, i64, i32, i32, i32, i32, i32, i32, i64,
+                                             dbl, P, i64, P, i32]
     for f in (lib.oracle_indexer_scores, lib.oracle_topk_select, lib.oracle_sparse_mla_attn,
               lib.oracle_prefill_chunk, lib.oracle_decode_step, lib.oracle_cache_write,
-              lib.oracle_router_topk, lib.oracle_value_up_proj, lib.oracle_o_proj):
+              lib.oracle_router_topk, lib.oracle_value_up_proj, lib.oracle_o_proj,
+              lib.oracle_selection_mask, lib.oracle_dense_masked_attn):
         f.restype = ctypes.c_int
     return lib
 
@@ -226,3 +230,34 @@ def o_proj(x, wo, rows=None) -> np.ndarray:
     y = np.empty((rows.size, Nout), dtype=np.float64)
     _check(_load().oracle_o_proj(_p(x), _p(wo), T, Kin, Nout, _p(rows), rows.size, _p(y)), "o_proj")
     return y
+
+
+def mask_words(N: int) -> int:
+    """Words per mask row: the keys rounded up to a whole 64-key tile."""
+    return 2 * ((N + 63) // 64)
+
+
+def selection_mask(idx, count, N: int, q_start: int, W: Optional[int] = None) -> np.ndarray:
+    """Boolean selection mask [L, W] uint32: bit j % 32 of word j // 32 is set
+    iff key j is selected, in [0, N) and causal for the query."""
+    idx, count = _c(idx, np.int32), _c(count, np.int32)
+    L, top_k = idx.shape
+    W = mask_words(N) if W is None else W
+    mask = np.empty((L, W), dtype=np.uint32)
+    _check(_load().oracle_selection_mask(_p(idx), _p(count), L, top_k, N, q_start, W, _p(mask)), "mask")
+    return mask
+
+
+def dense_masked_attn(q, kvb, kv, mask, d_nope: int, d_rope: int, d_v: int, rope_col: int,
+                      scale: float, rows=None, nthreads: Optional[int] = None) -> np.ndarray:
+    """Non-absorbed attention under a boolean mask: out [rows, H, d_v] float64."""
+    q, kvb, kv, mask = _c(q, np.uint16), _c(kvb, np.uint16), _c(kv, np.uint16), _c(mask, np.uint32)
+    L, H, Dq = q.shape
+    N, Dc = kv.shape
+    assert Dq == d_nope + d_rope and kvb.shape == (N, H, d_nope + d_v) and mask.shape[0] == L
+    rows = _rows(rows, L)
+    out = np.empty((rows.size, H, d_v), dtype=np.float64)
+    _check(_load().oracle_dense_masked_attn(_p(q), _p(kvb), _p(kv), _p(mask), L, N, H, d_nope, d_rope, d_v,
+                                            Dc, rope_col, mask.shape[1], scale, _p(rows), rows.size, _p(out),
+                                            nthreads or default_threads()), "dense attention")
+    return out

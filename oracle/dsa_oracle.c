@@ -579,3 +579,93 @@ int oracle_o_proj(const uint16_t* x, const uint16_t* wo, int64_t T, int32_t Kin,
     free(xr);
     return 0;
 }
+
+/* ==========================================================================
+ * Dense masked attention in the non-absorbed form (exo PR #2539, Prefill
+ * section, dense attention in one product: below 8192 keys of context each
+ * head's 192 no-rope and 64 rope dimensions are scored in one 256-wide
+ * product under a boolean mask).  The head widths come from the config line
+ * of the pipeline trace (qk_nope 192, qk_rope 64, v_head_dim 256); section 4
+ * of the trace splits the kv_b output per head into the no-rope key and the
+ * value, and the rope key is the one shared k_pe of the cache row.
+ * Readings: the boolean mask is the query's DSA selection (for a query with
+ * no more causal keys than top_k that is every earlier key), restricted to
+ * causal keys j <= p; the scale is the one the absorbed form uses.
+ * ======================================================================== */
+
+/* mask[i, w] bit b set iff key 32 w + b is among idx[i, :count[i]], lies in
+ * [0, N) and is causal for the query at position q_start + i.
+ * mask [L, W] uint32 with W >= ceil(N / 32); bits at or past N stay 0. */
+int oracle_selection_mask(const int32_t* idx, const int32_t* count, int64_t L, int32_t top_k,
+                          int64_t N, int64_t q_start, int64_t W, uint32_t* mask) {
+    if (!idx || !count || !mask || L < 0 || top_k <= 0 || N <= 0 || W * 32 < N) return -1;
+    for (int64_t i = 0; i < L; ++i) {
+        uint32_t* row = mask + i * W;
+        for (int64_t w = 0; w < W; ++w) row[w] = 0u;
+        const int64_t p = q_start + i;
+        int32_t c = count[i];
+        if (c < 0) c = 0;
+        if (c > top_k) c = top_k;
+        for (int32_t t = 0; t < c; ++t) {
+            const int64_t j = idx[i * top_k + t];
+            if (j >= 0 && j < N && j <= p) row[j / 32] |= 1u << (j % 32);
+        }
+    }
+    return 0;
+}
+
+typedef struct {
+    const uint16_t *q, *kvb, *kv; const uint32_t* mask;
+    int64_t N, W; int32_t H, Dn, Dr, Dv, Dc, rope_col; double scale;
+    const int64_t* rows; double* out;
+} dense_ctx;
+
+/* One query, every head: s_j = scale * (q_nope . k_nope_j + q_pe . k_pe_j)
+ * over the keys the mask holds, softmax, out = sum_j p_j v_j. */
+static void dense_task(void* c, int64_t r, void* scratch) {
+    dense_ctx* x = (dense_ctx*)c;
+    const int64_t i = x->rows[r];
+    double* s = (double*)scratch;                                /* [N] */
+    const uint32_t* mrow = x->mask + i * x->W;
+    const int32_t Dq = x->Dn + x->Dr, Dkv = x->Dn + x->Dv;
+    for (int32_t h = 0; h < x->H; ++h) {
+        const uint16_t* qh = x->q + (i * x->H + h) * Dq;
+        double* oh = x->out + (r * x->H + h) * x->Dv;
+        for (int32_t e = 0; e < x->Dv; ++e) oh[e] = 0.0;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < x->N; ++j) {
+            if (!((mrow[j / 32] >> (j % 32)) & 1u)) { s[j] = -INFINITY; continue; }
+            const uint16_t* kn = x->kvb + (j * x->H + h) * Dkv;        /* no-rope key of head h */
+            const uint16_t* kp = x->kv + j * x->Dc + x->rope_col;      /* shared rope key */
+            double dot = 0.0;
+            for (int32_t d = 0; d < x->Dn; ++d) dot += bf16_to_double(qh[d]) * bf16_to_double(kn[d]);
+            for (int32_t d = 0; d < x->Dr; ++d) dot += bf16_to_double(qh[x->Dn + d]) * bf16_to_double(kp[d]);
+            s[j] = x->scale * dot;
+            if (s[j] > m) m = s[j];
+        }
+        if (m == -INFINITY) continue;                              /* no key: zeros */
+        double Z = 0.0;
+        for (int64_t j = 0; j < x->N; ++j)
+            if (s[j] != -INFINITY) Z += exp(s[j] - m);
+        for (int64_t j = 0; j < x->N; ++j) {
+            if (s[j] == -INFINITY) continue;
+            const double pj = exp(s[j] - m) / Z;
+            const uint16_t* v = x->kvb + (j * x->H + h) * Dkv + x->Dn;  /* value of head h */
+            for (int32_t e = 0; e < x->Dv; ++e) oh[e] += pj * bf16_to_double(v[e]);
+        }
+    }
+}
+
+int oracle_dense_masked_attn(const uint16_t* q, const uint16_t* kvb, const uint16_t* kv,
+                             const uint32_t* mask, int64_t L, int64_t N, int32_t H, int32_t Dn,
+                             int32_t Dr, int32_t Dv, int32_t Dc, int32_t rope_col, int64_t W,
+                             double scale, const int64_t* rows, int64_t nrows, double* out,
+                             int32_t nthreads) {
+    if (!q || !kvb || !kv || !mask || !rows || !out) return -1;
+    if (L <= 0 || N <= 0 || H <= 0 || Dn < 0 || Dr < 0 || Dv <= 0 || rope_col < 0 ||
+        rope_col + Dr > Dc || W * 32 < N || nrows < 0)
+        return -1;
+    if (!rows_ok(rows, nrows, L)) return -1;
+    dense_ctx x = {q, kvb, kv, mask, N, W, H, Dn, Dr, Dv, Dc, rope_col, scale, rows, out};
+    return parallel_rows(dense_task, &x, nrows, nthreads, (size_t)N * sizeof(double));
+}

@@ -117,6 +117,22 @@ int oracle_value_up_proj(const float* o, const uint16_t* wv, int64_t T, int32_t 
 int oracle_o_proj(const uint16_t* x, const uint16_t* wo, int64_t T, int32_t Kin, int32_t Nout,
                   const int64_t* rows, int64_t nrows, double* y);
 
+/* Dense masked attention, non-absorbed form (exo PR #2539, Prefill section:
+ * one 256-wide product per head under a boolean mask).
+ * oracle_selection_mask: mask [L, W] uint32, bit j%32 of word j/32 set iff
+ *   key j is in idx[i, :count[i]], 0 <= j < N and j <= q_start + i.
+ * oracle_dense_masked_attn: q [L, H, Dn+Dr] bf16 (no-rope | rope);
+ *   kvb [N, H, Dn+Dv] bf16 (no-rope key | value per head); kv [N, Dc] bf16
+ *   whose columns rope_col .. rope_col+Dr-1 hold the shared rope key;
+ *   out [nrows, H, Dv] double; a query with no masked-in key gets zeros. */
+int oracle_selection_mask(const int32_t* idx, const int32_t* count, int64_t L, int32_t top_k,
+                          int64_t N, int64_t q_start, int64_t W, uint32_t* mask);
+int oracle_dense_masked_attn(const uint16_t* q, const uint16_t* kvb, const uint16_t* kv,
+                             const uint32_t* mask, int64_t L, int64_t N, int32_t H, int32_t Dn,
+                             int32_t Dr, int32_t Dv, int32_t Dc, int32_t rope_col, int64_t W,
+                             double scale, const int64_t* rows, int64_t nrows, double* out,
+                             int32_t nthreads);
+
 #ifdef __cplusplus
 }
 #endif

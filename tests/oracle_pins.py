@@ -692,4 +692,99 @@ def pin_o_proj_one_hot_rows():
     assert np.array_equal(y, _f(x)[:, cols])
 
 
+# --------------------------------------------------------------------------
+# dense masked attention, non-absorbed form
+# --------------------------------------------------------------------------
+def _dense_absorbed_pair(rng, L, N, H, Dl, Dn, Dr, Dv, q_start, top_k, scale):
+    """Both forms of one attention on integer-valued data: latent rows, rope
+    keys, projection weights and queries are small integers, so every bf16
+    input of both forms (the up-projected keys and values, the absorbed
+    query) is exact and the forms must agree to double rounding."""
+    lat = rng.integers(-2, 3, size=(N, Dl))
+    rope = rng.integers(-2, 3, size=(N, Dr))
+    wkb = rng.integers(-1, 2, size=(H, Dn, Dl))
+    wvb = rng.integers(-1, 2, size=(H, Dv, Dl))
+    qn = rng.integers(-1, 2, size=(L, H, Dn))
+    qp = rng.integers(-1, 2, size=(L, H, Dr))
+    kn = np.einsum("hdc,jc->jhd", wkb, lat)
+    v = np.einsum("hec,jc->jhe", wvb, lat)
+    qabs = np.einsum("ihd,hdc->ihc", qn, wkb)
+    assert max(np.abs(kn).max(), np.abs(v).max(), np.abs(qabs).max()) <= 256   # exact in bf16
+    kv = _bf(np.concatenate([lat, rope], axis=1))
+    q_abs = _bf(np.concatenate([qabs, qp], axis=2))
+    q_dense = _bf(np.concatenate([qn, qp], axis=2))
+    kvb = _bf(np.concatenate([kn, v], axis=2))
+    S = rng.standard_normal((L, N)).astype(np.float32)
+    pos = q_start + np.arange(L)
+    S[np.arange(N)[None, :] > pos[:, None]] = -np.inf
+    idx, cnt = oracle.topk_select(S, pos, top_k)
+    sparse = oracle.sparse_mla_attn(q_abs, kv, idx, cnt, Dl, scale)
+    expected = np.einsum("ihc,hec->ihe", sparse, wvb.astype(np.float64))
+    mask = oracle.selection_mask(idx, cnt, N, q_start)
+    dense = oracle.dense_masked_attn(q_dense, kvb, kv, mask, Dn, Dr, Dv, Dl, scale)
+    return dense, expected, dict(q=q_dense, kvb=kvb, kv=kv, mask=mask, idx=idx, cnt=cnt)
+
+
+def pin_dense_equals_absorbed_then_up_projected():
+    """With the no-rope keys and the values up-projected from the latent
+    rows (k = Wkb c, v = Wvb c) and the absorbed query Wkb^T q_nope, the
+    dense masked form equals the absorbed sparse attention (itself pinned)
+    followed by the value up-projection, in exact arithmetic.  Positions
+    span both regimes: fewer causal keys than top_k (every earlier key) and
+    a real top-k selection."""
+    rng = np.random.default_rng(21)
+    dense, expected, _ = _dense_absorbed_pair(rng, L=24, N=30, H=3, Dl=64, Dn=48, Dr=16, Dv=40,
+                                              q_start=4, top_k=16, scale=1 / 8)
+    assert np.abs(expected).max() > 1
+    assert np.allclose(dense, expected, rtol=1e-11, atol=1e-11 * np.abs(expected).max())
+
+
+def pin_selection_mask_brute_force():
+    """The mask holds exactly the selected keys that are in range and
+    causal: padding (-1), ids at or past N, keys after the query's position
+    and entries past count are left out; count is clamped to [0, top_k]."""
+    idx = np.array([[0, 3, 5, -1], [2, 9, 40, 1], [7, 6, 33, 64], [1, 2, 3, 4], [0, 1, 2, 3]], np.int32)
+    cnt = np.array([3, 4, 4, -2, 9], np.int32)
+    q_start, N = 5, 40
+    mask = oracle.selection_mask(idx, cnt, N, q_start)
+    assert mask.shape == (5, 2)
+    for i in range(5):
+        want = set()
+        for t in range(max(0, min(int(cnt[i]), 4))):
+            j = int(idx[i, t])
+            if 0 <= j < N and j <= q_start + i:
+                want.add(j)
+        got = {32 * w + b for w in range(mask.shape[1]) for b in range(32) if (int(mask[i, w]) >> b) & 1}
+        assert got == want, (i, got, want)
+    assert oracle.selection_mask(idx, cnt, N, q_start, W=3).shape == (5, 3)
+
+
+def pin_dense_closed_forms():
+    """One masked-in key returns that key's value exactly; no masked-in key
+    returns zeros; two keys whose scores differ by d split their weight as
+    1 : e^(scale d), through the rope part alone."""
+    rng = np.random.default_rng(22)
+    L, N, H, Dn, Dr, Dv = 3, 6, 2, 32, 16, 24
+    q = _bf(rng.standard_normal((L, H, Dn + Dr)).astype(np.float32))
+    kvb = _bf(rng.standard_normal((N, H, Dn + Dv)).astype(np.float32))
+    kv = _bf(rng.standard_normal((N, 8 + Dr)).astype(np.float32))
+    mask = np.zeros((L, 2), np.uint32)
+    mask[0, 0] = 1 << 4          # key 4 only
+    mask[2, 0] = (1 << 1) | (1 << 5)
+    out = oracle.dense_masked_attn(q, kvb, kv, mask, Dn, Dr, Dv, 8, 0.125)
+    assert np.array_equal(out[0], _f(kvb[4, :, Dn:]))
+    assert np.array_equal(out[1], np.zeros((H, Dv)))
+    # keys 1 and 5 with equal no-rope keys; the rope keys differ in one column
+    q2 = np.zeros((L, H, Dn + Dr), np.float32)
+    q2[2, :, Dn + 3] = 2.0
+    kvb2 = _f(kvb).astype(np.float32)
+    kvb2[5, :, :Dn] = kvb2[1, :, :Dn]
+    kv2 = np.zeros((N, 8 + Dr), np.float32)
+    kv2[1, 8 + 3], kv2[5, 8 + 3] = 1.5, -0.5
+    out = oracle.dense_masked_attn(_bf(q2), _bf(kvb2), _bf(kv2), mask, Dn, Dr, Dv, 8, 0.125)
+    w1 = 1.0 / (1.0 + math.exp(0.125 * 2.0 * (-0.5 - 1.5)))
+    want = w1 * kvb2[1, :, Dn:].astype(np.float64) + (1 - w1) * kvb2[5, :, Dn:].astype(np.float64)
+    assert np.allclose(out[2], want, rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -82,6 +82,18 @@ MUTATIONS = [
      "double acc = 0.0;\n            for (int32_t k = 0; k < Kin; ++k) acc += xr[k] * bf16_to_double(wo[((int64_t)k * Nout + n) % ((int64_t)Nout * Kin)]);"),
     ("positions taken as 1-based rows", "uint16_t* dst = kv_cache + pos[t] * Dqk;",
      "uint16_t* dst = kv_cache + (pos[t] > 0 ? pos[t] - 1 : 0) * Dqk;"),
+    ("dense rope term dropped",
+     "for (int32_t d = 0; d < x->Dr; ++d) dot += bf16_to_double(qh[x->Dn + d]) * bf16_to_double(kp[d]);", ""),
+    ("dense value read from the key columns", "const uint16_t* v = x->kvb + (j * x->H + h) * Dkv + x->Dn;",
+     "const uint16_t* v = x->kvb + (j * x->H + h) * Dkv;"),
+    ("dense key ignores the head", "const uint16_t* kn = x->kvb + (j * x->H + h) * Dkv;",
+     "const uint16_t* kn = x->kvb + (j * x->H) * Dkv;"),
+    ("dense mask bits reversed", "if (!((mrow[j / 32] >> (j % 32)) & 1u))", "if (!((mrow[j / 32] >> (31 - j % 32)) & 1u))"),
+    ("dense softmax scale dropped", "s[j] = x->scale * dot;", "s[j] = dot;"),
+    ("dense softmax not normalised", "const double pj = exp(s[j] - m) / Z;", "const double pj = exp(s[j] - m);"),
+    ("mask keeps non-causal keys", "if (j >= 0 && j < N && j <= p) row[j / 32]", "if (j >= 0 && j < N) row[j / 32]"),
+    ("mask ignores count", "for (int32_t t = 0; t < c; ++t) {\n            const int64_t j = idx[i * top_k + t];",
+     "for (int32_t t = 0; t < top_k; ++t) {\n            const int64_t j = idx[i * top_k + t];"),
 ]
 
 _RUNNER = r"""
