@@ -246,6 +246,46 @@ dsa_status dsa_value_up_proj(const dsa_shape* shape, const float* o, const uint1
 dsa_status dsa_o_proj(const uint16_t* x, const uint16_t* wo, int32_t T, int32_t k_in, int32_t n_out, float* y,
                       void* stream);
 
+/* Selection mask for the dense path (exo PR #2539, Prefill section: below
+ * 8192 keys the attention runs dense under a boolean mask; the mask is the
+ * query's DSA selection, which for a query with no more causal keys than
+ * top_k is every earlier key):
+ *   mask[i, w] bit b set  iff  key j = 32 w + b is among idx[i, :count[i]],
+ *                              0 <= j < N and j <= q_start + i.
+ * idx [dev] [L, top_k] int32 (as dsa_topk_select writes it; other entries are
+ * ignored, a key listed twice is set once); count [dev] [L] int32 (clamped to
+ * [0, top_k]); mask [dev] [L, mask_words] uint32, fully written (bits at or
+ * past N are 0).  Requires L >= 0 (0: nothing is enqueued), top_k >= 1,
+ * N >= 1, q_start >= 0, mask_words >= 2 * ceil(N / 64) (whole 64-key tiles);
+ * mask_words <= 16384 (DSA_ERR_UNSUPPORTED otherwise). */
+dsa_status dsa_selection_mask(const int32_t* idx, const int32_t* count, int32_t L, int32_t top_k, int32_t N,
+                              int32_t q_start, int32_t mask_words, uint32_t* mask, void* stream);
+
+/* Dense masked attention, non-absorbed form (exo PR #2539, Prefill section,
+ * dense attention in one product: each head's no-rope and rope dimensions
+ * are scored in one product under a boolean mask; widths from the config
+ * line of "GLM-5.2-Vision: llama.cpp vs vLLM line-by-line pipeline trace":
+ * qk_nope 192, qk_rope 64, v_head_dim 256; its section 4 splits the kv_b
+ * output per head into the no-rope key and the value, and k_pe is shared):
+ *   s[i,h,j] = scale * ( q[i,h,:Dn] . kvb[j,h,:Dn] + q[i,h,Dn:] . kv[j, rope_col : rope_col+Dr] )
+ *   out[i,h,:] = sum over masked-in j of softmax_j(s) * kvb[j,h,Dn:Dn+Dv]
+ * for the query at position q_start + i; keys after it are never used.
+ * q [dev] [L, H, Dn+Dr] bf16; kvb [dev] [N, H, Dn+Dv] bf16 (the kv_b
+ * projection of the latent rows); kv [dev] [N, kv_cols] bf16 (cache rows,
+ * rope key at rope_col); mask [dev] [L, mask_words] as dsa_selection_mask
+ * writes it; out [dev] [L, H, Dv] fp32; a query with no masked-in key gets
+ * zeros.  bf16 score products with fp32 sums, fp32 softmax, probabilities
+ * rounded to fp16 and values converted to fp16 for the value product (|v|
+ * must stay below 65504).  (Dn, Dr, Dv) must be (192, 64, 256) or
+ * (32, 32, 64) (DSA_ERR_UNSUPPORTED otherwise); q, kvb, kv, out 16-byte
+ * aligned, mask 4-byte aligned; kv_cols and rope_col multiples of 8;
+ * mask_words >= 2 * ceil(N / 64); scale finite and > 0; L >= 0 (0: nothing
+ * is enqueued), N >= 1, H >= 1. */
+dsa_status dsa_dense_masked_attn(const uint16_t* q, const uint16_t* kvb, const uint16_t* kv, int32_t kv_cols,
+                                 int32_t rope_col, const uint32_t* mask, int32_t mask_words, int32_t L,
+                                 int32_t N, int32_t q_start, int32_t H, int32_t d_nope, int32_t d_rope,
+                                 int32_t d_v, float scale, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,7 @@ __all__ = [
     "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn", "dsa_latent_to_f16",
     "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
     "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write", "dsa_router_topk",
-    "dsa_value_up_proj", "dsa_o_proj", "dsa_status_string",
+    "dsa_value_up_proj", "dsa_o_proj", "dsa_selection_mask", "dsa_dense_masked_attn", "dsa_status_string",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -29,7 +29,7 @@ EXPORTED_SYMBOLS = (
     "dsa_status_string", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn",
     "dsa_latent_to_f16", "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
     "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write", "dsa_router_topk",
-    "dsa_value_up_proj", "dsa_o_proj",
+    "dsa_value_up_proj", "dsa_o_proj", "dsa_selection_mask", "dsa_dense_masked_attn",
 )
 
 
@@ -83,6 +83,9 @@ def _load() -> ctypes.CDLL:
         "dsa_router_topk": (ctypes.c_int, [P, P, i32, i32, i32, ctypes.c_float, P, P, P]),
         "dsa_value_up_proj": (ctypes.c_int, [SP, P, P, i32, i32, P, P]),
         "dsa_o_proj": (ctypes.c_int, [P, P, i32, i32, i32, P, P]),
+        "dsa_selection_mask": (ctypes.c_int, [P, P, i32, i32, i32, i32, i32, P, P]),
+        "dsa_dense_masked_attn": (ctypes.c_int, [P, P, P, i32, i32, P, i32, i32, i32, i32, i32, i32, i32, i32,
+                                                 ctypes.c_float, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -230,3 +233,23 @@ def dsa_value_up_proj(shape, o, wv, T: int, d_v: int, out_v, stream=None) -> Non
 def dsa_o_proj(x, wo, T: int, k_in: int, n_out: int, y, stream=None) -> None:
     _check("dsa_o_proj", lib.dsa_o_proj(_bits(x, "x"), _bits(wo, "wo"), T, k_in, n_out,
                                         _ptr(y, torch.float32, "y"), _stream(stream)))
+
+
+def mask_words(N: int) -> int:
+    """Words per selection-mask row: N keys rounded up to whole 64-key tiles."""
+    return 2 * ((N + 63) // 64)
+
+
+def dsa_selection_mask(idx, count, L: int, top_k: int, N: int, q_start: int, mask, stream=None) -> None:
+    _check("dsa_selection_mask", lib.dsa_selection_mask(
+        _ptr(idx, torch.int32, "idx"), _ptr(count, torch.int32, "count"), L, top_k, N, q_start,
+        mask.shape[1] if mask is not None and mask.dim() == 2 else 0, _ptr(mask, torch.int32, "mask"),
+        _stream(stream)))
+
+
+def dsa_dense_masked_attn(q, kvb, kv, kv_cols: int, rope_col: int, mask, L: int, N: int, q_start: int, H: int,
+                          d_nope: int, d_rope: int, d_v: int, scale: float, out, stream=None) -> None:
+    _check("dsa_dense_masked_attn", lib.dsa_dense_masked_attn(
+        _bits(q, "q"), _bits(kvb, "kvb"), _bits(kv, "kv"), kv_cols, rope_col, _ptr(mask, torch.int32, "mask"),
+        mask.shape[1] if mask is not None and mask.dim() == 2 else 0, L, N, q_start, H, d_nope, d_rope, d_v,
+        scale, _ptr(out, torch.float32, "out"), _stream(stream)))

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["dsa_api.hip", "indexer.hip", "topk.hip", "attention.hip", "cache_write.hip", "router.hip", "proj.hip"]
+SOURCES = ["dsa_api.hip", "indexer.hip", "topk.hip", "attention.hip", "cache_write.hip", "router.hip", "proj.hip", "dense.hip"]
 HEADERS = [os.path.join(CSRC, "dsa_kernels.h"), os.path.join(ROOT, "include", "dsa.h")]
 
 HIPCC_FLAGS = [

@@ -4,6 +4,8 @@
 #include "../../include/dsa.h"
 #include "dsa_kernels.h"
 
+#include <cmath>
+
 #include <math.h>
 #include <string.h>
 
@@ -290,6 +292,45 @@ dsa_status dsa_o_proj(const uint16_t* x, const uint16_t* wo, int32_t T, int32_t 
     if (st) return st;
     dsa::GemmArgs g{x, k_in, 0, wo, k_in, 0, y, n_out, 0, T, n_out, k_in};
     return launched(dsa::launch_o_proj(g, (hipStream_t)stream));
+}
+
+dsa_status dsa_selection_mask(const int32_t* idx, const int32_t* count, int32_t L, int32_t top_k, int32_t N,
+                              int32_t q_start, int32_t mask_words, uint32_t* mask, void* stream) {
+    if (!idx || !count || !mask || L < 0 || top_k <= 0 || N <= 0 || q_start < 0 ||
+        (int64_t)q_start + L > INT32_MAX || (int64_t)mask_words < 2 * (((int64_t)N + 63) / 64))
+        return DSA_ERR_INVALID_ARG;
+    if ((int64_t)mask_words * 4 > 65536) return DSA_ERR_UNSUPPORTED;
+    if (L == 0) return DSA_OK;
+    dsa_status st = check_device();
+    if (st) return st;
+    dsa::MaskArgs a{idx, count, L, top_k, N, q_start, mask_words, mask};
+    return launched(dsa::launch_selection_mask(a, (hipStream_t)stream));
+}
+
+dsa_status dsa_dense_masked_attn(const uint16_t* q, const uint16_t* kvb, const uint16_t* kv, int32_t kv_cols,
+                                 int32_t rope_col, const uint32_t* mask, int32_t mask_words, int32_t L,
+                                 int32_t N, int32_t q_start, int32_t H, int32_t d_nope, int32_t d_rope,
+                                 int32_t d_v, float scale, float* out, void* stream) {
+    if (!q || !kvb || !kv || !mask || !out || !aligned16(q) || !aligned16(kvb) || !aligned16(kv) ||
+        !aligned16(out) || ((uintptr_t)mask & 3u))
+        return DSA_ERR_INVALID_ARG;
+    if (L < 0 || N <= 0 || H <= 0 || q_start < 0 || (int64_t)q_start + L > INT32_MAX || rope_col < 0 ||
+        d_rope < 0 || (int64_t)rope_col + d_rope > kv_cols || kv_cols % 8 != 0 || rope_col % 8 != 0 ||
+        (int64_t)mask_words < 2 * (((int64_t)N + 63) / 64) || !(scale > 0.f) || !std::isfinite(scale))
+        return DSA_ERR_INVALID_ARG;
+    int shape_id;
+    if (d_nope == 192 && d_rope == 64 && d_v == 256) shape_id = 0;
+    else if (d_nope == 32 && d_rope == 32 && d_v == 64) shape_id = 1;
+    else return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)H * (d_nope + d_v) * 2 * 64 > INT32_MAX || (int64_t)kv_cols * 2 * 64 > INT32_MAX ||
+        (int64_t)mask_words * 4 * 128 > INT32_MAX || ((int64_t)L + 127) / 128 * H > INT32_MAX)
+        return DSA_ERR_UNSUPPORTED;
+    if (L == 0) return DSA_OK;
+    dsa_status st = check_device();
+    if (st) return st;
+    dsa::DenseArgs a{q, kvb, kv, mask, L, N, H, q_start, kv_cols, rope_col, mask_words,
+                     (float)((double)scale * 1.4426950408889634), out};
+    return launched(dsa::launch_dense_attn(shape_id, a, (hipStream_t)stream));
 }
 
 dsa_status dsa_sparse_mla_attn_f16(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv16,

@@ -67,9 +67,16 @@ __device__ inline uint32_t lds_addr(const void* p) {
 // 32-bit offset) to LDS at m0 + 16 * lane, without passing through VGPRs.
 // Completion is counted by vmcnt only: the compiler does not see these
 // loads, so the kernel waits for them itself (wait_vmcnt) before a barrier.
-// M0 is written here and nowhere else in these kernels.
+// M0 is written here and in load4_to_lds, nowhere else in these kernels.
 __device__ inline void gather16_to_lds(const void* base, uint32_t voff, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(base) : "memory");
+}
+
+// 4 bytes per lane from base + voff to LDS at m0 + 4 * lane; otherwise as
+// gather16_to_lds (counted by vmcnt only, M0 written here).
+__device__ inline void load4_to_lds(const void* base, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
                  :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(base) : "memory");
 }
 
@@ -184,5 +191,29 @@ struct GemmArgs {            // C[m, n] = sum_k A[m, k] B[n, k], per batch z
 hipError_t launch_value_up_proj(const GemmArgs& g, int batch, hipStream_t s);
 // output projection: A bf16, C float32, N % 192 == 0, K % 64 == 0
 hipError_t launch_o_proj(const GemmArgs& g, hipStream_t s);
+
+// Selection mask: row i of mask [L, W] has bit j set iff key j is among
+// idx[i, :count[i]], 0 <= j < N and j <= q_start + i.
+struct MaskArgs {
+    const int32_t* idx;    // [L, top_k]
+    const int32_t* count;  // [L]
+    int32_t L, top_k, N, q_start, W;
+    uint32_t* mask;        // [L, W]
+};
+hipError_t launch_selection_mask(const MaskArgs& a, hipStream_t s);
+
+// Dense masked attention, non-absorbed form: per head, one (Dn + Dr)-wide
+// score product against [no-rope key | shared rope key], keys limited to
+// the mask bits, values the head's Dv columns of kvb.
+struct DenseArgs {
+    const uint16_t* q;      // [L, H, Dn + Dr]
+    const uint16_t* kvb;    // [N, H, Dn + Dv]
+    const uint16_t* kv;     // [N, kv_cols]; rope key at columns rope_col ..
+    const uint32_t* mask;   // [L, W]
+    int32_t L, N, H, q_start, kv_cols, rope_col, W;
+    float scale_log2;       // softmax_scale * log2(e)
+    float* out;             // [L, H, Dv]
+};
+hipError_t launch_dense_attn(int shape_id, const DenseArgs& a, hipStream_t s);
 
 }  // namespace dsa

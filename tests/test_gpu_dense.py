@@ -1,0 +1,95 @@
+"""GPU parity of the dense masked path (dsa_selection_mask,
+dsa_dense_masked_attn) against the CPU oracle on the same seeded inputs and
+the same selection (the oracle's top-k of seeded indexer scores).
+
+- selection mask: integer work, bit-exact over every row;
+- attention: max over (query, head) rows of max|o - r| / max|r| <= 2e-3.
+  The GPU sums bf16 products in fp32, rounds the probabilities to fp16
+  (relative 2^-11) and converts the values to fp16 (exact here); the oracle
+  is fp64 throughout.  The rounding of the probabilities dominates: about
+  2^-11 / sqrt(3) of the row's scale, well inside the bound.
+Cases: 160 GLM-width queries over 700 keys (ragged query block and key
+tile), two tiny-width chunks (several query blocks and tiles, a first chunk
+whose early queries take every earlier key, a row with an empty selection),
+and the 8k-key chunk the benchmark times (4096 queries, every head; the
+oracle runs on a seeded sample of rows)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests.gpu_util import ATTN_TOL, dev, host, requires_gpu, row_rel_err, say
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def select(cfg, d, empty_rows=()):
+    pos = cfg.q_start + np.arange(cfg.L)
+    S = d["S"].copy()
+    S[np.arange(cfg.N)[None, :] > pos[:, None]] = -np.inf
+    idx, cnt = oracle.topk_select(S, pos, cfg.top_k)
+    for r in empty_rows:
+        cnt[r] = 0
+    return idx, cnt
+
+
+def run(cfg, empty_rows=(), rows=None):
+    import torch
+    import sparse_attention_scores_amd as dsa
+    d = W.make_dense(cfg)
+    idx, cnt = select(cfg, d, empty_rows)
+    Wm = dsa.mask_words(cfg.N)
+    say("dense", cfg.name, "L", cfg.L, "N", cfg.N, "q_start", cfg.q_start, "H", cfg.H)
+    mask = torch.empty((cfg.L, Wm), dtype=torch.int32, device="cuda")
+    dsa.dsa_selection_mask(dev(idx), dev(cnt), cfg.L, cfg.top_k, cfg.N, cfg.q_start, mask)
+    mask_h = host(mask).view(np.uint32)
+    mask_ref = oracle.selection_mask(idx, cnt, cfg.N, cfg.q_start, W=Wm)
+    assert np.array_equal(mask_h, mask_ref)
+    out = torch.empty((cfg.L, cfg.H, cfg.Dv), dtype=torch.float32, device="cuda")
+    dsa.dsa_dense_masked_attn(dev(d["q"]), dev(d["kvb"]), dev(d["kv"]), cfg.Dl + cfg.Dr, cfg.Dl, mask,
+                              cfg.L, cfg.N, cfg.q_start, cfg.H, cfg.Dn, cfg.Dr, cfg.Dv, 1.0 / 16, out)
+    got = host(out)
+    assert np.isfinite(got).all()
+    rows = np.arange(cfg.L) if rows is None else rows
+    ref = oracle.dense_masked_attn(d["q"], d["kvb"], d["kv"], mask_ref, cfg.Dn, cfg.Dr, cfg.Dv, cfg.Dl,
+                                   1.0 / 16, rows=rows)
+    err = row_rel_err(got[rows], ref)
+    assert err <= ATTN_TOL, err
+    for r in empty_rows:
+        assert not got[r].any()
+    return got
+
+
+def test_dense_tiny():
+    run(W.DENSE["tiny"], empty_rows=(3, 199))
+
+
+def test_dense_tiny_first_chunk():
+    run(W.DENSE["tiny_first"])
+
+
+def test_dense_glm_small():
+    run(W.DENSE["glm_small"], empty_rows=(7,))
+
+
+def test_dense_glm_8k_chunk_sampled():
+    cfg = W.DENSE["glm_8k_chunk"]
+    run(cfg, rows=W.sample_rows(cfg.L, 12, seed=9, must=[0, 127, 128, cfg.L - 1]))
+
+
+def test_dense_rejects_bad_arguments():
+    import torch
+    import sparse_attention_scores_amd as dsa
+    cfg = W.DENSE["tiny"]
+    q = torch.zeros((cfg.L, cfg.H, 64), dtype=torch.int16, device="cuda")
+    kvb = torch.zeros((cfg.N, cfg.H, 96), dtype=torch.int16, device="cuda")
+    kv = torch.zeros((cfg.N, 96), dtype=torch.int16, device="cuda")
+    mask = torch.zeros((cfg.L, dsa.mask_words(cfg.N)), dtype=torch.int32, device="cuda")
+    out = torch.empty((cfg.L, cfg.H, 64), dtype=torch.float32, device="cuda")
+    say("dense argument checks")
+    with pytest.raises(dsa.DsaError):   # unsupported widths
+        dsa.dsa_dense_masked_attn(q, kvb, kv, 96, 64, mask, cfg.L, cfg.N, 0, cfg.H, 48, 16, 64, 0.0625, out)
+    with pytest.raises(dsa.DsaError):   # mask rows too short for N
+        dsa.dsa_dense_masked_attn(q, kvb, kv, 96, 64, mask[:, :2].contiguous(), cfg.L, cfg.N, 0, cfg.H, 32, 32, 64, 0.0625, out)
+    with pytest.raises(dsa.DsaError):   # rope key past the cache row
+        dsa.dsa_dense_masked_attn(q, kvb, kv, 96, 72, mask, cfg.L, cfg.N, 0, cfg.H, 32, 32, 64, 0.0625, out)

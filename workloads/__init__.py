@@ -303,3 +303,48 @@ def make_proj(cfg: Proj) -> Dict[str, np.ndarray]:
     wo = to_bf16_bits(nrm(cfg.hidden, cfg.H * cfg.Dv) * np.float32(1.0 / np.sqrt(cfg.H * cfg.Dv)))
     x = to_bf16_bits(nrm(cfg.T, cfg.H * cfg.Dv) * np.float32(0.1))
     return {"o": np.ascontiguousarray(o), "wv": wv, "wo": wo, "x": x}
+
+
+@dataclasses.dataclass(frozen=True)
+class Dense:
+    """A prefill chunk on the dense masked path, non-absorbed form: L queries
+    at positions q_start .. q_start+L-1 over N keys.  Per head the query is
+    [no-rope Dn | rope Dr] and kvb holds [no-rope key Dn | value Dv]; the rope
+    key is the cache row's columns Dl .. Dl+Dr-1.  The selection is the top_k
+    of seeded random indexer scores (GLM: 64 heads, 192 + 64 score dims,
+    v_head_dim 256, top_k 2048, dense below 8192 keys of context, chunks of
+    4096 tokens)."""
+    name: str
+    L: int
+    N: int
+    q_start: int
+    seed: int
+    H: int = 64
+    Dn: int = 192
+    Dr: int = 64
+    Dv: int = 256
+    Dl: int = 512
+    top_k: int = 2048
+
+
+DENSE: Dict[str, Dense] = {
+    "glm_8k_chunk": Dense("glm_8k_chunk", 4096, 8192, 4096, 61),
+    "glm_4k_first": Dense("glm_4k_first", 4096, 4096, 0, 62),
+    "glm_small": Dense("glm_small", 160, 700, 540, 63, top_k=128),
+    "tiny": Dense("tiny", 200, 300, 100, 64, H=4, Dn=32, Dr=32, Dv=64, Dl=64, top_k=64),
+    "tiny_first": Dense("tiny_first", 150, 150, 0, 65, H=3, Dn=32, Dr=32, Dv=64, Dl=64, top_k=64),
+}
+
+
+def make_dense(cfg: Dense) -> Dict[str, np.ndarray]:
+    """q, kvb and the cache rows kv ~ N(0,1) rounded to bf16; indexer scores
+    S ~ N(0,1) in float32 for the selection (the causal limit is applied by
+    the selection step).  Drawn in the order q, kvb, kv, S."""
+    rng = np.random.default_rng(cfg.seed)
+    nrm = lambda *shp: rng.standard_normal(size=shp, dtype=np.float32)
+    q = to_bf16_bits(nrm(cfg.L, cfg.H, cfg.Dn + cfg.Dr))
+    kvb = to_bf16_bits(nrm(cfg.N, cfg.H, cfg.Dn + cfg.Dv))
+    kv = to_bf16_bits(nrm(cfg.N, cfg.Dl + cfg.Dr))
+    S = nrm(cfg.L, cfg.N)
+    return {"q": q, "kvb": kvb, "kv": kv, "S": S}
+
