@@ -277,7 +277,7 @@ dsa_status dsa_selection_mask(const int32_t* idx, const int32_t* count, int32_t 
  * zeros.  bf16 score products with fp32 sums, fp32 softmax, probabilities
  * rounded to fp16 and values converted to fp16 for the value product (|v|
  * must stay below 65504).  (Dn, Dr, Dv) must be (192, 64, 256) or
- * (32, 32, 64) (DSA_ERR_UNSUPPORTED otherwise); q, kvb, kv, out 16-byte
+ * (64, 64, 64) (DSA_ERR_UNSUPPORTED otherwise); q, kvb, kv, out 16-byte
  * aligned, mask 4-byte aligned; kv_cols and rope_col multiples of 8;
  * mask_words >= 2 * ceil(N / 64); scale finite and > 0; L >= 0 (0: nothing
  * is enqueued), N >= 1, H >= 1. */
@@ -285,6 +285,24 @@ dsa_status dsa_dense_masked_attn(const uint16_t* q, const uint16_t* kvb, const u
                                  int32_t rope_col, const uint32_t* mask, int32_t mask_words, int32_t L,
                                  int32_t N, int32_t q_start, int32_t H, int32_t d_nope, int32_t d_rope,
                                  int32_t d_v, float scale, float* out, void* stream);
+
+/* dsa_dense_masked_attn with the value columns of kvb16 stored as fp16
+ * (as dsa_values_to_f16 leaves them) instead of bf16; the no-rope key
+ * columns stay bf16.  Same arguments, results and requirements otherwise;
+ * the conversion then happens once per value rather than in every block
+ * that reads it. */
+dsa_status dsa_dense_masked_attn_f16(const uint16_t* q, const uint16_t* kvb16, const uint16_t* kv, int32_t kv_cols,
+                                     int32_t rope_col, const uint32_t* mask, int32_t mask_words, int32_t L,
+                                     int32_t N, int32_t q_start, int32_t H, int32_t d_nope, int32_t d_rope,
+                                     int32_t d_v, float scale, float* out, void* stream);
+
+/* Rewrites the value columns of kvb [dev] [N, H, d_nope + d_v] in place from
+ * bf16 to fp16 bits, round to nearest even (exact for |v| in
+ * [2^-14, 65504]; smaller magnitudes become fp16 subnormals, larger ones
+ * infinities); the no-rope key columns are left alone.  Requires kvb
+ * 16-byte aligned, N >= 0 (0: nothing is enqueued), H >= 1, d_nope and d_v
+ * multiples of 8. */
+dsa_status dsa_values_to_f16(uint16_t* kvb, int32_t N, int32_t H, int32_t d_nope, int32_t d_v, void* stream);
 
 #ifdef __cplusplus
 }

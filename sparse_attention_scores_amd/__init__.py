@@ -21,7 +21,8 @@ __all__ = [
     "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn", "dsa_latent_to_f16",
     "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
     "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write", "dsa_router_topk",
-    "dsa_value_up_proj", "dsa_o_proj", "dsa_selection_mask", "dsa_dense_masked_attn", "dsa_status_string",
+    "dsa_value_up_proj", "dsa_o_proj", "dsa_selection_mask", "dsa_dense_masked_attn",
+    "dsa_dense_masked_attn_f16", "dsa_values_to_f16", "dsa_status_string",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -30,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "dsa_latent_to_f16", "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
     "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write", "dsa_router_topk",
     "dsa_value_up_proj", "dsa_o_proj", "dsa_selection_mask", "dsa_dense_masked_attn",
+    "dsa_dense_masked_attn_f16", "dsa_values_to_f16",
 )
 
 
@@ -86,6 +88,9 @@ def _load() -> ctypes.CDLL:
         "dsa_selection_mask": (ctypes.c_int, [P, P, i32, i32, i32, i32, i32, P, P]),
         "dsa_dense_masked_attn": (ctypes.c_int, [P, P, P, i32, i32, P, i32, i32, i32, i32, i32, i32, i32, i32,
                                                  ctypes.c_float, P, P]),
+        "dsa_dense_masked_attn_f16": (ctypes.c_int, [P, P, P, i32, i32, P, i32, i32, i32, i32, i32, i32, i32,
+                                                     i32, ctypes.c_float, P, P]),
+        "dsa_values_to_f16": (ctypes.c_int, [P, i32, i32, i32, i32, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -253,3 +258,16 @@ def dsa_dense_masked_attn(q, kvb, kv, kv_cols: int, rope_col: int, mask, L: int,
         _bits(q, "q"), _bits(kvb, "kvb"), _bits(kv, "kv"), kv_cols, rope_col, _ptr(mask, torch.int32, "mask"),
         mask.shape[1] if mask is not None and mask.dim() == 2 else 0, L, N, q_start, H, d_nope, d_rope, d_v,
         scale, _ptr(out, torch.float32, "out"), _stream(stream)))
+
+
+def dsa_dense_masked_attn_f16(q, kvb16, kv, kv_cols: int, rope_col: int, mask, L: int, N: int, q_start: int,
+                              H: int, d_nope: int, d_rope: int, d_v: int, scale: float, out, stream=None) -> None:
+    _check("dsa_dense_masked_attn_f16", lib.dsa_dense_masked_attn_f16(
+        _bits(q, "q"), _bits(kvb16, "kvb16"), _bits(kv, "kv"), kv_cols, rope_col, _ptr(mask, torch.int32, "mask"),
+        mask.shape[1] if mask is not None and mask.dim() == 2 else 0, L, N, q_start, H, d_nope, d_rope, d_v,
+        scale, _ptr(out, torch.float32, "out"), _stream(stream)))
+
+
+def dsa_values_to_f16(kvb, N: int, H: int, d_nope: int, d_v: int, stream=None) -> None:
+    _check("dsa_values_to_f16", lib.dsa_values_to_f16(_bits(kvb, "kvb"), N, H, d_nope, d_v, _stream(stream)))
+

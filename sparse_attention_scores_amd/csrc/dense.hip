@@ -10,7 +10,9 @@
 // mask is the query's selection, limited to causal keys.
 //
 // Layout and schedule:
-//  - one block = one head x 128 queries (4 waves x 32 queries); the keys
+//  - one block = one head x 128 queries (8 waves x 16 queries, two waves
+//    per SIMD, so that one wave's MFMAs run beside the other's softmax,
+//    LDS reads and DMA issue); the keys
 //    stream in 64-key tiles through two LDS buffers filled by LDS-DMA
 //    (global_load_lds), so key and value rows never pass through VGPRs.  A
 //    tile holds the no-rope keys [64][Dn], the rope keys [64][Dr], the
@@ -19,12 +21,15 @@
 //    in registers for the whole loop), an fp32 online softmax whose
 //    reference maximum only moves when a score clears it by kLazy (log2
 //    units), P in fp16, O^T += V^T P^T on fp16 MFMA with V read transposed
-//    (ds_read_b64_tr_b16) and converted to fp16 in registers;
+//    (ds_read_b64_tr_b16): either converted to fp16 in registers, or stored
+//    as fp16 beforehand (values_to_f16_kernel), which takes the conversion
+//    (a third of the loop's vector instructions) out of the loop;
 //  - the blocks of one head are consecutive in one XCD's share of the
 //    dispatch order, so that head's keys and values stream through that
 //    XCD's L2 once for all its query blocks.
 // Numerics: bf16 products summed in fp32; P rounded to fp16 (relative 2^-11)
-// and V converted bf16 -> fp16 (exact for |v| in [2^-14, 65504]).
+// and V converted bf16 -> fp16 (exact for |v| in [2^-14, 65504]; smaller
+// magnitudes become fp16 subnormals, error at most 2^-25).
 #include "dsa_kernels.h"
 
 #include <math.h>
@@ -34,7 +39,9 @@ namespace {
 
 constexpr int kDTK = 64;      // keys per tile
 constexpr int kDQB = 128;     // queries per block
-constexpr int kDNT = 256;     // threads per block (4 waves)
+constexpr int kDNW = 8;       // waves per block
+constexpr int kDQW = kDQB / kDNW;   // queries per wave (16)
+constexpr int kDNT = 64 * kDNW;
 constexpr float kDLazy = 8.f;
 
 // Chunk XORs of LDS tile rows (rows 16 apart share one).  Value rows (512 B)
@@ -88,7 +95,8 @@ struct DenseShape {
     static_assert(DN % 32 == 0 && DR % 32 == 0 && DV % 16 == 0, "head widths");
     static constexpr int DQ = DN + DR, DKV = DN + DV;
     static constexpr int CN = DN / 8, CR = DR / 8, CV = DV / 8;   // 16-byte chunks per row
-    static_assert(CN % 4 == 0 && CR % 4 == 0 && CV % 4 == 0, "each wave issues a whole share of every region");
+    static_assert((kDTK * CN / 64) % kDNW == 0 && (kDTK * CR / 64) % kDNW == 0 && (kDTK * CV / 64) % kDNW == 0,
+                  "each wave issues a whole share of every region");
     static constexpr int KS = DQ / 32, KSN = DN / 32;             // score k-steps, no-rope first
     static constexpr int FB = DV / 16;                            // 16-feature output blocks
     static constexpr int SWN = swz_mask(CN, 8), SWR = swz_mask(CR, 8), SWV = swz_mask(CV, 16);
@@ -96,12 +104,14 @@ struct DenseShape {
         u32x4 kn[kDTK * CN];
         u32x4 kr[kDTK * CR];
         u32x4 v[kDTK * CV];
-        uint32_t m[kDQB * 2];    // [wave][query of the wave][2 words]
+        uint32_t m[kDQB * 2];    // [query of the block][2 words]
     };
 };
 
-template <int DN, int DR, int DV>
-__global__ __launch_bounds__(kDNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// VF16: the value columns of kvb hold fp16 (see values_to_f16_kernel)
+// rather than bf16; the no-rope key columns are bf16 either way.
+template <int DN, int DR, int DV, bool VF16>
+__global__ __launch_bounds__(kDNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_attn_kernel(DenseArgs a) {
     using C = DenseShape<DN, DR, DV>;
     __shared__ __attribute__((aligned(16))) typename C::Buf buf[2];
@@ -119,14 +129,13 @@ void dense_attn_kernel(DenseArgs a) {
     const int nkeys = min(a.N, a.q_start + qlast + 1);      // keys after the last query are never visible
     const int ntiles = (nkeys + kDTK - 1) / kDTK;
 
-    // this lane's queries (B operand: query c16 of each 16-query half, dims 8g..8g+7 of each k-step)
-    u32x4 qf[2][C::KS];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int qq = min(q0 + 32 * w + 16 * qb + c16, a.L - 1);
+    // this lane's query (B operand: query c16 of the wave, dims 8g..8g+7 of each k-step)
+    u32x4 qf[C::KS];
+    {
+        const int qq = min(q0 + kDQW * w + c16, a.L - 1);
         const uint16_t* qr = a.q + ((int64_t)qq * a.H + h) * C::DQ + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) qf[qb][ks] = ldg16(qr + 32 * ks);
+        for (int ks = 0; ks < C::KS; ++ks) qf[ks] = ldg16(qr + 32 * ks);
     }
 
     // LDS-DMA of tile t into buffer bi.  Instruction n of a region writes its
@@ -134,40 +143,52 @@ void dense_attn_kernel(DenseArgs a) {
     // P % chunks, which holds logical chunk (P % chunks) ^ swizzle(row).
     // Rows past the last key repeat it (their mask bits are 0).
     const uint32_t rs_kvb = (uint32_t)a.H * C::DKV * 2u, rs_kv = (uint32_t)a.kv_cols * 2u;
+    constexpr int IN = kDTK * C::CN / 64 / kDNW, IR = kDTK * C::CR / 64 / kDNW,
+                  IV = kDTK * C::CV / 64 / kDNW;   // instructions per wave and region
+    uint32_t off[IN + IR + IV];   // byte offset of this lane's chunk from the tile's first row
+    int row[IN + IR + IV];        // ... and its tile row
+#pragma unroll
+    for (int n = 0; n < IN + IR + IV; ++n) {
+        const int ch = n < IN ? C::CN : n < IN + IR ? C::CR : C::CV;
+        const int i = w * (n < IN ? IN : n < IN + IR ? IR : IV) + (n < IN ? n : n < IN + IR ? n - IN : n - IN - IR);
+        const int P = 64 * i + l, r = P / ch;
+        const int x = n < IN ? swz_key(r & 15) & C::SWN : n < IN + IR ? swz_key(r & 15) & C::SWR : swz_val(r & 15) & C::SWV;
+        row[n] = r;
+        off[n] = (uint32_t)r * (n < IN + IR && n >= IN ? rs_kv : rs_kvb) + 16u * ((P % ch) ^ x);
+    }
     auto issue = [&](int t, int bi) {
         typename C::Buf& B = buf[bi];
         const int k0 = t * kDTK;
-        const int jmax = a.N - 1 - k0;
         const uint16_t* kvb_t = a.kvb + ((int64_t)k0 * a.H + h) * C::DKV;
         const uint16_t* kv_t = a.kv + (int64_t)k0 * a.kv_cols + a.rope_col;
+        // the tile reaches past the last key: its extra rows repeat the last key
+        const bool clamp = k0 + kDTK > a.N;
+        const int jmax = a.N - 1 - k0;
+        auto o = [&](int n, uint32_t rs) {
+            return clamp && row[n] > jmax ? off[n] - (uint32_t)(row[n] - jmax) * rs : off[n];
+        };
 #pragma unroll
-        for (int n = 0; n < C::CN / 4; ++n) {
-            const int i = w * (C::CN / 4) + n, P = 64 * i + l, r = P / C::CN;
-            const int c = (P % C::CN) ^ (swz_key(r & 15) & C::SWN);
-            gather16_to_lds(kvb_t, (uint32_t)min(r, jmax) * rs_kvb + 16u * c, lds_addr(&B.kn[64 * i]));
-        }
+        for (int n = 0; n < IN; ++n)
+            gather16_to_lds(kvb_t, o(n, rs_kvb), lds_addr(&B.kn[64 * (w * IN + n)]));
 #pragma unroll
-        for (int n = 0; n < C::CR / 4; ++n) {
-            const int i = w * (C::CR / 4) + n, P = 64 * i + l, r = P / C::CR;
-            const int c = (P % C::CR) ^ (swz_key(r & 15) & C::SWR);
-            gather16_to_lds(kv_t, (uint32_t)min(r, jmax) * rs_kv + 16u * c, lds_addr(&B.kr[64 * i]));
-        }
+        for (int n = 0; n < IR; ++n)
+            gather16_to_lds(kv_t, o(IN + n, rs_kv), lds_addr(&B.kr[64 * (w * IR + n)]));
 #pragma unroll
-        for (int n = 0; n < C::CV / 4; ++n) {
-            const int i = w * (C::CV / 4) + n, P = 64 * i + l, r = P / C::CV;
-            const int c = (P % C::CV) ^ (swz_val(r & 15) & C::SWV);
-            gather16_to_lds(kvb_t + DN, (uint32_t)min(r, jmax) * rs_kvb + 16u * c, lds_addr(&B.v[64 * i]));
-        }
-        // mask words: lane l -> query 32w + l / 2 of the block, word l % 2 of the tile
+        for (int n = 0; n < IV; ++n)
+            gather16_to_lds(kvb_t + DN, o(IN + IR + n, rs_kvb), lds_addr(&B.v[64 * (w * IV + n)]));
+        // mask words: lane l < 32 -> query 16w + l / 2 of the block, word l % 2 of the tile
         const uint32_t* mb = a.mask + (int64_t)q0 * a.W + k0 / 32;
-        const int qi = min(32 * w + (l >> 1), a.L - 1 - q0);
-        load4_to_lds(mb, (uint32_t)(qi * a.W + (l & 1)) * 4u, lds_addr(&B.m[64 * w]));
+        const int qi = min(kDQW * w + (l >> 1), a.L - 1 - q0);
+        if (l < 2 * kDQW) load4_to_lds(mb, (uint32_t)(qi * a.W + (l & 1)) * 4u, lds_addr(&B.m[2 * kDQW * w]));
     };
 
-    f32x4 o[C::FB][2];
+    f32x4 o[C::FB];
 #pragma unroll
-    for (int f = 0; f < C::FB; ++f) o[f][0] = o[f][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float mref[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+    for (int f = 0; f < C::FB; ++f) o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the reference maximum starts finite, so that exp2(-inf - mref) = 0 for a
+    // masked-out key even before the first visible one
+    constexpr float kStart = -1e30f;
+    float mref = kStart, lsum = 0.f;
 
     // per-lane LDS read offsets
     const int xn = swz_key(c16) & C::SWN, xr = swz_key(c16) & C::SWR;
@@ -183,12 +204,10 @@ void dense_attn_kernel(DenseArgs a) {
         if (t + 1 < ntiles) issue(t + 1, bi ^ 1);
         const typename C::Buf& B = buf[bi];
 
-        // scores: s[qb][kb] holds keys 16kb + 4g + i of query 16qb + c16
-        f32x4 s[2][4];
+        // scores: s[kb] holds keys 16kb + 4g + i of query c16
+        f32x4 s[4];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < 4; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
             u32x4 ka[4];
@@ -199,36 +218,36 @@ void dense_attn_kernel(DenseArgs a) {
                                      : B.kr[r * C::CR + ((4 * (ks - C::KSN) + g) ^ xr)];
             }
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) s[qb][kb] = mfma16_bf16(ka[kb], qf[qb][ks], s[qb][kb]);
+            for (int kb = 0; kb < 4; ++kb) s[kb] = mfma16_bf16(ka[kb], qf[ks], s[kb]);
         }
 
         // mask, online softmax, P^T fragments (keys 4g..4g+3 and 16+4g..16+4g+3
         // of each 32-key step, matching the transposed value read)
-        u32x4 pf[2][2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const uint64_t mw = *reinterpret_cast<const uint64_t*>(&B.m[64 * w + 2 * (16 * qb + c16)]);
+        u32x4 pf[2];
+        {
+            const uint32_t* mw = &B.m[2 * (kDQW * w + c16)];
             float x[4][4];
             float mt = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < 4; ++kb) {
+                const uint32_t nib = mw[kb >> 1] >> (16 * (kb & 1) + 4 * g);   // this lane's 4 keys
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const bool ok = (mw >> (16 * kb + 4 * g + i)) & 1u;
-                    x[kb][i] = ok ? s[qb][kb][i] * a.scale_log2 : -INFINITY;
+                    // 0 for a visible key, -inf (bits 0xff800000) for a masked one
+                    const float bias = __uint_as_float(((nib >> i) & 1u) ? 0u : 0xff800000u);
+                    x[kb][i] = fmaf(s[kb][i], a.scale_log2, bias);
                     mt = fmaxf(mt, x[kb][i]);
                 }
+            }
             mt = max_q4(mt);
-            const bool up = mt > mref[qb] + kDLazy;
+            const bool up = mt > mref + kDLazy;
             if (__ballot(up)) {   // wave-uniform; rare after the first tiles
-                const float mn = up ? mt : mref[qb];
-                const float alpha = up ? __builtin_amdgcn_exp2f(mref[qb] - mn) : 1.f;
-                mref[qb] = mn;
-                lsum[qb] *= alpha;
+                const float mn = up ? mt : mref;
+                const float alpha = up ? __builtin_amdgcn_exp2f(mref - mn) : 1.f;
+                mref = mn;
+                lsum *= alpha;
 #pragma unroll
-                for (int f = 0; f < C::FB; ++f) o[f][qb] *= alpha;
+                for (int f = 0; f < C::FB; ++f) o[f] *= alpha;
             }
             float p[4][4];
             float ps = 0.f;
@@ -236,15 +255,15 @@ void dense_attn_kernel(DenseArgs a) {
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[kb][i] = x[kb][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[kb][i] - mref[qb]);
+                    p[kb][i] = __builtin_amdgcn_exp2f(x[kb][i] - mref);
                     ps += p[kb][i];
                 }
-            lsum[qb] += ps;
+            lsum += ps;
 #pragma unroll
             for (int st = 0; st < 2; ++st)
-                pf[qb][st] = u32x4{pack2_f16(p[2 * st][0], p[2 * st][1]), pack2_f16(p[2 * st][2], p[2 * st][3]),
-                                   pack2_f16(p[2 * st + 1][0], p[2 * st + 1][1]),
-                                   pack2_f16(p[2 * st + 1][2], p[2 * st + 1][3])};
+                pf[st] = u32x4{pack2_f16(p[2 * st][0], p[2 * st][1]), pack2_f16(p[2 * st][2], p[2 * st][3]),
+                               pack2_f16(p[2 * st + 1][0], p[2 * st + 1][1]),
+                               pack2_f16(p[2 * st + 1][2], p[2 * st + 1][3])};
         }
 
         // O^T[feature][query] += V^T P^T
@@ -253,28 +272,29 @@ void dense_attn_kernel(DenseArgs a) {
         for (int st = 0; st < 2; ++st) {
 #pragma unroll
             for (int f = 0; f < C::FB; ++f) {
-                const int off = (32 * st) * C::CV * 16 + vrow + 16 * ((2 * f) ^ vx);
-                const u32x2 v0 = bf16x4_f16x4(read_tr16(vt + off));
-                const u32x2 v1 = bf16x4_f16x4(read_tr16(vt + off + 16 * C::CV * 16));
+                const int voff = (32 * st) * C::CV * 16 + vrow + 16 * ((2 * f) ^ vx);
+                u32x2 v0 = read_tr16(vt + voff), v1 = read_tr16(vt + voff + 16 * C::CV * 16);
+                if constexpr (!VF16) {
+                    v0 = bf16x4_f16x4(v0);
+                    v1 = bf16x4_f16x4(v1);
+                }
                 const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) o[f][qb] = mfma16_f16(av, pf[qb][st], o[f][qb]);
+                o[f] = mfma16_f16(av, pf[st], o[f]);
             }
         }
         wait_vmcnt<0>();     // this wave's share of tile t+1 has landed
         __syncthreads();     // ... and everyone's; buffer bi is free again
     }
 
-    // normalise and store: lane holds features 16f + 4g .. +3 of query 16qb + c16
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const float tot = sum_q4(lsum[qb]);
+    // normalise and store: lane holds features 16f + 4g .. +3 of query c16
+    {
+        const float tot = sum_q4(lsum);
         const float inv = tot > 0.f ? 1.f / tot : 0.f;
-        const int qq = q0 + 32 * w + 16 * qb + c16;
+        const int qq = q0 + kDQW * w + c16;
         if (qq < a.L) {
             float* orow = a.out + ((int64_t)qq * a.H + h) * DV + 4 * g;
 #pragma unroll
-            for (int f = 0; f < C::FB; ++f) *reinterpret_cast<f32x4*>(orow + 16 * f) = o[f][qb] * inv;
+            for (int f = 0; f < C::FB; ++f) *reinterpret_cast<f32x4*>(orow + 16 * f) = o[f] * inv;
         }
     }
 }
@@ -297,7 +317,33 @@ __global__ __launch_bounds__(256) void selection_mask_kernel(MaskArgs a) {
     for (int k = threadIdx.x; k < a.W; k += 256) row[k] = bits[k];
 }
 
+// bf16 -> fp16 bits, round to nearest even (exact for |v| in [2^-14, 65504];
+// larger magnitudes become infinities)
+__device__ inline uint32_t bf16x2_f16x2_rne(uint32_t d) {
+    const _Float16 lo = (_Float16)__uint_as_float(d << 16);
+    const _Float16 hi = (_Float16)__uint_as_float(d & 0xFFFF0000u);
+    return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+// The value columns of kvb [N, H, Dn + Dv], bf16 -> fp16 in place; 8 values
+// per thread.
+__global__ __launch_bounds__(256) void values_to_f16_kernel(uint16_t* kvb, int64_t rows, int dn, int dv) {
+    const int vpr = dv / 8;   // 16-byte vectors per (key, head) row
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= rows * vpr) return;
+    u32x4* p = reinterpret_cast<u32x4*>(kvb + (i / vpr) * (dn + dv) + dn) + i % vpr;
+    const u32x4 x = *p;
+    *p = u32x4{bf16x2_f16x2_rne(x[0]), bf16x2_f16x2_rne(x[1]), bf16x2_f16x2_rne(x[2]), bf16x2_f16x2_rne(x[3])};
+}
+
 }  // namespace
+
+hipError_t launch_values_to_f16(uint16_t* kvb, int64_t rows, int dn, int dv, hipStream_t s) {
+    const int64_t n = rows * (dv / 8);
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(values_to_f16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, kvb, rows, dn, dv);
+    return hipGetLastError();
+}
 
 hipError_t launch_selection_mask(const MaskArgs& a, hipStream_t s) {
     if (a.L <= 0) return hipSuccess;
@@ -305,12 +351,17 @@ hipError_t launch_selection_mask(const MaskArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_dense_attn(int shape_id, const DenseArgs& a, hipStream_t s) {
+hipError_t launch_dense_attn(int shape_id, const DenseArgs& a, bool values_f16, hipStream_t s) {
     if (a.L <= 0 || a.N <= 0) return hipSuccess;
     const int nqb = (a.L + kDQB - 1) / kDQB;
     const dim3 grid((unsigned)(nqb * a.H)), block(kDNT);
-    if (shape_id == 0) hipLaunchKernelGGL((dense_attn_kernel<192, 64, 256>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((dense_attn_kernel<32, 32, 64>), grid, block, 0, s, a);
+    if (shape_id == 0) {
+        if (values_f16) hipLaunchKernelGGL((dense_attn_kernel<192, 64, 256, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((dense_attn_kernel<192, 64, 256, false>), grid, block, 0, s, a);
+    } else {
+        if (values_f16) hipLaunchKernelGGL((dense_attn_kernel<64, 64, 64, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((dense_attn_kernel<64, 64, 64, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

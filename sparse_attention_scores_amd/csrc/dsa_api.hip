@@ -307,10 +307,11 @@ dsa_status dsa_selection_mask(const int32_t* idx, const int32_t* count, int32_t 
     return launched(dsa::launch_selection_mask(a, (hipStream_t)stream));
 }
 
-dsa_status dsa_dense_masked_attn(const uint16_t* q, const uint16_t* kvb, const uint16_t* kv, int32_t kv_cols,
-                                 int32_t rope_col, const uint32_t* mask, int32_t mask_words, int32_t L,
-                                 int32_t N, int32_t q_start, int32_t H, int32_t d_nope, int32_t d_rope,
-                                 int32_t d_v, float scale, float* out, void* stream) {
+namespace {
+dsa_status dense_attn(const uint16_t* q, const uint16_t* kvb, const uint16_t* kv, int32_t kv_cols, int32_t rope_col,
+                      const uint32_t* mask, int32_t mask_words, int32_t L, int32_t N, int32_t q_start, int32_t H,
+                      int32_t d_nope, int32_t d_rope, int32_t d_v, float scale, float* out, bool values_f16,
+                      void* stream) {
     if (!q || !kvb || !kv || !mask || !out || !aligned16(q) || !aligned16(kvb) || !aligned16(kv) ||
         !aligned16(out) || ((uintptr_t)mask & 3u))
         return DSA_ERR_INVALID_ARG;
@@ -320,7 +321,7 @@ dsa_status dsa_dense_masked_attn(const uint16_t* q, const uint16_t* kvb, const u
         return DSA_ERR_INVALID_ARG;
     int shape_id;
     if (d_nope == 192 && d_rope == 64 && d_v == 256) shape_id = 0;
-    else if (d_nope == 32 && d_rope == 32 && d_v == 64) shape_id = 1;
+    else if (d_nope == 64 && d_rope == 64 && d_v == 64) shape_id = 1;
     else return DSA_ERR_UNSUPPORTED;
     if ((int64_t)H * (d_nope + d_v) * 2 * 64 > INT32_MAX || (int64_t)kv_cols * 2 * 64 > INT32_MAX ||
         (int64_t)mask_words * 4 * 128 > INT32_MAX || ((int64_t)L + 127) / 128 * H > INT32_MAX)
@@ -330,7 +331,34 @@ dsa_status dsa_dense_masked_attn(const uint16_t* q, const uint16_t* kvb, const u
     if (st) return st;
     dsa::DenseArgs a{q, kvb, kv, mask, L, N, H, q_start, kv_cols, rope_col, mask_words,
                      (float)((double)scale * 1.4426950408889634), out};
-    return launched(dsa::launch_dense_attn(shape_id, a, (hipStream_t)stream));
+    return launched(dsa::launch_dense_attn(shape_id, a, values_f16, (hipStream_t)stream));
+}
+}  // namespace
+
+dsa_status dsa_dense_masked_attn(const uint16_t* q, const uint16_t* kvb, const uint16_t* kv, int32_t kv_cols,
+                                 int32_t rope_col, const uint32_t* mask, int32_t mask_words, int32_t L,
+                                 int32_t N, int32_t q_start, int32_t H, int32_t d_nope, int32_t d_rope,
+                                 int32_t d_v, float scale, float* out, void* stream) {
+    return dense_attn(q, kvb, kv, kv_cols, rope_col, mask, mask_words, L, N, q_start, H, d_nope, d_rope, d_v,
+                      scale, out, false, stream);
+}
+
+dsa_status dsa_dense_masked_attn_f16(const uint16_t* q, const uint16_t* kvb16, const uint16_t* kv, int32_t kv_cols,
+                                     int32_t rope_col, const uint32_t* mask, int32_t mask_words, int32_t L,
+                                     int32_t N, int32_t q_start, int32_t H, int32_t d_nope, int32_t d_rope,
+                                     int32_t d_v, float scale, float* out, void* stream) {
+    return dense_attn(q, kvb16, kv, kv_cols, rope_col, mask, mask_words, L, N, q_start, H, d_nope, d_rope, d_v,
+                      scale, out, true, stream);
+}
+
+dsa_status dsa_values_to_f16(uint16_t* kvb, int32_t N, int32_t H, int32_t d_nope, int32_t d_v, void* stream) {
+    if (!kvb || !aligned16(kvb) || N < 0 || H <= 0 || d_nope < 0 || d_v <= 0 || d_nope % 8 != 0 || d_v % 8 != 0)
+        return DSA_ERR_INVALID_ARG;
+    if ((int64_t)N * H * (d_v / 8) >= ((int64_t)1 << 40)) return DSA_ERR_UNSUPPORTED;
+    if (N == 0) return DSA_OK;
+    dsa_status st = check_device();
+    if (st) return st;
+    return launched(dsa::launch_values_to_f16(kvb, (int64_t)N * H, d_nope, d_v, (hipStream_t)stream));
 }
 
 dsa_status dsa_sparse_mla_attn_f16(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv16,

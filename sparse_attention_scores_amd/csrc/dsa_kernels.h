@@ -214,6 +214,8 @@ struct DenseArgs {
     float scale_log2;       // softmax_scale * log2(e)
     float* out;             // [L, H, Dv]
 };
-hipError_t launch_dense_attn(int shape_id, const DenseArgs& a, hipStream_t s);
+hipError_t launch_dense_attn(int shape_id, const DenseArgs& a, bool values_f16, hipStream_t s);
+// The value columns of kvb [rows, Dn + Dv] converted bf16 -> fp16 in place.
+hipError_t launch_values_to_f16(uint16_t* kvb, int64_t rows, int dn, int dv, hipStream_t s);
 
 }  // namespace dsa

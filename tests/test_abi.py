@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     assert sorted(dsa.EXPORTED_SYMBOLS) == names
     raw = ctypes.CDLL(dsa._build.LIB)
     for n in names:
@@ -162,10 +162,10 @@ def test_dense_validation():
     assert L.dsa_selection_mask(fake(), fake(), 8, 0, 300, 0, W, fake(), None) == INVALID
     assert L.dsa_selection_mask(fake(), fake(), 8, 64, 600000, 0, 2 * 9375, fake(), None) == UNSUPPORTED
     assert L.dsa_selection_mask(fake(), fake(), 0, 64, 300, 0, W, fake(), None) == OK
-    # dense attention: (Dn, Dr, Dv) = (32, 32, 64), rope at column 64 of 96
-    args = lambda **k: [k.get("q", fake()), k.get("kvb", fake()), k.get("kv", fake()), k.get("kv_cols", 96),
+    # dense attention: (Dn, Dr, Dv) = (64, 64, 64), rope at column 64 of 128
+    args = lambda **k: [k.get("q", fake()), k.get("kvb", fake()), k.get("kv", fake()), k.get("kv_cols", 128),
                         k.get("rope_col", 64), k.get("mask", fake()), k.get("W", W), k.get("Lq", 8),
-                        k.get("N", 300), k.get("q_start", 0), k.get("H", 4), k.get("dn", 32), k.get("dr", 32),
+                        k.get("N", 300), k.get("q_start", 0), k.get("H", 4), k.get("dn", 64), k.get("dr", 64),
                         k.get("dv", 64), k.get("scale", 0.0625), k.get("out", fake()), None]
     f = L.dsa_dense_masked_attn
     assert f(*args(Lq=0)) == OK
@@ -174,7 +174,7 @@ def test_dense_validation():
     assert f(*args(out=None)) == INVALID
     assert f(*args(W=W - 2)) == INVALID
     assert f(*args(rope_col=72)) == INVALID
-    assert f(*args(kv_cols=100)) == INVALID
+    assert f(*args(kv_cols=132)) == INVALID
     assert f(*args(N=0)) == INVALID
     assert f(*args(H=0)) == INVALID
     assert f(*args(q_start=-1)) == INVALID
@@ -182,4 +182,13 @@ def test_dense_validation():
     assert f(*args(scale=float("inf"))) == INVALID
     assert f(*args(dn=48, dr=16)) == UNSUPPORTED
     assert f(*args(dn=192, dr=64, dv=256, kv_cols=576, rope_col=512, Lq=0)) == OK
+    g = L.dsa_dense_masked_attn_f16
+    assert g(*args(Lq=0)) == OK
+    assert g(*args(W=W - 2)) == INVALID
+    assert g(*args(dn=32, dr=32)) == UNSUPPORTED
+    assert L.dsa_values_to_f16(None, 8, 4, 64, 64, None) == INVALID
+    assert L.dsa_values_to_f16(fake(0x1008), 8, 4, 64, 64, None) == INVALID
+    assert L.dsa_values_to_f16(fake(), 8, 4, 60, 64, None) == INVALID
+    assert L.dsa_values_to_f16(fake(), 8, 0, 64, 64, None) == INVALID
+    assert L.dsa_values_to_f16(fake(), 0, 4, 192, 256, None) == OK
 

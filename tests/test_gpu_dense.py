@@ -1,8 +1,10 @@
 """GPU parity of the dense masked path (dsa_selection_mask,
-dsa_dense_masked_attn) against the CPU oracle on the same seeded inputs and
+dsa_dense_masked_attn, dsa_values_to_f16 + dsa_dense_masked_attn_f16) against the CPU oracle on the same seeded inputs and
 the same selection (the oracle's top-k of seeded indexer scores).
 
 - selection mask: integer work, bit-exact over every row;
+- value conversion: bit-exact against numpy's round-to-nearest-even
+  float32 -> float16 of the decoded bf16 values (key columns untouched);
 - attention: max over (query, head) rows of max|o - r| / max|r| <= 2e-3.
   The GPU sums bf16 products in fp32, rounds the probabilities to fp16
   (relative 2^-11) and converts the values to fp16 (exact here); the oracle
@@ -57,6 +59,21 @@ def run(cfg, empty_rows=(), rows=None):
     assert err <= ATTN_TOL, err
     for r in empty_rows:
         assert not got[r].any()
+    # the fp16-value entry on the same inputs: values converted in place first
+    kvb16 = dev(d["kvb"])
+    dsa.dsa_values_to_f16(kvb16, cfg.N, cfg.H, cfg.Dn, cfg.Dv)
+    conv = host(kvb16)
+    want = W.bf16_bits_to_f32(d["kvb"][..., cfg.Dn:]).astype(np.float16).view(np.uint16)
+    assert np.array_equal(conv[..., :cfg.Dn], d["kvb"][..., :cfg.Dn])
+    assert np.array_equal(conv[..., cfg.Dn:], want)
+    out16 = torch.empty_like(out)
+    dsa.dsa_dense_masked_attn_f16(dev(d["q"]), kvb16, dev(d["kv"]), cfg.Dl + cfg.Dr, cfg.Dl, mask,
+                                  cfg.L, cfg.N, cfg.q_start, cfg.H, cfg.Dn, cfg.Dr, cfg.Dv, 1.0 / 16, out16)
+    got16 = host(out16)
+    err16 = row_rel_err(got16[rows], ref)
+    assert err16 <= ATTN_TOL, err16
+    for r in empty_rows:
+        assert not got16[r].any()
     return got
 
 
@@ -81,15 +98,15 @@ def test_dense_rejects_bad_arguments():
     import torch
     import sparse_attention_scores_amd as dsa
     cfg = W.DENSE["tiny"]
-    q = torch.zeros((cfg.L, cfg.H, 64), dtype=torch.int16, device="cuda")
-    kvb = torch.zeros((cfg.N, cfg.H, 96), dtype=torch.int16, device="cuda")
-    kv = torch.zeros((cfg.N, 96), dtype=torch.int16, device="cuda")
+    q = torch.zeros((cfg.L, cfg.H, 128), dtype=torch.int16, device="cuda")
+    kvb = torch.zeros((cfg.N, cfg.H, 128), dtype=torch.int16, device="cuda")
+    kv = torch.zeros((cfg.N, 128), dtype=torch.int16, device="cuda")
     mask = torch.zeros((cfg.L, dsa.mask_words(cfg.N)), dtype=torch.int32, device="cuda")
     out = torch.empty((cfg.L, cfg.H, 64), dtype=torch.float32, device="cuda")
     say("dense argument checks")
     with pytest.raises(dsa.DsaError):   # unsupported widths
-        dsa.dsa_dense_masked_attn(q, kvb, kv, 96, 64, mask, cfg.L, cfg.N, 0, cfg.H, 48, 16, 64, 0.0625, out)
+        dsa.dsa_dense_masked_attn(q, kvb, kv, 128, 64, mask, cfg.L, cfg.N, 0, cfg.H, 48, 16, 64, 0.0625, out)
     with pytest.raises(dsa.DsaError):   # mask rows too short for N
-        dsa.dsa_dense_masked_attn(q, kvb, kv, 96, 64, mask[:, :2].contiguous(), cfg.L, cfg.N, 0, cfg.H, 32, 32, 64, 0.0625, out)
+        dsa.dsa_dense_masked_attn(q, kvb, kv, 128, 64, mask[:, :2].contiguous(), cfg.L, cfg.N, 0, cfg.H, 64, 64, 64, 0.0625, out)
     with pytest.raises(dsa.DsaError):   # rope key past the cache row
-        dsa.dsa_dense_masked_attn(q, kvb, kv, 96, 72, mask, cfg.L, cfg.N, 0, cfg.H, 32, 32, 64, 0.0625, out)
+        dsa.dsa_dense_masked_attn(q, kvb, kv, 128, 72, mask, cfg.L, cfg.N, 0, cfg.H, 64, 64, 64, 0.0625, out)

@@ -331,8 +331,8 @@ DENSE: Dict[str, Dense] = {
     "glm_8k_chunk": Dense("glm_8k_chunk", 4096, 8192, 4096, 61),
     "glm_4k_first": Dense("glm_4k_first", 4096, 4096, 0, 62),
     "glm_small": Dense("glm_small", 160, 700, 540, 63, top_k=128),
-    "tiny": Dense("tiny", 200, 300, 100, 64, H=4, Dn=32, Dr=32, Dv=64, Dl=64, top_k=64),
-    "tiny_first": Dense("tiny_first", 150, 150, 0, 65, H=3, Dn=32, Dr=32, Dv=64, Dl=64, top_k=64),
+    "tiny": Dense("tiny", 200, 300, 100, 64, H=4, Dn=64, Dr=64, Dv=64, Dl=64, top_k=64),
+    "tiny_first": Dense("tiny_first", 150, 150, 0, 65, H=3, Dn=64, Dr=64, Dv=64, Dl=64, top_k=64),
 }
 
 
