@@ -14,6 +14,7 @@ the timed region starts.  One JSON line is printed on stdout.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -34,6 +35,7 @@ KERNEL_SOURCES = {
     "indexer": "sparse_attention_scores_amd/csrc/indexer.hip",
     "topk": "sparse_attention_scores_amd/csrc/topk.hip",
     "cache_write": "sparse_attention_scores_amd/csrc/cache_write.hip",
+    "dense": "sparse_attention_scores_amd/csrc/dense.hip",
 }
 CACHE_WRITE = "glm_16k_chunk"
 
@@ -60,13 +62,14 @@ def measured_traffic(stage: str):
     return t.get("bytes_per_launch")
 
 
-PROFILE_STAGES = ("prefill", "indexer", "topk", "attention", "decode", "cache_write", "copy")
+PROFILE_STAGES = ("prefill", "indexer", "topk", "attention", "decode", "cache_write", "dense", "copy")
 COPY_BYTES = 1 << 30            # plain copy used to scale the HBM byte counters
 STAGE_KERNELS = {
     "attention": "attention_kernel<",
     "indexer": "indexer_prefill_kernel<",
     "topk": "topk_prefill_kernel<",
     "cache_write": "cache_write_kernel<",
+    "dense": "dense_attn_kernel<192, 64, 256, true>",
 }
 
 
@@ -87,6 +90,98 @@ def cache_write_setup(np, torch, dsa, W):
     return cw, f, per_token * cw.T + 4 * sh.d_latent
 
 
+DENSE = "glm_8k_chunk"
+
+
+def dense_setup(np, torch, dsa, W, cfg):
+    """Device inputs of a dense-path chunk and calls that run its steps: the
+    selection (the library's top-k of the workload's seeded indexer scores),
+    the selection mask, the in-place value conversion and the two attention
+    entries.  Also the chunk's algorithmic work: dense flops over every
+    causal key, and bytes of the mask and conversion passes."""
+    d = W.make_dense(cfg)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else a).cuda()
+    t = {k: to(d[k]) for k in ("q", "kvb", "kv", "S")}
+    sh = dataclasses.replace(W.GLM, top_k=cfg.top_k)
+    idx = torch.empty((cfg.L, cfg.top_k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((cfg.L,), dtype=torch.int32, device="cuda")
+    dsa.dsa_topk_select(sh, t["S"], cfg.L, cfg.N, cfg.q_start, idx, cnt)
+    del t["S"]
+    mask = torch.empty((cfg.L, dsa.mask_words(cfg.N)), dtype=torch.int32, device="cuda")
+    kvb16 = t["kvb"].clone()
+    out = torch.empty((cfg.L, cfg.H, cfg.Dv), dtype=torch.float32, device="cuda")
+    kc, rc = cfg.Dl + cfg.Dr, cfg.Dl
+    args = lambda kvb: (t["q"], kvb, t["kv"], kc, rc, mask, cfg.L, cfg.N, cfg.q_start, cfg.H, cfg.Dn, cfg.Dr,
+                        cfg.Dv, 1.0 / 16, out)
+    f = {"mask": lambda: dsa.dsa_selection_mask(idx, cnt, cfg.L, cfg.top_k, cfg.N, cfg.q_start, mask),
+         "convert": lambda: dsa.dsa_values_to_f16(kvb16, cfg.N, cfg.H, cfg.Dn, cfg.Dv),
+         "attn_f16": lambda: dsa.dsa_dense_masked_attn_f16(*args(kvb16)),
+         "attn_bf16": lambda: dsa.dsa_dense_masked_attn(*args(t["kvb"]))}
+    visible = sum(min(p + 1, cfg.N) for p in range(cfg.q_start, cfg.q_start + cfg.L))
+    work = {"flop": 2.0 * cfg.H * (cfg.Dn + cfg.Dr + cfg.Dv) * visible,
+            "mask_bytes": 4 * cfg.L * cfg.top_k + 4 * cfg.L + 4 * cfg.L * mask.shape[1],
+            "convert_bytes": 2 * 2 * cfg.N * cfg.H * cfg.Dv}
+    return f, work, (t, idx, cnt, mask, kvb16, out)
+
+
+def crossover(np, torch, dsa, W, reps: int) -> int:
+    """Dense masked (non-absorbed) against sparse (absorbed) attention of a
+    4096-query chunk at the end of N keys of context, one JSON line per N.
+    sparse: indexer, top-k, latent -> fp16, gathered attention, value
+    up-projection; dense: the same indexer and top-k, the selection mask,
+    value -> fp16, dense attention.  Not timed on either side: the key
+    up-projection kv_b of every key (dense) and the query absorption
+    (sparse), for which this library has no entry point; their flops are
+    given."""
+    base = W.PREFILL["glm_8k"]
+    pc = W.PROJ["glm_16k_chunk"]
+    wv = torch.from_numpy(W.make_proj(pc)["wv"].view(np.int16)).cuda()
+    for N in (4096, 6144, 8192, 10240, 12288, 16384):
+        L = 4096
+        cfg = dataclasses.replace(base, q_start=N - L)
+        sh = cfg.shape
+        d = W.make_prefill(cfg)
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else a).cuda()
+        q, qI, w, kv, kI = (to(d[k]) for k in ("q", "qI", "w", "kv", "kI"))
+        del d
+        S = torch.empty((L, N), dtype=torch.float32, device="cuda")
+        idx = torch.empty((L, sh.top_k), dtype=torch.int32, device="cuda")
+        cnt = torch.empty((L,), dtype=torch.int32, device="cuda")
+        kv16 = torch.empty_like(kv)
+        o = torch.empty((L, sh.n_heads, sh.d_latent), dtype=torch.float32, device="cuda")
+        ov = torch.empty((L, sh.n_heads, 256), dtype=torch.int16, device="cuda")
+        sp = {"indexer": lambda: dsa.dsa_indexer_scores(sh, qI, kI, w, L, N, cfg.q_start, S),
+              "topk": lambda: dsa.dsa_topk_select(sh, S, L, N, cfg.q_start, idx, cnt),
+              "latent_f16": lambda: dsa.dsa_latent_to_f16(sh, kv, N, kv16),
+              "attention": lambda: dsa.dsa_sparse_mla_attn_f16(sh, q, kv16, idx, cnt, L, N, o, None),
+              "value_up_proj": lambda: dsa.dsa_value_up_proj(sh, o, wv, L, 256, ov)}
+        ts = {}
+        for k, f in sp.items():
+            f()
+            torch.cuda.synchronize()
+            ts[k] = timed_events(f, reps, torch) * 1e6
+        del q, qI, w, kI, kv16, o, ov
+        dc = W.Dense("crossover", L, N, N - L, 0)
+        fd, work, keep = dense_setup(np, torch, dsa, W, dc)
+        td = {}
+        for k in ("mask", "convert", "attn_f16"):
+            fd[k]()
+            torch.cuda.synchronize()
+            td[k] = timed_events(fd[k], reps, torch) * 1e6
+        del keep, fd, S, idx, cnt, kv
+        torch.cuda.empty_cache()
+        sparse_us = sum(ts.values())
+        dense_us = ts["indexer"] + ts["topk"] + td["mask"] + td["convert"] + td["attn_f16"]
+        print(json.dumps({"crossover_keys": N, "queries": L, "sparse_us": round(sparse_us, 1),
+                          "dense_us": round(dense_us, 1), "sparse": {k: round(v, 1) for k, v in ts.items()},
+                          "dense": {k: round(v, 1) for k, v in td.items()},
+                          "dense_attn_tflops": round(work["flop"] / td["attn_f16"] / 1e6, 1),
+                          "untimed_gflop": {"kv_b_all_keys": round(2.0 * N * 512 * 64 * 448 / 1e9, 1),
+                                            "q_absorption": round(2.0 * L * 64 * 192 * 512 / 1e9, 1)}}),
+              flush=True)
+    return 0
+
+
 def profile_stage(stage, reps, np, torch, dsa, W) -> int:
     """Run one stage of the headline chunk reps times and nothing else that
     matters (inputs are generated first).  `copy` runs a plain device copy of
@@ -98,6 +193,15 @@ def profile_stage(stage, reps, np, torch, dsa, W) -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         log("copy done", reps)
+        return 0
+    if stage == "dense":
+        f, _, keep = dense_setup(np, torch, dsa, W, W.DENSE[DENSE])
+        f["convert"]()
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            f["attn_f16"]()
+        torch.cuda.synchronize()
+        log("dense done", reps)
         return 0
     if stage == "cache_write":
         _, f, _ = cache_write_setup(np, torch, dsa, W)
@@ -242,6 +346,8 @@ def main() -> int:
                     help="turn FETCH_SIZE/WRITE_SIZE counter CSVs in DIR into profiles/traffic.json")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-stages", action="store_true")
+    ap.add_argument("--crossover", action="store_true",
+                    help="dense masked against sparse attention over a range of context lengths (JSON lines)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path (a chunk would shard by "
@@ -261,6 +367,8 @@ def main() -> int:
     K, Wm = args.steps, args.warmup
     if args.profile_stage:
         return profile_stage(args.profile_stage, K, np, torch, dsa, W)
+    if args.crossover:
+        return crossover(np, torch, dsa, W, max(K // 4, 3))
 
     # ---------------- prefill chunk (headline) ----------------
     cfg = W.PREFILL[PREFILL]
@@ -387,6 +495,30 @@ def main() -> int:
                             "tflops": op_flop / t_op / 1e12, "frac": op_flop / t_op / 1e12 / PEAK_MFMA_TFLOPS,
                             "workload": "[%d x %d] bf16 x [%d x %d]^T bf16 -> fp32" % (pc.T, pc.H * pc.Dv, pc.hidden, pc.H * pc.Dv)}
         del p_o, p_wv, p_wo, p_x, p_out, p_y
+        log("dense-path stages")
+        dcfg = W.DENSE[DENSE]
+        fd, dwork, keep = dense_setup(np, torch, dsa, W, dcfg)
+        td = {}
+        for k in ("mask", "convert", "attn_f16", "attn_bf16"):
+            fd[k]()
+            torch.cuda.synchronize()
+            td[k] = timed_events(fd[k], max(n // 2, 3), torch)
+        dwl = "%d queries at %d..%d over %d keys, %d heads, scores %d+%d, values %d, top_k %d" % (
+            dcfg.L, dcfg.q_start, dcfg.q_start + dcfg.L - 1, dcfg.N, dcfg.H, dcfg.Dn, dcfg.Dr, dcfg.Dv, dcfg.top_k)
+        stages["selection_mask"] = {"kernel": "selection_mask_kernel", "us": td["mask"] * 1e6,
+                                    "gbps": dwork["mask_bytes"] / td["mask"] / 1e9,
+                                    "frac": dwork["mask_bytes"] / td["mask"] / 1e9 / PEAK_HBM_GBPS, "workload": dwl}
+        stages["values_to_f16"] = {"kernel": "values_to_f16_kernel", "us": td["convert"] * 1e6,
+                                   "gbps": dwork["convert_bytes"] / td["convert"] / 1e9,
+                                   "frac": dwork["convert_bytes"] / td["convert"] / 1e9 / PEAK_HBM_GBPS,
+                                   "workload": dwl}
+        for k, kern in (("attn_f16", "dense_attn_kernel<192,64,256,true>"),
+                        ("attn_bf16", "dense_attn_kernel<192,64,256,false>")):
+            tf = dwork["flop"] / td[k] / 1e12
+            stages["dense_" + k] = {"kernel": kern, "us": td[k] * 1e6, "tflops": tf, "frac": tf / PEAK_MFMA_TFLOPS,
+                                    "traffic": measured_traffic("dense") if k == "attn_f16" else None,
+                                    "workload": dwl + " (flops over every causal key)"}
+        del keep, fd
         result["stages"] = stages
         dom = max(("indexer", t_idx), ("topk", t_topk), ("attention", t_attn), key=lambda x: x[1])[0]
         if dom == "topk":
