@@ -50,12 +50,13 @@ def _configure(lib):
     lib.oracle_value_up_proj.argtypes = [P, P, i64, i32, i32, i32, P]
     lib.oracle_o_proj.argtypes = [P, P, i64, i32, i32, P, i64, P]
     lib.oracle_selection_mask.argtypes = [P, P, i64, i32, i64, i64, i64, P]
+    lib.oracle_kv_b_proj.argtypes = [P, i32, P, i64, i32, i32, i32, i32, i32, P]
     lib.oracle_dense_masked_attn.argtypes = [P, P, P, P, i64, i64, i32, i32, i32, i32, i32, i32, i64,
                                              dbl, P, i64, P, i32]
     for f in (lib.oracle_indexer_scores, lib.oracle_topk_select, lib.oracle_sparse_mla_attn,
               lib.oracle_prefill_chunk, lib.oracle_decode_step, lib.oracle_cache_write,
               lib.oracle_router_topk, lib.oracle_value_up_proj, lib.oracle_o_proj,
-              lib.oracle_selection_mask, lib.oracle_dense_masked_attn):
+              lib.oracle_selection_mask, lib.oracle_dense_masked_attn, lib.oracle_kv_b_proj):
         f.restype = ctypes.c_int
     return lib
 
@@ -261,3 +262,16 @@ def dense_masked_attn(q, kvb, kv, mask, d_nope: int, d_rope: int, d_v: int, rope
                                             Dc, rope_col, mask.shape[1], scale, _p(rows), rows.size, _p(out),
                                             nthreads or default_threads()), "dense attention")
     return out
+
+
+def kv_b_proj(kv, w, H: int, d_latent: int, d_nope: int, d_v: int, values_f16: bool) -> np.ndarray:
+    """kvb [N, H, d_nope + d_v] as uint16 bits: bf16 no-rope keys, and values
+    in bf16 or (values_f16) fp16."""
+    kv, w = _c(kv, np.uint16), _c(w, np.uint16)
+    N, kv_cols = kv.shape
+    assert w.shape == (H * (d_nope + d_v), d_latent)
+    out = np.empty((N, H, d_nope + d_v), dtype=np.uint16)
+    _check(_load().oracle_kv_b_proj(_p(kv), kv_cols, _p(w), N, H, d_latent, d_nope, d_v, int(values_f16), _p(out)),
+           "kv_b")
+    return out
+

@@ -669,3 +669,55 @@ int oracle_dense_masked_attn(const uint16_t* q, const uint16_t* kvb, const uint1
     dense_ctx x = {q, kvb, kv, mask, N, W, H, Dn, Dr, Dv, Dc, rope_col, scale, rows, out};
     return parallel_rows(dense_task, &x, nrows, nthreads, (size_t)N * sizeof(double));
 }
+
+/* ==========================================================================
+ * The kv_b up-projection of the dense path (pipeline trace, section 4: the
+ * kv_b projection of the normalised latent gives, per head, the no-rope key
+ * and the value; config line: qk_nope 192, v_head_dim 256).  Readings: the
+ * weight is stored [H * (Dn + Dv), Dl] ([out, in]); the latent is the first
+ * Dl columns of each cache row; the sums are exact here (double) and each
+ * result is rounded once, to bf16 for the no-rope key columns and, when
+ * values_f16 is set, to fp16 for the value columns (the form the dense
+ * attention's value product reads).
+ * ======================================================================== */
+
+/* double -> IEEE binary16 bits, round to nearest with ties to even;
+ * magnitudes from 65520 up become infinities. */
+static uint16_t double_to_f16(double v) {
+    const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    const double a = fabs(v);
+    if (a == 0.0) return sign;
+    int e;
+    const double m = frexp(a, &e);                 /* a = m * 2^e, m in [0.5, 1) */
+    int E = e - 1;                                  /* a = (2m) * 2^E */
+    if (E < -14) {                                  /* subnormal: spacing 2^-24 */
+        const double n = nearbyint(ldexp(a, 24));   /* 1024 lands on the smallest normal */
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    double n = nearbyint(ldexp(m, 11));             /* 11 significant bits, in [1024, 2048] */
+    if (n == 2048.0) { n = 1024.0; ++E; }
+    if (E > 15) return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(n - 1024.0));
+}
+
+/* kvb[j, h, c] = round( sum_d kv[j, d] * w[h * (Dn + Dv) + c, d] ),  d < Dl. */
+int oracle_kv_b_proj(const uint16_t* kv, int32_t kv_cols, const uint16_t* w, int64_t N, int32_t H,
+                     int32_t Dl, int32_t Dn, int32_t Dv, int32_t values_f16, uint16_t* kvb) {
+    if (!kv || !w || !kvb || N < 0 || H <= 0 || Dl <= 0 || Dl > kv_cols || Dn < 0 || Dv <= 0) return -1;
+    const int32_t C = Dn + Dv;
+    double* x = (double*)malloc((size_t)Dl * sizeof(double));
+    if (!x) return -8;
+    for (int64_t j = 0; j < N; ++j) {
+        for (int32_t d = 0; d < Dl; ++d) x[d] = bf16_to_double(kv[j * kv_cols + d]);
+        for (int32_t h = 0; h < H; ++h) {
+            for (int32_t c = 0; c < C; ++c) {
+                const uint16_t* wrow = w + ((int64_t)h * C + c) * Dl;
+                double acc = 0.0;
+                for (int32_t d = 0; d < Dl; ++d) acc += x[d] * bf16_to_double(wrow[d]);
+                kvb[(j * H + h) * C + c] = (values_f16 && c >= Dn) ? double_to_f16(acc) : double_to_bf16(acc);
+            }
+        }
+    }
+    free(x);
+    return 0;
+}

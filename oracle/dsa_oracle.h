@@ -133,6 +133,13 @@ int oracle_dense_masked_attn(const uint16_t* q, const uint16_t* kvb, const uint1
                              double scale, const int64_t* rows, int64_t nrows, double* out,
                              int32_t nthreads);
 
+/* The dense path's kv_b up-projection: kvb[j, h, c] = round(sum_d kv[j, d] *
+ * w[h*(Dn+Dv) + c, d]) over the first Dl columns of each cache row (row
+ * stride kv_cols); bf16 for c < Dn, and for c >= Dn too unless values_f16,
+ * which rounds the value columns to fp16 instead (nearest even). */
+int oracle_kv_b_proj(const uint16_t* kv, int32_t kv_cols, const uint16_t* w, int64_t N, int32_t H,
+                     int32_t Dl, int32_t Dn, int32_t Dv, int32_t values_f16, uint16_t* kvb);
+
 #ifdef __cplusplus
 }
 #endif

@@ -787,4 +787,66 @@ def pin_dense_closed_forms():
     assert np.allclose(out[2], want, rtol=1e-12, atol=1e-12)
 
 
+def _f16_bits_to_f64(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def pin_kv_b_f16_rounding_closed_forms():
+    """One-hot weights copy a latent value: bf16 keys unchanged, values as
+    numpy's float16 of it; sums that land between fp16 neighbours round to
+    nearest with ties to even (1 + 2^-11 -> 1, 1 + 3*2^-11 -> 1 + 2^-9,
+    65504 + 16 -> inf, 2^-25 + 2^-26 -> the smallest subnormal 2^-24)."""
+    N, H, Dl, Dn, Dv = 3, 2, 64, 8, 8
+    rng = np.random.default_rng(31)
+    kv = _bf(rng.standard_normal((N, Dl + 16)).astype(np.float32))
+    w = np.zeros((H * (Dn + Dv), Dl), np.uint16)
+    cols = rng.integers(0, Dl, size=H * (Dn + Dv))
+    w[np.arange(H * (Dn + Dv)), cols] = 0x3F80
+    for f16 in (False, True):
+        out = oracle.kv_b_proj(kv, w, H, Dl, Dn, Dv, f16).reshape(N, H * (Dn + Dv))
+        lat = kv[:, cols].reshape(N, H, Dn + Dv)
+        got = out.reshape(N, H, Dn + Dv)
+        assert np.array_equal(got[..., :Dn], lat[..., :Dn])
+        want_v = W.bf16_bits_to_f32(lat[..., Dn:]).astype(np.float16).view(np.uint16) if f16 else lat[..., Dn:]
+        assert np.array_equal(got[..., Dn:], want_v)
+    # two-term sums around fp16 rounding points (value column 0 of head 0)
+    cases = [(1.0, 2.0 ** -11, 1.0), (1.0, 3 * 2.0 ** -11, 1.0 + 2.0 ** -9), (65504.0, 16.0, np.inf),
+             (2.0 ** -25, 2.0 ** -26, 2.0 ** -24), (-1.0, -(2.0 ** -11), -1.0)]
+    for a, b, want in cases:
+        kv2 = np.zeros((1, Dl), np.uint16)
+        kv2[0, 0], kv2[0, 1] = _bf(np.float32(a)), _bf(np.float32(b))
+        w2 = np.zeros((Dn + Dv, Dl), np.uint16)
+        w2[Dn, 0] = w2[Dn, 1] = 0x3F80
+        got = _f16_bits_to_f64(oracle.kv_b_proj(kv2, w2, 1, Dl, Dn, Dv, True)[0, 0, Dn])
+        assert got == want, (a, b, got, want)
+
+
+def pin_kv_b_matches_numpy():
+    """Random bf16 latent rows and weights: every output within half a unit
+    of its format (bf16 keys, fp16 or bf16 values) of numpy's float64
+    product; integer data gives the exact sums."""
+    rng = np.random.default_rng(32)
+    N, H, Dl, Dn, Dv, kc = 7, 3, 64, 16, 24, 80
+    kv = _bf(rng.standard_normal((N, kc)).astype(np.float32))
+    w = _bf((rng.standard_normal((H * (Dn + Dv), Dl)) / 8).astype(np.float32))
+    ref = (_f(kv)[:, :Dl] @ _f(w).T).reshape(N, H, Dn + Dv)
+    for f16 in (False, True):
+        got = oracle.kv_b_proj(kv, w, H, Dl, Dn, Dv, f16)
+        k = _f(got[..., :Dn])
+        assert np.all(np.abs(k - ref[..., :Dn]) <= _half_ulp_bf16(ref[..., :Dn]) * 1.0000001 + 1e-30)
+        if f16:
+            v = _f16_bits_to_f64(got[..., Dn:])
+            r = ref[..., Dn:]
+            ulp = np.spacing(np.abs(r).astype(np.float16)).astype(np.float64)
+            assert np.all(np.abs(v - r) <= ulp / 2 * 1.0000001 + 2.0 ** -25)
+        else:
+            assert np.all(np.abs(_f(got[..., Dn:]) - ref[..., Dn:]) <= _half_ulp_bf16(ref[..., Dn:]) * 1.0000001 + 1e-30)
+    lat = rng.integers(-2, 3, size=(N, Dl))
+    wi = rng.integers(-1, 2, size=(H * (Dn + Dv), Dl))
+    got = oracle.kv_b_proj(_bf(lat), _bf(wi), H, Dl, Dn, Dv, True)
+    exact = (lat @ wi.T).reshape(N, H, Dn + Dv)
+    assert np.array_equal(_f(got[..., :Dn]), exact[..., :Dn])
+    assert np.array_equal(_f16_bits_to_f64(got[..., Dn:]), exact[..., Dn:])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

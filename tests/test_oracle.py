@@ -94,6 +94,12 @@ MUTATIONS = [
     ("mask keeps non-causal keys", "if (j >= 0 && j < N && j <= p) row[j / 32]", "if (j >= 0 && j < N) row[j / 32]"),
     ("mask ignores count", "for (int32_t t = 0; t < c; ++t) {\n            const int64_t j = idx[i * top_k + t];",
      "for (int32_t t = 0; t < top_k; ++t) {\n            const int64_t j = idx[i * top_k + t];"),
+    ("kv_b weight read transposed", "const uint16_t* wrow = w + ((int64_t)h * C + c) * Dl;\n                double acc = 0.0;\n                for (int32_t d = 0; d < Dl; ++d) acc += x[d] * bf16_to_double(wrow[d]);",
+     "const uint16_t* wrow = w + ((int64_t)h * C + c) * Dl;\n                double acc = 0.0;\n                for (int32_t d = 0; d < Dl; ++d) acc += x[d] * bf16_to_double(w[((int64_t)h * C + (d % C)) * Dl + (c % Dl)]);"),
+    ("kv_b values left in bf16", "(values_f16 && c >= Dn) ? double_to_f16(acc) : double_to_bf16(acc)", "double_to_bf16(acc)"),
+    ("fp16 rounding truncates", "double n = nearbyint(ldexp(m, 11));", "double n = floor(ldexp(m, 11));"),
+    ("fp16 subnormals flushed", "const double n = nearbyint(ldexp(a, 24));   /* 1024 lands on the smallest normal */",
+     "const double n = 0.0;"),
 ]
 
 _RUNNER = r"""
