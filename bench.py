@@ -109,19 +109,23 @@ def dense_setup(np, torch, dsa, W, cfg):
     del t["S"]
     mask = torch.empty((cfg.L, dsa.mask_words(cfg.N)), dtype=torch.int32, device="cuda")
     kvb16 = t["kvb"].clone()
+    wkvb = torch.from_numpy(W.make_kvb_weight(cfg).view(np.int16)).cuda()
+    kvb_out = torch.empty_like(t["kvb"])
     out = torch.empty((cfg.L, cfg.H, cfg.Dv), dtype=torch.float32, device="cuda")
     kc, rc = cfg.Dl + cfg.Dr, cfg.Dl
     args = lambda kvb: (t["q"], kvb, t["kv"], kc, rc, mask, cfg.L, cfg.N, cfg.q_start, cfg.H, cfg.Dn, cfg.Dr,
                         cfg.Dv, 1.0 / 16, out)
     f = {"mask": lambda: dsa.dsa_selection_mask(idx, cnt, cfg.L, cfg.top_k, cfg.N, cfg.q_start, mask),
          "convert": lambda: dsa.dsa_values_to_f16(kvb16, cfg.N, cfg.H, cfg.Dn, cfg.Dv),
+         "kv_b": lambda: dsa.dsa_kv_b_proj(t["kv"], kc, wkvb, cfg.N, cfg.H, cfg.Dl, cfg.Dn, cfg.Dv, True, kvb_out),
          "attn_f16": lambda: dsa.dsa_dense_masked_attn_f16(*args(kvb16)),
          "attn_bf16": lambda: dsa.dsa_dense_masked_attn(*args(t["kvb"]))}
     visible = sum(min(p + 1, cfg.N) for p in range(cfg.q_start, cfg.q_start + cfg.L))
     work = {"flop": 2.0 * cfg.H * (cfg.Dn + cfg.Dr + cfg.Dv) * visible,
             "mask_bytes": 4 * cfg.L * cfg.top_k + 4 * cfg.L + 4 * cfg.L * mask.shape[1],
-            "convert_bytes": 2 * 2 * cfg.N * cfg.H * cfg.Dv}
-    return f, work, (t, idx, cnt, mask, kvb16, out)
+            "convert_bytes": 2 * 2 * cfg.N * cfg.H * cfg.Dv,
+            "kv_b_flop": 2.0 * cfg.N * cfg.Dl * cfg.H * (cfg.Dn + cfg.Dv)}
+    return f, work, (t, idx, cnt, mask, kvb16, out, wkvb, kvb_out)
 
 
 def crossover(np, torch, dsa, W, reps: int) -> int:
@@ -129,10 +133,9 @@ def crossover(np, torch, dsa, W, reps: int) -> int:
     4096-query chunk at the end of N keys of context, one JSON line per N.
     sparse: indexer, top-k, latent -> fp16, gathered attention, value
     up-projection; dense: the same indexer and top-k, the selection mask,
-    value -> fp16, dense attention.  Not timed on either side: the key
-    up-projection kv_b of every key (dense) and the query absorption
-    (sparse), for which this library has no entry point; their flops are
-    given."""
+    the kv_b up-projection of every key (values written as fp16), dense
+    attention.  Not timed: the sparse side's query absorption, for which
+    this library has no entry point; its flops are given."""
     base = W.PREFILL["glm_8k"]
     pc = W.PROJ["glm_16k_chunk"]
     wv = torch.from_numpy(W.make_proj(pc)["wv"].view(np.int16)).cuda()
@@ -164,20 +167,20 @@ def crossover(np, torch, dsa, W, reps: int) -> int:
         dc = W.Dense("crossover", L, N, N - L, 0)
         fd, work, keep = dense_setup(np, torch, dsa, W, dc)
         td = {}
-        for k in ("mask", "convert", "attn_f16"):
+        for k in ("mask", "kv_b", "attn_f16"):
             fd[k]()
             torch.cuda.synchronize()
             td[k] = timed_events(fd[k], reps, torch) * 1e6
         del keep, fd, S, idx, cnt, kv
         torch.cuda.empty_cache()
         sparse_us = sum(ts.values())
-        dense_us = ts["indexer"] + ts["topk"] + td["mask"] + td["convert"] + td["attn_f16"]
+        dense_us = ts["indexer"] + ts["topk"] + td["mask"] + td["kv_b"] + td["attn_f16"]
         print(json.dumps({"crossover_keys": N, "queries": L, "sparse_us": round(sparse_us, 1),
                           "dense_us": round(dense_us, 1), "sparse": {k: round(v, 1) for k, v in ts.items()},
                           "dense": {k: round(v, 1) for k, v in td.items()},
                           "dense_attn_tflops": round(work["flop"] / td["attn_f16"] / 1e6, 1),
-                          "untimed_gflop": {"kv_b_all_keys": round(2.0 * N * 512 * 64 * 448 / 1e9, 1),
-                                            "q_absorption": round(2.0 * L * 64 * 192 * 512 / 1e9, 1)}}),
+                          "kv_b_tflops": round(work["kv_b_flop"] / td["kv_b"] / 1e6, 1),
+                          "untimed_gflop": {"q_absorption": round(2.0 * L * 64 * 192 * 512 / 1e9, 1)}}),
               flush=True)
     return 0
 
@@ -499,7 +502,7 @@ def main() -> int:
         dcfg = W.DENSE[DENSE]
         fd, dwork, keep = dense_setup(np, torch, dsa, W, dcfg)
         td = {}
-        for k in ("mask", "convert", "attn_f16", "attn_bf16"):
+        for k in ("mask", "convert", "kv_b", "attn_f16", "attn_bf16"):
             fd[k]()
             torch.cuda.synchronize()
             td[k] = timed_events(fd[k], max(n // 2, 3), torch)
@@ -512,6 +515,11 @@ def main() -> int:
                                    "gbps": dwork["convert_bytes"] / td["convert"] / 1e9,
                                    "frac": dwork["convert_bytes"] / td["convert"] / 1e9 / PEAK_HBM_GBPS,
                                    "workload": dwl}
+        tk = dwork["kv_b_flop"] / td["kv_b"] / 1e12
+        stages["kv_b_proj"] = {"kernel": "gemm_nt_kernel<false,false,256>", "us": td["kv_b"] * 1e6, "tflops": tk,
+                               "frac": tk / PEAK_MFMA_TFLOPS,
+                               "workload": "%d latent rows [%d] -> %d heads x [%d key bf16 | %d value fp16]" % (
+                                   dcfg.N, dcfg.Dl, dcfg.H, dcfg.Dn, dcfg.Dv)}
         for k, kern in (("attn_f16", "dense_attn_kernel<192,64,256,true>"),
                         ("attn_bf16", "dense_attn_kernel<192,64,256,false>")):
             tf = dwork["flop"] / td[k] / 1e12

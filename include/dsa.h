@@ -304,6 +304,25 @@ dsa_status dsa_dense_masked_attn_f16(const uint16_t* q, const uint16_t* kvb16, c
  * multiples of 8. */
 dsa_status dsa_values_to_f16(uint16_t* kvb, int32_t N, int32_t H, int32_t d_nope, int32_t d_v, void* stream);
 
+/* kv_b up-projection of the latent rows for the dense path ("GLM-5.2-Vision:
+ * llama.cpp vs vLLM line-by-line pipeline trace", section 4: the kv_b
+ * projection of the normalised latent gives each head's no-rope key and
+ * value; config line: qk_nope 192, v_head_dim 256):
+ *   kvb[j, h, c] = sum_d kv[j, d] * wkvb[h * (d_nope + d_v) + c, d],  d < d_latent
+ * kv [dev] [N, kv_cols] bf16 (the cache rows; the latent is their first
+ * d_latent columns); wkvb [dev] [H * (d_nope + d_v), d_latent] bf16 (stored
+ * [out, in]); kvb [dev] [N, H, d_nope + d_v]: bf16 no-rope keys, and values
+ * in bf16, or in fp16 when values_f16 = 1 (the form
+ * dsa_dense_masked_attn_f16 reads; magnitudes from 65520 up become
+ * infinities).  bf16 products, fp32 sums, each result rounded once (nearest
+ * even).  Requires N >= 0 (0: nothing is enqueued), H >= 1, pointers 16-byte
+ * aligned, kv_cols a multiple of 8, values_f16 0 or 1; d_latent a multiple
+ * of 64 and H * (d_nope + d_v) a multiple of 256 (DSA_ERR_UNSUPPORTED
+ * otherwise). */
+dsa_status dsa_kv_b_proj(const uint16_t* kv, int32_t kv_cols, const uint16_t* wkvb, int32_t N, int32_t H,
+                         int32_t d_latent, int32_t d_nope, int32_t d_v, int32_t values_f16, uint16_t* kvb,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,7 @@ __all__ = [
     "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
     "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write", "dsa_router_topk",
     "dsa_value_up_proj", "dsa_o_proj", "dsa_selection_mask", "dsa_dense_masked_attn",
-    "dsa_dense_masked_attn_f16", "dsa_values_to_f16", "dsa_status_string",
+    "dsa_dense_masked_attn_f16", "dsa_values_to_f16", "dsa_kv_b_proj", "dsa_status_string",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -31,7 +31,7 @@ EXPORTED_SYMBOLS = (
     "dsa_latent_to_f16", "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
     "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write", "dsa_router_topk",
     "dsa_value_up_proj", "dsa_o_proj", "dsa_selection_mask", "dsa_dense_masked_attn",
-    "dsa_dense_masked_attn_f16", "dsa_values_to_f16",
+    "dsa_dense_masked_attn_f16", "dsa_values_to_f16", "dsa_kv_b_proj",
 )
 
 
@@ -91,6 +91,7 @@ def _load() -> ctypes.CDLL:
         "dsa_dense_masked_attn_f16": (ctypes.c_int, [P, P, P, i32, i32, P, i32, i32, i32, i32, i32, i32, i32,
                                                      i32, ctypes.c_float, P, P]),
         "dsa_values_to_f16": (ctypes.c_int, [P, i32, i32, i32, i32, P]),
+        "dsa_kv_b_proj": (ctypes.c_int, [P, i32, P, i32, i32, i32, i32, i32, i32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -270,4 +271,10 @@ def dsa_dense_masked_attn_f16(q, kvb16, kv, kv_cols: int, rope_col: int, mask, L
 
 def dsa_values_to_f16(kvb, N: int, H: int, d_nope: int, d_v: int, stream=None) -> None:
     _check("dsa_values_to_f16", lib.dsa_values_to_f16(_bits(kvb, "kvb"), N, H, d_nope, d_v, _stream(stream)))
+
+
+def dsa_kv_b_proj(kv, kv_cols: int, wkvb, N: int, H: int, d_latent: int, d_nope: int, d_v: int, values_f16: bool,
+                  kvb, stream=None) -> None:
+    _check("dsa_kv_b_proj", lib.dsa_kv_b_proj(_bits(kv, "kv"), kv_cols, _bits(wkvb, "wkvb"), N, H, d_latent, d_nope,
+                                              d_v, int(values_f16), _bits(kvb, "kvb"), _stream(stream)))
 

@@ -361,6 +361,28 @@ dsa_status dsa_values_to_f16(uint16_t* kvb, int32_t N, int32_t H, int32_t d_nope
     return launched(dsa::launch_values_to_f16(kvb, (int64_t)N * H, d_nope, d_v, (hipStream_t)stream));
 }
 
+dsa_status dsa_kv_b_proj(const uint16_t* kv, int32_t kv_cols, const uint16_t* wkvb, int32_t N, int32_t H,
+                         int32_t d_latent, int32_t d_nope, int32_t d_v, int32_t values_f16, uint16_t* kvb,
+                         void* stream) {
+    if (!kv || !wkvb || !kvb || !aligned16(kv) || !aligned16(wkvb) || !aligned16(kvb) || N < 0 || H <= 0 ||
+        d_latent <= 0 || d_latent > kv_cols || kv_cols % 8 != 0 || d_nope < 0 || d_v <= 0 ||
+        (values_f16 != 0 && values_f16 != 1))
+        return DSA_ERR_INVALID_ARG;
+    const int64_t n_out = (int64_t)H * (d_nope + d_v);
+    if (d_latent % 64 != 0 || n_out % 256 != 0 || n_out > INT32_MAX || (int64_t)N * kv_cols * 2 >= (1ll << 32) ||
+        n_out * d_latent * 2 >= (1ll << 32))
+        return DSA_ERR_UNSUPPORTED;
+    if (N == 0) return DSA_OK;
+    dsa_status st = check_device();
+    if (st) return st;
+    dsa::GemmArgs g{kv, kv_cols, 0, wkvb, d_latent, 0, kvb, n_out, 0, N, (int32_t)n_out, d_latent};
+    if (values_f16) {
+        g.f16_from = d_nope;
+        g.f16_period = d_nope + d_v;
+    }
+    return launched(dsa::launch_kv_b_proj(g, (hipStream_t)stream));
+}
+
 dsa_status dsa_sparse_mla_attn_f16(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv16,
                                    const int32_t* idx, const int32_t* count, int32_t L, int32_t N,
                                    float* out, float* lse, void* stream) {

@@ -186,11 +186,16 @@ struct GemmArgs {            // C[m, n] = sum_k A[m, k] B[n, k], per batch z
     void* C;                 // element (z, m, n) at z*c_batch + m*ldc + n (bf16 or float32)
     int64_t ldc, c_batch;
     int32_t M, N, K;
+    // bf16 output only: columns n with n % f16_period >= f16_from are written
+    // as fp16 instead (0 / 0: none)
+    int32_t f16_from = 0, f16_period = 0;
 };
 // value up-projection: A float32, C bf16, N == 256, K % 64 == 0
 hipError_t launch_value_up_proj(const GemmArgs& g, int batch, hipStream_t s);
 // output projection: A bf16, C float32, N % 192 == 0, K % 64 == 0
 hipError_t launch_o_proj(const GemmArgs& g, hipStream_t s);
+// kv_b up-projection: A bf16 (latent rows), C bf16 / fp16 columns, N % 256 == 0, K % 64 == 0
+hipError_t launch_kv_b_proj(const GemmArgs& g, hipStream_t s);
 
 // Selection mask: row i of mask [L, W] has bit j set iff key j is among
 // idx[i, :count[i]], 0 <= j < N and j <= q_start + i.

@@ -237,9 +237,12 @@ void gemm_nt_kernel(GemmArgs g) {
             if (m >= g.M) continue;
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-                const int64_t off = z * g.c_batch + (int64_t)m * g.ldc + n0 + (BN / 2) * wn + 32 * j + (l & 31);
+                const int n = n0 + (BN / 2) * wn + 32 * j + (l & 31);
+                const int64_t off = z * g.c_batch + (int64_t)m * g.ldc + n;
                 if constexpr (C_F32) {
                     static_cast<float*>(g.C)[off] = acc[i][j][r];
+                } else if (g.f16_period > 0 && n % g.f16_period >= g.f16_from) {
+                    static_cast<uint16_t*>(g.C)[off] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][r]);
                 } else {
                     const uint32_t u = __float_as_uint(acc[i][j][r]);
                     static_cast<uint16_t*>(g.C)[off] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
@@ -267,6 +270,16 @@ hipError_t launch_o_proj(const GemmArgs& g, hipStream_t s) {
     const int tiles = (g.M + kBM - 1) / kBM * (g.N / 192);
     const dim3 grid((unsigned)(8 * ((tiles + 7) / 8)), 1, 1);
     hipLaunchKernelGGL((gemm_nt_kernel<false, true, 192>), grid, dim3(kGemmThreads), 0, s, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_b_proj(const GemmArgs& g, hipStream_t s) {
+    if (g.M <= 0) return hipSuccess;
+    if (g.N % 256 != 0 || g.K % kBK != 0) return hipErrorInvalidValue;
+    if ((int64_t)g.M * g.lda * 2 >= (1ll << 32) || (int64_t)g.N * g.ldb * 2 >= (1ll << 32)) return hipErrorInvalidValue;
+    const int tiles = (g.M + kBM - 1) / kBM * (g.N / 256);
+    const dim3 grid((unsigned)(8 * ((tiles + 7) / 8)), 1, 1);
+    hipLaunchKernelGGL((gemm_nt_kernel<false, false, 256>), grid, dim3(kGemmThreads), 0, s, g);
     return hipGetLastError();
 }
 

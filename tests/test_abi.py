@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     assert sorted(dsa.EXPORTED_SYMBOLS) == names
     raw = ctypes.CDLL(dsa._build.LIB)
     for n in names:
@@ -191,4 +191,12 @@ def test_dense_validation():
     assert L.dsa_values_to_f16(fake(), 8, 4, 60, 64, None) == INVALID
     assert L.dsa_values_to_f16(fake(), 8, 0, 64, 64, None) == INVALID
     assert L.dsa_values_to_f16(fake(), 0, 4, 192, 256, None) == OK
+    k = L.dsa_kv_b_proj
+    assert k(fake(), 576, fake(), 0, 64, 512, 192, 256, 1, fake(), None) == OK
+    assert k(None, 576, fake(), 8, 64, 512, 192, 256, 1, fake(), None) == INVALID
+    assert k(fake(), 576, fake(), 8, 64, 512, 192, 256, 2, fake(), None) == INVALID
+    assert k(fake(), 576, fake(), 8, 64, 640, 192, 256, 1, fake(), None) == INVALID
+    assert k(fake(), 572, fake(), 8, 64, 512, 192, 256, 1, fake(), None) == INVALID
+    assert k(fake(), 576, fake(), 8, 64, 480, 192, 256, 1, fake(), None) == UNSUPPORTED
+    assert k(fake(), 576, fake(), 8, 3, 512, 192, 256, 1, fake(), None) == UNSUPPORTED
 

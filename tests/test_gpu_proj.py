@@ -1,5 +1,5 @@
-"""GPU parity of the downstream projections (dsa_value_up_proj, dsa_o_proj)
-against the CPU oracle on the same seeded inputs.
+"""GPU parity of the projections (dsa_value_up_proj, dsa_o_proj, and the
+dense path's dsa_kv_b_proj) against the CPU oracle on the same seeded inputs.
 
 Tolerances, from the arithmetic:
 - up-projection: both sides round the float32 attention output to bf16 and
@@ -112,3 +112,44 @@ def test_projections_end_to_end():
     ref = oracle.o_proj(ov.reshape(cfg.T, cfg.H * cfg.Dv), d["wo"])
     err = row_rel_err(y, ref)
     assert err <= 1e-3, err
+
+
+# ---------------------------------------------------------------- kv_b (dense path)
+def _values(bits, f16):
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.view(np.float16) if f16 else W.bf16_bits_to_f32(b)).astype(np.float64)
+
+
+@pytest.mark.parametrize("name,f16", [("glm_8k_chunk", True), ("glm_small", True), ("glm_small", False),
+                                      ("tiny", True)])
+def test_kv_b_proj_matches_oracle(name, f16):
+    """bf16 keys and fp16 (or bf16) values of the kv_b product, against the
+    oracle's exactly summed, once-rounded results: both sides take the same
+    bf16 operands and round once; they differ in the summation (fp32 against
+    exact).  Bound per output: one unit of its format + 2^-20 * sum |terms|,
+    and under 1% of outputs differ at all.  glm_8k_chunk: 8192 keys (the
+    benchmark's launch), on a seeded sample of 48 rows; glm_small: 700 keys
+    (a partial row tile); tiny: 4 heads x (64 + 64)."""
+    import torch
+    import sparse_attention_scores_amd as dsa
+    cfg = W.DENSE[name]
+    d = W.make_dense(cfg)
+    w = W.make_kvb_weight(cfg)
+    C = cfg.Dn + cfg.Dv
+    kc = cfg.Dl + cfg.Dr
+    say("kv_b_proj", name, "N=%d" % cfg.N, "f16" if f16 else "bf16")
+    out = torch.empty((cfg.N, cfg.H, C), dtype=torch.int16, device="cuda")
+    dsa.dsa_kv_b_proj(dev(d["kv"]), kc, dev(w), cfg.N, cfg.H, cfg.Dl, cfg.Dn, cfg.Dv, f16, out)
+    got = host(out)
+    rows = np.arange(cfg.N) if cfg.N <= 1024 else W.sample_rows(cfg.N, 48, seed=11, must=[0, cfg.N - 1])
+    want = oracle.kv_b_proj(d["kv"][rows], w, cfg.H, cfg.Dl, cfg.Dn, cfg.Dv, f16)
+    g = got[rows]
+    assert (g != want).mean() < 0.01, float((g != want).mean())
+    lat = np.abs(W.bf16_bits_to_f32(d["kv"][rows, :cfg.Dl]).astype(np.float64))
+    terms = (lat @ np.abs(W.bf16_bits_to_f32(w).astype(np.float64)).T).reshape(len(rows), cfg.H, C)
+    for sl, is16, mant in ((np.s_[..., :cfg.Dn], False, 7), (np.s_[..., cfg.Dn:], f16, 10 if f16 else 7)):
+        gv, rv = _values(g[sl], is16), _values(want[sl], is16)
+        assert np.isfinite(gv).all()
+        unit = np.ldexp(1.0, (np.floor(np.log2(np.maximum(np.abs(rv), 2.0 ** -14))) - mant).astype(int))
+        excess = np.abs(gv - rv) - (unit + 2.0 ** -20 * terms[sl])
+        assert excess.max() <= 0, float(excess.max())

@@ -348,3 +348,11 @@ def make_dense(cfg: Dense) -> Dict[str, np.ndarray]:
     S = nrm(cfg.L, cfg.N)
     return {"q": q, "kvb": kvb, "kv": kv, "S": S}
 
+
+def make_kvb_weight(cfg: Dense) -> np.ndarray:
+    """The kv_b weight [H * (Dn + Dv), Dl] ~ N(0,1)/sqrt(Dl) rounded to bf16,
+    from a stream of its own (seed + 1000), so make_dense's draws stay put."""
+    rng = np.random.default_rng(cfg.seed + 1000)
+    w = rng.standard_normal(size=(cfg.H * (cfg.Dn + cfg.Dv), cfg.Dl), dtype=np.float32)
+    return to_bf16_bits(w * np.float32(1.0 / np.sqrt(cfg.Dl)))
+
