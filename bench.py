@@ -557,10 +557,35 @@ def main() -> int:
             dstep()
         torch.cuda.synchronize()
         tdec = (time.perf_counter() - t0) / nd
+        # the same step captured once into a HIP graph and replayed: one launch
+        # per step instead of five (the serving-loop form); every replay is
+        # checked against the eager output before timing
+        ref_out = dout.clone()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            dstep()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            dstep()
+        for _ in range(3):
+            dout.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(dout, ref_out):
+                raise SystemExit("decode graph replay differs from the eager step")
+        t0 = time.perf_counter()
+        for _ in range(nd):
+            graph.replay()
+        torch.cuda.synchronize()
+        tgraph = (time.perf_counter() - t0) / nd
+        del graph
         sum_ctx = int(sum(dc.ctx))
         moved = 2 * sh.d_idx * sum_ctx + 2 * sh.d_qk * sum(min(c, sh.top_k) for c in dc.ctx)
         result["decode"] = {"workload": "batched decode, 8 sequences x 1 query, contexts "
                                         + ",".join(str(c) for c in dc.ctx), "us_per_step": tdec * 1e6,
+                            "us_per_step_graph": tgraph * 1e6,
                             "steps": nd, "hbm_floor_us": moved / (PEAK_HBM_GBPS * 1e9) * 1e6}
 
     # ---------------- CPU oracle on a bounded sample ----------------
