@@ -34,7 +34,7 @@ namespace {
 
 constexpr int kBins = 256;
 constexpr int kMaxLevels = 4;
-constexpr int kDecodeSeg = 8192;    // keys per decode segment block
+constexpr int kDecodeSeg = 16384;   // keys per decode segment block (a 64k context: 4 segments, 8192 candidates)
 
 // Larger float -> larger key; -0 ranks equal to +0 (the floats compare equal).
 __device__ inline uint32_t order_key(float f) {

@@ -375,11 +375,11 @@ def test_decode_step(name):
 
 @pytest.mark.parametrize("case", ["all_ties", "one_segment"])
 def test_decode_segmented_topk(case):
-    """Decode selection over sequences longer than one top-k segment (8192
+    """Decode selection over sequences longer than one top-k segment (16384
     keys): ties spanning every segment (all scores equal: the first top_k
     keys win), and a selection held entirely by one segment (the others'
     candidates must all lose)."""
-    cfg = W.Decode("seg_" + case, W.GLM, (20000, 8193, 9000), 31, 8, 0.05, 0.05)
+    cfg = W.Decode("seg_" + case, W.GLM, (40000, 16385, 18000), 31, 8, 0.05, 0.05)
     d = W.make_decode(cfg)
     top_k = cfg.shape.top_k
     if case == "all_ties":
@@ -388,7 +388,7 @@ def test_decode_segmented_topk(case):
     else:
         one, eight = W.to_bf16_bits(np.float32(1.0)), W.to_bf16_bits(np.float32(8.0))
         d["qI"][0] = one                  # sequence 0: every q.k is the sum of k
-        lo = 9000                         # keys 9000..11047 sit in the second segment
+        lo = 17000                        # keys 17000..19047 sit in the second segment
         d["kI"][lo:lo + top_k] = eight    # the only keys reaching 128 * 8 per head
         want0 = np.arange(lo, lo + top_k)
     say("decode-seg", case, cfg.ctx)
