@@ -122,9 +122,9 @@ void dense_attn_kernel(DenseArgs a) {
     const int nqb = (a.L + kDQB - 1) / kDQB;
     const int total = nqb * a.H;
     const int b = blockIdx.x;
-    const int v = (total % 8 == 0) ? (b % 8) * (total / 8) + b / 8 : b;
-    const int h = v / nqb;
-    const int q0 = (nqb - 1 - v % nqb) * kDQB;
+    const int lin = (total % 8 == 0) ? (b % 8) * (total / 8) + b / 8 : b;
+    const int h = lin / nqb;
+    const int q0 = (nqb - 1 - lin % nqb) * kDQB;
     const int qlast = min(q0 + kDQB, a.L) - 1;
     const int nkeys = min(a.N, a.q_start + qlast + 1);      // keys after the last query are never visible
     const int ntiles = (nkeys + kDTK - 1) / kDTK;
@@ -164,18 +164,18 @@ void dense_attn_kernel(DenseArgs a) {
         // the tile reaches past the last key: its extra rows repeat the last key
         const bool clamp = k0 + kDTK > a.N;
         const int jmax = a.N - 1 - k0;
-        auto o = [&](int n, uint32_t rs) {
+        auto src_off = [&](int n, uint32_t rs) {
             return clamp && row[n] > jmax ? off[n] - (uint32_t)(row[n] - jmax) * rs : off[n];
         };
 #pragma unroll
         for (int n = 0; n < IN; ++n)
-            gather16_to_lds(kvb_t, o(n, rs_kvb), lds_addr(&B.kn[64 * (w * IN + n)]));
+            gather16_to_lds(kvb_t, src_off(n, rs_kvb), lds_addr(&B.kn[64 * (w * IN + n)]));
 #pragma unroll
         for (int n = 0; n < IR; ++n)
-            gather16_to_lds(kv_t, o(IN + n, rs_kv), lds_addr(&B.kr[64 * (w * IR + n)]));
+            gather16_to_lds(kv_t, src_off(IN + n, rs_kv), lds_addr(&B.kr[64 * (w * IR + n)]));
 #pragma unroll
         for (int n = 0; n < IV; ++n)
-            gather16_to_lds(kvb_t + DN, o(IN + IR + n, rs_kvb), lds_addr(&B.v[64 * (w * IV + n)]));
+            gather16_to_lds(kvb_t + DN, src_off(IN + IR + n, rs_kvb), lds_addr(&B.v[64 * (w * IV + n)]));
         // mask words: lane l < 32 -> query 16w + l / 2 of the block, word l % 2 of the tile
         const uint32_t* mb = a.mask + (int64_t)q0 * a.W + k0 / 32;
         const int qi = min(kDQW * w + (l >> 1), a.L - 1 - q0);
