@@ -108,24 +108,24 @@ def dense_setup(np, torch, dsa, W, cfg):
     dsa.dsa_topk_select(sh, t["S"], cfg.L, cfg.N, cfg.q_start, idx, cnt)
     del t["S"]
     mask = torch.empty((cfg.L, dsa.mask_words(cfg.N)), dtype=torch.int32, device="cuda")
-    kvb16 = t["kvb"].clone()
+    vt = torch.empty((cfg.H, cfg.Dv, dsa.vt_keys(cfg.N)), dtype=torch.int16, device="cuda")
     wkvb = torch.from_numpy(W.make_kvb_weight(cfg).view(np.int16)).cuda()
     kvb_out = torch.empty_like(t["kvb"])
+    vt_out = torch.empty_like(vt)
     out = torch.empty((cfg.L, cfg.H, cfg.Dv), dtype=torch.float32, device="cuda")
     kc, rc = cfg.Dl + cfg.Dr, cfg.Dl
-    args = lambda kvb: (t["q"], kvb, t["kv"], kc, rc, mask, cfg.L, cfg.N, cfg.q_start, cfg.H, cfg.Dn, cfg.Dr,
-                        cfg.Dv, 1.0 / 16, out)
+    tail = (t["kv"], kc, rc, mask, cfg.L, cfg.N, cfg.q_start, cfg.H, cfg.Dn, cfg.Dr, cfg.Dv, 1.0 / 16, out)
     f = {"mask": lambda: dsa.dsa_selection_mask(idx, cnt, cfg.L, cfg.top_k, cfg.N, cfg.q_start, mask),
-         "convert": lambda: dsa.dsa_values_to_f16(kvb16, cfg.N, cfg.H, cfg.Dn, cfg.Dv),
-         "kv_b": lambda: dsa.dsa_kv_b_proj(t["kv"], kc, wkvb, cfg.N, cfg.H, cfg.Dl, cfg.Dn, cfg.Dv, True, kvb_out),
-         "attn_f16": lambda: dsa.dsa_dense_masked_attn_f16(*args(kvb16)),
-         "attn_bf16": lambda: dsa.dsa_dense_masked_attn(*args(t["kvb"]))}
+         "convert": lambda: dsa.dsa_values_to_f16(t["kvb"], cfg.N, cfg.H, cfg.Dn, cfg.Dv, vt),
+         "kv_b": lambda: dsa.dsa_kv_b_proj(t["kv"], kc, wkvb, cfg.N, cfg.H, cfg.Dl, cfg.Dn, cfg.Dv, kvb_out, vt_out),
+         "attn_f16": lambda: dsa.dsa_dense_masked_attn_f16(t["q"], t["kvb"], vt, *tail),
+         "attn_bf16": lambda: dsa.dsa_dense_masked_attn(t["q"], t["kvb"], *tail)}
     visible = sum(min(p + 1, cfg.N) for p in range(cfg.q_start, cfg.q_start + cfg.L))
     work = {"flop": 2.0 * cfg.H * (cfg.Dn + cfg.Dr + cfg.Dv) * visible,
             "mask_bytes": 4 * cfg.L * cfg.top_k + 4 * cfg.L + 4 * cfg.L * mask.shape[1],
-            "convert_bytes": 2 * 2 * cfg.N * cfg.H * cfg.Dv,
+            "convert_bytes": 2 * 2 * cfg.N * cfg.H * cfg.Dv,   # bf16 value columns in, fp16 vt out
             "kv_b_flop": 2.0 * cfg.N * cfg.Dl * cfg.H * (cfg.Dn + cfg.Dv)}
-    return f, work, (t, idx, cnt, mask, kvb16, out, wkvb, kvb_out)
+    return f, work, (t, idx, cnt, mask, vt, out, wkvb, kvb_out, vt_out)
 
 
 def crossover(np, torch, dsa, W, reps: int) -> int:

@@ -286,23 +286,30 @@ dsa_status dsa_dense_masked_attn(const uint16_t* q, const uint16_t* kvb, const u
                                  int32_t N, int32_t q_start, int32_t H, int32_t d_nope, int32_t d_rope,
                                  int32_t d_v, float scale, float* out, void* stream);
 
-/* dsa_dense_masked_attn with the value columns of kvb16 stored as fp16
- * (as dsa_values_to_f16 leaves them) instead of bf16; the no-rope key
- * columns stay bf16.  Same arguments, results and requirements otherwise;
- * the conversion then happens once per value rather than in every block
- * that reads it. */
-dsa_status dsa_dense_masked_attn_f16(const uint16_t* q, const uint16_t* kvb16, const uint16_t* kv, int32_t kv_cols,
-                                     int32_t rope_col, const uint32_t* mask, int32_t mask_words, int32_t L,
-                                     int32_t N, int32_t q_start, int32_t H, int32_t d_nope, int32_t d_rope,
-                                     int32_t d_v, float scale, float* out, void* stream);
+/* dsa_dense_masked_attn with the values in the fp16 form vt instead of the
+ * bf16 value columns of kvb (whose no-rope key columns are still read):
+ *   vt [dev] [H, d_v, Np] fp16, Np = N rounded up to a multiple of 64,
+ *   positions N..Np-1 zero; feature row (h, f) holds key k at position
+ *   32 * (k / 32) + vt_pos(k % 32), vt_pos(x) = 8 * ((x % 16) / 4) +
+ *   4 * (x / 16) + x % 4 (the order in which the kernel's probability
+ *   fragments list a 32-key step's keys, so one 16-byte read is one matrix
+ *   operand).  dsa_values_to_f16 or dsa_kv_b_proj writes it.  Same
+ *   arguments, results and requirements otherwise; vt must be non-null and
+ *   16-byte aligned. */
+dsa_status dsa_dense_masked_attn_f16(const uint16_t* q, const uint16_t* kvb, const uint16_t* vt, const uint16_t* kv,
+                                     int32_t kv_cols, int32_t rope_col, const uint32_t* mask, int32_t mask_words,
+                                     int32_t L, int32_t N, int32_t q_start, int32_t H, int32_t d_nope,
+                                     int32_t d_rope, int32_t d_v, float scale, float* out, void* stream);
 
-/* Rewrites the value columns of kvb [dev] [N, H, d_nope + d_v] in place from
- * bf16 to fp16 bits, round to nearest even (exact for |v| in
- * [2^-14, 65504]; smaller magnitudes become fp16 subnormals, larger ones
- * infinities); the no-rope key columns are left alone.  Requires kvb
- * 16-byte aligned, N >= 0 (0: nothing is enqueued), H >= 1, d_nope and d_v
- * multiples of 8. */
-dsa_status dsa_values_to_f16(uint16_t* kvb, int32_t N, int32_t H, int32_t d_nope, int32_t d_v, void* stream);
+/* The value columns of kvb [dev] [N, H, d_nope + d_v] (bf16) into the fp16
+ * form vt [dev] [H, d_v, Np] that dsa_dense_masked_attn_f16 reads (layout
+ * there), rounded to nearest even (exact for |v| in [2^-14, 65504]; smaller
+ * magnitudes become fp16 subnormals, larger ones infinities), positions
+ * N..Np-1 zero.  Requires kvb and vt 16-byte aligned and not overlapping,
+ * N >= 0 (0: nothing is enqueued), H >= 1, d_nope a multiple of 8; d_v 64
+ * or 256 (DSA_ERR_UNSUPPORTED otherwise). */
+dsa_status dsa_values_to_f16(const uint16_t* kvb, int32_t N, int32_t H, int32_t d_nope, int32_t d_v, uint16_t* vt,
+                             void* stream);
 
 /* kv_b up-projection of the latent rows for the dense path ("GLM-5.2-Vision:
  * llama.cpp vs vLLM line-by-line pipeline trace", section 4: the kv_b
@@ -311,16 +318,17 @@ dsa_status dsa_values_to_f16(uint16_t* kvb, int32_t N, int32_t H, int32_t d_nope
  *   kvb[j, h, c] = sum_d kv[j, d] * wkvb[h * (d_nope + d_v) + c, d],  d < d_latent
  * kv [dev] [N, kv_cols] bf16 (the cache rows; the latent is their first
  * d_latent columns); wkvb [dev] [H * (d_nope + d_v), d_latent] bf16 (stored
- * [out, in]); kvb [dev] [N, H, d_nope + d_v]: bf16 no-rope keys, and values
- * in bf16, or in fp16 when values_f16 = 1 (the form
- * dsa_dense_masked_attn_f16 reads; magnitudes from 65520 up become
- * infinities).  bf16 products, fp32 sums, each result rounded once (nearest
+ * [out, in]); kvb [dev] [N, H, d_nope + d_v] receives the bf16 no-rope keys
+ * and, when vt is NULL, the bf16 values; with vt non-null the values go to
+ * vt [dev] [H, d_v, Np] in fp16 instead (the form dsa_dense_masked_attn_f16
+ * reads, layout there; magnitudes from 65520 up become infinities;
+ * positions N..Np-1 written as zeros) and kvb's value columns are left
+ * alone.  bf16 products, fp32 sums, each result rounded once (nearest
  * even).  Requires N >= 0 (0: nothing is enqueued), H >= 1, pointers 16-byte
- * aligned, kv_cols a multiple of 8, values_f16 0 or 1; d_latent a multiple
- * of 64 and H * (d_nope + d_v) a multiple of 256 (DSA_ERR_UNSUPPORTED
- * otherwise). */
+ * aligned, kv_cols a multiple of 8; d_latent a multiple of 64 and
+ * H * (d_nope + d_v) a multiple of 256 (DSA_ERR_UNSUPPORTED otherwise). */
 dsa_status dsa_kv_b_proj(const uint16_t* kv, int32_t kv_cols, const uint16_t* wkvb, int32_t N, int32_t H,
-                         int32_t d_latent, int32_t d_nope, int32_t d_v, int32_t values_f16, uint16_t* kvb,
+                         int32_t d_latent, int32_t d_nope, int32_t d_v, uint16_t* kvb, uint16_t* vt,
                          void* stream);
 
 #ifdef __cplusplus

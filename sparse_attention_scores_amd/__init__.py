@@ -88,10 +88,10 @@ def _load() -> ctypes.CDLL:
         "dsa_selection_mask": (ctypes.c_int, [P, P, i32, i32, i32, i32, i32, P, P]),
         "dsa_dense_masked_attn": (ctypes.c_int, [P, P, P, i32, i32, P, i32, i32, i32, i32, i32, i32, i32, i32,
                                                  ctypes.c_float, P, P]),
-        "dsa_dense_masked_attn_f16": (ctypes.c_int, [P, P, P, i32, i32, P, i32, i32, i32, i32, i32, i32, i32,
+        "dsa_dense_masked_attn_f16": (ctypes.c_int, [P, P, P, P, i32, i32, P, i32, i32, i32, i32, i32, i32, i32,
                                                      i32, ctypes.c_float, P, P]),
-        "dsa_values_to_f16": (ctypes.c_int, [P, i32, i32, i32, i32, P]),
-        "dsa_kv_b_proj": (ctypes.c_int, [P, i32, P, i32, i32, i32, i32, i32, i32, P, P]),
+        "dsa_values_to_f16": (ctypes.c_int, [P, i32, i32, i32, i32, P, P]),
+        "dsa_kv_b_proj": (ctypes.c_int, [P, i32, P, i32, i32, i32, i32, i32, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -261,20 +261,27 @@ def dsa_dense_masked_attn(q, kvb, kv, kv_cols: int, rope_col: int, mask, L: int,
         scale, _ptr(out, torch.float32, "out"), _stream(stream)))
 
 
-def dsa_dense_masked_attn_f16(q, kvb16, kv, kv_cols: int, rope_col: int, mask, L: int, N: int, q_start: int,
+def vt_keys(N: int) -> int:
+    """Key stride of the fp16 value form vt [H, d_v, Np]: N rounded up to 64."""
+    return 64 * ((N + 63) // 64)
+
+
+def dsa_dense_masked_attn_f16(q, kvb, vt, kv, kv_cols: int, rope_col: int, mask, L: int, N: int, q_start: int,
                               H: int, d_nope: int, d_rope: int, d_v: int, scale: float, out, stream=None) -> None:
     _check("dsa_dense_masked_attn_f16", lib.dsa_dense_masked_attn_f16(
-        _bits(q, "q"), _bits(kvb16, "kvb16"), _bits(kv, "kv"), kv_cols, rope_col, _ptr(mask, torch.int32, "mask"),
+        _bits(q, "q"), _bits(kvb, "kvb"), _bits(vt, "vt"), _bits(kv, "kv"), kv_cols, rope_col,
+        _ptr(mask, torch.int32, "mask"),
         mask.shape[1] if mask is not None and mask.dim() == 2 else 0, L, N, q_start, H, d_nope, d_rope, d_v,
         scale, _ptr(out, torch.float32, "out"), _stream(stream)))
 
 
-def dsa_values_to_f16(kvb, N: int, H: int, d_nope: int, d_v: int, stream=None) -> None:
-    _check("dsa_values_to_f16", lib.dsa_values_to_f16(_bits(kvb, "kvb"), N, H, d_nope, d_v, _stream(stream)))
+def dsa_values_to_f16(kvb, N: int, H: int, d_nope: int, d_v: int, vt, stream=None) -> None:
+    _check("dsa_values_to_f16", lib.dsa_values_to_f16(_bits(kvb, "kvb"), N, H, d_nope, d_v, _bits(vt, "vt"),
+                                                      _stream(stream)))
 
 
-def dsa_kv_b_proj(kv, kv_cols: int, wkvb, N: int, H: int, d_latent: int, d_nope: int, d_v: int, values_f16: bool,
-                  kvb, stream=None) -> None:
+def dsa_kv_b_proj(kv, kv_cols: int, wkvb, N: int, H: int, d_latent: int, d_nope: int, d_v: int, kvb, vt=None,
+                  stream=None) -> None:
     _check("dsa_kv_b_proj", lib.dsa_kv_b_proj(_bits(kv, "kv"), kv_cols, _bits(wkvb, "wkvb"), N, H, d_latent, d_nope,
-                                              d_v, int(values_f16), _bits(kvb, "kvb"), _stream(stream)))
+                                              d_v, _bits(kvb, "kvb"), _bits(vt, "vt"), _stream(stream)))
 

@@ -20,10 +20,14 @@
 //  - scores S^T = K Q^T on bf16 MFMA 16x16x32 (each wave keeps its queries
 //    in registers for the whole loop), an fp32 online softmax whose
 //    reference maximum only moves when a score clears it by kLazy (log2
-//    units), P in fp16, O^T += V^T P^T on fp16 MFMA with V read transposed
-//    (ds_read_b64_tr_b16): either converted to fp16 in registers, or stored
-//    as fp16 beforehand (values_to_f16_kernel), which takes the conversion
-//    (a third of the loop's vector instructions) out of the loop;
+//    units), P in fp16, O^T += V^T P^T on fp16 MFMA.  The values come in one
+//    of two forms: the kv_b output's bf16 columns, read transposed
+//    (ds_read_b64_tr_b16) and converted to fp16 in registers; or a
+//    feature-major fp16 copy vt [H][Dv][Np] (values_to_vt_kernel, or the
+//    kv_b product directly), read as plain 16-byte fragments.  The fp16 form
+//    takes the conversion (a third of the loop's vector instructions) out of
+//    the loop, and its reads are conflict-free b128 reads (8% faster than
+//    the transposing reads);
 //  - the blocks of one head are consecutive in one XCD's share of the
 //    dispatch order, so that head's keys and values stream through that
 //    XCD's L2 once for all its query blocks.
@@ -103,14 +107,18 @@ struct DenseShape {
     struct Buf {
         u32x4 kn[kDTK * CN];
         u32x4 kr[kDTK * CR];
-        u32x4 v[kDTK * CV];
+        u32x4 v[kDTK * CV];      // [key][Dv] (bf16 form) or [Dv][key] (vt form): same size
         uint32_t m[kDQB * 2];    // [query of the block][2 words]
     };
 };
 
-// VF16: the value columns of kvb hold fp16 (see values_to_f16_kernel)
-// rather than bf16; the no-rope key columns are bf16 either way.
-template <int DN, int DR, int DV, bool VF16>
+// VT: the values come from vt [H][Dv][Np] fp16 (Np = N rounded up to 64,
+// zero past N): feature row f of head h holds key k at position
+// 32 (k / 32) + vt_pos(k % 32), the order in which the P fragments list a
+// 32-key step's keys (lane group g: keys 4g..4g+3, then 16+4g..16+4g+3), so
+// that one 16-byte read is one MFMA operand.  Otherwise the values are the
+// kvb columns Dn..Dn+Dv-1 in bf16.
+template <int DN, int DR, int DV, bool VT>
 __global__ __launch_bounds__(kDNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dense_attn_kernel(DenseArgs a) {
     using C = DenseShape<DN, DR, DV>;
@@ -156,6 +164,13 @@ void dense_attn_kernel(DenseArgs a) {
         row[n] = r;
         off[n] = (uint32_t)r * (n < IN + IR && n >= IN ? rs_kv : rs_kvb) + 16u * ((P % ch) ^ x);
     }
+    // vt form: the lane's chunk of each value instruction, from its tile's first key
+    uint32_t voff[IV];
+#pragma unroll
+    for (int n = 0; n < IV; ++n) {
+        const int P = 64 * (w * IV + n) + l, r = P / 8;
+        voff[n] = (uint32_t)r * (uint32_t)a.Np * 2u + 16u * ((P % 8) ^ (swz_key(r & 15) & 7));
+    }
     auto issue = [&](int t, int bi) {
         typename C::Buf& B = buf[bi];
         const int k0 = t * kDTK;
@@ -173,9 +188,17 @@ void dense_attn_kernel(DenseArgs a) {
 #pragma unroll
         for (int n = 0; n < IR; ++n)
             gather16_to_lds(kv_t, src_off(IN + n, rs_kv), lds_addr(&B.kr[64 * (w * IR + n)]));
+        if constexpr (VT) {
+            // feature rows of 64 keys (128 B, 8 chunks), chunk XOR as for the rope rows
+            const uint16_t* vbase = a.vt + (int64_t)h * DV * a.Np + k0;
 #pragma unroll
-        for (int n = 0; n < IV; ++n)
-            gather16_to_lds(kvb_t + DN, src_off(IN + IR + n, rs_kvb), lds_addr(&B.v[64 * (w * IV + n)]));
+            for (int n = 0; n < IV; ++n)
+                gather16_to_lds(vbase, voff[n], lds_addr(&B.v[64 * (w * IV + n)]));
+        } else {
+#pragma unroll
+            for (int n = 0; n < IV; ++n)
+                gather16_to_lds(kvb_t + DN, src_off(IN + IR + n, rs_kvb), lds_addr(&B.v[64 * (w * IV + n)]));
+        }
         // mask words: lane l < 32 -> query 16w + l / 2 of the block, word l % 2 of the tile
         const uint32_t* mb = a.mask + (int64_t)q0 * a.W + k0 / 32;
         const int qi = min(kDQW * w + (l >> 1), a.L - 1 - q0);
@@ -191,7 +214,7 @@ void dense_attn_kernel(DenseArgs a) {
     float mref = kStart, lsum = 0.f;
 
     // per-lane LDS read offsets
-    const int xn = swz_key(c16) & C::SWN, xr = swz_key(c16) & C::SWR;
+    const int xn = swz_key(c16) & C::SWN, xr = swz_key(c16) & C::SWR, xr8 = swz_key(c16) & 7;
     const int trow = 4 * g + (c16 >> 2);
     const int vx = (swz_val(trow) & C::SWV) ^ ((c16 >> 1) & 1);
     const int vrow = trow * C::CV * 16 + 8 * (c16 & 1);
@@ -277,13 +300,15 @@ void dense_attn_kernel(DenseArgs a) {
         for (int st = 0; st < 2; ++st) {
 #pragma unroll
             for (int f = 0; f < C::FB; ++f) {
-                const int voff = (32 * st) * C::CV * 16 + vrow + 16 * ((2 * f) ^ vx);
-                u32x2 v0 = read_tr16(vt + voff), v1 = read_tr16(vt + voff + 16 * C::CV * 16);
-                if constexpr (!VF16) {
-                    v0 = bf16x4_f16x4(v0);
-                    v1 = bf16x4_f16x4(v1);
+                u32x4 av;
+                if constexpr (VT) {
+                    av = *reinterpret_cast<const u32x4*>(vt + (16 * f + c16) * 128 + 16 * ((4 * st + g) ^ xr8));
+                } else {
+                    const int off = (32 * st) * C::CV * 16 + vrow + 16 * ((2 * f) ^ vx);
+                    const u32x2 v0 = bf16x4_f16x4(read_tr16(vt + off));
+                    const u32x2 v1 = bf16x4_f16x4(read_tr16(vt + off + 16 * C::CV * 16));
+                    av = u32x4{v0[0], v0[1], v1[0], v1[1]};
                 }
-                const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
                 o[f] = mfma16_f16(av, pf[st], o[f]);
             }
         }
@@ -322,31 +347,52 @@ __global__ __launch_bounds__(256) void selection_mask_kernel(MaskArgs a) {
     for (int k = threadIdx.x; k < a.W; k += 256) row[k] = bits[k];
 }
 
-// bf16 -> fp16 bits, round to nearest even (exact for |v| in [2^-14, 65504];
-// larger magnitudes become infinities)
-__device__ inline uint32_t bf16x2_f16x2_rne(uint32_t d) {
-    const _Float16 lo = (_Float16)__uint_as_float(d << 16);
-    const _Float16 hi = (_Float16)__uint_as_float(d & 0xFFFF0000u);
-    return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-}
-
-// The value columns of kvb [N, H, Dn + Dv], bf16 -> fp16 in place; 8 values
-// per thread.
-__global__ __launch_bounds__(256) void values_to_f16_kernel(uint16_t* kvb, int64_t rows, int dn, int dv) {
-    const int vpr = dv / 8;   // 16-byte vectors per (key, head) row
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= rows * vpr) return;
-    u32x4* p = reinterpret_cast<u32x4*>(kvb + (i / vpr) * (dn + dv) + dn) + i % vpr;
-    const u32x4 x = *p;
-    *p = u32x4{bf16x2_f16x2_rne(x[0]), bf16x2_f16x2_rne(x[1]), bf16x2_f16x2_rne(x[2]), bf16x2_f16x2_rne(x[3])};
+// kvb's value columns (bf16) -> vt [H][Dv][Np] fp16, round to nearest even
+// (exact for |v| in [2^-14, 65504]; larger magnitudes become infinities),
+// keys past N zero.  Block = one head x 64 keys: the 64 value rows go through
+// LDS and come out as 16-byte pieces of the feature rows.  Position p of a
+// 32-key group holds key 4(p / 8) + (p % 4) + 16((p / 4) % 2).
+template <int DV>
+__global__ __launch_bounds__(256) void values_to_vt_kernel(const uint16_t* kvb, int N, int H, int dn, int Np,
+                                                           uint16_t* vt) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64][DV + 8];   // [key][feature], rows padded by 16 B
+    const int h = blockIdx.y, k0 = blockIdx.x * 64, tid = threadIdx.x;
+    const int64_t rowlen = (int64_t)H * (dn + DV);
+    for (int i = tid; i < 64 * DV / 8; i += 256) {
+        const int k = i / (DV / 8), c = i % (DV / 8);
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (k0 + k < N) x = ldg16(kvb + (int64_t)(k0 + k) * rowlen + (int64_t)h * (dn + DV) + dn + 8 * c);
+        *reinterpret_cast<u32x4*>(&tile[k][8 * c]) = x;
+    }
+    __syncthreads();
+    for (int i = tid; i < DV * 8; i += 256) {   // piece: feature f, tile positions 8q..8q+7
+        const int f = i / 8, q = i % 8;
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            uint32_t two = 0;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int p = 8 * (q & 3) + j + e;                              // position in the group
+                const int k = 32 * (q >> 2) + 4 * (p >> 3) + (p & 3) + 16 * ((p >> 2) & 1);
+                const _Float16 x = (_Float16)__uint_as_float((uint32_t)tile[k][f] << 16);
+                two |= (uint32_t)__builtin_bit_cast(uint16_t, x) << (16 * e);
+            }
+            o[j / 2] = two;
+        }
+        *reinterpret_cast<u32x4*>(vt + ((int64_t)h * DV + f) * Np + k0 + 8 * q) = o;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_values_to_f16(uint16_t* kvb, int64_t rows, int dn, int dv, hipStream_t s) {
-    const int64_t n = rows * (dv / 8);
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(values_to_f16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, kvb, rows, dn, dv);
+hipError_t launch_values_to_vt(const uint16_t* kvb, int N, int H, int dn, int dv, int Np, uint16_t* vt,
+                               hipStream_t s) {
+    if (N <= 0) return hipSuccess;
+    const dim3 grid((unsigned)(Np / 64), (unsigned)H);
+    if (dv == 256) hipLaunchKernelGGL(values_to_vt_kernel<256>, grid, dim3(256), 0, s, kvb, N, H, dn, Np, vt);
+    else if (dv == 64) hipLaunchKernelGGL(values_to_vt_kernel<64>, grid, dim3(256), 0, s, kvb, N, H, dn, Np, vt);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -356,7 +402,8 @@ hipError_t launch_selection_mask(const MaskArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_dense_attn(int shape_id, const DenseArgs& a, bool values_f16, hipStream_t s) {
+hipError_t launch_dense_attn(int shape_id, const DenseArgs& a, hipStream_t s) {
+    const bool values_f16 = a.vt != nullptr;
     if (a.L <= 0 || a.N <= 0) return hipSuccess;
     const int nqb = (a.L + kDQB - 1) / kDQB;
     const dim3 grid((unsigned)(nqb * a.H)), block(kDNT);

@@ -310,10 +310,10 @@ dsa_status dsa_selection_mask(const int32_t* idx, const int32_t* count, int32_t 
 namespace {
 dsa_status dense_attn(const uint16_t* q, const uint16_t* kvb, const uint16_t* kv, int32_t kv_cols, int32_t rope_col,
                       const uint32_t* mask, int32_t mask_words, int32_t L, int32_t N, int32_t q_start, int32_t H,
-                      int32_t d_nope, int32_t d_rope, int32_t d_v, float scale, float* out, bool values_f16,
+                      int32_t d_nope, int32_t d_rope, int32_t d_v, float scale, float* out, const uint16_t* vt,
                       void* stream) {
     if (!q || !kvb || !kv || !mask || !out || !aligned16(q) || !aligned16(kvb) || !aligned16(kv) ||
-        !aligned16(out) || ((uintptr_t)mask & 3u))
+        !aligned16(out) || ((uintptr_t)mask & 3u) || (vt && !aligned16(vt)))
         return DSA_ERR_INVALID_ARG;
     if (L < 0 || N <= 0 || H <= 0 || q_start < 0 || (int64_t)q_start + L > INT32_MAX || rope_col < 0 ||
         d_rope < 0 || (int64_t)rope_col + d_rope > kv_cols || kv_cols % 8 != 0 || rope_col % 8 != 0 ||
@@ -323,15 +323,17 @@ dsa_status dense_attn(const uint16_t* q, const uint16_t* kvb, const uint16_t* kv
     if (d_nope == 192 && d_rope == 64 && d_v == 256) shape_id = 0;
     else if (d_nope == 64 && d_rope == 64 && d_v == 64) shape_id = 1;
     else return DSA_ERR_UNSUPPORTED;
+    const int64_t Np = ((int64_t)N + 63) / 64 * 64;
     if ((int64_t)H * (d_nope + d_v) * 2 * 64 > INT32_MAX || (int64_t)kv_cols * 2 * 64 > INT32_MAX ||
-        (int64_t)mask_words * 4 * 128 > INT32_MAX || ((int64_t)L + 127) / 128 * H > INT32_MAX)
+        (int64_t)mask_words * 4 * 128 > INT32_MAX || ((int64_t)L + 127) / 128 * H > INT32_MAX ||
+        (vt && d_v * Np * 2 > INT32_MAX))
         return DSA_ERR_UNSUPPORTED;
     if (L == 0) return DSA_OK;
     dsa_status st = check_device();
     if (st) return st;
     dsa::DenseArgs a{q, kvb, kv, mask, L, N, H, q_start, kv_cols, rope_col, mask_words,
-                     (float)((double)scale * 1.4426950408889634), out};
-    return launched(dsa::launch_dense_attn(shape_id, a, values_f16, (hipStream_t)stream));
+                     (float)((double)scale * 1.4426950408889634), out, vt, (int32_t)Np};
+    return launched(dsa::launch_dense_attn(shape_id, a, (hipStream_t)stream));
 }
 }  // namespace
 
@@ -340,33 +342,36 @@ dsa_status dsa_dense_masked_attn(const uint16_t* q, const uint16_t* kvb, const u
                                  int32_t N, int32_t q_start, int32_t H, int32_t d_nope, int32_t d_rope,
                                  int32_t d_v, float scale, float* out, void* stream) {
     return dense_attn(q, kvb, kv, kv_cols, rope_col, mask, mask_words, L, N, q_start, H, d_nope, d_rope, d_v,
-                      scale, out, false, stream);
+                      scale, out, nullptr, stream);
 }
 
-dsa_status dsa_dense_masked_attn_f16(const uint16_t* q, const uint16_t* kvb16, const uint16_t* kv, int32_t kv_cols,
-                                     int32_t rope_col, const uint32_t* mask, int32_t mask_words, int32_t L,
-                                     int32_t N, int32_t q_start, int32_t H, int32_t d_nope, int32_t d_rope,
-                                     int32_t d_v, float scale, float* out, void* stream) {
-    return dense_attn(q, kvb16, kv, kv_cols, rope_col, mask, mask_words, L, N, q_start, H, d_nope, d_rope, d_v,
-                      scale, out, true, stream);
+dsa_status dsa_dense_masked_attn_f16(const uint16_t* q, const uint16_t* kvb, const uint16_t* vt, const uint16_t* kv,
+                                     int32_t kv_cols, int32_t rope_col, const uint32_t* mask, int32_t mask_words,
+                                     int32_t L, int32_t N, int32_t q_start, int32_t H, int32_t d_nope,
+                                     int32_t d_rope, int32_t d_v, float scale, float* out, void* stream) {
+    if (!vt) return DSA_ERR_INVALID_ARG;
+    return dense_attn(q, kvb, kv, kv_cols, rope_col, mask, mask_words, L, N, q_start, H, d_nope, d_rope, d_v,
+                      scale, out, vt, stream);
 }
 
-dsa_status dsa_values_to_f16(uint16_t* kvb, int32_t N, int32_t H, int32_t d_nope, int32_t d_v, void* stream) {
-    if (!kvb || !aligned16(kvb) || N < 0 || H <= 0 || d_nope < 0 || d_v <= 0 || d_nope % 8 != 0 || d_v % 8 != 0)
+dsa_status dsa_values_to_f16(const uint16_t* kvb, int32_t N, int32_t H, int32_t d_nope, int32_t d_v, uint16_t* vt,
+                             void* stream) {
+    if (!kvb || !vt || !aligned16(kvb) || !aligned16(vt) || N < 0 || H <= 0 || d_nope < 0 || d_nope % 8 != 0)
         return DSA_ERR_INVALID_ARG;
-    if ((int64_t)N * H * (d_v / 8) >= ((int64_t)1 << 40)) return DSA_ERR_UNSUPPORTED;
+    if (d_v != 256 && d_v != 64) return DSA_ERR_UNSUPPORTED;
+    const int64_t Np = ((int64_t)N + 63) / 64 * 64;
+    if (Np > INT32_MAX || Np / 64 > 0x7FFFFFFF || H > 65535) return DSA_ERR_UNSUPPORTED;
     if (N == 0) return DSA_OK;
     dsa_status st = check_device();
     if (st) return st;
-    return launched(dsa::launch_values_to_f16(kvb, (int64_t)N * H, d_nope, d_v, (hipStream_t)stream));
+    return launched(dsa::launch_values_to_vt(kvb, N, H, d_nope, d_v, (int)Np, vt, (hipStream_t)stream));
 }
 
 dsa_status dsa_kv_b_proj(const uint16_t* kv, int32_t kv_cols, const uint16_t* wkvb, int32_t N, int32_t H,
-                         int32_t d_latent, int32_t d_nope, int32_t d_v, int32_t values_f16, uint16_t* kvb,
+                         int32_t d_latent, int32_t d_nope, int32_t d_v, uint16_t* kvb, uint16_t* vt,
                          void* stream) {
-    if (!kv || !wkvb || !kvb || !aligned16(kv) || !aligned16(wkvb) || !aligned16(kvb) || N < 0 || H <= 0 ||
-        d_latent <= 0 || d_latent > kv_cols || kv_cols % 8 != 0 || d_nope < 0 || d_v <= 0 ||
-        (values_f16 != 0 && values_f16 != 1))
+    if (!kv || !wkvb || !kvb || !aligned16(kv) || !aligned16(wkvb) || !aligned16(kvb) || (vt && !aligned16(vt)) ||
+        N < 0 || H <= 0 || d_latent <= 0 || d_latent > kv_cols || kv_cols % 8 != 0 || d_nope < 0 || d_v <= 0)
         return DSA_ERR_INVALID_ARG;
     const int64_t n_out = (int64_t)H * (d_nope + d_v);
     if (d_latent % 64 != 0 || n_out % 256 != 0 || n_out > INT32_MAX || (int64_t)N * kv_cols * 2 >= (1ll << 32) ||
@@ -375,10 +380,14 @@ dsa_status dsa_kv_b_proj(const uint16_t* kv, int32_t kv_cols, const uint16_t* wk
     if (N == 0) return DSA_OK;
     dsa_status st = check_device();
     if (st) return st;
+    const int64_t Np = ((int64_t)N + 63) / 64 * 64;
+    if (vt && (int64_t)H * d_v * Np >= ((int64_t)1 << 40)) return DSA_ERR_UNSUPPORTED;
     dsa::GemmArgs g{kv, kv_cols, 0, wkvb, d_latent, 0, kvb, n_out, 0, N, (int32_t)n_out, d_latent};
-    if (values_f16) {
-        g.f16_from = d_nope;
-        g.f16_period = d_nope + d_v;
+    if (vt) {
+        g.vt = vt;
+        g.vt_from = d_nope;
+        g.vt_period = d_nope + d_v;
+        g.vt_np = (int32_t)Np;
     }
     return launched(dsa::launch_kv_b_proj(g, (hipStream_t)stream));
 }

@@ -186,9 +186,12 @@ struct GemmArgs {            // C[m, n] = sum_k A[m, k] B[n, k], per batch z
     void* C;                 // element (z, m, n) at z*c_batch + m*ldc + n (bf16 or float32)
     int64_t ldc, c_batch;
     int32_t M, N, K;
-    // bf16 output only: columns n with n % f16_period >= f16_from are written
-    // as fp16 instead (0 / 0: none)
-    int32_t f16_from = 0, f16_period = 0;
+    // bf16 output only, the kv_b value form: column n with
+    // n % vt_period >= vt_from goes to vt[n / vt_period][n % vt_period -
+    // vt_from][.] in fp16 (keys in the dense tile order, stride vt_np, rows
+    // from M up to vt_np written as zeros) instead of to C
+    uint16_t* vt = nullptr;
+    int32_t vt_from = 0, vt_period = 0, vt_np = 0;
 };
 // value up-projection: A float32, C bf16, N == 256, K % 64 == 0
 hipError_t launch_value_up_proj(const GemmArgs& g, int batch, hipStream_t s);
@@ -218,9 +221,12 @@ struct DenseArgs {
     int32_t L, N, H, q_start, kv_cols, rope_col, W;
     float scale_log2;       // softmax_scale * log2(e)
     float* out;             // [L, H, Dv]
+    const uint16_t* vt;     // fp16 values [H][Dv][Np] in the tile key order, or null: bf16 values in kvb
+    int32_t Np;             // vt's key stride: N rounded up to 64
 };
-hipError_t launch_dense_attn(int shape_id, const DenseArgs& a, bool values_f16, hipStream_t s);
-// The value columns of kvb [rows, Dn + Dv] converted bf16 -> fp16 in place.
-hipError_t launch_values_to_f16(uint16_t* kvb, int64_t rows, int dn, int dv, hipStream_t s);
+hipError_t launch_dense_attn(int shape_id, const DenseArgs& a, hipStream_t s);
+// The value columns of kvb [N, H, Dn + Dv] -> vt [H][Dv][Np] fp16 (tile key order, zero past N).
+hipError_t launch_values_to_vt(const uint16_t* kvb, int N, int H, int dn, int dv, int Np, uint16_t* vt,
+                               hipStream_t s);
 
 }  // namespace dsa

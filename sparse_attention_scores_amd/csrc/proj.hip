@@ -229,6 +229,47 @@ void gemm_nt_kernel(GemmArgs g) {
     }
 
     // accumulator element r of tile (i, j): row 8(r/4) + 4(lane/32) + r%4, column lane%32
+    if constexpr (!C_F32) {
+        if (g.vt) {
+            // kv_b value form: a lane's 4 consecutive rows of a value column
+            // are 4 consecutive positions of one vt feature row (8 bytes)
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int mb = m0 + 64 * wm + 32 * i + 8 * q + 4 * (l >> 5);
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) {
+                        const int n = n0 + (BN / 2) * wn + 32 * j + (l & 31), c = n % g.vt_period;
+                        if (c >= g.vt_from) {
+                            if (mb >= g.vt_np) continue;
+                            uint32_t two[2];
+#pragma unroll
+                            for (int e = 0; e < 2; ++e) {
+                                const float lo = mb + 2 * e < g.M ? acc[i][j][4 * q + 2 * e] : 0.f;
+                                const float hi = mb + 2 * e + 1 < g.M ? acc[i][j][4 * q + 2 * e + 1] : 0.f;
+                                two[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+                                         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+                            }
+                            const int64_t frow = (int64_t)(n / g.vt_period) * (g.vt_period - g.vt_from) + (c - g.vt_from);
+                            const int k = mb & 31;
+                            *reinterpret_cast<u32x2*>(g.vt + frow * g.vt_np + (mb - k) + 8 * ((k & 15) >> 2) + 4 * (k >> 4)) =
+                                u32x2{two[0], two[1]};
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                if (mb + e >= g.M) continue;
+                                const uint32_t u = __float_as_uint(acc[i][j][4 * q + e]);
+                                static_cast<uint16_t*>(g.C)[(int64_t)(mb + e) * g.ldc + n] =
+                                    (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+                            }
+                        }
+                    }
+                }
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -241,8 +282,6 @@ void gemm_nt_kernel(GemmArgs g) {
                 const int64_t off = z * g.c_batch + (int64_t)m * g.ldc + n;
                 if constexpr (C_F32) {
                     static_cast<float*>(g.C)[off] = acc[i][j][r];
-                } else if (g.f16_period > 0 && n % g.f16_period >= g.f16_from) {
-                    static_cast<uint16_t*>(g.C)[off] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][r]);
                 } else {
                     const uint32_t u = __float_as_uint(acc[i][j][r]);
                     static_cast<uint16_t*>(g.C)[off] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);

@@ -50,3 +50,19 @@ def row_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
     if (~ok).any():   # rows whose reference is exactly zero must be exactly zero
         worst = max(worst, float(num[~ok].max()) * 1e30)
     return worst
+
+
+def vt_position(k: np.ndarray) -> np.ndarray:
+    """Position of key k in a feature row of the dense path's fp16 value form
+    (include/dsa.h, dsa_dense_masked_attn_f16): 32 (k / 32) + vt_pos(k % 32)."""
+    x = k % 32
+    return 32 * (k // 32) + 8 * ((x % 16) // 4) + 4 * (x // 16) + x % 4
+
+
+def vt_layout(vals: np.ndarray, Np: int) -> np.ndarray:
+    """[N, H, Dv] 16-bit patterns -> the [H, Dv, Np] value form, zeros past N."""
+    N, H, Dv = vals.shape
+    out = np.zeros((H, Dv, Np), dtype=vals.dtype)
+    out[:, :, vt_position(np.arange(N))] = np.transpose(vals, (1, 2, 0))
+    return out
+

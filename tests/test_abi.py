@@ -183,20 +183,26 @@ def test_dense_validation():
     assert f(*args(dn=48, dr=16)) == UNSUPPORTED
     assert f(*args(dn=192, dr=64, dv=256, kv_cols=576, rope_col=512, Lq=0)) == OK
     g = L.dsa_dense_masked_attn_f16
-    assert g(*args(Lq=0)) == OK
-    assert g(*args(W=W - 2)) == INVALID
-    assert g(*args(dn=32, dr=32)) == UNSUPPORTED
-    assert L.dsa_values_to_f16(None, 8, 4, 64, 64, None) == INVALID
-    assert L.dsa_values_to_f16(fake(0x1008), 8, 4, 64, 64, None) == INVALID
-    assert L.dsa_values_to_f16(fake(), 8, 4, 60, 64, None) == INVALID
-    assert L.dsa_values_to_f16(fake(), 8, 0, 64, 64, None) == INVALID
-    assert L.dsa_values_to_f16(fake(), 0, 4, 192, 256, None) == OK
+    gargs = lambda **kw: args(**kw)[:2] + [kw.get("vt", fake())] + args(**kw)[2:]
+    assert g(*gargs(Lq=0)) == OK
+    assert g(*gargs(vt=None)) == INVALID
+    assert g(*gargs(vt=fake(0x1008), Lq=0)) == INVALID
+    assert g(*gargs(W=W - 2)) == INVALID
+    assert g(*gargs(dn=32, dr=32)) == UNSUPPORTED
+    v = L.dsa_values_to_f16
+    assert v(None, 8, 4, 64, 64, fake(), None) == INVALID
+    assert v(fake(), 8, 4, 64, 64, None, None) == INVALID
+    assert v(fake(0x1008), 8, 4, 64, 64, fake(), None) == INVALID
+    assert v(fake(), 8, 4, 60, 64, fake(), None) == INVALID
+    assert v(fake(), 8, 0, 64, 64, fake(), None) == INVALID
+    assert v(fake(), 8, 4, 64, 128, fake(), None) == UNSUPPORTED
+    assert v(fake(), 0, 4, 192, 256, fake(), None) == OK
     k = L.dsa_kv_b_proj
-    assert k(fake(), 576, fake(), 0, 64, 512, 192, 256, 1, fake(), None) == OK
-    assert k(None, 576, fake(), 8, 64, 512, 192, 256, 1, fake(), None) == INVALID
-    assert k(fake(), 576, fake(), 8, 64, 512, 192, 256, 2, fake(), None) == INVALID
-    assert k(fake(), 576, fake(), 8, 64, 640, 192, 256, 1, fake(), None) == INVALID
-    assert k(fake(), 572, fake(), 8, 64, 512, 192, 256, 1, fake(), None) == INVALID
-    assert k(fake(), 576, fake(), 8, 64, 480, 192, 256, 1, fake(), None) == UNSUPPORTED
-    assert k(fake(), 576, fake(), 8, 3, 512, 192, 256, 1, fake(), None) == UNSUPPORTED
-
+    assert k(fake(), 576, fake(), 0, 64, 512, 192, 256, fake(), fake(), None) == OK
+    assert k(fake(), 576, fake(), 0, 64, 512, 192, 256, fake(), None, None) == OK
+    assert k(None, 576, fake(), 8, 64, 512, 192, 256, fake(), fake(), None) == INVALID
+    assert k(fake(), 576, fake(), 8, 64, 512, 192, 256, fake(), fake(0x1008), None) == INVALID
+    assert k(fake(), 576, fake(), 8, 64, 640, 192, 256, fake(), fake(), None) == INVALID
+    assert k(fake(), 572, fake(), 8, 64, 512, 192, 256, fake(), fake(), None) == INVALID
+    assert k(fake(), 576, fake(), 8, 64, 480, 192, 256, fake(), fake(), None) == UNSUPPORTED
+    assert k(fake(), 576, fake(), 8, 3, 512, 192, 256, fake(), fake(), None) == UNSUPPORTED

@@ -4,7 +4,8 @@ the same selection (the oracle's top-k of seeded indexer scores).
 
 - selection mask: integer work, bit-exact over every row;
 - value conversion: bit-exact against numpy's round-to-nearest-even
-  float32 -> float16 of the decoded bf16 values (key columns untouched);
+  float32 -> float16 of the decoded bf16 values, laid out in the vt form
+  (feature-major, keys in the tile order, zero padding);
 - attention: max over (query, head) rows of max|o - r| / max|r| <= 2e-3.
   The GPU sums bf16 products in fp32, rounds the probabilities to fp16
   (relative 2^-11) and converts the values to fp16 (exact here); the oracle
@@ -20,7 +21,7 @@ import pytest
 
 import oracle
 import workloads as W
-from tests.gpu_util import ATTN_TOL, dev, host, requires_gpu, row_rel_err, say
+from tests.gpu_util import ATTN_TOL, dev, host, requires_gpu, row_rel_err, say, vt_layout
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -59,15 +60,15 @@ def run(cfg, empty_rows=(), rows=None):
     assert err <= ATTN_TOL, err
     for r in empty_rows:
         assert not got[r].any()
-    # the fp16-value entry on the same inputs: values converted in place first
-    kvb16 = dev(d["kvb"])
-    dsa.dsa_values_to_f16(kvb16, cfg.N, cfg.H, cfg.Dn, cfg.Dv)
-    conv = host(kvb16)
-    want = W.bf16_bits_to_f32(d["kvb"][..., cfg.Dn:]).astype(np.float16).view(np.uint16)
-    assert np.array_equal(conv[..., :cfg.Dn], d["kvb"][..., :cfg.Dn])
-    assert np.array_equal(conv[..., cfg.Dn:], want)
+    # the fp16-value entry on the same inputs: values converted to the vt form first
+    Np = dsa.vt_keys(cfg.N)
+    kvb_d = dev(d["kvb"])
+    vt = torch.full((cfg.H, cfg.Dv, Np), -1, dtype=torch.int16, device="cuda")   # padding must be written
+    dsa.dsa_values_to_f16(kvb_d, cfg.N, cfg.H, cfg.Dn, cfg.Dv, vt)
+    want = vt_layout(W.bf16_bits_to_f32(d["kvb"][..., cfg.Dn:]).astype(np.float16).view(np.uint16), Np)
+    assert np.array_equal(host(vt), want)
     out16 = torch.empty_like(out)
-    dsa.dsa_dense_masked_attn_f16(dev(d["q"]), kvb16, dev(d["kv"]), cfg.Dl + cfg.Dr, cfg.Dl, mask,
+    dsa.dsa_dense_masked_attn_f16(dev(d["q"]), kvb_d, vt, dev(d["kv"]), cfg.Dl + cfg.Dr, cfg.Dl, mask,
                                   cfg.L, cfg.N, cfg.q_start, cfg.H, cfg.Dn, cfg.Dr, cfg.Dv, 1.0 / 16, out16)
     got16 = host(out16)
     err16 = row_rel_err(got16[rows], ref)

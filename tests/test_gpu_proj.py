@@ -20,7 +20,7 @@ import pytest
 
 import oracle
 import workloads as W
-from tests.gpu_util import dev, host, requires_gpu, row_rel_err, say
+from tests.gpu_util import dev, host, requires_gpu, row_rel_err, say, vt_position
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -138,9 +138,17 @@ def test_kv_b_proj_matches_oracle(name, f16):
     C = cfg.Dn + cfg.Dv
     kc = cfg.Dl + cfg.Dr
     say("kv_b_proj", name, "N=%d" % cfg.N, "f16" if f16 else "bf16")
-    out = torch.empty((cfg.N, cfg.H, C), dtype=torch.int16, device="cuda")
-    dsa.dsa_kv_b_proj(dev(d["kv"]), kc, dev(w), cfg.N, cfg.H, cfg.Dl, cfg.Dn, cfg.Dv, f16, out)
+    out = torch.zeros((cfg.N, cfg.H, C), dtype=torch.int16, device="cuda")
+    Np = dsa.vt_keys(cfg.N)
+    vt = torch.full((cfg.H, cfg.Dv, Np), -1, dtype=torch.int16, device="cuda") if f16 else None
+    dsa.dsa_kv_b_proj(dev(d["kv"]), kc, dev(w), cfg.N, cfg.H, cfg.Dl, cfg.Dn, cfg.Dv, out, vt)
     got = host(out)
+    if f16:
+        # values from the vt form back to [N, H, Dv]; its padding must be zeros
+        vh = host(vt)
+        pos = vt_position(np.arange(cfg.N))
+        assert not vh[:, :, np.setdiff1d(np.arange(Np), pos)].any()
+        got[..., cfg.Dn:] = np.transpose(vh[:, :, pos], (2, 0, 1))
     rows = np.arange(cfg.N) if cfg.N <= 1024 else W.sample_rows(cfg.N, 48, seed=11, must=[0, cfg.N - 1])
     want = oracle.kv_b_proj(d["kv"][rows], w, cfg.H, cfg.Dl, cfg.Dn, cfg.Dv, f16)
     g = got[rows]
