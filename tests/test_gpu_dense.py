@@ -14,8 +14,9 @@ the same selection (the oracle's top-k of seeded indexer scores).
 Cases: 160 GLM-width queries over 700 keys (ragged query block and key
 tile), two tiny-width chunks (several query blocks and tiles, a first chunk
 whose early queries take every earlier key, a row with an empty selection),
-and the 8k-key chunk the benchmark times (4096 queries, every head; the
-oracle runs on a seeded sample of rows)."""
+the 8k-key chunk the benchmark times (4096 queries, every head; the oracle
+runs on a seeded sample of rows), the first 4096-query chunk at GLM widths,
+and the widest selection mask the entry takes."""
 import numpy as np
 import pytest
 
@@ -111,3 +112,34 @@ def test_dense_rejects_bad_arguments():
         dsa.dsa_dense_masked_attn(q, kvb, kv, 128, 64, mask[:, :2].contiguous(), cfg.L, cfg.N, 0, cfg.H, 64, 64, 64, 0.0625, out)
     with pytest.raises(dsa.DsaError):   # rope key past the cache row
         dsa.dsa_dense_masked_attn(q, kvb, kv, 128, 72, mask, cfg.L, cfg.N, 0, cfg.H, 64, 64, 64, 0.0625, out)
+
+
+def test_dense_glm_first_chunk_sampled():
+    """The first 4096-query chunk at GLM widths: queries 0..2047 take every
+    earlier key (the causal regime the pages route to a causal kernel), the
+    rest a real top-2048 selection."""
+    cfg = W.DENSE["glm_4k_first"]
+    run(cfg, rows=W.sample_rows(cfg.L, 12, seed=10, must=[0, 1, 2046, 2047, 2048, cfg.L - 1]))
+
+
+def test_selection_mask_widest_rows():
+    """The widest mask the entry takes (16384 words: 524288 keys) is written
+    bit-exactly, padding and out-of-range ids included; one word wider is
+    refused."""
+    import torch
+    import sparse_attention_scores_amd as dsa
+    L, top_k, N = 6, 2048, 524288
+    rng = np.random.default_rng(12)
+    q_start = N - L
+    idx = np.sort(rng.choice(N, size=(L, top_k), replace=True), axis=1).astype(np.int32)
+    idx[:, :3] = [-1, N, N + 7]          # ignored entries
+    idx[0, -1] = q_start + 5             # after query 0's position: not causal for it
+    cnt = np.array([top_k, top_k - 1, 0, 17, top_k, 1000], np.int32)
+    say("selection mask widest", N)
+    mask = torch.empty((L, dsa.mask_words(N)), dtype=torch.int32, device="cuda")
+    dsa.dsa_selection_mask(dev(idx), dev(cnt), L, top_k, N, q_start, mask)
+    want = oracle.selection_mask(idx, cnt, N, q_start)
+    assert np.array_equal(host(mask).view(np.uint32), want)
+    wide = torch.empty((L, dsa.mask_words(N) + 2), dtype=torch.int32, device="cuda")
+    with pytest.raises(dsa.DsaError):
+        dsa.dsa_selection_mask(dev(idx), dev(cnt), L, top_k, N + 64, q_start, wide)
