@@ -307,7 +307,7 @@ dsa_status dsa_dense_masked_attn_f16(const uint16_t* q, const uint16_t* kvb, con
  * magnitudes become fp16 subnormals, larger ones infinities), positions
  * N..Np-1 zero.  Requires kvb and vt 16-byte aligned and not overlapping,
  * N >= 0 (0: nothing is enqueued), H >= 1, d_nope a multiple of 8; d_v 64
- * or 256 (DSA_ERR_UNSUPPORTED otherwise). */
+ * or 256 and H <= 65535 (DSA_ERR_UNSUPPORTED otherwise). */
 dsa_status dsa_values_to_f16(const uint16_t* kvb, int32_t N, int32_t H, int32_t d_nope, int32_t d_v, uint16_t* vt,
                              void* stream);
 

@@ -360,7 +360,7 @@ dsa_status dsa_values_to_f16(const uint16_t* kvb, int32_t N, int32_t H, int32_t 
         return DSA_ERR_INVALID_ARG;
     if (d_v != 256 && d_v != 64) return DSA_ERR_UNSUPPORTED;
     const int64_t Np = ((int64_t)N + 63) / 64 * 64;
-    if (Np > INT32_MAX || Np / 64 > 0x7FFFFFFF || H > 65535) return DSA_ERR_UNSUPPORTED;
+    if (Np > INT32_MAX || H > 65535) return DSA_ERR_UNSUPPORTED;   // grid (Np / 64, H)
     if (N == 0) return DSA_OK;
     dsa_status st = check_device();
     if (st) return st;
