@@ -233,14 +233,17 @@ void gemm_nt_kernel(GemmArgs g) {
         if (g.vt) {
             // kv_b value form: a lane's 4 consecutive rows of a value column
             // are 4 consecutive positions of one vt feature row (8 bytes)
+            // the column (and so the target) depends on j only: one division per j
 #pragma unroll
-            for (int i = 0; i < MT; ++i) {
+            for (int j = 0; j < NT; ++j) {
+                const int n = n0 + (BN / 2) * wn + 32 * j + (l & 31);
+                const int hq = n / g.vt_period, c = n - hq * g.vt_period;
+                const int64_t frow = (int64_t)hq * (g.vt_period - g.vt_from) + (c - g.vt_from);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int mb = m0 + 64 * wm + 32 * i + 8 * q + 4 * (l >> 5);
+                for (int i = 0; i < MT; ++i) {
 #pragma unroll
-                    for (int j = 0; j < NT; ++j) {
-                        const int n = n0 + (BN / 2) * wn + 32 * j + (l & 31), c = n % g.vt_period;
+                    for (int q = 0; q < 4; ++q) {
+                        const int mb = m0 + 64 * wm + 32 * i + 8 * q + 4 * (l >> 5);
                         if (c >= g.vt_from) {
                             if (mb >= g.vt_np) continue;
                             uint32_t two[2];
@@ -251,7 +254,6 @@ void gemm_nt_kernel(GemmArgs g) {
                                 two[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
                                          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
                             }
-                            const int64_t frow = (int64_t)(n / g.vt_period) * (g.vt_period - g.vt_from) + (c - g.vt_from);
                             const int k = mb & 31;
                             *reinterpret_cast<u32x2*>(g.vt + frow * g.vt_np + (mb - k) + 8 * ((k & 15) >> 2) + 4 * (k >> 4)) =
                                 u32x2{two[0], two[1]};
