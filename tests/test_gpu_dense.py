@@ -143,3 +143,12 @@ def test_selection_mask_widest_rows():
     wide = torch.empty((L, dsa.mask_words(N) + 2), dtype=torch.int32, device="cuda")
     with pytest.raises(dsa.DsaError):
         dsa.dsa_selection_mask(dev(idx), dev(cnt), L, top_k, N + 64, q_start, wide)
+
+
+def test_dense_single_query():
+    """One query (a block of one row: 127 query slots and 7 of 8 waves idle)
+    at the end of a ragged key range, and one at position 0 (a single key)."""
+    import dataclasses
+    for q_start, N in ((299, 300), (0, 1)):
+        cfg = dataclasses.replace(W.DENSE["tiny"], name="tiny_one_%d" % q_start, L=1, N=N, q_start=q_start)
+        run(cfg)
