@@ -58,7 +58,7 @@ extern "C" {
 typedef enum {
     DSA_OK = 0,
     DSA_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size or position */
-    DSA_ERR_UNSUPPORTED = -2,   /* shape, size or device this build does not handle */
+    DSA_ERR_UNSUPPORTED = -2,   /* shape, size or device this library does not handle */
     DSA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
     DSA_ERR_HIP = -4            /* a HIP runtime call or kernel launch failed */
 } dsa_status;

@@ -173,7 +173,7 @@ const char* dsa_status_string(dsa_status status) {
     switch (status) {
         case DSA_OK: return "DSA_OK";
         case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG: null or misaligned pointer, or bad size/position";
-        case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: shape, size or device not handled by this build";
+        case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: shape, size or device not handled by this library";
         case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
         case DSA_ERR_HIP: return "DSA_ERR_HIP: a HIP call or kernel launch failed";
     }

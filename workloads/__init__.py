@@ -11,7 +11,7 @@ description in exo PR #2539 (Prefill section, float32 indexer item: 32
 indexer heads).  The indexer width 128 is not on the pages; it is the
 DeepSeek-V3.2 indexer head size and is taken as a parameter.
 
-Value recipe (stated once here, repeated in the design doc):
+Value recipe:
   draw order  qI, kI, w, q, kv from ``numpy.random.default_rng(seed)``;
   qI, kI      integers uniform in [-r, r] (r = 4 tiny, 8 GLM), exact in bf16;
   w           uniform choice of {0.5, 1, 2} (powers of two), fp32;
