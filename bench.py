@@ -325,6 +325,11 @@ def timed_events(fn, n: int, torch):
 
 
 def cpu_baseline(cfg, d, rows_n: int):
+    """The oracle as it stands on a bounded, evenly spaced sample of the
+    chunk's queries.  It runs one thread per visible host core, capped at
+    oracle.MAX_THREADS (the CPU share a GPU gets on the measurement hosts);
+    `cores` is the number of threads it actually used, and the host's own
+    core counts are reported beside it."""
     import numpy as np
     import oracle
     rows = np.linspace(0, cfg.L - 1, rows_n).round().astype(np.int64)
@@ -332,9 +337,144 @@ def cpu_baseline(cfg, d, rows_n: int):
     t0 = time.perf_counter()
     oracle.prefill_chunk(d, cfg.shape, cfg.q_start, rows=rows, nthreads=threads)
     dt = time.perf_counter() - t0
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     return {"value": rows.size / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "host_cpus_usable": affinity, "thread_cap": oracle.MAX_THREADS,
+            "capped": bool(affinity and affinity > threads),
             "sample": "%d evenly spaced queries of the same 16k chunk (indexer, top-k and attention per "
-                      "query, fp64), %.1f s wall" % (rows.size, dt)}
+                      "query, fp64), %.1f s wall on %d threads" % (rows.size, dt, threads)}
+
+
+def describe_prefill(cfg) -> str:
+    sh = cfg.shape
+    return ("prefill chunk: L=%d queries at positions %d..%d over N=%d keys; %d heads x %d (%d latent + %d rope), "
+            "value %d; indexer %d x %d; top_k %d" % (cfg.L, cfg.q_start, cfg.q_start + cfg.L - 1, cfg.N, sh.n_heads,
+                                                     sh.d_qk, sh.d_latent, sh.d_rope, sh.d_latent, sh.n_idx_heads,
+                                                     sh.d_idx, sh.top_k))
+
+
+ATTN_KERNELS = {64: "attention_kernel<64,512,64,true>", 4: "attention_kernel<4,64,16,true>"}
+
+
+def prefill_case(name, K, Wm, n_stage, np, torch, dsa, W, d=None):
+    """One prefill chunk end to end (dsa_prefill_chunk, K timed steps after
+    Wm warm-ups, wall clock around synchronisations), then each stage it runs
+    as a standalone call on the same inputs, timed by HIP events: the
+    indexer over the scored rows only (p + 1 > top_k), the top-k, the latent
+    conversion and the attention; for a chunk that holds both kinds of rows
+    the attention of its dense-causal rows (every earlier key) and of its
+    sparse rows are also timed apart.  Returns (result dict, tensors)."""
+    cfg = W.PREFILL[name]
+    sh = cfg.shape
+    log("generating", name)
+    if d is None:
+        d = W.make_prefill(cfg)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else a).cuda()
+    q, qI, w, kv, kI = (to(d[k]) for k in ("q", "qI", "w", "kv", "kI"))
+    out = torch.empty((cfg.L, sh.n_heads, sh.d_latent), dtype=torch.float32, device="cuda")
+    idx = torch.empty((cfg.L, sh.top_k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((cfg.L,), dtype=torch.int32, device="cuda")
+    ws = torch.empty((dsa.dsa_prefill_workspace_bytes(sh, cfg.L, cfg.N, cfg.q_start),), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        dsa.dsa_prefill_chunk(sh, q, qI, w, kv, kI, cfg.L, cfg.N, cfg.q_start, out, idx, cnt, ws)
+
+    log(name, "warmup", Wm)
+    for _ in range(Wm):
+        step()
+    torch.cuda.synchronize()
+    log(name, "timed", K)
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / K
+    wk = work_prefill(cfg)
+    flop = wk["idx_flop"] + wk["attn_flop"]
+    res = {"workload": describe_prefill(cfg), "L": cfg.L, "q_start": cfg.q_start, "N": cfg.N, "top_k": sh.top_k,
+           "ms_per_step": dt * 1e3, "queries_per_s": cfg.L / dt, "tflops": flop / dt / 1e12,
+           "mfma_peak_frac": flop / dt / 1e12 / PEAK_MFMA_TFLOPS}
+    if n_stage <= 0:
+        return res, (q, kv, idx, cnt)
+    row0 = max(0, min(cfg.L, sh.top_k - cfg.q_start))
+    S = torch.empty((cfg.L, cfg.N), dtype=torch.float32, device="cuda")
+    idx2, cnt2, out2 = torch.empty_like(idx), torch.empty_like(cnt), torch.empty_like(out)
+    kv16 = torch.empty_like(kv)
+    calls = {}
+    if row0 < cfg.L:
+        calls["indexer"] = lambda: dsa.dsa_indexer_scores(sh, qI[row0:], kI, w[row0:], cfg.L - row0, cfg.N,
+                                                          cfg.q_start + row0, S[row0:])
+    calls["topk"] = lambda: dsa.dsa_topk_select(sh, S, cfg.L, cfg.N, cfg.q_start, idx2, cnt2)
+    calls["latent_to_f16"] = lambda: dsa.dsa_latent_to_f16(sh, kv, cfg.N, kv16)
+    calls["attention"] = lambda: dsa.dsa_sparse_mla_attn_f16(sh, q, kv16, idx, cnt, cfg.L, cfg.N, out2, None)
+    if 0 < row0 < cfg.L:
+        calls["attention_dense_rows"] = lambda: dsa.dsa_sparse_mla_attn_f16(
+            sh, q[:row0], kv16, idx[:row0], cnt[:row0], row0, cfg.N, out2[:row0], None)
+        calls["attention_sparse_rows"] = lambda: dsa.dsa_sparse_mla_attn_f16(
+            sh, q[row0:], kv16, idx[row0:], cnt[row0:], cfg.L - row0, cfg.N, out2[row0:], None)
+    for f in calls.values():
+        f()
+    torch.cuda.synchronize()
+    t = {k: timed_events(f, n_stage, torch) for k, f in calls.items()}
+    st = {}
+    if "indexer" in t:
+        tf = wk["idx_flop"] / t["indexer"] / 1e12
+        st["indexer"] = {"us": t["indexer"] * 1e6, "tflops": tf, "frac": tf / PEAK_MFMA_TFLOPS,
+                         "rows": cfg.L - row0,
+                         "note": "rows with p+1 > top_k only (the chunk's own indexer work); the standalone "
+                                 "call also writes -inf past each query"}
+    gb = wk["topk_bytes"] / t["topk"] / 1e9
+    st["topk"] = {"us": t["topk"] * 1e6, "gbps": gb, "frac": gb / PEAK_HBM_GBPS}
+    conv_bytes = 2 * 2 * sh.d_qk * cfg.N
+    gb = conv_bytes / t["latent_to_f16"] / 1e9
+    st["latent_to_f16"] = {"us": t["latent_to_f16"] * 1e6, "gbps": gb, "frac": gb / PEAK_HBM_GBPS}
+    tf = wk["attn_flop"] / t["attention"] / 1e12
+    st["attention"] = {"kernel": ATTN_KERNELS[sh.n_heads], "us": t["attention"] * 1e6, "tflops": tf,
+                       "frac": tf / PEAK_MFMA_TFLOPS,
+                       "gather_logical_gbps": wk["gather_bytes"] / t["attention"] / 1e9,
+                       "gather_note": "selected-row bytes per second, cache hits included (not HBM traffic)"}
+    if "attention_dense_rows" in t:
+        top_k = sh.top_k
+        for key, rows in (("attention_dense_rows", range(cfg.q_start, cfg.q_start + row0)),
+                          ("attention_sparse_rows", range(cfg.q_start + row0, cfg.q_start + cfg.L))):
+            fl = 2.0 * sh.n_heads * (sh.d_qk + sh.d_latent) * sum(min(p + 1, top_k) for p in rows)
+            tf = fl / t[key] / 1e12
+            st[key] = {"us": t[key] * 1e6, "rows": len(rows), "tflops": tf, "frac": tf / PEAK_MFMA_TFLOPS}
+    res["stages"] = st
+    del S, idx2, cnt2, out2, kv16
+    return res, (q, kv, idx, cnt)
+
+
+def kernel_breakdown(fn, n: int, torch):
+    """Average device time (us) per call of each kernel fn launches, from the
+    torch profiler's device activity trace over n calls; None if the
+    profiler is unavailable."""
+    import re
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+        out = {}
+        for e in prof.key_averages():
+            dt = getattr(e, "self_device_time_total", None)
+            if dt is None:
+                dt = getattr(e, "self_cuda_time_total", 0)
+            if not dt or "kernel" not in e.key:
+                continue
+            m = re.search(r"(\w+_kernel)(<[^>]*>)?", e.key)
+            name = (m.group(1) + (m.group(2) or "")).replace(" ", "") if m else e.key[:60]
+            out[name] = out.get(name, 0.0) + dt / n
+        return out or None
+    except Exception as ex:   # the profiler is a diagnostic, never a failure of the run
+        log("kernel breakdown unavailable:", repr(ex)[:200])
+        return None
 
 
 def main() -> int:
@@ -376,82 +516,44 @@ def main() -> int:
     # ---------------- prefill chunk (headline) ----------------
     cfg = W.PREFILL[PREFILL]
     sh = cfg.shape
-    log("generating", PREFILL)
     d = W.make_prefill(cfg)
-    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else a).cuda()
-    q, qI, w, kv, kI = (to(d[k]) for k in ("q", "qI", "w", "kv", "kI"))
-    out = torch.empty((cfg.L, sh.n_heads, sh.d_latent), dtype=torch.float32, device="cuda")
-    idx = torch.empty((cfg.L, sh.top_k), dtype=torch.int32, device="cuda")
-    cnt = torch.empty((cfg.L,), dtype=torch.int32, device="cuda")
-    ws = torch.empty((dsa.dsa_prefill_workspace_bytes(sh, cfg.L, cfg.N, cfg.q_start),), dtype=torch.uint8,
-                     device="cuda")
-    torch.cuda.synchronize()
-
-    def step():
-        dsa.dsa_prefill_chunk(sh, q, qI, w, kv, kI, cfg.L, cfg.N, cfg.q_start, out, idx, cnt, ws)
-
-    log("prefill warmup", Wm)
-    for _ in range(Wm):
-        step()
-    torch.cuda.synchronize()
-    log("prefill timed", K)
-    t0 = time.perf_counter()
-    for _ in range(K):
-        step()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / K
-    wk = work_prefill(cfg)
-    tflops = (wk["idx_flop"] + wk["attn_flop"]) / dt / 1e12
+    n = max(K, 3)
+    head, keep = prefill_case(PREFILL, K, Wm, 0 if args.skip_stages else n, np, torch, dsa, W, d=d)
+    dt = head["ms_per_step"] / 1e3
     result = {
-        "metric": METRIC, "value": cfg.L / dt, "unit": "queries/s", "n_gpus": 1, "steps": K, "warmup": Wm,
-        "ms_per_step": dt * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "prefill chunk, GLM-5.x shapes: L=4096 queries at positions 12288..16383 over "
-                               "N=16384 keys; 64 heads x 576 (512 latent + 64 rope), value 512; indexer 32 x 128; "
-                               "top_k 2048", "L": cfg.L, "q_start": cfg.q_start, "N": cfg.N,
-                   "top_k": sh.top_k},
-        "tflops": tflops, "mfma_peak_frac": tflops / PEAK_MFMA_TFLOPS,
+        "metric": METRIC, "value": head["queries_per_s"], "unit": "queries/s", "n_gpus": 1, "steps": K,
+        "warmup": Wm, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16+fp16",
+        "dtype_detail": "bf16 inputs; indexer and the rope part of the score on bf16 MFMA; the latent part of the "
+                        "score and the value product on fp16 MFMA (latent cache converted bf16->fp16 once per "
+                        "chunk, probabilities rounded to fp16 nearest-even); fp32 accumulation and softmax; "
+                        "latent values must lie within +-65504",
+        "data": "synthetic",
+        "config": {"workload": head["workload"], "L": cfg.L, "q_start": cfg.q_start, "N": cfg.N, "top_k": sh.top_k},
+        "tflops": head["tflops"], "mfma_peak_frac": head["mfma_peak_frac"],
     }
+    del keep
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else a).cuda()
 
     # ---------------- per-stage rooflines (same kernels, same inputs) ----------------
     if not args.skip_stages:
-        S = torch.empty((cfg.L, cfg.N), dtype=torch.float32, device="cuda")
-        idx2 = torch.empty_like(idx)
-        cnt2 = torch.empty_like(cnt)
-        out2 = torch.empty_like(out)
-        n = max(K, 3)
-        kv16 = torch.empty_like(kv)
-        f_idx = lambda: dsa.dsa_indexer_scores(sh, qI, kI, w, cfg.L, cfg.N, cfg.q_start, S)
-        f_topk = lambda: dsa.dsa_topk_select(sh, S, cfg.L, cfg.N, cfg.q_start, idx2, cnt2)
-        f_conv = lambda: dsa.dsa_latent_to_f16(sh, kv, cfg.N, kv16)
-        # the attention kernel the chunk runs: fp16-latent cache
-        f_attn = lambda: dsa.dsa_sparse_mla_attn_f16(sh, q, kv16, idx, cnt, cfg.L, cfg.N, out2, None)
-        for f in (f_idx, f_topk, f_conv, f_attn):
-            f()
-        torch.cuda.synchronize()
-        log("stage timing", n)
-        t_idx = timed_events(f_idx, n, torch)
-        t_topk = timed_events(f_topk, n, torch)
-        t_conv = timed_events(f_conv, n, torch)
-        t_attn = timed_events(f_attn, n, torch)
-        conv_bytes = 2 * 2 * sh.d_qk * cfg.N
-        stages = {
-            "indexer": {"kernel": "indexer_prefill_kernel<32,128>", "us": t_idx * 1e6,
-                        "tflops": wk["idx_flop"] / t_idx / 1e12,
-                        "frac": wk["idx_flop"] / t_idx / 1e12 / PEAK_MFMA_TFLOPS,
-                        "note": "standalone call also writes -inf past each query"},
-            "topk": {"kernel": "topk_prefill_kernel<512,32>", "us": t_topk * 1e6,
-                     "gbps": wk["topk_bytes"] / t_topk / 1e9,
-                     "frac": wk["topk_bytes"] / t_topk / 1e9 / PEAK_HBM_GBPS},
-            "latent_to_f16": {"kernel": "latent_to_f16_kernel<512,64>", "us": t_conv * 1e6,
-                              "gbps": conv_bytes / t_conv / 1e9,
-                              "frac": conv_bytes / t_conv / 1e9 / PEAK_HBM_GBPS},
-            "attention": {"kernel": "attention_kernel<64,512,64,true>", "us": t_attn * 1e6,
-                          "tflops": wk["attn_flop"] / t_attn / 1e12,
-                          "frac": wk["attn_flop"] / t_attn / 1e12 / PEAK_MFMA_TFLOPS,
-                          "gather_gbps": wk["gather_bytes"] / t_attn / 1e9,
-                          "gather_hbm_frac": wk["gather_bytes"] / t_attn / 1e9 / PEAK_HBM_GBPS},
-        }
+        stages = head["stages"]
+        stages["indexer"]["kernel"] = "indexer_prefill_kernel<32,128>"
+        stages["topk"]["kernel"] = "topk_prefill_kernel<512,32>"
+        stages["latent_to_f16"]["kernel"] = "latent_to_f16_kernel<512,64>"
+        t_idx, t_topk, t_attn = (stages[k]["us"] / 1e6 for k in ("indexer", "topk", "attention"))
+        tr = measured_traffic("attention")
+        if tr is not None:
+            stages["attention"]["hbm_bytes_per_launch"] = tr
+            stages["attention"]["hbm_gbps"] = tr / t_attn / 1e9
+            stages["attention"]["hbm_frac"] = tr / t_attn / 1e9 / PEAK_HBM_GBPS
+        # the other configurations: each chunk end to end and by stage
+        result["configs"] = {}
+        for name in ("tiny", "glm_8k", "glm_first_4k"):
+            res, keep = prefill_case(name, K, Wm, n, np, torch, dsa, W)
+            result["configs"][name] = res
+            del keep
+            torch.cuda.empty_cache()
         log("cache write stage")
         cw, f_cw, cw_bytes = cache_write_setup(np, torch, dsa, W)
         f_cw()
@@ -535,7 +637,6 @@ def main() -> int:
             ach, bound, unit, peak = stages[dom]["tflops"], "mfma", "TFLOP/s", PEAK_MFMA_TFLOPS
         result["roofline"] = {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
                               "traffic": measured_traffic(dom), "kernel": stages[dom]["kernel"]}
-        del S, idx2, cnt2, out2
 
     # ---------------- batched decode ----------------
     if not args.skip_decode:
@@ -586,7 +687,9 @@ def main() -> int:
         result["decode"] = {"workload": "batched decode, 8 sequences x 1 query, contexts "
                                         + ",".join(str(c) for c in dc.ctx), "us_per_step": tdec * 1e6,
                             "us_per_step_graph": tgraph * 1e6,
-                            "steps": nd, "hbm_floor_us": moved / (PEAK_HBM_GBPS * 1e9) * 1e6}
+                            "steps": nd, "hbm_floor_us": moved / (PEAK_HBM_GBPS * 1e9) * 1e6,
+                            "hbm_floor_bytes": moved,
+                            "kernels_us": kernel_breakdown(dstep, nd, torch)}
 
     # ---------------- CPU oracle on a bounded sample ----------------
     if args.cpu_rows > 0:

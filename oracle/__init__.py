@@ -81,13 +81,16 @@ def using_library(path: str):
         _lib = saved
 
 
+MAX_THREADS = 16   # the CPU share one GPU gets on the measurement hosts
+
+
 def default_threads() -> int:
-    """Host threads for the oracle: the visible cores, at most 16."""
+    """Host threads for the oracle: the usable cores, at most MAX_THREADS."""
     try:
         n = len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
         n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+    return max(1, min(n, MAX_THREADS))
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:

@@ -45,8 +45,10 @@
 //    rows addressed by lanes i/4 + 4k) and are converted bf16 -> fp16 in
 //    registers.  The key order of a producer lane's score accumulators is
 //    exactly the consumer's probability operand.
-//  - probabilities enter the value product as fp16 (11-bit significand): a
-//    bf16 probability operand alone would cost about 1.5e-3 relative error.
+//  - probabilities enter the value product as fp16 (11-bit significand,
+//    rounded to nearest even, so the rounding is unbiased against the fp32
+//    denominator): a bf16 probability operand alone would cost about 1.5e-3
+//    relative error.
 //    Latent values are exact in fp16 for |v| in [2^-14, 65504]; smaller ones
 //    become fp16 subnormals (error at most 2^-25).
 #include "dsa_kernels.h"
@@ -111,9 +113,7 @@ __device__ inline int swz_lat(int r) {
 }
 __device__ inline int swz_rope(int r) { return (r >> 1) & 7; }
 
-__device__ inline uint32_t pack_f16(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
-}
+__device__ inline uint32_t pack_f16(float a, float b) { return pack_f16_rne(a, b); }
 
 // 4 bf16 (two dwords) -> 4 fp16
 __device__ inline u32x2 bf16x4_to_f16x4(const u32x2& d) {

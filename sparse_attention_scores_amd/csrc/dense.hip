@@ -70,9 +70,7 @@ __device__ inline u32x2 read_tr16(const unsigned char* p) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((DSA_LDS lds_bf16x4_t*)a));
 }
 
-__device__ inline uint32_t pack2_f16(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
-}
+__device__ inline uint32_t pack2_f16(float a, float b) { return pack_f16_rne(a, b); }
 
 // 4 bf16 -> 4 fp16 (exact in the fp16 normal range)
 __device__ inline u32x2 bf16x4_f16x4(const u32x2& d) {

@@ -57,6 +57,16 @@ __device__ inline f32x16 mfma32_f16(u32x4 a, u32x4 b, f32x16 c) {
 
 __device__ inline u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two fp16 in one dword (a in the low half), rounded to
+// nearest even (v_cvt_pk_f16_f32).  Unbiased: a probability rounded this way
+// keeps the value product's numerator and the fp32 denominator consistent
+// on average, where truncation would scale every output down by about 2^-11.
+__device__ inline uint32_t pack_f16_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+
 #define DSA_LDS __attribute__((address_space(3)))
 
 __device__ inline uint32_t lds_addr(const void* p) {

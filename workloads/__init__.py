@@ -31,7 +31,7 @@ import numpy as np
 
 __all__ = [
     "Shape", "TINY", "GLM", "Prefill", "Decode", "PREFILL", "DECODE",
-    "to_bf16_bits", "bf16_bits_to_f32", "make_prefill", "make_decode",
+    "to_bf16_bits", "bf16_bits_to_f32", "make_prefill", "make_prefill_fp16_range", "make_decode",
     "CacheWrite", "CACHE_WRITE", "make_cache_write", "Router", "ROUTER", "make_router",
     "Proj", "PROJ", "make_proj",
 ]
@@ -147,6 +147,35 @@ def make_prefill(cfg: Prefill) -> Dict[str, np.ndarray]:
     """Inputs of one prefill chunk.  Keys sit at positions 0..N-1."""
     rng = np.random.default_rng(cfg.seed)
     return _draw(rng, cfg.shape, cfg.L, cfg.N, cfg.int_range, cfg.q_scale, cfg.kv_scale)
+
+
+def make_prefill_fp16_range(cfg: Prefill) -> Dict[str, np.ndarray]:
+    """Inputs of one prefill chunk whose attention operands span the fp16
+    range: the indexer operands as make_prefill draws them, then (from a
+    second generator seeded cfg.seed + 1000) q and kv with a log-uniform
+    magnitude per element, rounded to bf16.
+      kv latent   N(0,1) * 2**U(-27, 15), clipped to +-2**15 (a third of the
+                  values below fp16's normal range 2**-14, the largest 2**15);
+      kv rope     N(0,1) * 2**U(-6, 2);
+      q latent    N(0,1) * 2**U(-30, -9) (most values fp16 subnormals);
+      q rope      N(0,1) * 2**U(-8, -3).
+    The softmax stays spread (the largest probability of a row is typically
+    about 0.3)."""
+    d = make_prefill(cfg)
+    rng = np.random.default_rng(cfg.seed + 1000)
+    sh = cfg.shape
+
+    def wide(shape, lo, hi, cap=None):
+        x = rng.standard_normal(size=shape) * 2.0 ** rng.uniform(lo, hi, size=shape)
+        if cap is not None:
+            x = np.clip(x, -cap, cap)
+        return x.astype(np.float32)
+
+    kv = np.concatenate([wide((cfg.N, sh.d_latent), -27, 15, 2.0 ** 15), wide((cfg.N, sh.d_rope), -6, 2)], axis=1)
+    q = np.concatenate([wide((cfg.L, sh.n_heads, sh.d_latent), -30, -9),
+                        wide((cfg.L, sh.n_heads, sh.d_rope), -8, -3)], axis=2)
+    d["q"], d["kv"] = to_bf16_bits(q), to_bf16_bits(kv)
+    return d
 
 
 def make_decode(cfg: Decode) -> Dict[str, np.ndarray]:
