@@ -31,7 +31,8 @@
  *    aligned, dense row-major with the shapes given.  [host] pointers are
  *    read during the call only.  bf16 data is passed as uint16_t bits.
  *  - The library allocates nothing and keeps no state beyond a per-device
- *    architecture check.  Every call is asynchronous on `stream` (a
+ *    architecture check and the device array dsa_decode_step_noalloc uses
+ *    as its workspace.  Every call is asynchronous on `stream` (a
  *    hipStream_t; NULL = the default stream); it never synchronises and
  *    never reads device data on the host.
  *  - Arguments are validated before anything is enqueued; on any error
@@ -171,6 +172,29 @@ dsa_status dsa_decode_step(const dsa_shape* shape, int32_t B, const int64_t* ctx
                            const uint16_t* q, const uint16_t* qI, const float* w,
                            const uint16_t* kv, const uint16_t* kI, float* out, int32_t* idx_out,
                            int32_t* count_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the device-resident workspace dsa_decode_step_noalloc uses. */
+#define DSA_DECODE_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* dsa_decode_step without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same operation, arguments, results
+ * and errors, with the workspace taken from a device array of
+ * DSA_DECODE_STATIC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on, from its first call there until the process ends.  A step whose
+ * workspace (dsa_decode_workspace_bytes) exceeds that size is rejected with
+ * DSA_ERR_WORKSPACE before anything is enqueued (the 8-sequence 4k..64k
+ * step needs about 17 MiB; 128 sequences of 65536 keys do not fit).  The
+ * call itself allocates nothing; the first call on a device looks up the
+ * array's device address once.  Every call on a GPU shares that GPU's
+ * array, and every buffer in it is written before it is read, so nothing
+ * from an earlier call leaks into a later one; calls that overlap on one
+ * GPU (concurrent streams, or threads) race on it and must be serialised
+ * by the caller. */
+dsa_status dsa_decode_step_noalloc(const dsa_shape* shape, int32_t B, const int64_t* ctx,
+                                   const uint16_t* q, const uint16_t* qI, const float* w,
+                                   const uint16_t* kv, const uint16_t* kI, float* out, int32_t* idx_out,
+                                   int32_t* count_out, void* stream);
 
 /* Upstream cache write of T new tokens ("GLM-5.2-Vision: llama.cpp vs vLLM
  * line-by-line pipeline trace", section 4, KV compression path: kv_cmpr and

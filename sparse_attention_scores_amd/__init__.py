@@ -20,19 +20,21 @@ __all__ = [
     "DsaError", "Shape", "GLM", "TINY", "lib",
     "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn", "dsa_latent_to_f16",
     "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
-    "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write", "dsa_router_topk",
-    "dsa_value_up_proj", "dsa_o_proj", "dsa_selection_mask", "dsa_dense_masked_attn",
+    "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_decode_step_noalloc", "dsa_cache_write",
+    "dsa_router_topk", "dsa_value_up_proj", "dsa_o_proj", "dsa_selection_mask", "dsa_dense_masked_attn",
     "dsa_dense_masked_attn_f16", "dsa_values_to_f16", "dsa_kv_b_proj", "dsa_status_string",
-    "EXPORTED_SYMBOLS",
+    "EXPORTED_SYMBOLS", "DECODE_STATIC_SCRATCH_BYTES",
 ]
 
 EXPORTED_SYMBOLS = (
     "dsa_status_string", "dsa_indexer_scores", "dsa_topk_select", "dsa_sparse_mla_attn",
     "dsa_latent_to_f16", "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
-    "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_cache_write", "dsa_router_topk",
-    "dsa_value_up_proj", "dsa_o_proj", "dsa_selection_mask", "dsa_dense_masked_attn",
+    "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_decode_step_noalloc", "dsa_cache_write",
+    "dsa_router_topk", "dsa_value_up_proj", "dsa_o_proj", "dsa_selection_mask", "dsa_dense_masked_attn",
     "dsa_dense_masked_attn_f16", "dsa_values_to_f16", "dsa_kv_b_proj",
 )
+
+DECODE_STATIC_SCRATCH_BYTES = 32 << 20   # DSA_DECODE_STATIC_SCRATCH_BYTES in include/dsa.h
 
 
 class DsaError(RuntimeError):
@@ -80,6 +82,7 @@ def _load() -> ctypes.CDLL:
         "dsa_prefill_chunk": (ctypes.c_int, [SP, P, P, P, P, P, i32, i32, i64, P, P, P, P, sz, P]),
         "dsa_decode_workspace_bytes": (sz, [SP, i32, P]),
         "dsa_decode_step": (ctypes.c_int, [SP, i32, P, P, P, P, P, P, P, P, P, P, sz, P]),
+        "dsa_decode_step_noalloc": (ctypes.c_int, [SP, i32, P, P, P, P, P, P, P, P, P, P]),
         "dsa_cache_write": (ctypes.c_int, [SP, P, P, ctypes.c_float, P, i32, i32, P, P, P, P, P, i32,
                                            ctypes.c_float, P]),
         "dsa_router_topk": (ctypes.c_int, [P, P, i32, i32, i32, ctypes.c_float, P, P, P]),
@@ -209,6 +212,16 @@ def dsa_decode_step(shape, ctx: Sequence[int], q, qI, w, kv, kI, out, idx_out=No
         _ptr(w, torch.float32, "w"), _bits(kv, "kv"), _bits(kI, "kI"), _ptr(out, torch.float32, "out"),
         _ptr(idx_out, torch.int32, "idx_out"), _ptr(count_out, torch.int32, "count_out"),
         ws_ptr, ws_bytes, _stream(stream)))
+
+
+def dsa_decode_step_noalloc(shape, ctx: Sequence[int], q, qI, w, kv, kI, out, idx_out=None, count_out=None,
+                            stream=None) -> None:
+    sh = Shape.of(shape)
+    arr = _ctx_array(ctx)
+    _check("dsa_decode_step_noalloc", lib.dsa_decode_step_noalloc(
+        ctypes.byref(sh), len(ctx), ctypes.cast(arr, ctypes.c_void_p), _bits(q, "q"), _bits(qI, "qI"),
+        _ptr(w, torch.float32, "w"), _bits(kv, "kv"), _bits(kI, "kI"), _ptr(out, torch.float32, "out"),
+        _ptr(idx_out, torch.int32, "idx_out"), _ptr(count_out, torch.int32, "count_out"), _stream(stream)))
 
 
 def dsa_cache_write(shape, kv_a, norm_w, eps: float, pos, T: int, N: int, kv, kI_new=None, kI=None,

@@ -165,6 +165,69 @@ dsa_status decode_layout(const dsa_shape* s, int32_t B, const int64_t* ctx, Deco
     return DSA_OK;
 }
 
+// Argument checks and geometry shared by both decode entry points (no HIP
+// call, nothing enqueued).
+dsa_status decode_check(const dsa_shape* shape, int32_t B, const int64_t* ctx, const uint16_t* q,
+                        const uint16_t* qI, const float* w, const uint16_t* kv, const uint16_t* kI,
+                        const float* out, const int32_t* idx_out, const int32_t* count_out, DecodeLayout& d) {
+    dsa_status st = check_shape(shape);
+    if (st) return st;
+    if (!q || !qI || !w || !kv || !kI || !out)
+        return DSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(qI) || !aligned16(w) || !aligned16(kv) || !aligned16(kI) ||
+        !aligned16(out) || (idx_out && !aligned16(idx_out)) || (count_out && !aligned16(count_out)))
+        return DSA_ERR_INVALID_ARG;
+    return decode_layout(shape, B, ctx, d);
+}
+
+// The decode kernels over a workspace at `base` laid out as d says.
+dsa_status decode_run(const dsa_shape* shape, const uint16_t* q, const uint16_t* qI, const float* w,
+                      const uint16_t* kv, const uint16_t* kI, float* out, int32_t* idx_out, int32_t* count_out,
+                      const DecodeLayout& d, char* base, hipStream_t s) {
+    dsa_status st;
+    const int sid = shape_id(shape);
+    float* S = reinterpret_cast<float*>(base + d.s_off);
+    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + d.idx_off);
+    int32_t* cnt = count_out ? count_out : reinterpret_cast<int32_t*>(base + d.cnt_off);
+    if ((st = launched(dsa::launch_indexer_decode(sid, qI, kI, w, S, d.idx_meta, d.idx_blocks, s)))) return st;
+    if ((st = launched(dsa::launch_topk_decode(S, d.topk_meta, shape->top_k, idx, cnt,
+                                               reinterpret_cast<int32_t*>(base + d.cand_off), d.n_max, s))))
+        return st;
+    dsa::AttnSplitArgs aa{q, kv, idx, shape->top_k, d.chunk, scale_log2(shape),
+                          reinterpret_cast<float*>(base + d.po_off), reinterpret_cast<float*>(base + d.pml_off),
+                          out};
+    return launched(dsa::launch_attention_split(sid, aa, d.attn_meta, d.attn_items, s));
+}
+
+}  // namespace
+
+// Workspace of dsa_decode_step_noalloc: one array per device, resident from
+// the library's first use on that device until the process ends.  Host code
+// never passes the array's name to a kernel or a copy: the name is a
+// host-side stand-in, and the device address comes from
+// hipGetSymbolAddress (static_scratch below).
+__device__ __attribute__((aligned(256))) unsigned char scratch[DSA_DECODE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+dsa_status static_scratch(void** ptr) {
+    static std::mutex mu;
+    static void* addr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_HIP;
+    if (dev < 0 || dev >= 64) return DSA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DSA_ERR_HIP;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -462,32 +525,28 @@ dsa_status dsa_decode_step(const dsa_shape* shape, int32_t B, const int64_t* ctx
                            const uint16_t* q, const uint16_t* qI, const float* w,
                            const uint16_t* kv, const uint16_t* kI, float* out, int32_t* idx_out,
                            int32_t* count_out, void* ws, size_t ws_bytes, void* stream) {
-    dsa_status st = check_shape(shape);
-    if (st) return st;
-    if (!q || !qI || !w || !kv || !kI || !out)
-        return DSA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(qI) || !aligned16(w) || !aligned16(kv) || !aligned16(kI) ||
-        !aligned16(out) || (idx_out && !aligned16(idx_out)) || (count_out && !aligned16(count_out)))
-        return DSA_ERR_INVALID_ARG;
     static thread_local DecodeLayout d;
-    if ((st = decode_layout(shape, B, ctx, d))) return st;
+    dsa_status st = decode_check(shape, B, ctx, q, qI, w, kv, kI, out, idx_out, count_out, d);
+    if (st) return st;
     if (!ws || !aligned16(ws) || ws_bytes < d.total) return DSA_ERR_WORKSPACE;
     if ((st = check_device())) return st;
-    hipStream_t s = (hipStream_t)stream;
-    const int sid = shape_id(shape);
-    char* base = static_cast<char*>(ws);
-    float* S = reinterpret_cast<float*>(base + d.s_off);
-    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + d.idx_off);
-    int32_t* cnt = count_out ? count_out : reinterpret_cast<int32_t*>(base + d.cnt_off);
+    return decode_run(shape, q, qI, w, kv, kI, out, idx_out, count_out, d, static_cast<char*>(ws),
+                      (hipStream_t)stream);
+}
 
-    if ((st = launched(dsa::launch_indexer_decode(sid, qI, kI, w, S, d.idx_meta, d.idx_blocks, s)))) return st;
-    if ((st = launched(dsa::launch_topk_decode(S, d.topk_meta, shape->top_k, idx, cnt,
-                                               reinterpret_cast<int32_t*>(base + d.cand_off), d.n_max, s))))
-        return st;
-    dsa::AttnSplitArgs aa{q, kv, idx, shape->top_k, d.chunk, scale_log2(shape),
-                          reinterpret_cast<float*>(base + d.po_off), reinterpret_cast<float*>(base + d.pml_off),
-                          out};
-    return launched(dsa::launch_attention_split(sid, aa, d.attn_meta, d.attn_items, s));
+dsa_status dsa_decode_step_noalloc(const dsa_shape* shape, int32_t B, const int64_t* ctx,
+                                   const uint16_t* q, const uint16_t* qI, const float* w,
+                                   const uint16_t* kv, const uint16_t* kI, float* out, int32_t* idx_out,
+                                   int32_t* count_out, void* stream) {
+    static thread_local DecodeLayout d;
+    dsa_status st = decode_check(shape, B, ctx, q, qI, w, kv, kI, out, idx_out, count_out, d);
+    if (st) return st;
+    if (d.total > DSA_DECODE_STATIC_SCRATCH_BYTES) return DSA_ERR_WORKSPACE;
+    if ((st = check_device())) return st;
+    void* scratch_dev = nullptr;
+    if ((st = static_scratch(&scratch_dev))) return st;
+    return decode_run(shape, q, qI, w, kv, kI, out, idx_out, count_out, d, static_cast<char*>(scratch_dev),
+                      (hipStream_t)stream);
 }
 
 }  // extern "C"
