@@ -185,10 +185,11 @@ def crossover(np, torch, dsa, W, reps: int) -> int:
     return 0
 
 
-def profile_stage(stage, reps, np, torch, dsa, W) -> int:
-    """Run one stage of the headline chunk reps times and nothing else that
-    matters (inputs are generated first).  `copy` runs a plain device copy of
-    COPY_BYTES, whose counter readings scale FETCH_SIZE / WRITE_SIZE."""
+def profile_stage(stage, reps, np, torch, dsa, W, config=PREFILL) -> int:
+    """Run one stage of a prefill chunk (the headline chunk unless `config`
+    names another) reps times and nothing else that matters (inputs are
+    generated first).  `copy` runs a plain device copy of COPY_BYTES, whose
+    counter readings scale FETCH_SIZE / WRITE_SIZE."""
     if stage == "copy":
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -227,7 +228,7 @@ def profile_stage(stage, reps, np, torch, dsa, W) -> int:
         torch.cuda.synchronize()
         log("decode done", reps)
         return 0
-    cfg = W.PREFILL[PREFILL]
+    cfg = W.PREFILL[config]
     sh = cfg.shape
     d = W.make_prefill(cfg)
     to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else a).cuda()
@@ -485,6 +486,8 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle sample size (0 = skip)")
     ap.add_argument("--profile-stage", choices=PROFILE_STAGES,
                     help="only run one stage (or a plain copy) --steps times, for rocprofv3 counter runs")
+    ap.add_argument("--config", default=PREFILL,
+                    help="prefill chunk for --profile-stage prefill/indexer/topk/attention (default %s)" % PREFILL)
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="turn FETCH_SIZE/WRITE_SIZE counter CSVs in DIR into profiles/traffic.json")
     ap.add_argument("--skip-decode", action="store_true")
@@ -509,7 +512,10 @@ def main() -> int:
         return 2
     K, Wm = args.steps, args.warmup
     if args.profile_stage:
-        return profile_stage(args.profile_stage, K, np, torch, dsa, W)
+        if args.config not in W.PREFILL:
+            print("unknown --config %s (one of %s)" % (args.config, ", ".join(W.PREFILL)), file=sys.stderr)
+            return 2
+        return profile_stage(args.profile_stage, K, np, torch, dsa, W, args.config)
     if args.crossover:
         return crossover(np, torch, dsa, W, max(K // 4, 3))
 
