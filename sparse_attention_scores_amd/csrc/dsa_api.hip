@@ -161,7 +161,7 @@ dsa_status decode_layout(const dsa_shape* s, int32_t B, const int64_t* ctx, Deco
     d.po_off = d.cnt_off + align_up((size_t)B * sizeof(int32_t));
     d.pml_off = d.po_off + align_up((size_t)items * s->n_heads * s->d_latent * sizeof(float));
     d.cand_off = d.pml_off + align_up((size_t)items * s->n_heads * 2 * sizeof(float));
-    d.total = d.cand_off + align_up((size_t)tblk * s->top_k * sizeof(int32_t));
+    d.total = d.cand_off + align_up((size_t)tblk * s->top_k * dsa::topk_decode_candidate_bytes());
     return DSA_OK;
 }
 
@@ -191,7 +191,7 @@ dsa_status decode_run(const dsa_shape* shape, const uint16_t* q, const uint16_t*
     int32_t* cnt = count_out ? count_out : reinterpret_cast<int32_t*>(base + d.cnt_off);
     if ((st = launched(dsa::launch_indexer_decode(sid, qI, kI, w, S, d.idx_meta, d.idx_blocks, s)))) return st;
     if ((st = launched(dsa::launch_topk_decode(S, d.topk_meta, shape->top_k, idx, cnt,
-                                               reinterpret_cast<int32_t*>(base + d.cand_off), d.n_max, s))))
+                                               base + d.cand_off, d.n_max, s))))
         return st;
     dsa::AttnSplitArgs aa{q, kv, idx, shape->top_k, d.chunk, scale_log2(shape),
                           reinterpret_cast<float*>(base + d.po_off), reinterpret_cast<float*>(base + d.pml_off),

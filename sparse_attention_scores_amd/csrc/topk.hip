@@ -54,55 +54,84 @@ __device__ inline int count_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-template <int NT, int EPT>
+// ---- wave primitives on DPP (every lane of the wave active) ----
+
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each 16-lane row
+
+// A permutation inside each 16-lane row: every lane has a source.
+template <int CTRL>
+__device__ inline int dpp_perm(int x) {
+    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ inline float dpp_perm(float x) {
+    return __builtin_bit_cast(float, dpp_perm<CTRL>(__builtin_bit_cast(int, x)));
+}
+__device__ inline float readlane_f(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+struct MinOp { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
+struct MaxOp { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+
+// op over the wave, wave-uniform: every lane of a row gets the row's result
+// through four in-row exchanges, then the four rows are read out.
+template <typename Op>
+__device__ inline float wave_reduce(float x, Op op) {
+    x = op(x, dpp_perm<kDppXor1>(x));
+    x = op(x, dpp_perm<kDppXor2>(x));
+    x = op(x, dpp_perm<kDppHalfMirror>(x));
+    x = op(x, dpp_perm<kDppMirror>(x));
+    return op(op(readlane_f(x, 0), readlane_f(x, 16)), op(readlane_f(x, 32), readlane_f(x, 48)));
+}
+
+// Sum over aligned groups of P lanes (P a power of two up to 16, uniform).
+__device__ inline int group_sum(int x, int P) {
+    if (P >= 2) x += dpp_perm<kDppXor1>(x);
+    if (P >= 4) x += dpp_perm<kDppXor2>(x);
+    if (P >= 8) x += dpp_perm<kDppHalfMirror>(x);
+    if (P >= 16) x += dpp_perm<kDppMirror>(x);
+    return x;
+}
+
+// Inclusive sum over the lanes at or below this one: row shifts inside each
+// 16-lane row (zeros shifted in), then the totals of earlier rows broadcast.
+__device__ inline int wave_inclusive_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
+template <int NT, int EPT, bool VALS>
 struct TopkSmem {
     static constexpr int NW = NT / 64;
-    float red[2][2][NW];             // min / max partials, double buffered
-    int cnt[2][NW];                  // bisection counts, double buffered
-    int hist[kBins];
-    float cand[NT];
+    float red[2][2][NW] __attribute__((aligned(16)));   // min / max partials, double buffered
+    int cnt[2][NW];                                     // bisection counts, double buffered
+    int hist[kBins] __attribute__((aligned(16)));
+    float cand[NT + 64] __attribute__((aligned(16)));   // the boundary bin's values, NaN past them
+    int pre_gt[EPT * NW] __attribute__((aligned(16)));  // packed key counts per (element, wave) group
+    int outk[kMaxTopK];                                 // kept keys in output order
+    float outv[VALS ? kMaxTopK : 1];                    // and their scores, where the output carries them
     int ncand;
     int bstar, above, inbin;
     float T;
     int keep;
-    int pre_gt[EPT * NW];
-    int pre_eq[EPT * NW];
-    int wsum_gt[NW];
-    int wsum_eq[NW];
 };
 
-// Block-wide exclusive scan of (a, b) held one pair per thread.
-template <int NT, int EPT>
-__device__ inline void block_exclusive_scan2(int& a, int& b, TopkSmem<NT, EPT>& sm) {
-    constexpr int NW = NT / 64;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int ia = a, ib = b;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int ya = __shfl_up(ia, d), yb = __shfl_up(ib, d);
-        if (lane >= d) { ia += ya; ib += yb; }
-    }
-    if (lane == 63) { sm.wsum_gt[wave] = ia; sm.wsum_eq[wave] = ib; }
-    __syncthreads();
-    int oa = 0, ob = 0;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-        if (v < wave) { oa += sm.wsum_gt[v]; ob += sm.wsum_eq[v]; }
-    }
-    a = oa + ia - a;
-    b = ob + ib - b;
-}
-
 // Block-wide minimum and maximum (every thread gets both).
-template <int NT, int EPT>
-__device__ inline void block_minmax(float& lo, float& hi, int& par, TopkSmem<NT, EPT>& sm) {
-    constexpr int NW = NT / 64;
+template <typename Sm>
+__device__ inline void block_minmax(float& lo, float& hi, int& par, Sm& sm) {
+    constexpr int NW = Sm::NW;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        lo = fminf(lo, __shfl_xor(lo, d));
-        hi = fmaxf(hi, __shfl_xor(hi, d));
-    }
+    lo = wave_reduce(lo, MinOp{});
+    hi = wave_reduce(hi, MaxOp{});
     if (lane == 0) { sm.red[par][0][wave] = lo; sm.red[par][1][wave] = hi; }
     __syncthreads();
 #pragma unroll
@@ -112,67 +141,114 @@ __device__ inline void block_minmax(float& lo, float& hi, int& par, TopkSmem<NT,
     par ^= 1;
 }
 
-// The bin of a live value: trunc((v - lo) * scale) clamped to [0, 255].  A
-// non-decreasing function of v (each rounding is monotone), so higher bins
-// hold larger values and equal values share a bin.
-__device__ inline int value_bin(float v, float lo, float scale) {
-    const int b = (int)((v - lo) * scale);
+// The bin of a live value: trunc(v * scale + off) clamped to [0, 255], with
+// off = -lo * scale, in one fused multiply-add.  A non-decreasing function of
+// v (each rounding is monotone), so higher bins hold larger values and equal
+// values share a bin.
+__device__ inline int value_bin(float v, float scale, float off) {
+    const int b = (int)__builtin_fmaf(v, scale, off);
     return min(max(b, 0), kBins - 1);
 }
 
-// Element k of a row: its score, and the key index written for it.
-struct DirectRow {   // element k is key k
-    static constexpr bool kRemap = false;
+// Element k of a row: its score and the key index written for it.
+// Loads go through a buffer resource sized to the row's n elements, so a
+// read past the row returns zero instead of touching memory beyond it.
+__device__ inline __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+struct DirectRow {   // element k is key k0 + k
+    static constexpr bool kKeys = false;   // key indices follow from the position
     const float* __restrict__ s;
-    __device__ __forceinline__ float load(int k) const { return s[k]; }
-    __device__ __forceinline__ int32_t index(int k) const { return k; }
+    int k0;
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int n) const { return row_rsrc(s, 4 * n); }
+    __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, int k, int&) const {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 4 * k, 0, 0));   // raw bits
+    }
+    __device__ __forceinline__ float load(int k, int&) const { return s[k]; }
+    __device__ __forceinline__ int32_t key(int k) const { return k0 + k; }
+};
+// A candidate of a segmented sequence: a kept key of one segment and its
+// (NaN-free) score.
+struct CandEntry {
+    int32_t key;
+    float score;
 };
 // The candidates of a segmented row: the concatenated selections of its
-// segments (seg keys each, top_k entries per segment, each in ascending
-// order and padded with -1), so element order is key order.  An entry holds
-// a key index local to its segment.  Padding entries score -inf; they are
-// never kept, because every full segment brings top_k finite scores.
+// segments (top_k entries per segment, each in ascending key order, padded
+// with key -1), so element order is key order.  Padding scores -inf and sits
+// after every real candidate, and the first segment alone brings top_k real
+// ones, so padding is never kept.
 struct CandRow {
-    static constexpr bool kRemap = true;   // outputs are element positions until remapped
-    const float* __restrict__ s;       // the sequence's scores
-    const int32_t* __restrict__ cand;
-    int top_k, seg;
-    __device__ __forceinline__ int32_t key(int k) const {
-        const int c = cand[k];
-        return c < 0 ? -1 : (k / top_k) * seg + c;
+    static constexpr bool kKeys = true;    // key indices travel with the scores
+    const CandEntry* __restrict__ c;
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int n) const { return row_rsrc(c, 8 * n); }
+    __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, int k, int& key) const {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * k, 0, 0);
+        key = (int32_t)v[0];
+        return key < 0 ? -INFINITY : __uint_as_float(v[1]);
     }
-    __device__ __forceinline__ float load(int k) const {
-        const int j = key(k);
-        return j < 0 ? -INFINITY : s[j];
+    __device__ __forceinline__ float load(int k, int& key) const {
+        const CandEntry e = c[k];
+        key = e.key;
+        return e.key < 0 ? -INFINITY : e.score;
     }
-    __device__ __forceinline__ int32_t index(int k) const { return key(k); }
+    __device__ __forceinline__ int32_t key(int k) const { return c[k].key; }
 };
 
-template <int NT, int EPT, typename Row>
-__device__ __forceinline__ void topk_row(const Row& row, int n, int top_k,
-                                         int32_t* __restrict__ out, int32_t* count, TopkSmem<NT, EPT>& sm) {
+// Where the kept keys go: a plain index list, or candidate entries (index
+// and score) for a later merge.
+struct KeySink {
+    static constexpr bool kVals = false;
+    int32_t* __restrict__ out;
+    __device__ __forceinline__ void write(int t, int32_t key, float) const { out[t] = key; }
+};
+struct CandSink {
+    static constexpr bool kVals = true;
+    CandEntry* __restrict__ out;
+    __device__ __forceinline__ void write(int t, int32_t key, float v) const { out[t] = CandEntry{key, v}; }
+};
+
+template <int NT, int EPT, typename Row, typename Sink, typename Sm>
+__device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const Sink& sink, int32_t* count,
+                                         Sm& sm) {
     static_assert(NT >= kBins && NT % 64 == 0 && EPT >= 1 && EPT <= 64, "topk geometry");
-    static_assert(EPT * (NT / 64) <= NT, "one scan slot per thread");
+    static_assert(kBins == 4 * 64, "one wave scans the histogram, four bins per lane");
+    static_assert(!Sink::kVals || sizeof(sm.outv) == sizeof(sm.outk), "an output with scores stages them");
     constexpr int NW = NT / 64;
+    static_assert(NW % 4 == 0 || NW < 4, "group counts are read four at a time");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (n <= top_k) {   // every earlier key; the scores are not read
-        for (int t = tid; t < top_k; t += NT) out[t] = t < n ? t : -1;
+    const float kNone = __int_as_float(0x7FC00000);
+    if (n <= top_k) {   // every earlier key (its score is read only where the output carries it)
+        for (int t = tid; t < top_k; t += NT) {
+            if (t < n) {
+                float v = 0.f;
+                int key = row.key(t);
+                if constexpr (Sink::kVals) {
+                    v = row.load(t, key);
+                    v = v == v ? v : -INFINITY;
+                }
+                sink.write(t, key, v);
+            } else {
+                sink.write(t, -1, -INFINITY);
+            }
+        }
         if (tid == 0 && count) *count = n;
         return;
     }
     // Scores in registers.  A NaN score ranks as -inf; keys past the row are
     // NaN, which every comparison below treats as "not a candidate".
-    const float kNone = __int_as_float(0x7FC00000);
     float f[EPT];
-    const int nfull = n / NT;     // elements every lane of the block holds
+    int kid[Row::kKeys ? EPT : 1];
+    {
+        const auto rs = row.rsrc(n);
 #pragma unroll
-    for (int e = 0; e < EPT; ++e)   // every load in bounds; no waits between them
-        f[e] = row.load(e < nfull ? e * NT + tid : min(e * NT + tid, n - 1));
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        const float x = f[e] == f[e] ? f[e] : -INFINITY;
-        f[e] = e * NT + tid < n ? x : kNone;
+        for (int e = 0; e < EPT; ++e)   // no waits between the loads
+            f[e] = row.load(rs, e * NT + tid, kid[Row::kKeys ? e : 0]);
     }
+    // fmaxf against -inf turns NaN into -inf and leaves the rest
+    const int lim = n - tid;   // element e is in the row when e * NT < lim
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) f[e] = e * NT < lim ? fmaxf(f[e], -INFINITY) : kNone;
     if (tid == 0) { sm.ncand = 0; sm.T = INFINITY; sm.keep = 0; }
     if (tid < kBins) sm.hist[tid] = 0;
 
@@ -181,7 +257,7 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k,
 #pragma unroll
     for (int e = 0; e < EPT; ++e) { lo = fminf(lo, f[e]); hi = fmaxf(hi, f[e]); }
     int par = 0;
-    block_minmax<NT, EPT>(lo, hi, par, sm);
+    block_minmax(lo, hi, par, sm);
     int krem = top_k;
     bool found = false;
     float T = 0.f;
@@ -189,31 +265,33 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k,
     for (int lev = 0; lev < kMaxLevels; ++lev) {
         if (!(lo < hi)) { T = lo; found = true; break; }   // every live value equal (-0 == +0)
         const float scale = (float)kBins / (hi - lo);
-        // finite positive scale only (excludes infinities and overflowing ranges)
-        if (!(scale > 0.f && scale < 3.0e38f)) break;
+        const float off = -lo * scale;
+        // finite positive scale and finite offset only (excludes infinities
+        // and overflowing ranges)
+        if (!(scale > 0.f && scale < 3.0e38f && fabsf(off) < 3.0e38f)) break;
+        // Every value lies in the first level's range: there a key is live
+        // unless it is padding (NaN).
+        if (lev == 0) {
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const bool live = f[e] >= lo && f[e] <= hi;
-            if (__ballot(live)) {
-                if (live) atomicAdd(&sm.hist[value_bin(f[e], lo, scale)], 1);
-            }
+            for (int e = 0; e < EPT; ++e)
+                if (f[e] == f[e]) atomicAdd(&sm.hist[value_bin(f[e], scale, off)], 1);
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                if (f[e] >= lo && f[e] <= hi) atomicAdd(&sm.hist[value_bin(f[e], scale, off)], 1);
         }
         __syncthreads();
         if (wave == 0) {
-            // bins 4*lane .. 4*lane+3; keys in higher bins come from higher lanes
-            int h[4], tot = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) { h[k] = sm.hist[4 * lane + k]; tot += h[k]; }
-            int suf = tot;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int y = __shfl_down(suf, d);
-                if (lane + d < 64) suf += y;
-            }
-            int gt = suf - tot;
+            // lane l holds bins b0 .. b0+3 with b0 = 252 - 4l: lower lanes
+            // hold higher bins, so an inclusive lane sum counts from the top
+            const int b0 = kBins - 4 - 4 * lane;
+            const int4 hv = *reinterpret_cast<const int4*>(&sm.hist[b0]);
+            const int h[4] = {hv.x, hv.y, hv.z, hv.w};
+            const int tot = h[0] + h[1] + h[2] + h[3];
+            int gt = wave_inclusive_sum(tot) - tot;   // live keys in bins above b0 + 3
 #pragma unroll
             for (int k = 3; k >= 0; --k) {
-                if (gt < krem && gt + h[k] >= krem) { sm.bstar = 4 * lane + k; sm.above = gt; sm.inbin = h[k]; }
+                if (gt < krem && gt + h[k] >= krem) { sm.bstar = b0 + k; sm.above = gt; sm.inbin = h[k]; }
                 gt += h[k];
             }
         }
@@ -226,23 +304,27 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k,
         const int inbin = __builtin_amdgcn_readfirstlane(sm.inbin);
         krem -= __builtin_amdgcn_readfirstlane(sm.above);
         if (inbin <= NT) {
-            // rank the keys of the bin directly: gather them, then each thread
-            // counts the gathered values above and at its own
+            // rank the keys of the bin directly: gather them (a slot
+            // reservation per element group, broadcast without a lane
+            // exchange), then each key counts the gathered values above and
+            // at its own
 #pragma unroll
             for (int e = 0; e < EPT; ++e) {
-                const bool a = f[e] >= lo && f[e] <= hi && value_bin(f[e], lo, scale) == bstar;
+                const bool a = f[e] >= lo && f[e] <= hi && value_bin(f[e], scale, off) == bstar;
                 const uint64_t m = __ballot(a);
                 if (m) {
                     int base = 0;
-                    if (lane == 0) base = atomicAdd(&sm.ncand, __popcll(m));
-                    base = __shfl(base, 0);
+                    if (lane == 0) base = atomicAdd(&sm.ncand, (int)__popcll(m));
+                    base = __builtin_amdgcn_readfirstlane(base);
                     const int slot = base + count_below(m);
                     if (a && slot < NT) sm.cand[slot] = f[e];
                 }
             }
+            if (tid < 64) sm.cand[inbin + tid] = kNone;   // whole groups of four past the bin
             __syncthreads();
             // each key of the bin is ranked by P lanes (a power of two, up to
-            // 16), which split the comparisons and combine them by shuffles
+            // 16), which split the comparisons four values at a time and
+            // combine their counts in-row
             int lg = 0;
             while (lg < 4 && (inbin << (lg + 1)) <= NT) ++lg;
             const int P = 1 << lg;
@@ -250,17 +332,18 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k,
             int gt = 0, ge = 0;
             const float v = sm.cand[min(c, max(inbin - 1, 0))];
             if (c < inbin) {
-#pragma unroll 4
-                for (int i = part; i < inbin; i += P) {
-                    const float x = sm.cand[i];
-                    gt += x > v;
-                    ge += x >= v;
+#pragma unroll 2
+                for (int i = 4 * part; i < inbin; i += 4 * P) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.cand[i]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        gt += x[j] > v;
+                        ge += x[j] >= v;
+                    }
                 }
             }
-            for (int d = 1; d < P; d <<= 1) {
-                gt += __shfl_xor(gt, d);
-                ge += __shfl_xor(ge, d);
-            }
+            gt = group_sum(gt, P);
+            ge = group_sum(ge, P);
             if (c < inbin && part == 0 && gt < krem && krem <= ge) { sm.T = v; sm.keep = krem - gt; }
             __syncthreads();
             T = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sm.T)));
@@ -272,14 +355,14 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k,
         float nlo = INFINITY, nhi = -INFINITY;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            const bool a = f[e] >= lo && f[e] <= hi && value_bin(f[e], lo, scale) == bstar;
+            const bool a = f[e] >= lo && f[e] <= hi && value_bin(f[e], scale, off) == bstar;
             nlo = a ? fminf(nlo, f[e]) : nlo;
             nhi = a ? fmaxf(nhi, f[e]) : nhi;
         }
         if (tid < kBins) sm.hist[tid] = 0;
         lo = nlo;
         hi = nhi;
-        block_minmax<NT, EPT>(lo, hi, par, sm);
+        block_minmax(lo, hi, par, sm);
     }
 
     if (!found) {
@@ -315,82 +398,107 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k,
     // keep every key > T and the first krem keys == T (NaN padding is neither)
     const int keep = krem;
 
-    // per (element, wave) counts of keys > T and == T; lane e of each wave
-    // collects element e's counts
-    int cg = 0, cq = 0;
+    // Keys in output order are grouped by (element e, wave w, lane): group
+    // (e, w) holds keys e*NT + 64w .. e*NT + 64w + 63.  A group's counts of
+    // keys > T and == T travel packed as gt + (eq << kEqShift): sums of them
+    // never carry between the fields (at most top_k - 1 keys exceed T, and
+    // top_k <= 2048), so every sum and scan below runs on the packed value.
+    // Lane e of each wave collects its group (e, wave).
+    constexpr int kEqShift = 13;
+    static_assert(kMaxTopK < (1 << kEqShift) && (int64_t)kMaxSelectKeys << kEqShift <= 0x7FFFFFFF, "count packing");
+    int cgq = 0;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
         const int ng = __popcll(__ballot(f[e] > T));
         const int nq = __popcll(__ballot(f[e] == T));
-        cg = (lane == e) ? ng : cg;
-        cq = (lane == e) ? nq : cq;
+        cgq = lane == e ? ng + (nq << kEqShift) : cgq;
     }
-    if (lane < EPT) { sm.pre_gt[lane * NW + wave] = cg; sm.pre_eq[lane * NW + wave] = cq; }
+    if (lane < EPT) sm.pre_gt[lane * NW + wave] = cgq;
     __syncthreads();
-    int a = 0, b = 0;
-    if (tid < EPT * NW) { a = sm.pre_gt[tid]; b = sm.pre_eq[tid]; }
-    block_exclusive_scan2<NT, EPT>(a, b, sm);
-    __syncthreads();
-    if (tid < EPT * NW) { sm.pre_gt[tid] = a; sm.pre_eq[tid] = b; }
-    __syncthreads();
-    // lane e holds element e's exclusive counts (read back one per element)
-    const int pg_l = lane < EPT ? sm.pre_gt[lane * NW + wave] : 0;
-    const int pq_l = lane < EPT ? sm.pre_eq[lane * NW + wave] : 0;
+    // Each wave forms its own groups' offsets: lane e sums row e of the
+    // counts (all waves, and the waves before this one), and an exclusive
+    // lane sum of the row totals adds every earlier element.
+    int rs = 0, ws = 0;
+    if (lane < EPT) {
+#pragma unroll
+        for (int v = 0; v < NW; v += 4) {
+            const int4 x = *reinterpret_cast<const int4*>(&sm.pre_gt[lane * NW + v]);
+            const int x4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int j = 0; j < 4 && v + j < NW; ++j) {
+                rs += x4[j];
+                ws += v + j < wave ? x4[j] : 0;
+            }
+        }
+    }
+    const int pgq_l = wave_inclusive_sum(rs) - rs + ws;   // lane e: counts before group (e, wave)
+    const int kb = row.key(tid);                          // key of element 0; element e adds e * NT
 
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
         // one element at a time: keeps the compiler from computing all
         // 2*EPT lane masks up front (they would spill)
         asm volatile("" : "+v"(f[e]));
-        int t_ = tid;                      // fresh copy: the key index is not kept from the loads
-        asm volatile("" : "+v"(t_));
-        const uint64_t gm = __ballot(f[e] > T);
-        const uint64_t qm = __ballot(f[e] == T);
+        const bool gt = f[e] > T, eq = f[e] == T;
+        const uint64_t gm = __ballot(gt);
+        const uint64_t qm = __ballot(eq);
         if (gm | qm) {
-            const int pg = __builtin_amdgcn_readlane(pg_l, e);
-            const int pq = __builtin_amdgcn_readlane(pq_l, e);
+            const int pp = __builtin_amdgcn_readlane(pgq_l, e);
+            const int pg = pp & ((1 << kEqShift) - 1), pq = pp >> kEqShift;
             // the group's keys equal to T that are kept: the first (keep - pq)
-            uint64_t qsel = 0;
             const int room = keep - pq;              // signed: negative once every tie is placed
-            if (room >= (int)__popcll(qm)) {
-                qsel = qm;
-            } else if (room > 0) {
-                uint64_t m = qm;
+            uint64_t sel;
+            bool kept;
+            if (room >= (int)__popcll(qm)) {         // every tie of the group
+                sel = gm | qm;
+                kept = gt || eq;
+            } else if (room <= 0) {                  // none
+                sel = gm;
+                kept = gt;
+            } else {                                 // the lowest `room` lanes of them
+                uint64_t qsel = 0, m = qm;
                 for (int k = 0; k < room; ++k) { qsel |= m & (~m + 1); m &= m - 1; }
+                sel = gm | qsel;
+                kept = gt || (eq && ((qsel >> lane) & 1));
             }
-            const uint64_t sel = gm | qsel;
-            const int base = pg + min(pq, keep);    // kept keys in earlier groups
-            const int slot = base + count_below(sel);
-            if (((sel >> lane) & 1) && slot >= 0 && slot < top_k) out[slot] = e * NT + t_;
+            const int slot = pg + min(pq, keep) + count_below(sel);   // kept keys before this one
+            if (kept && slot < top_k) {
+                int key;
+                if constexpr (Row::kKeys) key = kid[e];
+                else key = kb + e * NT;
+                sm.outk[slot] = key;
+                if constexpr (Sink::kVals) sm.outv[slot] = f[e];
+            }
         }
     }
-    if constexpr (Row::kRemap) {
-        // element positions -> key indices, in one coalesced pass (a lookup
-        // per kept element inside the loop above would serialise its loads)
-        __syncthreads();
-        for (int t = tid; t < top_k; t += NT) out[t] = row.index(out[t]);
+    // the top_k kept keys leave in one coalesced pass
+    __syncthreads();
+    for (int t = tid; t < top_k; t += NT) {
+        if constexpr (Sink::kVals) sink.write(t, sm.outk[t], sm.outv[t]);
+        else sink.write(t, sm.outk[t], 0.f);
     }
     if (tid == 0 && count) *count = top_k;
 }
 
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_prefill_kernel(TopkArgs a) {
-    __shared__ TopkSmem<NT, EPT> sm;
+    __shared__ TopkSmem<NT, EPT, false> sm;
     const int r = blockIdx.x;
     const int64_t p = a.pos0 + r;
     const int n = (int)(p + 1);
     const float* srow = (n > a.top_k) ? a.S + (int64_t)(r - a.s_row0) * a.ldS : nullptr;
-    topk_row<NT, EPT>(DirectRow{srow}, n, a.top_k, a.idx + (int64_t)r * a.top_k, a.count ? a.count + r : nullptr,
-                      sm);
+    topk_row<NT, EPT>(DirectRow{srow, 0}, n, a.top_k, KeySink{a.idx + (int64_t)r * a.top_k},
+                      a.count ? a.count + r : nullptr, sm);
 }
 
 // Decode, phase 1: block -> (sequence b, segment g) of kDecodeSeg keys.  A
 // sequence of one segment is finished here; otherwise the segment's
-// selection goes to the candidate list (top_k entries per segment block).
+// selection (key and score, top_k entries per segment block) goes to the
+// candidate list.
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_decode_kernel(
-        const float* S, SeqMeta m, int top_k, int32_t* idx, int32_t* count, int32_t* cand) {
-    __shared__ TopkSmem<NT, EPT> sm;
+        const float* S, SeqMeta m, int top_k, int32_t* idx, int32_t* count, CandEntry* cand) {
+    __shared__ TopkSmem<NT, EPT, true> sm;
     const int b = seq_of_block(m, blockIdx.x);
     const int g = blockIdx.x - m.blk0[b];
     const int ctx = m.ctx[b];
@@ -398,22 +506,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     const int n = min(ctx - k0, kDecodeSeg);
     const float* srow = S + m.s_off[b] + k0;
     if (ctx <= kDecodeSeg)
-        topk_row<NT, EPT>(DirectRow{srow}, n, top_k, idx + (int64_t)b * top_k, count ? count + b : nullptr, sm);
+        topk_row<NT, EPT>(DirectRow{srow, 0}, n, top_k, KeySink{idx + (int64_t)b * top_k}, count ? count + b : nullptr,
+                          sm);
     else
-        topk_row<NT, EPT>(DirectRow{srow}, n, top_k, cand + (int64_t)blockIdx.x * top_k, nullptr, sm);
+        topk_row<NT, EPT>(DirectRow{srow, k0}, n, top_k, CandSink{cand + (int64_t)blockIdx.x * top_k}, nullptr, sm);
 }
 
 // Decode, phase 2: block b selects sequence b's top_k among the candidates
 // of its segments (sequences of one segment have nothing to do).
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_merge_kernel(
-        const float* S, SeqMeta m, int top_k, int32_t* idx, int32_t* count, const int32_t* cand) {
-    __shared__ TopkSmem<NT, EPT> sm;
+        SeqMeta m, int top_k, int32_t* idx, int32_t* count, const CandEntry* cand) {
+    __shared__ TopkSmem<NT, EPT, false> sm;
     const int b = blockIdx.x;
     const int nseg = m.blk0[b + 1] - m.blk0[b];
     if (nseg < 2) return;
-    const CandRow row{S + m.s_off[b], cand + (int64_t)m.blk0[b] * top_k, top_k, kDecodeSeg};
-    topk_row<NT, EPT>(row, nseg * top_k, top_k, idx + (int64_t)b * top_k, count ? count + b : nullptr, sm);
+    topk_row<NT, EPT>(CandRow{cand + (int64_t)m.blk0[b] * top_k}, nseg * top_k, top_k,
+                      KeySink{idx + (int64_t)b * top_k}, count ? count + b : nullptr, sm);
 }
 
 // Block shape by row length: up to 32 keys per thread in 256-, then 512-,
@@ -463,8 +572,9 @@ hipError_t launch_topk_prefill(const TopkArgs& a, int n_max, hipStream_t s) {
 int topk_decode_segments(int ctx) { return (ctx + kDecodeSeg - 1) / kDecodeSeg; }
 
 hipError_t launch_topk_decode(const float* S, const SeqMeta& m, int top_k, int32_t* idx, int32_t* count,
-                              int32_t* cand, int n_max, hipStream_t s) {
+                              void* cand_buf, int n_max, hipStream_t s) {
     if (m.B <= 0) return hipSuccess;
+    CandEntry* cand = static_cast<CandEntry*>(cand_buf);
     const int blocks = m.blk0[m.B];
     hipError_t e = dispatch_wide(min(n_max, kDecodeSeg), [&](auto nt, auto ept) {
         constexpr int NT = decltype(nt)::value, EPT = decltype(ept)::value;
@@ -474,9 +584,11 @@ hipError_t launch_topk_decode(const float* S, const SeqMeta& m, int top_k, int32
     if (e != hipSuccess || n_max <= kDecodeSeg) return e;
     return dispatch_wide(topk_decode_segments(n_max) * top_k, [&](auto nt, auto ept) {
         constexpr int NT = decltype(nt)::value, EPT = decltype(ept)::value;
-        hipLaunchKernelGGL((topk_merge_kernel<NT, EPT>), dim3(m.B), dim3(NT), 0, s, S, m, top_k, idx, count, cand);
+        hipLaunchKernelGGL((topk_merge_kernel<NT, EPT>), dim3(m.B), dim3(NT), 0, s, m, top_k, idx, count, cand);
         return hipGetLastError();
     });
 }
+
+size_t topk_decode_candidate_bytes() { return sizeof(CandEntry); }
 
 }  // namespace dsa
