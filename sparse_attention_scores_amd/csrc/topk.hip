@@ -6,9 +6,9 @@
 // are written in ascending key order and padded with -1.
 //
 // Design: one block per query row; the row's scores stay in VGPRs (EPT per
-// thread, element e of thread t is key e*NT + t, so loads are coalesced) as
-// order-preserving uint32 keys.  The selection only needs T, the top_k-th
-// largest key, and krem, how many keys equal to T are kept:
+// thread, element e of thread t is key e*NT + t, so loads are coalesced).
+// The selection only needs T, the top_k-th largest score, and krem, how many
+// keys equal to T are kept:
 //   1. Value-linear histogram levels.  Live keys ("alive": every key the
 //      levels so far have not ruled out) are binned by a monotone map of
 //      their float value onto [0, 256) between the live minimum and maximum.
@@ -16,15 +16,21 @@
 //      bins below are dropped.  Bins that follow the value (not the float's
 //      exponent bits) spread a bell-shaped score row over many LDS counters,
 //      so the atomics rarely collide.
-//   2. Once at most NT keys are alive they are ranked directly (each thread
-//      counts the live keys above its own), which yields T exactly.
+//   2. Once at most NT keys are alive they are gathered (each wave into its
+//      own LDS slice) and ranked directly, which yields T exactly.
 //   3. Degenerate rows (non-finite values, a value range too wide or too
 //      narrow for fp32 binning, too many levels) finish with an exact
 //      32-step bisection over the live keys.  Every loop is bounded.
-// Finally every kept key's output slot is the number of kept keys with a
-// lower index (ballot counts per (element, wave) plus one block-wide scan),
-// so the output is in ascending key order with no sort.  Every decision is
-// taken on integer keys: the result is exact.
+// Finally the kept keys go to an LDS bitmap (bit k is element k: each wave
+// stores its 64-lane ballot masks), and each thread walks a few consecutive
+// words of it after one block-wide scan of their counts, so the output is in
+// ascending key order with no sort.  Every decision is an exact float
+// comparison (-0 and +0 compare equal; NaN scores count as -inf): the
+// result is exact.
+//
+// The kernel is bound by vector-ALU issue (a 64-lane instruction occupies a
+// 16-lane SIMD for four cycles), so each pass over the keys is kept to a few
+// instructions per key.
 #include "dsa_kernels.h"
 
 #include <type_traits>
@@ -109,20 +115,34 @@ __device__ inline int wave_inclusive_sum(int x) {
     return x;
 }
 
-template <int NT, int EPT, bool VALS>
+template <int NT, int EPT, bool VALS, bool KEYS>
 struct TopkSmem {
     static constexpr int NW = NT / 64;
+    static constexpr int NE = NT * EPT;                           // elements of a row
+    static constexpr int NB = NE / 32;                            // bitmap words, bit k is element k
+    static constexpr int kSlice = NT < 64 * EPT ? NT : 64 * EPT;  // a wave's most boundary-bin keys
     float red[2][2][NW] __attribute__((aligned(16)));   // min / max partials, double buffered
     int cnt[2][NW];                                     // bisection counts, double buffered
+    int wsum[NW];                                       // block-scan partials
     int hist[kBins] __attribute__((aligned(16)));
     float cand[NT + 64] __attribute__((aligned(16)));   // the boundary bin's values, NaN past them
-    int pre_gt[EPT * NW] __attribute__((aligned(16)));  // packed key counts per (element, wave) group
-    int outk[kMaxTopK];                                 // kept keys in output order
-    float outv[VALS ? kMaxTopK : 1];                    // and their scores, where the output carries them
-    int ncand;
-    int bstar, above, inbin;
+    int keyof[KEYS ? NE : 1];                           // key index of each element, where keys travel
+    union {
+        struct {                                        // gathering the boundary bin
+            float slice[NW][kSlice];                    // each wave's boundary-bin values
+            int wcnt[NW];                               // and their number
+        } g;
+        struct {                                        // writing the selection
+            uint64_t keep[NB / 2];                      // kept elements (above T, or at T when all ties stay)
+            uint64_t tie[NB / 2];                       // elements equal to T, where only some stay
+            float vals[VALS ? NE : 1];                  // kept elements' scores, where the output carries them
+            int outk[kMaxTopK];                         // kept keys in output order
+            float outv[VALS ? kMaxTopK : 1];            // and their scores
+        } c;
+    } u;
+    int bstar, above, inbin;                            // the level's boundary bin
     float T;
-    int keep;
+    int keep, neq;
 };
 
 // Block-wide minimum and maximum (every thread gets both).
@@ -213,7 +233,9 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
                                          Sm& sm) {
     static_assert(NT >= kBins && NT % 64 == 0 && EPT >= 1 && EPT <= 64, "topk geometry");
     static_assert(kBins == 4 * 64, "one wave scans the histogram, four bins per lane");
-    static_assert(!Sink::kVals || sizeof(sm.outv) == sizeof(sm.outk), "an output with scores stages them");
+    static_assert(!Sink::kVals || sizeof(sm.u.c.outv) == sizeof(sm.u.c.outk), "an output with scores stages them");
+    static_assert(!Row::kKeys || sizeof(sm.keyof) == sizeof(int) * NT * EPT, "a row with keys stages them");
+    static_assert((NT * EPT) % 64 == 0, "whole groups");
     constexpr int NW = NT / 64;
     static_assert(NW % 4 == 0 || NW < 4, "group counts are read four at a time");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -249,7 +271,11 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
     const int lim = n - tid;   // element e is in the row when e * NT < lim
 #pragma unroll
     for (int e = 0; e < EPT; ++e) f[e] = e * NT < lim ? fmaxf(f[e], -INFINITY) : kNone;
-    if (tid == 0) { sm.ncand = 0; sm.T = INFINITY; sm.keep = 0; }
+    if constexpr (Row::kKeys) {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) sm.keyof[e * NT + tid] = kid[e];
+    }
+    if (tid == 0) { sm.T = INFINITY; sm.keep = 0; sm.neq = -1; }
     if (tid < kBins) sm.hist[tid] = 0;
 
     // the live set is every key with lo <= value <= hi; krem of them are kept
@@ -304,21 +330,33 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
         const int inbin = __builtin_amdgcn_readfirstlane(sm.inbin);
         krem -= __builtin_amdgcn_readfirstlane(sm.above);
         if (inbin <= NT) {
-            // rank the keys of the bin directly: gather them (a slot
-            // reservation per element group, broadcast without a lane
-            // exchange), then each key counts the gathered values above and
-            // at its own
+            // rank the keys of the bin directly: each wave gathers its own
+            // into its slice of LDS (a running count, no atomics), the
+            // slices are packed into one list, then each key counts the
+            // gathered values above and at its own
+            int wc = 0;
 #pragma unroll
             for (int e = 0; e < EPT; ++e) {
                 const bool a = f[e] >= lo && f[e] <= hi && value_bin(f[e], scale, off) == bstar;
                 const uint64_t m = __ballot(a);
                 if (m) {
-                    int base = 0;
-                    if (lane == 0) base = atomicAdd(&sm.ncand, (int)__popcll(m));
-                    base = __builtin_amdgcn_readfirstlane(base);
-                    const int slot = base + count_below(m);
-                    if (a && slot < NT) sm.cand[slot] = f[e];
+                    if (a) sm.u.g.slice[wave][wc + count_below(m)] = f[e];
+                    wc += (int)__popcll(m);
                 }
+            }
+            if (lane == 0) sm.u.g.wcnt[wave] = wc;
+            __syncthreads();
+            if (tid < inbin) {
+                // key tid sits in the first slice whose running total exceeds it
+                int w = 0, base = 0, cum = 0;
+#pragma unroll
+                for (int v = 0; v < NW; ++v) {
+                    cum += sm.u.g.wcnt[v];
+                    const bool past = tid >= cum;
+                    w = past ? v + 1 : w;
+                    base = past ? cum : base;
+                }
+                sm.cand[tid] = sm.u.g.slice[w][tid - base];
             }
             if (tid < 64) sm.cand[inbin + tid] = kNone;   // whole groups of four past the bin
             __syncthreads();
@@ -344,7 +382,7 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
             }
             gt = group_sum(gt, P);
             ge = group_sum(ge, P);
-            if (c < inbin && part == 0 && gt < krem && krem <= ge) { sm.T = v; sm.keep = krem - gt; }
+            if (c < inbin && part == 0 && gt < krem && krem <= ge) { sm.T = v; sm.keep = krem - gt; sm.neq = ge - gt; }
             __syncthreads();
             T = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sm.T)));
             krem = __builtin_amdgcn_readfirstlane(sm.keep);
@@ -395,94 +433,107 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
         }
         T = key_value(t);
     }
-    // keep every key > T and the first krem keys == T (NaN padding is neither)
+    // Keep every key > T and the first krem keys == T in key order (NaN
+    // padding is neither).  When the kept ties are all the ties (always, for
+    // distinct scores) that is every key >= T.
     const int keep = krem;
+    const bool all_ties = keep == __builtin_amdgcn_readfirstlane(sm.neq);
+    constexpr int NB = Sm::NB;
 
-    // Keys in output order are grouped by (element e, wave w, lane): group
-    // (e, w) holds keys e*NT + 64w .. e*NT + 64w + 63.  A group's counts of
-    // keys > T and == T travel packed as gt + (eq << kEqShift): sums of them
-    // never carry between the fields (at most top_k - 1 keys exceed T, and
-    // top_k <= 2048), so every sum and scan below runs on the packed value.
-    // Lane e of each wave collects its group (e, wave).
-    constexpr int kEqShift = 13;
-    static_assert(kMaxTopK < (1 << kEqShift) && (int64_t)kMaxSelectKeys << kEqShift <= 0x7FFFFFFF, "count packing");
-    int cgq = 0;
+    // Pass 1: lane 0 of each wave stores its group's 64-lane masks, which
+    // are bits e*NT + 64w .. +63 of the element bitmaps; kept lanes stage
+    // their scores where the output carries them.
+    if (all_ties) {
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        const int ng = __popcll(__ballot(f[e] > T));
-        const int nq = __popcll(__ballot(f[e] == T));
-        cgq = lane == e ? ng + (nq << kEqShift) : cgq;
-    }
-    if (lane < EPT) sm.pre_gt[lane * NW + wave] = cgq;
-    __syncthreads();
-    // Each wave forms its own groups' offsets: lane e sums row e of the
-    // counts (all waves, and the waves before this one), and an exclusive
-    // lane sum of the row totals adds every earlier element.
-    int rs = 0, ws = 0;
-    if (lane < EPT) {
+        for (int e = 0; e < EPT; ++e) {
+            asm volatile("" : "+v"(f[e]));   // one element at a time: no hoisted masks
+            const bool k = f[e] >= T;
+            const uint64_t m = __ballot(k);
+            if (lane == 0) sm.u.c.keep[(e * NT + 64 * wave) / 64] = m;
+            if constexpr (Sink::kVals) if (k) sm.u.c.vals[e * NT + tid] = f[e];
+        }
+    } else {
 #pragma unroll
-        for (int v = 0; v < NW; v += 4) {
-            const int4 x = *reinterpret_cast<const int4*>(&sm.pre_gt[lane * NW + v]);
-            const int x4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-            for (int j = 0; j < 4 && v + j < NW; ++j) {
-                rs += x4[j];
-                ws += v + j < wave ? x4[j] : 0;
+        for (int e = 0; e < EPT; ++e) {
+            asm volatile("" : "+v"(f[e]));
+            const uint64_t m = __ballot(f[e] > T);
+            const uint64_t q = __ballot(f[e] == T);
+            if (lane == 0) {
+                sm.u.c.keep[(e * NT + 64 * wave) / 64] = m;
+                sm.u.c.tie[(e * NT + 64 * wave) / 64] = q;
             }
+            if constexpr (Sink::kVals) if (f[e] >= T) sm.u.c.vals[e * NT + tid] = f[e];
         }
     }
-    const int pgq_l = wave_inclusive_sum(rs) - rs + ws;   // lane e: counts before group (e, wave)
-    const int kb = row.key(tid);                          // key of element 0; element e adds e * NT
+    __syncthreads();
 
+    // Pass 2: thread t owns bitmap words t*WPT .. t*WPT+WPT-1 (consecutive
+    // keys).  One block scan of its (kept, tie) counts, packed as
+    // kept + (tie << kEqShift), places its keys; the ties it keeps are the
+    // first (keep - ties before it) of its own.  Sums never carry between
+    // the fields: fewer than top_k <= 2048 keys are kept from the first map.
+    constexpr int kEqShift = 13;
+    static_assert(kMaxTopK < (1 << kEqShift) && (int64_t)kMaxSelectKeys << kEqShift <= 0x7FFFFFFF, "count packing");
+    constexpr int WPT = (NB + NT - 1) / NT;
+    const uint32_t* kwords = reinterpret_cast<const uint32_t*>(sm.u.c.keep);
+    const uint32_t* twords = reinterpret_cast<const uint32_t*>(sm.u.c.tie);
+    uint32_t kw[WPT], tw[WPT];
+    int ck = 0, ct = 0;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        // one element at a time: keeps the compiler from computing all
-        // 2*EPT lane masks up front (they would spill)
-        asm volatile("" : "+v"(f[e]));
-        const bool gt = f[e] > T, eq = f[e] == T;
-        const uint64_t gm = __ballot(gt);
-        const uint64_t qm = __ballot(eq);
-        if (gm | qm) {
-            const int pp = __builtin_amdgcn_readlane(pgq_l, e);
-            const int pg = pp & ((1 << kEqShift) - 1), pq = pp >> kEqShift;
-            // the group's keys equal to T that are kept: the first (keep - pq)
-            const int room = keep - pq;              // signed: negative once every tie is placed
-            uint64_t sel;
-            bool kept;
-            if (room >= (int)__popcll(qm)) {         // every tie of the group
-                sel = gm | qm;
-                kept = gt || eq;
-            } else if (room <= 0) {                  // none
-                sel = gm;
-                kept = gt;
-            } else {                                 // the lowest `room` lanes of them
-                uint64_t qsel = 0, m = qm;
-                for (int k = 0; k < room; ++k) { qsel |= m & (~m + 1); m &= m - 1; }
-                sel = gm | qsel;
-                kept = gt || (eq && ((qsel >> lane) & 1));
+    for (int j = 0; j < WPT; ++j) {
+        const int w = tid * WPT + j;
+        kw[j] = w < NB ? kwords[w] : 0u;
+        tw[j] = (!all_ties && w < NB) ? twords[w] : 0u;
+        ck += __popc(kw[j]);
+        ct += __popc(tw[j]);
+    }
+    const int mine = ck + (ct << kEqShift);
+    const int incl = wave_inclusive_sum(mine);
+    if (lane == 63) sm.wsum[wave] = incl;
+    __syncthreads();
+    int before = incl - mine;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) before += v < wave ? sm.wsum[v] : 0;
+    const int pk = before & ((1 << kEqShift) - 1), pt = before >> kEqShift;
+    int q = min(max(keep - pt, 0), ct);    // ties this thread keeps
+    int pos = pk + min(pt, keep);          // kept keys before its words
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+        uint32_t m = kw[j];
+        if (!all_ties) {
+            uint32_t t = tw[j];
+            const int c = __popc(t);
+            if (c <= q) {
+                m |= t;
+                q -= c;
+            } else {
+                for (; q > 0; --q) { m |= t & (0u - t); t &= t - 1; }   // the lowest q of them
             }
-            const int slot = pg + min(pq, keep) + count_below(sel);   // kept keys before this one
-            if (kept && slot < top_k) {
-                int key;
-                if constexpr (Row::kKeys) key = kid[e];
-                else key = kb + e * NT;
-                sm.outk[slot] = key;
-                if constexpr (Sink::kVals) sm.outv[slot] = f[e];
-            }
+        }
+        const int k0w = (tid * WPT + j) * 32;
+        while (m) {
+            const int k = k0w + __builtin_ctz(m);
+            m &= m - 1;
+            int key;
+            if constexpr (Row::kKeys) key = sm.keyof[k];
+            else key = row.key(k);
+            sm.u.c.outk[pos] = key;
+            if constexpr (Sink::kVals) sm.u.c.outv[pos] = sm.u.c.vals[k];
+            ++pos;
         }
     }
     // the top_k kept keys leave in one coalesced pass
     __syncthreads();
     for (int t = tid; t < top_k; t += NT) {
-        if constexpr (Sink::kVals) sink.write(t, sm.outk[t], sm.outv[t]);
-        else sink.write(t, sm.outk[t], 0.f);
+        if constexpr (Sink::kVals) sink.write(t, sm.u.c.outk[t], sm.u.c.outv[t]);
+        else sink.write(t, sm.u.c.outk[t], 0.f);
     }
     if (tid == 0 && count) *count = top_k;
 }
 
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_prefill_kernel(TopkArgs a) {
-    __shared__ TopkSmem<NT, EPT, false> sm;
+    __shared__ TopkSmem<NT, EPT, false, false> sm;
     const int r = blockIdx.x;
     const int64_t p = a.pos0 + r;
     const int n = (int)(p + 1);
@@ -498,7 +549,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_decode_kernel(
         const float* S, SeqMeta m, int top_k, int32_t* idx, int32_t* count, CandEntry* cand) {
-    __shared__ TopkSmem<NT, EPT, true> sm;
+    __shared__ TopkSmem<NT, EPT, true, false> sm;
     const int b = seq_of_block(m, blockIdx.x);
     const int g = blockIdx.x - m.blk0[b];
     const int ctx = m.ctx[b];
@@ -517,7 +568,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_merge_kernel(
         SeqMeta m, int top_k, int32_t* idx, int32_t* count, const CandEntry* cand) {
-    __shared__ TopkSmem<NT, EPT, false> sm;
+    __shared__ TopkSmem<NT, EPT, false, true> sm;
     const int b = blockIdx.x;
     const int nseg = m.blk0[b + 1] - m.blk0[b];
     if (nseg < 2) return;
