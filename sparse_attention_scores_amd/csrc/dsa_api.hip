@@ -135,7 +135,7 @@ dsa_status decode_layout(const dsa_shape* s, int32_t B, const int64_t* ctx, Deco
         d.topk_meta.s_off[b] = soff;
         d.topk_meta.ctx[b] = c;
         d.topk_meta.blk0[b] = tblk;
-        tblk += dsa::topk_decode_segments(c);
+        tblk += dsa::topk_decode_segments(c, s->top_k);
         // a sequence within top_k keeps every key: no scores needed
         if (c > s->top_k) iblk += (c + kpb - 1) / kpb;
         const int cnt = c < s->top_k ? c : s->top_k;
@@ -161,7 +161,7 @@ dsa_status decode_layout(const dsa_shape* s, int32_t B, const int64_t* ctx, Deco
     d.po_off = d.cnt_off + align_up((size_t)B * sizeof(int32_t));
     d.pml_off = d.po_off + align_up((size_t)items * s->n_heads * s->d_latent * sizeof(float));
     d.cand_off = d.pml_off + align_up((size_t)items * s->n_heads * 2 * sizeof(float));
-    d.total = d.cand_off + align_up((size_t)tblk * s->top_k * dsa::topk_decode_candidate_bytes());
+    d.total = d.cand_off + align_up(dsa::topk_decode_work_bytes(B, tblk, s->top_k));
     return DSA_OK;
 }
 
@@ -190,8 +190,7 @@ dsa_status decode_run(const dsa_shape* shape, const uint16_t* q, const uint16_t*
     int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + d.idx_off);
     int32_t* cnt = count_out ? count_out : reinterpret_cast<int32_t*>(base + d.cnt_off);
     if ((st = launched(dsa::launch_indexer_decode(sid, qI, kI, w, S, d.idx_meta, d.idx_blocks, s)))) return st;
-    if ((st = launched(dsa::launch_topk_decode(S, d.topk_meta, shape->top_k, idx, cnt,
-                                               base + d.cand_off, d.n_max, s))))
+    if ((st = launched(dsa::launch_topk_decode(S, d.topk_meta, shape->top_k, idx, cnt, base + d.cand_off, s))))
         return st;
     dsa::AttnSplitArgs aa{q, kv, idx, shape->top_k, d.chunk, scale_log2(shape),
                           reinterpret_cast<float*>(base + d.po_off), reinterpret_cast<float*>(base + d.pml_off),

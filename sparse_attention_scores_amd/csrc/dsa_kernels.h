@@ -126,14 +126,12 @@ struct TopkArgs {
 };
 hipError_t launch_topk_prefill(const TopkArgs& a, int n_max, hipStream_t s);
 // Decode top-k: m.blk0 numbers the segment blocks of each sequence
-// (topk_decode_segments(ctx) each); cand holds top_k candidate entries per
-// segment block and is used only when a sequence has more than one segment.
-int topk_decode_segments(int ctx);
+// (topk_decode_segments(ctx, top_k) each: none for a sequence of at most
+// top_k keys); `work` holds topk_decode_work_bytes(B, blocks, top_k) bytes.
+int topk_decode_segments(int ctx, int top_k);
+size_t topk_decode_work_bytes(int B, int blocks, int top_k);
 hipError_t launch_topk_decode(const float* S, const SeqMeta& m, int top_k, int32_t* idx,
-                              int32_t* count, void* cand, int n_max, hipStream_t s);
-// Bytes of one segment candidate (key index and score) in the decode
-// workspace; top_k of them per segment block.
-size_t topk_decode_candidate_bytes();
+                              int32_t* count, void* work, hipStream_t s);
 
 struct AttnArgs {
     const uint16_t* q;     // [rows, H, Dqk]

@@ -40,7 +40,6 @@ namespace {
 
 constexpr int kBins = 256;
 constexpr int kMaxLevels = 4;
-constexpr int kDecodeSeg = 16384;   // keys per decode segment block (a 64k context: 4 segments, 8192 candidates)
 
 // Larger float -> larger key; -0 ranks equal to +0 (the floats compare equal).
 __device__ inline uint32_t order_key(float f) {
@@ -115,7 +114,7 @@ __device__ inline int wave_inclusive_sum(int x) {
     return x;
 }
 
-template <int NT, int EPT, bool VALS, bool KEYS>
+template <int NT, int EPT>
 struct TopkSmem {
     static constexpr int NW = NT / 64;
     static constexpr int NE = NT * EPT;                           // elements of a row
@@ -126,7 +125,6 @@ struct TopkSmem {
     int wsum[NW];                                       // block-scan partials
     int hist[kBins] __attribute__((aligned(16)));
     float cand[NT + 64] __attribute__((aligned(16)));   // the boundary bin's values, NaN past them
-    int keyof[KEYS ? NE : 1];                           // key index of each element, where keys travel
     union {
         struct {                                        // gathering the boundary bin
             float slice[NW][kSlice];                    // each wave's boundary-bin values
@@ -135,9 +133,7 @@ struct TopkSmem {
         struct {                                        // writing the selection
             uint64_t keep[NB / 2];                      // kept elements (above T, or at T when all ties stay)
             uint64_t tie[NB / 2];                       // elements equal to T, where only some stay
-            float vals[VALS ? NE : 1];                  // kept elements' scores, where the output carries them
             int outk[kMaxTopK];                         // kept keys in output order
-            float outv[VALS ? kMaxTopK : 1];            // and their scores
         } c;
     } u;
     int bstar, above, inbin;                            // the level's boundary bin
@@ -177,55 +173,18 @@ __device__ inline __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
 }
 struct DirectRow {   // element k is key k0 + k
-    static constexpr bool kKeys = false;   // key indices follow from the position
     const float* __restrict__ s;
     int k0;
     __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int n) const { return row_rsrc(s, 4 * n); }
-    __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, int k, int&) const {
+    __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, int k) const {
         return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 4 * k, 0, 0));   // raw bits
     }
-    __device__ __forceinline__ float load(int k, int&) const { return s[k]; }
     __device__ __forceinline__ int32_t key(int k) const { return k0 + k; }
 };
-// A candidate of a segmented sequence: a kept key of one segment and its
-// (NaN-free) score.
-struct CandEntry {
-    int32_t key;
-    float score;
-};
-// The candidates of a segmented row: the concatenated selections of its
-// segments (top_k entries per segment, each in ascending key order, padded
-// with key -1), so element order is key order.  Padding scores -inf and sits
-// after every real candidate, and the first segment alone brings top_k real
-// ones, so padding is never kept.
-struct CandRow {
-    static constexpr bool kKeys = true;    // key indices travel with the scores
-    const CandEntry* __restrict__ c;
-    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int n) const { return row_rsrc(c, 8 * n); }
-    __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, int k, int& key) const {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * k, 0, 0);
-        key = (int32_t)v[0];
-        return key < 0 ? -INFINITY : __uint_as_float(v[1]);
-    }
-    __device__ __forceinline__ float load(int k, int& key) const {
-        const CandEntry e = c[k];
-        key = e.key;
-        return e.key < 0 ? -INFINITY : e.score;
-    }
-    __device__ __forceinline__ int32_t key(int k) const { return c[k].key; }
-};
-
-// Where the kept keys go: a plain index list, or candidate entries (index
-// and score) for a later merge.
+// Where the kept keys go.
 struct KeySink {
-    static constexpr bool kVals = false;
     int32_t* __restrict__ out;
-    __device__ __forceinline__ void write(int t, int32_t key, float) const { out[t] = key; }
-};
-struct CandSink {
-    static constexpr bool kVals = true;
-    CandEntry* __restrict__ out;
-    __device__ __forceinline__ void write(int t, int32_t key, float v) const { out[t] = CandEntry{key, v}; }
+    __device__ __forceinline__ void write(int t, int32_t key) const { out[t] = key; }
 };
 
 template <int NT, int EPT, typename Row, typename Sink, typename Sm>
@@ -233,48 +192,29 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
                                          Sm& sm) {
     static_assert(NT >= kBins && NT % 64 == 0 && EPT >= 1 && EPT <= 64, "topk geometry");
     static_assert(kBins == 4 * 64, "one wave scans the histogram, four bins per lane");
-    static_assert(!Sink::kVals || sizeof(sm.u.c.outv) == sizeof(sm.u.c.outk), "an output with scores stages them");
-    static_assert(!Row::kKeys || sizeof(sm.keyof) == sizeof(int) * NT * EPT, "a row with keys stages them");
     static_assert((NT * EPT) % 64 == 0, "whole groups");
     constexpr int NW = NT / 64;
     static_assert(NW % 4 == 0 || NW < 4, "group counts are read four at a time");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float kNone = __int_as_float(0x7FC00000);
-    if (n <= top_k) {   // every earlier key (its score is read only where the output carries it)
-        for (int t = tid; t < top_k; t += NT) {
-            if (t < n) {
-                float v = 0.f;
-                int key = row.key(t);
-                if constexpr (Sink::kVals) {
-                    v = row.load(t, key);
-                    v = v == v ? v : -INFINITY;
-                }
-                sink.write(t, key, v);
-            } else {
-                sink.write(t, -1, -INFINITY);
-            }
-        }
+    if (n <= top_k) {   // every earlier key; the scores are not read
+        for (int t = tid; t < top_k; t += NT) sink.write(t, t < n ? row.key(t) : -1);
         if (tid == 0 && count) *count = n;
         return;
     }
     // Scores in registers.  A NaN score ranks as -inf; keys past the row are
     // NaN, which every comparison below treats as "not a candidate".
     float f[EPT];
-    int kid[Row::kKeys ? EPT : 1];
     {
         const auto rs = row.rsrc(n);
 #pragma unroll
         for (int e = 0; e < EPT; ++e)   // no waits between the loads
-            f[e] = row.load(rs, e * NT + tid, kid[Row::kKeys ? e : 0]);
+            f[e] = row.load(rs, e * NT + tid);
     }
     // fmaxf against -inf turns NaN into -inf and leaves the rest
     const int lim = n - tid;   // element e is in the row when e * NT < lim
 #pragma unroll
     for (int e = 0; e < EPT; ++e) f[e] = e * NT < lim ? fmaxf(f[e], -INFINITY) : kNone;
-    if constexpr (Row::kKeys) {
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) sm.keyof[e * NT + tid] = kid[e];
-    }
     if (tid == 0) { sm.T = INFINITY; sm.keep = 0; sm.neq = -1; }
     if (tid < kBins) sm.hist[tid] = 0;
 
@@ -450,7 +390,6 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
             const bool k = f[e] >= T;
             const uint64_t m = __ballot(k);
             if (lane == 0) sm.u.c.keep[(e * NT + 64 * wave) / 64] = m;
-            if constexpr (Sink::kVals) if (k) sm.u.c.vals[e * NT + tid] = f[e];
         }
     } else {
 #pragma unroll
@@ -462,7 +401,6 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
                 sm.u.c.keep[(e * NT + 64 * wave) / 64] = m;
                 sm.u.c.tie[(e * NT + 64 * wave) / 64] = q;
             }
-            if constexpr (Sink::kVals) if (f[e] >= T) sm.u.c.vals[e * NT + tid] = f[e];
         }
     }
     __syncthreads();
@@ -514,26 +452,18 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
         while (m) {
             const int k = k0w + __builtin_ctz(m);
             m &= m - 1;
-            int key;
-            if constexpr (Row::kKeys) key = sm.keyof[k];
-            else key = row.key(k);
-            sm.u.c.outk[pos] = key;
-            if constexpr (Sink::kVals) sm.u.c.outv[pos] = sm.u.c.vals[k];
-            ++pos;
+            sm.u.c.outk[pos++] = row.key(k);
         }
     }
     // the top_k kept keys leave in one coalesced pass
     __syncthreads();
-    for (int t = tid; t < top_k; t += NT) {
-        if constexpr (Sink::kVals) sink.write(t, sm.u.c.outk[t], sm.u.c.outv[t]);
-        else sink.write(t, sm.u.c.outk[t], 0.f);
-    }
+    for (int t = tid; t < top_k; t += NT) sink.write(t, sm.u.c.outk[t]);
     if (tid == 0 && count) *count = top_k;
 }
 
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_prefill_kernel(TopkArgs a) {
-    __shared__ TopkSmem<NT, EPT, false, false> sm;
+    __shared__ TopkSmem<NT, EPT> sm;
     const int r = blockIdx.x;
     const int64_t p = a.pos0 + r;
     const int n = (int)(p + 1);
@@ -542,38 +472,303 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
                       a.count ? a.count + r : nullptr, sm);
 }
 
-// Decode, phase 1: block -> (sequence b, segment g) of kDecodeSeg keys.  A
-// sequence of one segment is finished here; otherwise the segment's
-// selection (key and score, top_k entries per segment block) goes to the
-// candidate list.
-template <int NT, int EPT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_decode_kernel(
-        const float* S, SeqMeta m, int top_k, int32_t* idx, int32_t* count, CandEntry* cand) {
-    __shared__ TopkSmem<NT, EPT, true, false> sm;
-    const int b = seq_of_block(m, blockIdx.x);
-    const int g = blockIdx.x - m.blk0[b];
-    const int ctx = m.ctx[b];
-    const int k0 = g * kDecodeSeg;
-    const int n = min(ctx - k0, kDecodeSeg);
-    const float* srow = S + m.s_off[b] + k0;
-    if (ctx <= kDecodeSeg)
-        topk_row<NT, EPT>(DirectRow{srow, 0}, n, top_k, KeySink{idx + (int64_t)b * top_k}, count ? count + b : nullptr,
-                          sm);
-    else
-        topk_row<NT, EPT>(DirectRow{srow, k0}, n, top_k, CandSink{cand + (int64_t)blockIdx.x * top_k}, nullptr, sm);
+// ---- Decode: one selection per sequence, spread over segment blocks ----
+//
+// A sequence with more than top_k keys is split into segments of kDecSeg
+// keys, one block each.  Every segment of a sequence bins its keys on one shared
+// value-linear map: kDecBins bins between the minimum and maximum of a fixed
+// sample of the sequence's scores.  Keys outside that range fall into the
+// end bins, so the map stays monotone and every key is counted, and the
+// segments' histograms add up to the sequence's.  Three launches:
+//   A. each segment block stores its histogram;
+//   B. each segment block sums its sequence's histograms and finds the bin
+//      holding the top_k-th key; its keys above that bin go to the
+//      sequence's list of sure keys and its keys in that bin (with scores)
+//      to the candidate list, at offsets the histograms give, so both lists
+//      are in key order;
+//   C. one block per sequence ranks the candidates (score, then lower key),
+//      keeps as many as the count still allows, and merges them into the
+//      sure keys by binary search.
+// A sequence whose sample gives no usable range, or whose boundary bin holds
+// more than kDecCap keys, is selected by its final block in one pass over
+// all of its keys instead: slower, same result.
+constexpr int kDecSeg = 8192;                 // keys per segment block
+constexpr int kDecT = 512;                    // threads of a segment block (one sample key each)
+constexpr int kDecEPT = kDecSeg / kDecT;
+constexpr int kDecBins = 1024;                // bins of the shared map
+constexpr int kDecCap = 1024;                 // boundary-bin keys the final block ranks
+constexpr int kDecFinT = 1024;                // threads of the final block
+static_assert(kDecBins == 16 * 64 && kDecBins == 2 * kDecT, "one wave scans the bins, sixteen per lane");
+static_assert(kDecSeg / 32 <= kDecT && kDecCap <= kDecFinT, "decode block shapes");
+
+struct DecCand {        // a boundary-bin key of a sequence and its score (NaN as -inf)
+    int32_t key;
+    float score;
+};
+struct DecSeqInfo {     // per sequence
+    float scale, off;   // the shared map: bin(v) = clamp(trunc(v * scale + off), 0, kDecBins - 1)
+    int degenerate;     // the sample gave no usable range
+    int fallback;       // the boundary bin holds more than kDecCap keys
+    int above, inbin;   // keys in bins above the boundary bin; keys in it
+    int pad_[2];
+};
+struct DecWork {
+    int* hist;          // [segment block][kDecBins]
+    DecSeqInfo* info;   // [B]
+    int32_t* sure;      // [B][top_k]: keys above the boundary bin, ascending
+    DecCand* cand;      // [B][kDecCap]: keys in it, ascending
+};
+
+// The shared bin of a (NaN-free) score: clamped in float, so +-inf and
+// values outside the sample range land in the end bins.
+__device__ inline int dec_bin(float v, float scale, float off) {
+    return (int)fminf(fmaxf(__builtin_fmaf(v, scale, off), 0.f), (float)(kDecBins - 1));
 }
 
-// Decode, phase 2: block b selects sequence b's top_k among the candidates
-// of its segments (sequences of one segment have nothing to do).
-template <int NT, int EPT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_merge_kernel(
-        SeqMeta m, int top_k, int32_t* idx, int32_t* count, const CandEntry* cand) {
-    __shared__ TopkSmem<NT, EPT, false, true> sm;
+// The sample range of sequence b, identical in every block: the minimum and
+// maximum of kDecT evenly spaced scores (NaN ignored).
+__device__ inline void dec_sample_range(const float* srow, int ctx, float& lo, float& hi, float (&red)[2][kDecT / 64]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float v = srow[(int)((int64_t)tid * ctx / kDecT)];
+    lo = wave_reduce(v == v ? v : INFINITY, MinOp{});
+    hi = wave_reduce(v == v ? v : -INFINITY, MaxOp{});
+    if (lane == 0) { red[0][wave] = lo; red[1][wave] = hi; }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kDecT / 64; ++w) { lo = fminf(lo, red[0][w]); hi = fmaxf(hi, red[1][w]); }
+}
+
+__device__ inline int lower_bound_lds(const int* a, int n, int x) {   // first index with a[i] >= x
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] < x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Pass A: block -> (sequence b, segment g).
+__global__ __launch_bounds__(kDecT) __attribute__((amdgpu_waves_per_eu(2, 8))) void topk_dec_hist_kernel(
+        const float* S, SeqMeta m, DecWork w) {
+    __shared__ int hist[kDecBins];
+    __shared__ float red[2][kDecT / 64];
+    const int tid = threadIdx.x;
+    const int b = seq_of_block(m, blockIdx.x), g = blockIdx.x - m.blk0[b];
+    const int ctx = m.ctx[b];
+    const float* srow = S + m.s_off[b];
+    const int k0 = g * kDecSeg, n = min(ctx - k0, kDecSeg);
+    float f[kDecEPT];
+    {
+        const auto rs = row_rsrc(srow + k0, 4 * n);   // reads past the segment return 0
+#pragma unroll
+        for (int e = 0; e < kDecEPT; ++e)
+            f[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (e * kDecT + tid), 0, 0));
+    }
+    for (int i = tid; i < kDecBins; i += kDecT) hist[i] = 0;
+    float lo, hi;
+    dec_sample_range(srow, ctx, lo, hi, red);   // ends with a barrier
+    const float scale = (float)kDecBins / (hi - lo), off = -lo * scale;
+    const bool degenerate = !(lo < hi) || !(scale > 0.f && scale < 3.0e38f && fabsf(off) < 3.0e38f);
+    if (!degenerate) {
+#pragma unroll
+        for (int e = 0; e < kDecEPT; ++e)
+            if (e * kDecT + tid < n) atomicAdd(&hist[dec_bin(fmaxf(f[e], -INFINITY), scale, off)], 1);
+    }
+    __syncthreads();
+    for (int i = tid; i < kDecBins; i += kDecT) w.hist[(int64_t)blockIdx.x * kDecBins + i] = hist[i];
+    if (g == 0 && tid == 0) w.info[b] = DecSeqInfo{scale, off, degenerate ? 1 : 0, 0, 0, 0, {0, 0}};
+}
+
+// Pass B: block -> (sequence b, segment g), for sequences of two or more.
+__global__ __launch_bounds__(kDecT) __attribute__((amdgpu_waves_per_eu(2, 8))) void topk_dec_split_kernel(
+        const float* S, SeqMeta m, int top_k, DecWork w) {
+    __shared__ int htot[kDecBins] __attribute__((aligned(16)));
+    __shared__ int hbef[kDecBins] __attribute__((aligned(16)));
+    __shared__ uint64_t bm_sure[kDecSeg / 64], bm_cand[kDecSeg / 64];
+    __shared__ float cval[kDecSeg];
+    __shared__ int wsum[kDecT / 64];
+    __shared__ int s_bstar, s_above, s_inbin, s_bef_above, s_bef_in;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = seq_of_block(m, blockIdx.x), g = blockIdx.x - m.blk0[b];
+    const int ctx = m.ctx[b], G = m.blk0[b + 1] - m.blk0[b];
+    const DecSeqInfo info = w.info[b];
+    if (info.degenerate) return;
+    const int k0 = g * kDecSeg, n = min(ctx - k0, kDecSeg);
+    float f[kDecEPT];
+    {
+        const auto rs = row_rsrc(S + m.s_off[b] + k0, 4 * n);
+#pragma unroll
+        for (int e = 0; e < kDecEPT; ++e)
+            f[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (e * kDecT + tid), 0, 0));
+    }
+    if (tid == 0) s_inbin = kDecCap + 1;   // stays so (fallback) if no bin were found
+    // the sequence's histogram, and the part of it from earlier segments
+    const int* h0 = w.hist + (int64_t)m.blk0[b] * kDecBins;
+#pragma unroll
+    for (int r = 0; r < kDecBins / kDecT; ++r) {
+        const int i = r * kDecT + tid;
+        int h[kMaxSelectKeys / kDecSeg];   // every segment's count, loads issued together
+#pragma unroll
+        for (int s = 0; s < kMaxSelectKeys / kDecSeg; ++s) h[s] = s < G ? h0[(int64_t)s * kDecBins + i] : 0;
+        int tot = 0, bef = 0;
+#pragma unroll
+        for (int s = 0; s < kMaxSelectKeys / kDecSeg; ++s) {
+            tot += h[s];
+            bef += s < g ? h[s] : 0;
+        }
+        htot[i] = tot;
+        hbef[i] = bef;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // lane l holds bins b0 .. b0+15 with b0 = kDecBins - 16(l+1): an
+        // inclusive lane sum counts from the top
+        const int b0 = kDecBins - 16 * (lane + 1);
+        int h[16], hb[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int4 x = *reinterpret_cast<const int4*>(&htot[b0 + 4 * q]);
+            const int4 y = *reinterpret_cast<const int4*>(&hbef[b0 + 4 * q]);
+            h[4 * q] = x.x; h[4 * q + 1] = x.y; h[4 * q + 2] = x.z; h[4 * q + 3] = x.w;
+            hb[4 * q] = y.x; hb[4 * q + 1] = y.y; hb[4 * q + 2] = y.z; hb[4 * q + 3] = y.w;
+        }
+        int t16 = 0, b16 = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) { t16 += h[k]; b16 += hb[k]; }
+        int gt = wave_inclusive_sum(t16) - t16, bgt = wave_inclusive_sum(b16) - b16;
+#pragma unroll
+        for (int k = 15; k >= 0; --k) {
+            if (gt < top_k && gt + h[k] >= top_k) {
+                s_bstar = b0 + k; s_above = gt; s_inbin = h[k]; s_bef_above = bgt; s_bef_in = hb[k];
+            }
+            gt += h[k];
+            bgt += hb[k];
+        }
+    }
+    __syncthreads();
+    const int bstar = __builtin_amdgcn_readfirstlane(s_bstar);
+    const int above = __builtin_amdgcn_readfirstlane(s_above);
+    const int inbin = __builtin_amdgcn_readfirstlane(s_inbin);
+    const int bef_above = __builtin_amdgcn_readfirstlane(s_bef_above);
+    const int bef_in = __builtin_amdgcn_readfirstlane(s_bef_in);
+    if (inbin > kDecCap) {
+        if (g == 0 && tid == 0) w.info[b].fallback = 1;
+        return;
+    }
+    if (g == 0 && tid == 0) { w.info[b].above = above; w.info[b].inbin = inbin; }
+    // this segment's sure keys and candidates as bitmaps (bit k: element k)
+#pragma unroll
+    for (int e = 0; e < kDecEPT; ++e) {
+        asm volatile("" : "+v"(f[e]));   // one element at a time: no hoisted masks
+        const bool in = e * kDecT + tid < n;
+        const float v = fmaxf(f[e], -INFINITY);
+        const int bin = dec_bin(v, info.scale, info.off);
+        const bool sure = in && bin > bstar, cd = in && bin == bstar;
+        const uint64_t ms = __ballot(sure), mc = __ballot(cd);
+        if (lane == 0) {
+            bm_sure[(e * kDecT + 64 * wave) / 64] = ms;
+            bm_cand[(e * kDecT + 64 * wave) / 64] = mc;
+        }
+        if (cd) cval[e * kDecT + tid] = v;
+    }
+    __syncthreads();
+    // thread t < kDecSeg / 32 owns bitmap word t (keys 32t .. 32t+31); one
+    // block scan of its (sure, candidate) counts, packed as sure + (cand <<
+    // 13): this segment holds fewer than top_k <= 2048 sure keys
+    constexpr int kShift = 13;
+    static_assert(kMaxTopK < (1 << kShift) && kDecCap < (1 << (31 - kShift)), "count packing");
+    const uint32_t* ws = reinterpret_cast<const uint32_t*>(bm_sure);
+    const uint32_t* wc = reinterpret_cast<const uint32_t*>(bm_cand);
+    uint32_t xs = tid < kDecSeg / 32 ? ws[tid] : 0u, xc = tid < kDecSeg / 32 ? wc[tid] : 0u;
+    const int mine = __popc(xs) + (__popc(xc) << kShift);
+    const int incl = wave_inclusive_sum(mine);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = incl - mine;
+#pragma unroll
+    for (int v = 0; v < kDecT / 64; ++v) before += v < wave ? wsum[v] : 0;
+    int ps = bef_above + (before & ((1 << kShift) - 1)), pc = bef_in + (before >> kShift);
+    int32_t* sure = w.sure + (int64_t)b * top_k;
+    DecCand* cand = w.cand + (int64_t)b * kDecCap;
+    // (the counts match the histograms bin for bin, so every offset is in
+    // range; the bounds below only guard the lists)
+    while (xs) {
+        const int k = 32 * tid + __builtin_ctz(xs);
+        xs &= xs - 1;
+        if (ps < above) sure[ps] = k0 + k;
+        ++ps;
+    }
+    while (xc) {
+        const int k = 32 * tid + __builtin_ctz(xc);
+        xc &= xc - 1;
+        if (pc < inbin) cand[pc] = DecCand{k0 + k, cval[k]};
+        ++pc;
+    }
+}
+
+// Pass C: block b finishes sequence b.
+__global__ __launch_bounds__(kDecFinT) void topk_dec_final_kernel(const float* S, SeqMeta m, int top_k, int32_t* idx,
+                                                                 int32_t* count, DecWork w) {
+    __shared__ TopkSmem<kDecFinT, kMaxSelectKeys / kDecFinT> sm;   // one pass over a whole sequence
+    __shared__ int sure_l[kMaxTopK], kept_l[kMaxTopK];
+    __shared__ float cv[kDecCap];
+    __shared__ int ck[kDecCap];
+    __shared__ int wsum[kDecFinT / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x;
-    const int nseg = m.blk0[b + 1] - m.blk0[b];
-    if (nseg < 2) return;
-    topk_row<NT, EPT>(CandRow{cand + (int64_t)m.blk0[b] * top_k}, nseg * top_k, top_k,
-                      KeySink{idx + (int64_t)b * top_k}, count ? count + b : nullptr, sm);
+    const int ctx = m.ctx[b];
+    int32_t* out = idx + (int64_t)b * top_k;
+    if (ctx <= top_k) {   // every earlier key
+        for (int t = tid; t < top_k; t += kDecFinT) out[t] = t < ctx ? t : -1;
+        if (tid == 0 && count) count[b] = ctx;
+        return;
+    }
+    const DecSeqInfo info = w.info[b];
+    if (info.degenerate || info.fallback) {
+        topk_row<kDecFinT, kMaxSelectKeys / kDecFinT>(DirectRow{S + m.s_off[b], 0}, ctx, top_k, KeySink{out},
+                                                       count ? count + b : nullptr, sm);
+        return;
+    }
+    const int above = info.above, inbin = info.inbin, krem = top_k - above;   // 1 <= krem <= inbin
+    const DecCand* cand = w.cand + (int64_t)b * kDecCap;
+    if (tid < inbin) { const DecCand c = cand[tid]; cv[tid] = c.score; ck[tid] = c.key; }
+    for (int i = tid; i < above; i += kDecFinT) sure_l[i] = w.sure[(int64_t)b * top_k + i];
+    __syncthreads();
+    // rank of candidate c: candidates with a higher score, or the same score
+    // and a lower key (a strict order: ranks 0 .. inbin-1), split over P lanes
+    int lg = 0;
+    while (lg < 4 && (inbin << (lg + 1)) <= kDecFinT) ++lg;
+    const int P = 1 << lg, c = tid >> lg, part = tid & (P - 1);
+    const float v = cv[min(c, inbin - 1)];
+    const int kc = ck[min(c, inbin - 1)];
+    int r = 0;
+    if (c < inbin)
+        for (int i = part; i < inbin; i += P) {
+            const float x = cv[i];
+            r += (x > v || (x == v && ck[i] < kc)) ? 1 : 0;
+        }
+    r = group_sum(r, P);
+    // the kept candidates in list (= key) order
+    const int flag = (c < inbin && part == 0 && r < krem) ? 1 : 0;
+    const int incl = wave_inclusive_sum(flag);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int pos = incl - flag;
+#pragma unroll
+    for (int q = 0; q < kDecFinT / 64; ++q) pos += q < wave ? wsum[q] : 0;
+    if (flag) kept_l[pos] = kc;
+    __syncthreads();
+    // merge the two ascending lists
+    for (int i = tid; i < above; i += kDecFinT) {
+        const int d = sure_l[i];
+        out[i + lower_bound_lds(kept_l, krem, d)] = d;
+    }
+    for (int j = tid; j < krem; j += kDecFinT) {
+        const int x = kept_l[j];
+        out[j + lower_bound_lds(sure_l, above, x)] = x;
+    }
+    if (tid == 0 && count) count[b] = top_k;
 }
 
 // Block shape by row length: up to 32 keys per thread in 256-, then 512-,
@@ -594,21 +789,6 @@ hipError_t dispatch_shape(int n_max, Launch&& launch) {
     return hipErrorInvalidValue;
 }
 
-// Decode: one row per sequence, so latency rather than throughput counts:
-// always 1024 threads, as few elements per thread as the row allows.
-template <typename Launch>
-hipError_t dispatch_wide(int n_max, Launch&& launch) {
-    using std::integral_constant;
-    if (n_max <= 1024) return launch(integral_constant<int, 1024>{}, integral_constant<int, 1>{});
-    if (n_max <= 2048) return launch(integral_constant<int, 1024>{}, integral_constant<int, 2>{});
-    if (n_max <= 4096) return launch(integral_constant<int, 1024>{}, integral_constant<int, 4>{});
-    if (n_max <= 8192) return launch(integral_constant<int, 1024>{}, integral_constant<int, 8>{});
-    // segments of kDecodeSeg keys, and at most 8 * kMaxTopK candidates
-    static_assert(kDecodeSeg <= 16384 && (kMaxSelectKeys / kDecodeSeg) * kMaxTopK <= 16384, "decode shapes");
-    if (n_max <= 16384) return launch(integral_constant<int, 1024>{}, integral_constant<int, 16>{});
-    return hipErrorInvalidValue;
-}
-
 }  // namespace
 
 hipError_t launch_topk_prefill(const TopkArgs& a, int n_max, hipStream_t s) {
@@ -620,26 +800,40 @@ hipError_t launch_topk_prefill(const TopkArgs& a, int n_max, hipStream_t s) {
     });
 }
 
-int topk_decode_segments(int ctx) { return (ctx + kDecodeSeg - 1) / kDecodeSeg; }
+int topk_decode_segments(int ctx, int top_k) { return ctx > top_k ? (ctx + kDecSeg - 1) / kDecSeg : 0; }
 
-hipError_t launch_topk_decode(const float* S, const SeqMeta& m, int top_k, int32_t* idx, int32_t* count,
-                              void* cand_buf, int n_max, hipStream_t s) {
-    if (m.B <= 0) return hipSuccess;
-    CandEntry* cand = static_cast<CandEntry*>(cand_buf);
-    const int blocks = m.blk0[m.B];
-    hipError_t e = dispatch_wide(min(n_max, kDecodeSeg), [&](auto nt, auto ept) {
-        constexpr int NT = decltype(nt)::value, EPT = decltype(ept)::value;
-        hipLaunchKernelGGL((topk_decode_kernel<NT, EPT>), dim3(blocks), dim3(NT), 0, s, S, m, top_k, idx, count, cand);
-        return hipGetLastError();
-    });
-    if (e != hipSuccess || n_max <= kDecodeSeg) return e;
-    return dispatch_wide(topk_decode_segments(n_max) * top_k, [&](auto nt, auto ept) {
-        constexpr int NT = decltype(nt)::value, EPT = decltype(ept)::value;
-        hipLaunchKernelGGL((topk_merge_kernel<NT, EPT>), dim3(m.B), dim3(NT), 0, s, m, top_k, idx, count, cand);
-        return hipGetLastError();
-    });
+namespace {
+constexpr size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+DecWork carve(void* base, int B, int blocks, int top_k) {
+    char* p = static_cast<char*>(base);
+    DecWork w;
+    w.hist = reinterpret_cast<int*>(p);
+    p += align256((size_t)blocks * kDecBins * sizeof(int));
+    w.info = reinterpret_cast<DecSeqInfo*>(p);
+    p += align256((size_t)B * sizeof(DecSeqInfo));
+    w.sure = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)B * top_k * sizeof(int32_t));
+    w.cand = reinterpret_cast<DecCand*>(p);
+    return w;
+}
+}  // namespace
+
+size_t topk_decode_work_bytes(int B, int blocks, int top_k) {
+    return align256((size_t)blocks * kDecBins * sizeof(int)) + align256((size_t)B * sizeof(DecSeqInfo)) +
+           align256((size_t)B * top_k * sizeof(int32_t)) + align256((size_t)B * kDecCap * sizeof(DecCand));
 }
 
-size_t topk_decode_candidate_bytes() { return sizeof(CandEntry); }
+hipError_t launch_topk_decode(const float* S, const SeqMeta& m, int top_k, int32_t* idx, int32_t* count,
+                              void* work, hipStream_t s) {
+    if (m.B <= 0) return hipSuccess;
+    const int blocks = m.blk0[m.B];
+    const DecWork w = carve(work, m.B, blocks, top_k);
+    if (blocks > 0) {
+        hipLaunchKernelGGL(topk_dec_hist_kernel, dim3(blocks), dim3(kDecT), 0, s, S, m, w);
+        hipLaunchKernelGGL(topk_dec_split_kernel, dim3(blocks), dim3(kDecT), 0, s, S, m, top_k, w);
+    }
+    hipLaunchKernelGGL(topk_dec_final_kernel, dim3(m.B), dim3(kDecFinT), 0, s, S, m, top_k, idx, count, w);
+    return hipGetLastError();
+}
 
 }  // namespace dsa

@@ -439,18 +439,28 @@ def test_decode_step(name):
     assert err <= ATTN_TOL, err
 
 
-@pytest.mark.parametrize("case", ["all_ties", "one_segment"])
+@pytest.mark.parametrize("case", ["all_ties", "one_segment", "ties_in_bin"])
 def test_decode_segmented_topk(case):
-    """Decode selection over sequences longer than one top-k segment (16384
+    """Decode selection over sequences longer than one segment block (8192
     keys): ties spanning every segment (all scores equal: the first top_k
-    keys win), and a selection held entirely by one segment (the others'
-    candidates must all lose)."""
-    cfg = W.Decode("seg_" + case, W.GLM, (40000, 16385, 18000), 31, 8, 0.05, 0.05)
+    keys win), a selection held entirely by one segment (the others' keys
+    must all lose; its top_k equal scores fill one bin), and scores from
+    1999 values repeated across the sequence, so the bin holding the top_k-th
+    key has a few dozen keys with ties inside it, ranked by the final block
+    (lower key first)."""
+    ctx = (65536, 40000, 16385, 8193, 18000) if case == "ties_in_bin" else (40000, 16385, 18000)
+    cfg = W.Decode("seg_" + case, W.GLM, ctx, 31, 8, 0.05, 0.05)
     d = W.make_decode(cfg)
     top_k = cfg.shape.top_k
+    want0 = None
     if case == "all_ties":
         d["qI"][:] = 0
         want0 = np.arange(top_k)
+    elif case == "ties_in_bin":
+        d["qI"][:] = W.to_bf16_bits(np.float32(1.0))   # every q.k is the sum of k
+        rows = np.arange(d["kI"].shape[0])
+        vals = W.to_bf16_bits(((rows % 1999) / 128.0).astype(np.float32))
+        d["kI"][:] = vals[:, None]
     else:
         one, eight = W.to_bf16_bits(np.float32(1.0)), W.to_bf16_bits(np.float32(8.0))
         d["qI"][0] = one                  # sequence 0: every q.k is the sum of k
@@ -460,7 +470,8 @@ def test_decode_segmented_topk(case):
     say("decode-seg", case, cfg.ctx)
     out, idx, cnt = run_decode(cfg, d)
     ref_idx, ref_cnt, ref_out = oracle.decode_step(d, cfg.shape)
-    assert np.array_equal(ref_idx[0], want0)
+    if want0 is not None:
+        assert np.array_equal(ref_idx[0], want0)
     assert np.array_equal(cnt, ref_cnt)
     assert np.array_equal(idx, ref_idx)
     assert row_rel_err(out, ref_out) <= ATTN_TOL
