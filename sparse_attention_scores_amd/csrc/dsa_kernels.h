@@ -30,11 +30,18 @@ struct SeqMeta {
     int32_t blk0[kMaxBatch + 1];      // first block of sequence b (per kernel)
 };
 
-// Which sequence owns block `blk` (blk0 is ascending, B small).
+// Which sequence owns block `blk`: the last b with blk0[b] <= blk (blk0 is
+// ascending and blk0[0] = 0), by bisection, so a block waits on log2(B)
+// dependent scalar loads rather than up to B.
 __device__ inline int seq_of_block(const SeqMeta& m, int blk) {
-    int b = 0;
-    while (b + 1 < m.B && blk >= m.blk0[b + 1]) ++b;
-    return b;
+    int lo = 0, n = m.B;   // the answer lies in [lo, lo + n)
+    while (n > 1) {
+        const int h = n >> 1;
+        const bool up = blk >= m.blk0[lo + h];
+        lo = up ? lo + h : lo;
+        n = up ? n - h : h;
+    }
+    return lo;
 }
 
 __device__ inline f32x4 mfma16_bf16(u32x4 a, u32x4 b, f32x4 c) {

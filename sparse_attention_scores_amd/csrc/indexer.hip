@@ -21,8 +21,9 @@
 // the chip (each query block's fragments are then loaded once), else the
 // keys are split so that the grid covers every compute unit.  Tiles past the
 // block's last causal key are not computed.
-// Decode: one query per sequence, so no reuse across queries: each wave reads
-// its keys straight from memory into MFMA operands (the step is HBM bound).
+// Decode: one query per sequence, so no reuse across queries: each wave
+// copies 64 key rows to LDS with whole-row loads and scores them from there
+// against the block's one LDS copy of the query (the step is HBM bound).
 #include "dsa_kernels.h"
 
 #include <math.h>
@@ -47,15 +48,26 @@ constexpr int kIdxChunks = kIdxSub / 32; // 32-key MFMA chunks per stage
 constexpr int kIdxCUs = 256;              // compute units the grid should cover
 
 constexpr int kIdxdWaves = 4;
-constexpr int kIdxdKeysPerWave = 128;
+constexpr int kIdxdKeysPerWave = 64;
 constexpr int kIdxdKeysPerBlock = kIdxdWaves * kIdxdKeysPerWave;
 
 // Head held by accumulator register r of lane-half `half` in the 32x32 layout.
 __device__ inline int acc_head(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
-// Query q's MFMA A fragments (rows = heads) and the weights of the 16 heads
-// this lane's accumulator holds.  Loads are unconditional (q must be a valid
-// row); rows past HI read as zero.
+// The weights of the 16 heads this lane's accumulator holds for query q
+// (heads past HI weigh zero).
+template <int HI>
+__device__ __forceinline__ void load_weights(const float* w, int64_t q, int half, float (&wr)[16]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int h = acc_head(r, half);
+        const float v = w[q * HI + (h < HI ? h : HI - 1)];
+        wr[r] = h < HI ? v : 0.f;
+    }
+}
+
+// Query q's MFMA A fragments (rows = heads) and its head weights.  Loads are
+// unconditional (q must be a valid row); rows past HI read as zero.
 template <int HI, int DI>
 __device__ __forceinline__ void load_query(const uint16_t* qI, const float* w, int64_t q, int col,
                                            int half, u32x4 (&qf)[IdxShape<HI, DI>::KS],
@@ -68,12 +80,16 @@ __device__ __forceinline__ void load_query(const uint16_t* qI, const float* w, i
         const u32x4 v = ldg16(qI + (q * HI + hc) * DI + ks * 16 + half * 8);
         qf[ks] = col < HI ? v : zero;
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int h = acc_head(r, half);
-        const float v = w[q * HI + (h < HI ? h : HI - 1)];
-        wr[r] = h < HI ? v : 0.f;
-    }
+    load_weights<HI>(w, q, half, wr);
+}
+
+// A wave-uniform address held in SGPRs.  readfirstlane returns int, so each
+// half is widened through uint32_t (the low half must not be sign-extended).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t a = (uint64_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return (const void*)(((uint64_t)hi << 32) | lo);
 }
 
 // relu as one integer max: a float's bit pattern read as int32 is negative
@@ -217,44 +233,85 @@ void indexer_prefill_kernel(IndexerArgs a) {
     put(nsub * kIdxChunks - 1, combine_halves(weighted_relu(pa, wa), weighted_relu(pb, wb)));
 }
 
+// Decode: each wave scores 64 consecutive keys of one sequence.  A load of
+// MFMA operands straight from memory touches 32 rows at 32 bytes each, which
+// costs far more memory-pipeline work per byte than whole rows, so rows go to
+// LDS first with direct global-to-LDS loads (each instruction moves 64/CPR
+// whole rows) and the operands are read back from there: each wave copies
+// its 64 key rows to a slab of its own, and the block's waves copy the
+// sequence's query (HI rows) once for all of them.  Row r's 16-byte piece c
+// sits at position c ^ (r mod CPR) of the row, so the 16 lanes of one
+// ds_read_b128 cycle (16 rows, one piece each) hit 16 different bank groups.
+// Key rows past the context read the last key (their scores are not stored).
 template <int HI, int DI>
 __global__ __launch_bounds__(kIdxdWaves * 64)
 void indexer_decode_kernel(const uint16_t* __restrict__ qI, const uint16_t* __restrict__ kI,
                            const float* __restrict__ w, float* __restrict__ S, SeqMeta m) {
     using C = IdxShape<HI, DI>;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    static_assert(kIdxdKeysPerWave == 64, "one 64-key LDS slab per wave");
+    constexpr int SLOTS = 64 * C::CPR;          // 16-byte slots per key slab
+    constexpr int QS = HI * C::CPR;             // 16-byte slots of the query
+    constexpr int QRUNS = (QS + 63) / 64;       // 64-slot copies of the query
+    __shared__ u32x4 lds[kIdxdWaves][SLOTS];
+    __shared__ u32x4 ldq[QRUNS * 64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, col = lane & 31;
     const int b = seq_of_block(m, blockIdx.x);
     const int ctx = m.ctx[b];
     const int kb = (blockIdx.x - m.blk0[b]) * kIdxdKeysPerBlock + wave * kIdxdKeysPerWave;
-    if (kb >= ctx) return;
+    const bool live = kb < ctx;   // wave-uniform; idle waves still help with the query
 
-    u32x4 qf[C::KS];
-    float wr[16];
-    load_query<HI, DI>(qI, w, b, col, half, qf, wr);
-    const uint16_t* kbase = kI + m.key_off[b] * DI;
-    float* srow = S + m.s_off[b];
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-
+    if (live) {
+        const void* kbase = uniform_ptr(kI + (m.key_off[b] + kb) * DI);
+        const int last = min(63, ctx - 1 - kb);
+        const uint32_t slab = lds_addr(&lds[wave][0]);
 #pragma unroll
-    for (int c = 0; c < kIdxdKeysPerWave / 32; c += 2) {
-        const int j0 = kb + 32 * c + col, j1 = j0 + 32;
-        u32x4 b0[C::KS], b1[C::KS];
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            b0[ks] = j0 < ctx ? ldg16(kbase + (int64_t)j0 * DI + ks * 16 + half * 8) : zero;
-            b1[ks] = j1 < ctx ? ldg16(kbase + (int64_t)j1 * DI + ks * 16 + half * 8) : zero;
+        for (int i = 0; i < C::CPR; ++i) {
+            const int slot = i * 64 + lane, r = slot / C::CPR, p = slot % C::CPR;
+            const int piece = p ^ (r % C::CPR);
+            gather16_to_lds(kbase, (uint32_t)(min(r, last) * DI * 2 + piece * 16), slab + i * 1024);
         }
-        f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            acc0 = mfma32_bf16(qf[ks], b0[ks], acc0);
-            acc1 = mfma32_bf16(qf[ks], b1[ks], acc1);
-        }
-        const float tot = combine_halves(weighted_relu(acc0, wr), weighted_relu(acc1, wr));
-        const int key = kb + 32 * (c + half) + col;
-        if (key < ctx) srow[key] = tot;   // the query sits at ctx-1: every cached key is visible
     }
+    {
+        const void* qbase = uniform_ptr(qI + (int64_t)b * HI * DI);
+        for (int i = wave; i < QRUNS; i += kIdxdWaves) {
+            // lanes past the query's slots copy its last slot (never read)
+            const int slot = min(i * 64 + lane, QS - 1), r = slot / C::CPR, p = slot % C::CPR;
+            gather16_to_lds(qbase, (uint32_t)(r * DI * 2 + (p ^ (r % C::CPR)) * 16), lds_addr(&ldq[i * 64]));
+        }
+    }
+    // the sequence's head weights: uniform addresses (scalar loads), the
+    // lane's 16 picked by its half
+    float wr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int h0 = acc_head(r, 0), h1 = acc_head(r, 1);
+        const float w0 = h0 < HI ? w[b * HI + h0] : 0.f, w1 = h1 < HI ? w[b * HI + h1] : 0.f;
+        wr[r] = half ? w1 : w0;
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (!live) return;
+
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 qf[C::KS], b0[C::KS], b1[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+        const int pos = (ks * 2 + half) ^ (col % C::CPR);   // rows col and col + 32 share the swizzle
+        qf[ks] = col < HI ? ldq[col * C::CPR + pos] : zero;
+        b0[ks] = lds[wave][col * C::CPR + pos];
+        b1[ks] = lds[wave][(col + 32) * C::CPR + pos];
+    }
+    f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+        acc0 = mfma32_bf16(qf[ks], b0[ks], acc0);
+        acc1 = mfma32_bf16(qf[ks], b1[ks], acc1);
+    }
+    const float tot = combine_halves(weighted_relu(acc0, wr), weighted_relu(acc1, wr));
+    const int key = kb + 32 * half + col;
+    if (key < ctx) S[m.s_off[b] + key] = tot;   // the query sits at ctx-1: every cached key is visible
 }
 
 }  // namespace
