@@ -40,7 +40,8 @@
  *    DSA_ERR_HIP.  Non-finite inputs give undefined results.
  *  - Supported shapes: (n_heads, d_latent, d_rope, n_idx_heads, d_idx) =
  *    (64, 512, 64, 32, 128) (GLM-5.x) or (4, 64, 16, 4, 32) (tiny check
- *    shape); 1 <= top_k <= 2048; key counts up to 65536 for selection.
+ *    shape); 1 <= top_k <= 2048; key counts up to DSA_MAX_SELECT_KEYS (262144)
+ *    for selection.
  *    Others return DSA_ERR_UNSUPPORTED.  The device must be gfx950.
  *  - The value product runs with fp16 operands (probabilities and the first
  *    d_latent latent columns) and fp32 accumulation: latent values must lie
@@ -94,7 +95,8 @@ dsa_status dsa_indexer_scores(const dsa_shape* shape, const uint16_t* qI, const 
  *   otherwise      : the top_k keys j <= p by (S desc, j asc), ascending.
  * S [dev] [L, N] fp32 (only j <= p read); idx [dev] [L, top_k] int32, padded
  * with -1; count [dev] [L] int32 = min(p + 1, top_k).  Requires
- * q_start + L <= N <= 65536. */
+ * q_start + L <= N <= DSA_MAX_SELECT_KEYS.  Rows of up to 65536 keys take one
+ * pass; longer rows take about (p + 1) / 63488 passes over pieces of the row. */
 dsa_status dsa_topk_select(const dsa_shape* shape, const float* S, int32_t L, int32_t N,
                            int64_t q_start, int32_t* idx, int32_t* count, void* stream);
 
@@ -156,6 +158,9 @@ dsa_status dsa_prefill_chunk(const dsa_shape* shape, const uint16_t* q, const ui
 
 /* Largest batch dsa_decode_step accepts. */
 #define DSA_MAX_DECODE_BATCH 128
+/* Most keys one selection reads (N of a prefill chunk, ctx of a decode
+ * sequence). */
+#define DSA_MAX_SELECT_KEYS 262144
 
 /* Workspace bytes dsa_decode_step needs (0 on invalid arguments). */
 size_t dsa_decode_workspace_bytes(const dsa_shape* shape, int32_t B, const int64_t* ctx);
@@ -163,7 +168,7 @@ size_t dsa_decode_workspace_bytes(const dsa_shape* shape, int32_t B, const int64
 /* One batched decode step (exo #2539, Decode): B sequences, one query each
  * at position ctx[b] - 1 over that sequence's ctx[b] cached keys.  Caches
  * are packed in sequence order: sequence b's rows start at sum(ctx[:b]).
- * ctx [host] [B], 1 <= ctx[b] <= 65536, B <= DSA_MAX_DECODE_BATCH;
+ * ctx [host] [B], 1 <= ctx[b] <= DSA_MAX_SELECT_KEYS, B <= DSA_MAX_DECODE_BATCH;
  * q [dev] [B,H,Dl+Dr], qI [dev] [B,Hi,Di] bf16; w [dev] [B,Hi] fp32;
  * kv [dev] [sum ctx, Dl+Dr], kI [dev] [sum ctx, Di] bf16;
  * out [dev] [B,H,Dl] fp32; idx_out [dev] [B,top_k] int32 (key ids local to

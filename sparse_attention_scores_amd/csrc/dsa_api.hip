@@ -11,6 +11,9 @@
 
 #include <mutex>
 
+static_assert(dsa::kMaxSelectKeys == DSA_MAX_SELECT_KEYS && dsa::kMaxBatch == DSA_MAX_DECODE_BATCH,
+              "header limits match the kernels'");
+
 namespace {
 
 using dsa::SeqMeta;

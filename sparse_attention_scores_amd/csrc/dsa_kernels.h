@@ -17,7 +17,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxBatch = 128;      // decode sequences per step
 constexpr int kMaxTopK = 2048;
-constexpr int kMaxSelectKeys = 65536;
+constexpr int kMaxSelectKeys = 1 << 18;   // keys one selection may read (262144)
 
 // Per-sequence geometry of a decode step, passed by value in kernel
 // arguments so that no host-to-device copy is needed.

@@ -27,6 +27,9 @@
 // ascending key order with no sort.  Every decision is an exact float
 // comparison (-0 and +0 compare equal; NaN scores count as -inf): the
 // result is exact.
+// A row longer than one block holds in registers (1024 x 64 keys) is taken
+// in pieces in key order, carrying the top_k kept so far into the next
+// piece (topk_row_long).
 //
 // The kernel is bound by vector-ALU issue (a 64-lane instruction occupies a
 // 16-lane SIMD for four cycles), so each pass over the keys is kept to a few
@@ -181,9 +184,32 @@ struct DirectRow {   // element k is key k0 + k
     }
     __device__ __forceinline__ int32_t key(int k) const { return k0 + k; }
 };
-// Where the kept keys go.
+// Where the kept keys go (global memory, or LDS through a generic pointer).
 struct KeySink {
     int32_t* __restrict__ out;
+    __device__ __forceinline__ void write(int t, int32_t key) const { out[t] = key; }
+};
+// A piece of a long row: element k < C is the kept key carry[k] (carried
+// from earlier pieces, ascending), element C + j is key k0 + j.  Every
+// carried key is below k0, so element order is key order.
+struct CarryRow {
+    const float* __restrict__ s;   // the whole row
+    const int32_t* carry;          // LDS
+    int C, k0;
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int n) const { return row_rsrc(s, 4 * (k0 + n - C)); }
+    __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, int k) const {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 4 * key(k), 0, 0));
+    }
+    // C <= kMaxTopK: the first test lets the compiler drop the select for
+    // elements past kMaxTopK; the clamp keeps a discarded read in the array
+    __device__ __forceinline__ int32_t key(int k) const {
+        return (k < kMaxTopK && k < C) ? carry[min(k, kMaxTopK - 1)] : k0 + k - C;
+    }
+};
+// Kept keys through a generic pointer: the LDS carry of a long row (which
+// the next piece's row reads: no restrict) or the output.
+struct LdsSink {
+    int32_t* out;
     __device__ __forceinline__ void write(int t, int32_t key) const { out[t] = key; }
 };
 
@@ -411,7 +437,7 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
     // first (keep - ties before it) of its own.  Sums never carry between
     // the fields: fewer than top_k <= 2048 keys are kept from the first map.
     constexpr int kEqShift = 13;
-    static_assert(kMaxTopK < (1 << kEqShift) && (int64_t)kMaxSelectKeys << kEqShift <= 0x7FFFFFFF, "count packing");
+    static_assert(kMaxTopK < (1 << kEqShift) && (int64_t)Sm::NE << kEqShift <= 0x7FFFFFFF, "count packing");
     constexpr int WPT = (NB + NT - 1) / NT;
     const uint32_t* kwords = reinterpret_cast<const uint32_t*>(sm.u.c.keep);
     const uint32_t* twords = reinterpret_cast<const uint32_t*>(sm.u.c.tie);
@@ -470,6 +496,50 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     const float* srow = (n > a.top_k) ? a.S + (int64_t)(r - a.s_row0) * a.ldS : nullptr;
     topk_row<NT, EPT>(DirectRow{srow, 0}, n, a.top_k, KeySink{a.idx + (int64_t)r * a.top_k},
                       a.count ? a.count + r : nullptr, sm);
+}
+
+// A row of n keys, of any length up to kMaxSelectKeys, in pieces in key
+// order: the first NE = NT * EPT keys, then each time the top_k keys kept so
+// far followed by the next NE - top_k keys (a row of at most NE keys is one
+// piece).  The top_k of the kept keys and a piece are the top_k of every key
+// read so far (a key left out already has top_k better ones), and the
+// carried keys are lower than the piece's and come first in element order,
+// so a tie still goes to the lower key.  One topk_row instance serves every
+// piece: its sink is the carry array for all but the last.
+// carry: kMaxTopK ints of LDS.
+// (A separate function per piece: inlined into the loop, the compiler hoists
+// the pass's per-element addresses out of it and spills.)
+template <int NT, int EPT, typename Sm>
+__device__ __noinline__ void topk_piece(const float* s, int32_t* carry, int C, int k0, int n, int top_k,
+                                        int32_t* out, int32_t* count, Sm& sm) {
+    topk_row<NT, EPT>(CarryRow{s, carry, C, k0}, n, top_k, LdsSink{out}, count, sm);
+}
+template <int NT, int EPT, typename Sm>
+__device__ __forceinline__ void topk_row_long(const float* s, int n, int top_k, int32_t* out, int32_t* count,
+                                              Sm& sm, int32_t* carry) {
+    constexpr int NE = NT * EPT;
+    static_assert(NE > kMaxTopK, "a piece must hold more than the carried keys");
+    for (int k0 = 0, C = 0;;) {   // each pass reads at least NE - top_k new keys
+        const int piece = min(n - k0, NE - C);
+        const bool last = k0 + piece >= n;
+        topk_piece<NT, EPT>(s, carry, C, k0, C + piece, top_k, last ? out : carry, last ? count : nullptr, sm);
+        if (last) return;
+        k0 += piece;
+        C = top_k;
+        __syncthreads();   // the carried keys are written
+    }
+}
+
+// Rows longer than the largest single-block shape (1024 x 64 keys).
+__global__ __launch_bounds__(1024) void topk_long_kernel(TopkArgs a) {
+    __shared__ TopkSmem<1024, 64> sm;
+    __shared__ int32_t carry[kMaxTopK];
+    const int r = blockIdx.x;
+    const int64_t p = a.pos0 + r;
+    const int n = (int)(p + 1);
+    const float* srow = (n > a.top_k) ? a.S + (int64_t)(r - a.s_row0) * a.ldS : nullptr;
+    topk_row_long<1024, 64>(srow, n, a.top_k, a.idx + (int64_t)r * a.top_k, a.count ? a.count + r : nullptr, sm,
+                            carry);
 }
 
 // ---- Decode: one selection per sequence, spread over segment blocks ----
@@ -608,14 +678,16 @@ __global__ __launch_bounds__(kDecT) __attribute__((amdgpu_waves_per_eu(2, 8))) v
 #pragma unroll
     for (int r = 0; r < kDecBins / kDecT; ++r) {
         const int i = r * kDecT + tid;
-        int h[kMaxSelectKeys / kDecSeg];   // every segment's count, loads issued together
-#pragma unroll
-        for (int s = 0; s < kMaxSelectKeys / kDecSeg; ++s) h[s] = s < G ? h0[(int64_t)s * kDecBins + i] : 0;
         int tot = 0, bef = 0;
+        for (int s0 = 0; s0 < G; s0 += 8) {   // eight segments' counts, loads issued together
+            int h[8];
 #pragma unroll
-        for (int s = 0; s < kMaxSelectKeys / kDecSeg; ++s) {
-            tot += h[s];
-            bef += s < g ? h[s] : 0;
+            for (int s = 0; s < 8; ++s) h[s] = s0 + s < G ? h0[(int64_t)(s0 + s) * kDecBins + i] : 0;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                tot += h[s];
+                bef += s0 + s < g ? h[s] : 0;
+            }
         }
         htot[i] = tot;
         hbef[i] = bef;
@@ -710,7 +782,7 @@ __global__ __launch_bounds__(kDecT) __attribute__((amdgpu_waves_per_eu(2, 8))) v
 // Pass C: block b finishes sequence b.
 __global__ __launch_bounds__(kDecFinT) void topk_dec_final_kernel(const float* S, SeqMeta m, int top_k, int32_t* idx,
                                                                  int32_t* count, DecWork w) {
-    __shared__ TopkSmem<kDecFinT, kMaxSelectKeys / kDecFinT> sm;   // one pass over a whole sequence
+    __shared__ TopkSmem<kDecFinT, 64> sm;   // the fallback's passes over a whole sequence
     __shared__ int sure_l[kMaxTopK], kept_l[kMaxTopK];
     __shared__ float cv[kDecCap];
     __shared__ int ck[kDecCap];
@@ -726,8 +798,8 @@ __global__ __launch_bounds__(kDecFinT) void topk_dec_final_kernel(const float* S
     }
     const DecSeqInfo info = w.info[b];
     if (info.degenerate || info.fallback) {
-        topk_row<kDecFinT, kMaxSelectKeys / kDecFinT>(DirectRow{S + m.s_off[b], 0}, ctx, top_k, KeySink{out},
-                                                       count ? count + b : nullptr, sm);
+        topk_row_long<kDecFinT, 64>(S + m.s_off[b], ctx, top_k, out, count ? count + b : nullptr, sm,
+                                    kept_l);   // kept_l is free on this path: it carries the long row's keys
         return;
     }
     const int above = info.above, inbin = info.inbin, krem = top_k - above;   // 1 <= krem <= inbin
@@ -786,13 +858,18 @@ hipError_t dispatch_shape(int n_max, Launch&& launch) {
     if (n_max <= 16384) return launch(integral_constant<int, 512>{}, integral_constant<int, 32>{});
     if (n_max <= 32768) return launch(integral_constant<int, 1024>{}, integral_constant<int, 32>{});
     if (n_max <= 65536) return launch(integral_constant<int, 1024>{}, integral_constant<int, 64>{});
-    return hipErrorInvalidValue;
+    return hipErrorInvalidValue;   // longer rows: topk_long_kernel
 }
 
 }  // namespace
 
 hipError_t launch_topk_prefill(const TopkArgs& a, int n_max, hipStream_t s) {
     if (a.rows <= 0) return hipSuccess;
+    if (n_max > 65536) {
+        if (n_max > kMaxSelectKeys) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(topk_long_kernel, dim3(a.rows), dim3(1024), 0, s, a);
+        return hipGetLastError();
+    }
     return dispatch_shape(n_max, [&](auto nt, auto ept) {
         constexpr int NT = decltype(nt)::value, EPT = decltype(ept)::value;
         hipLaunchKernelGGL((topk_prefill_kernel<NT, EPT>), dim3(a.rows), dim3(NT), 0, s, a);

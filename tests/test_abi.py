@@ -60,7 +60,7 @@ def test_pointer_and_size_validation():
     assert L.dsa_indexer_scores(sh, fake(), fake(), fake(), 0, 8, 0, fake(), None) == INVALID        # L = 0
     assert L.dsa_indexer_scores(sh, fake(), fake(), fake(), 4, 8, 5, fake(), None) == INVALID        # q_start+L > N
     assert L.dsa_indexer_scores(sh, fake(), fake(), fake(), 4, 8, -1, fake(), None) == INVALID
-    assert L.dsa_topk_select(sh, fake(), 4, 70000, 69996, fake(), fake(), None) == UNSUPPORTED      # > 65536 keys
+    assert L.dsa_topk_select(sh, fake(), 4, 262145, 262141, fake(), fake(), None) == UNSUPPORTED  # > 262144 keys
     assert L.dsa_sparse_mla_attn(sh, fake(), fake(), None, fake(), 1, 1, fake(), None, None) == INVALID
     assert L.dsa_sparse_mla_attn(sh, fake(), fake(), fake(), fake(), 1, 1, fake(), fake(0x1004), None) == INVALID
 
@@ -88,7 +88,8 @@ def test_decode_workspace_and_validation():
     ws = dsa.dsa_decode_workspace_bytes(dsa.GLM, ctx)
     assert ws >= sum(ctx) * 4
     assert dsa.dsa_decode_workspace_bytes(dsa.GLM, [0, 5]) == 0
-    assert dsa.dsa_decode_workspace_bytes(dsa.GLM, [70000]) == 0
+    assert dsa.dsa_decode_workspace_bytes(dsa.GLM, [262145]) == 0
+    assert dsa.dsa_decode_workspace_bytes(dsa.GLM, [262144]) > 0
     arr = (ctypes.c_int64 * 2)(100, 0)
     rc = L.dsa_decode_step(sh, 2, ctypes.cast(arr, ctypes.c_void_p), *([fake()] * 6), None, None,
                            fake(), 1 << 30, None)

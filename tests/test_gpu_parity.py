@@ -146,7 +146,8 @@ def test_topk_small_bit_exact(name):
 
 @pytest.mark.parametrize("N,top_k,levels", [(300, 32, 3), (5000, 2048, 5), (16384, 2048, 40),
                                             (16384, 2048, 2), (65536, 2048, 7), (3000, 1, 4),
-                                            (2049, 2048, 2)])
+                                            (2049, 2048, 2), (65537, 2048, 2), (131072, 2048, 7),
+                                            (200001, 100, 3), (262144, 2048, 40)])
 def test_topk_ties_and_sizes(N, top_k, levels):
     """Scores drawn from a few values (many ties at the boundary), negative
     values and -0.0/+0.0 included; every row at a different length."""
@@ -164,6 +165,30 @@ def test_topk_ties_and_sizes(N, top_k, levels):
     cnt = torch.empty((L,), dtype=torch.int32, device="cuda")
     say("topk-ties", N, top_k, levels)
     lib().dsa_topk_select(shape, dev(S), L, N, q_start, idx, cnt)
+    assert np.array_equal(host(cnt), ref_cnt)
+    assert np.array_equal(host(idx), ref_idx)
+
+
+@pytest.mark.parametrize("N", [65600, 150000, 262144])
+def test_topk_long_rows_boundary_ties(N):
+    """Rows longer than one block's 65536 keys are selected in pieces that
+    carry the kept keys forward.  Normal scores with the value ranked near
+    top_k planted on keys spread over every piece, so the ties at the
+    boundary span pieces and the lower keys must win."""
+    import torch
+    rng = np.random.default_rng(N)
+    L, top_k = 4, 2048
+    S = rng.standard_normal((L, N)).astype(np.float32)
+    for r in range(L):
+        v = np.sort(S[r])[::-1][top_k - 10]
+        S[r, rng.choice(N - L, size=60, replace=False)] = v   # 60 keys at the boundary value
+    q_start = N - L
+    pos = q_start + np.arange(L)
+    ref_idx, ref_cnt = oracle.topk_select(S, pos, top_k)
+    idx = torch.empty((L, top_k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((L,), dtype=torch.int32, device="cuda")
+    say("topk-long", N)
+    lib().dsa_topk_select(W.GLM, dev(S), L, N, q_start, idx, cnt)
     assert np.array_equal(host(cnt), ref_cnt)
     assert np.array_equal(host(idx), ref_idx)
 
@@ -394,7 +419,7 @@ def test_prefill_chunk_deterministic():
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 
 
-@pytest.mark.parametrize("L,q_start", [(1, 0), (1, 5000), (3, 2046), (129, 1919)])
+@pytest.mark.parametrize("L,q_start", [(1, 0), (1, 5000), (3, 2046), (129, 1919), (3, 99997)])
 def test_prefill_chunk_edges(L, q_start):
     """One query at position 0 (a single key), one deep query, a chunk that
     straddles the top_k boundary by one, and a ragged 129-query chunk."""
@@ -439,7 +464,7 @@ def test_decode_step(name):
     assert err <= ATTN_TOL, err
 
 
-@pytest.mark.parametrize("case", ["all_ties", "one_segment", "ties_in_bin"])
+@pytest.mark.parametrize("case", ["all_ties", "one_segment", "ties_in_bin", "long", "all_ties_long"])
 def test_decode_segmented_topk(case):
     """Decode selection over sequences longer than one segment block (8192
     keys): ties spanning every segment (all scores equal: the first top_k
@@ -447,15 +472,20 @@ def test_decode_segmented_topk(case):
     must all lose; its top_k equal scores fill one bin), and scores from
     1999 values repeated across the sequence, so the bin holding the top_k-th
     key has a few dozen keys with ties inside it, ranked by the final block
-    (lower key first)."""
-    ctx = (65536, 40000, 16385, 8193, 18000) if case == "ties_in_bin" else (40000, 16385, 18000)
+    (lower key first).  Contexts past 65536 keys: normal scores over 32
+    segments (the histogram counts summed eight segments at a time), and all
+    ties, where the final block selects the whole sequence in pieces."""
+    ctx = {"ties_in_bin": (65536, 40000, 16385, 8193, 18000), "long": (262144, 70001, 131072),
+           "all_ties_long": (262144, 70000)}.get(case, (40000, 16385, 18000))
     cfg = W.Decode("seg_" + case, W.GLM, ctx, 31, 8, 0.05, 0.05)
     d = W.make_decode(cfg)
     top_k = cfg.shape.top_k
     want0 = None
-    if case == "all_ties":
+    if case in ("all_ties", "all_ties_long"):
         d["qI"][:] = 0
         want0 = np.arange(top_k)
+    elif case == "long":
+        pass
     elif case == "ties_in_bin":
         d["qI"][:] = W.to_bf16_bits(np.float32(1.0))   # every q.k is the sum of k
         rows = np.arange(d["kI"].shape[0])
