@@ -156,8 +156,10 @@ dsa_status dsa_prefill_chunk(const dsa_shape* shape, const uint16_t* q, const ui
                              int32_t N, int64_t q_start, float* out, int32_t* idx_out,
                              int32_t* count_out, void* ws, size_t ws_bytes, void* stream);
 
-/* Largest batch dsa_decode_step accepts. */
-#define DSA_MAX_DECODE_BATCH 128
+/* Largest batch dsa_decode_step accepts.  Batches of more than 128
+ * sequences run as consecutive groups of 128 on the caller's stream (each
+ * group a full set of launches); the workspace covers the largest group. */
+#define DSA_MAX_DECODE_BATCH 16384
 /* Most keys one selection reads (N of a prefill chunk, ctx of a decode
  * sequence). */
 #define DSA_MAX_SELECT_KEYS 262144

@@ -11,8 +11,7 @@
 
 #include <mutex>
 
-static_assert(dsa::kMaxSelectKeys == DSA_MAX_SELECT_KEYS && dsa::kMaxBatch == DSA_MAX_DECODE_BATCH,
-              "header limits match the kernels'");
+static_assert(dsa::kMaxSelectKeys == DSA_MAX_SELECT_KEYS, "header limit matches the kernels'");
 
 namespace {
 
@@ -168,11 +167,40 @@ dsa_status decode_layout(const dsa_shape* s, int32_t B, const int64_t* ctx, Deco
     return DSA_OK;
 }
 
-// Argument checks and geometry shared by both decode entry points (no HIP
-// call, nothing enqueued).
+// Batches of more than kMaxBatch sequences (the most one launch's kernel
+// arguments describe) run as consecutive groups of kMaxBatch sequences on
+// the caller's stream, each group over the whole workspace (stream order
+// keeps them apart).  f(b0, n, key_row0) runs for each group in order.
+template <typename F>
+dsa_status for_each_group(int32_t B, const int64_t* ctx, F&& f) {
+    int64_t k0 = 0;
+    for (int32_t b0 = 0; b0 < B; b0 += dsa::kMaxBatch) {
+        const int32_t n = B - b0 < dsa::kMaxBatch ? B - b0 : dsa::kMaxBatch;
+        const dsa_status st = f(b0, n, k0);
+        if (st) return st;
+        for (int32_t b = b0; b < b0 + n; ++b) k0 += ctx[b];
+    }
+    return DSA_OK;
+}
+
+// Workspace bytes of a batch: the largest group's layout (no HIP call).
+dsa_status decode_need(const dsa_shape* s, int32_t B, const int64_t* ctx, size_t& need) {
+    if (B <= 0 || !ctx) return DSA_ERR_INVALID_ARG;
+    if (B > DSA_MAX_DECODE_BATCH) return DSA_ERR_UNSUPPORTED;
+    static thread_local DecodeLayout d;
+    need = 0;
+    return for_each_group(B, ctx, [&](int32_t b0, int32_t n, int64_t) {
+        const dsa_status st = decode_layout(s, n, ctx + b0, d);
+        if (!st && d.total > need) need = d.total;
+        return st;
+    });
+}
+
+// Argument checks and workspace size shared by both decode entry points (no
+// HIP call, nothing enqueued).
 dsa_status decode_check(const dsa_shape* shape, int32_t B, const int64_t* ctx, const uint16_t* q,
                         const uint16_t* qI, const float* w, const uint16_t* kv, const uint16_t* kI,
-                        const float* out, const int32_t* idx_out, const int32_t* count_out, DecodeLayout& d) {
+                        const float* out, const int32_t* idx_out, const int32_t* count_out, size_t& need) {
     dsa_status st = check_shape(shape);
     if (st) return st;
     if (!q || !qI || !w || !kv || !kI || !out)
@@ -180,7 +208,7 @@ dsa_status decode_check(const dsa_shape* shape, int32_t B, const int64_t* ctx, c
     if (!aligned16(q) || !aligned16(qI) || !aligned16(w) || !aligned16(kv) || !aligned16(kI) ||
         !aligned16(out) || (idx_out && !aligned16(idx_out)) || (count_out && !aligned16(count_out)))
         return DSA_ERR_INVALID_ARG;
-    return decode_layout(shape, B, ctx, d);
+    return decode_need(shape, B, ctx, need);
 }
 
 // The decode kernels over a workspace at `base` laid out as d says.
@@ -199,6 +227,27 @@ dsa_status decode_run(const dsa_shape* shape, const uint16_t* q, const uint16_t*
                           reinterpret_cast<float*>(base + d.po_off), reinterpret_cast<float*>(base + d.pml_off),
                           out};
     return launched(dsa::launch_attention_split(sid, aa, d.attn_meta, d.attn_items, s));
+}
+
+
+// Every group of a checked batch over the workspace at `base`.  Each group's
+// operands start at its first sequence (row b0 of q, qI, w, out, idx and
+// count; cache row key_row0 of kv and kI).  Every group's tensor offsets stay
+// 16-byte aligned: a sequence's rows and a cache row are whole multiples of
+// 16 bytes at the supported shapes.
+dsa_status decode_groups(const dsa_shape* s, int32_t B, const int64_t* ctx, const uint16_t* q,
+                         const uint16_t* qI, const float* w, const uint16_t* kv, const uint16_t* kI, float* out,
+                         int32_t* idx_out, int32_t* count_out, char* base, hipStream_t stream) {
+    static thread_local DecodeLayout d;
+    const int64_t dqk = (int64_t)s->d_latent + s->d_rope, dq = (int64_t)s->n_idx_heads * s->d_idx;
+    return for_each_group(B, ctx, [&](int32_t b0, int32_t n, int64_t k0) {
+        dsa_status st = decode_layout(s, n, ctx + b0, d);
+        if (st) return st;
+        return decode_run(s, q + b0 * s->n_heads * dqk, qI + b0 * dq, w + (int64_t)b0 * s->n_idx_heads,
+                          kv + k0 * dqk, kI + k0 * s->d_idx, out + (int64_t)b0 * s->n_heads * s->d_latent,
+                          idx_out ? idx_out + (int64_t)b0 * s->top_k : nullptr, count_out ? count_out + b0 : nullptr,
+                          d, base, stream);
+    });
 }
 
 }  // namespace
@@ -518,37 +567,36 @@ dsa_status dsa_prefill_chunk(const dsa_shape* shape, const uint16_t* q, const ui
 
 size_t dsa_decode_workspace_bytes(const dsa_shape* shape, int32_t B, const int64_t* ctx) {
     if (check_shape(shape) != DSA_OK) return 0;
-    static thread_local DecodeLayout d;
-    if (decode_layout(shape, B, ctx, d) != DSA_OK) return 0;
-    return d.total;
+    size_t need = 0;
+    return decode_need(shape, B, ctx, need) == DSA_OK ? need : 0;
 }
 
 dsa_status dsa_decode_step(const dsa_shape* shape, int32_t B, const int64_t* ctx,
                            const uint16_t* q, const uint16_t* qI, const float* w,
                            const uint16_t* kv, const uint16_t* kI, float* out, int32_t* idx_out,
                            int32_t* count_out, void* ws, size_t ws_bytes, void* stream) {
-    static thread_local DecodeLayout d;
-    dsa_status st = decode_check(shape, B, ctx, q, qI, w, kv, kI, out, idx_out, count_out, d);
+    size_t need = 0;
+    dsa_status st = decode_check(shape, B, ctx, q, qI, w, kv, kI, out, idx_out, count_out, need);
     if (st) return st;
-    if (!ws || !aligned16(ws) || ws_bytes < d.total) return DSA_ERR_WORKSPACE;
+    if (!ws || !aligned16(ws) || ws_bytes < need) return DSA_ERR_WORKSPACE;
     if ((st = check_device())) return st;
-    return decode_run(shape, q, qI, w, kv, kI, out, idx_out, count_out, d, static_cast<char*>(ws),
-                      (hipStream_t)stream);
+    return decode_groups(shape, B, ctx, q, qI, w, kv, kI, out, idx_out, count_out, static_cast<char*>(ws),
+                         (hipStream_t)stream);
 }
 
 dsa_status dsa_decode_step_noalloc(const dsa_shape* shape, int32_t B, const int64_t* ctx,
                                    const uint16_t* q, const uint16_t* qI, const float* w,
                                    const uint16_t* kv, const uint16_t* kI, float* out, int32_t* idx_out,
                                    int32_t* count_out, void* stream) {
-    static thread_local DecodeLayout d;
-    dsa_status st = decode_check(shape, B, ctx, q, qI, w, kv, kI, out, idx_out, count_out, d);
+    size_t need = 0;
+    dsa_status st = decode_check(shape, B, ctx, q, qI, w, kv, kI, out, idx_out, count_out, need);
     if (st) return st;
-    if (d.total > DSA_DECODE_STATIC_SCRATCH_BYTES) return DSA_ERR_WORKSPACE;
+    if (need > DSA_DECODE_STATIC_SCRATCH_BYTES) return DSA_ERR_WORKSPACE;
     if ((st = check_device())) return st;
     void* scratch_dev = nullptr;
     if ((st = static_scratch(&scratch_dev))) return st;
-    return decode_run(shape, q, qI, w, kv, kI, out, idx_out, count_out, d, static_cast<char*>(scratch_dev),
-                      (hipStream_t)stream);
+    return decode_groups(shape, B, ctx, q, qI, w, kv, kI, out, idx_out, count_out, static_cast<char*>(scratch_dev),
+                         (hipStream_t)stream);
 }
 
 }  // extern "C"

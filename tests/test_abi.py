@@ -98,8 +98,12 @@ def test_decode_workspace_and_validation():
     rc = L.dsa_decode_step(sh, 1, ctypes.cast(arr, ctypes.c_void_p), *([fake()] * 6), None, None,
                            fake(), 16, None)
     assert rc == WORKSPACE
-    many = (ctypes.c_int64 * 200)(*([10] * 200))
-    rc = L.dsa_decode_step(sh, 200, ctypes.cast(many, ctypes.c_void_p), *([fake()] * 6), None, None,
+    # batches past 128 sequences run in groups: the workspace covers the largest group
+    assert dsa.dsa_decode_workspace_bytes(dsa.GLM, [10] * 200) == dsa.dsa_decode_workspace_bytes(dsa.GLM, [10] * 128)
+    ws_a, ws_b = dsa.dsa_decode_workspace_bytes(dsa.GLM, [10] * 128), dsa.dsa_decode_workspace_bytes(dsa.GLM, [65536] * 3)
+    assert dsa.dsa_decode_workspace_bytes(dsa.GLM, [10] * 128 + [65536] * 3) == max(ws_a, ws_b)
+    many = (ctypes.c_int64 * 16385)(*([10] * 16385))
+    rc = L.dsa_decode_step(sh, 16385, ctypes.cast(many, ctypes.c_void_p), *([fake()] * 6), None, None,
                            fake(), 1 << 30, None)
     assert rc == UNSUPPORTED
 

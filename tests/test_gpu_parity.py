@@ -464,6 +464,26 @@ def test_decode_step(name):
     assert err <= ATTN_TOL, err
 
 
+@pytest.mark.parametrize("name,B", [("tiny", 300), ("glm", 131)])
+def test_decode_step_large_batch(name, B):
+    """Batches of more than 128 sequences run as groups of 128 that share
+    the workspace; every group's operands start at its first sequence.
+    Ragged contexts of 1 to 3000 keys (some below top_k, some above)."""
+    rng = np.random.default_rng(B)
+    shape = W.TINY if name == "tiny" else W.GLM
+    ctx = tuple(int(c) for c in rng.integers(1, 3000 if name == "glm" else 700, size=B))
+    cfg = W.Decode("batch_%s_%d" % (name, B), shape, ctx, 50 + B, 8 if name == "glm" else 4, 0.05, 0.05)
+    d = W.make_decode(cfg)
+    say("decode-batch", name, B)
+    out, idx, cnt = run_decode(cfg, d)
+    ref_idx, ref_cnt, ref_out = oracle.decode_step(d, cfg.shape)
+    assert np.array_equal(cnt, ref_cnt)
+    assert np.array_equal(idx, ref_idx)
+    err = row_rel_err(out, ref_out)
+    say("decode-batch", name, B, "max row-relative error %.3e" % err)
+    assert err <= ATTN_TOL, err
+
+
 @pytest.mark.parametrize("case", ["all_ties", "one_segment", "ties_in_bin", "long", "all_ties_long"])
 def test_decode_segmented_topk(case):
     """Decode selection over sequences longer than one segment block (8192
