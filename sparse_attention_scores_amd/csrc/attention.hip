@@ -593,19 +593,141 @@ void attention_kernel(AttnArgs a) {
     }
 }
 
+// The decode selection of one attention block: slots [t_begin, t_end) of
+// sequence b's ascending selection go to dsel (LDS) and out to idx.
+struct DecSelSmem {
+    int32_t sure[kMaxTopK];   // keys above the boundary bin, ascending
+    int32_t ck[kDecCap];      // candidates (boundary-bin keys), ascending
+    float cv[kDecCap];        // and their scores
+    int32_t kept[kDecCap];    // the kept candidates, ascending
+    int32_t dsel[kMaxTopK];   // this block's slots
+    int wcnt[16];
+};
+
+// Returns where the block's selection slots are (t_begin shifted to 0 when
+// they were built in LDS).  A sequence of at most top_k keys selects every
+// key; a sequence the top-k fallback selected is read from idx; otherwise
+// the candidates are ranked (higher score, then lower key: a strict order),
+// the best top_k - above are kept, and each slot of the block takes its
+// element of the merge of the sure and kept lists.  Every thread calls it;
+// ends with a barrier where it wrote LDS.
+template <int NT>
+__device__ __forceinline__ const int32_t* decode_selection(const AttnSplitArgs& a, const SeqMeta& m, int b,
+                                                           bool first, int& t_begin, int& t_end,
+                                                           DecSelSmem& ds) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ctx = m.ctx[b], top_k = a.top_k;
+    int32_t* idx_b = a.idx + (int64_t)b * top_k;
+    const int n = t_end - t_begin;
+    if (ctx <= top_k) {
+        for (int t = tid; t < n; t += NT) {
+            ds.dsel[t] = t_begin + t;
+            idx_b[t_begin + t] = t_begin + t;
+        }
+        if (first) {
+            for (int t = ctx + tid; t < top_k; t += NT) idx_b[t] = -1;
+            if (tid == 0) a.count[b] = ctx;
+        }
+        __syncthreads();
+        t_end -= t_begin;
+        t_begin = 0;
+        return ds.dsel;
+    }
+    // one round of loads: the sequence's counts and both lists at their full
+    // capacity (entries past the counts are ignored)
+    constexpr int SP = kMaxTopK / NT, CP = (kDecCap + NT - 1) / NT;
+    int32_t sv[SP];
+    DecCand cv[CP];
+    const int32_t* sure_g = a.dec.sure + (int64_t)b * top_k;
+    const DecCand* cand_g = a.dec.cand + (int64_t)b * kDecCap;
+#pragma unroll
+    for (int k = 0; k < SP; ++k) sv[k] = k * NT + tid < top_k ? sure_g[k * NT + tid] : 0;
+#pragma unroll
+    for (int k = 0; k < CP; ++k) cv[k] = k * NT + tid < kDecCap ? cand_g[k * NT + tid] : DecCand{0, 0.f};
+    const DecSeqInfo info = a.dec.info[b];
+    if (info.degenerate || info.fallback) return idx_b;
+    const int above = info.above, inbin = info.inbin, krem = top_k - above;   // 1 <= krem <= inbin
+#pragma unroll
+    for (int k = 0; k < SP; ++k)
+        if (k * NT + tid < above) ds.sure[k * NT + tid] = sv[k];
+#pragma unroll
+    for (int k = 0; k < CP; ++k)
+        if (k * NT + tid < inbin) {
+            ds.ck[k * NT + tid] = cv[k].key;
+            ds.cv[k * NT + tid] = cv[k].score;
+        }
+    __syncthreads();
+    // kept candidates, in list (= key) order: each candidate is ranked by P
+    // consecutive lanes (P = 16 for up to NT / 16 candidates)
+    int lg = 0;
+    while (lg < 4 && (inbin << (lg + 1)) <= NT) ++lg;
+    const int P = 1 << lg;
+    int base = 0;
+    for (int c0 = 0; c0 < inbin; c0 += NT >> lg) {
+        const int ci = c0 + (tid >> lg), part = tid & (P - 1);
+        int r = 0;
+        if (ci < inbin) {
+            const float v = ds.cv[ci];
+            const int32_t kc = ds.ck[ci];
+            for (int i = part; i < inbin; i += P) {
+                const float x = ds.cv[i];
+                r += (x > v || (x == v && ds.ck[i] < kc)) ? 1 : 0;
+            }
+        }
+        r = group_sum(r, P);
+        const bool keep = ci < inbin && part == 0 && r < krem;
+        const uint64_t mk = __ballot(keep);
+        if (lane == 0) ds.wcnt[wave] = __popcll(mk);
+        __syncthreads();
+        int off = base, tot = 0;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) {
+            const int x = ds.wcnt[w];
+            off += w < wave ? x : 0;
+            tot += x;
+        }
+        if (keep) ds.kept[off + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0))] = ds.ck[ci];
+        base += tot;
+        __syncthreads();
+    }
+    // slot p of the merged list (merge path): i = sure keys among the first
+    // p, found by bisection over the at most krem + 1 possible splits (sure
+    // and kept keys are distinct), then the smaller of sure[i] and kept[p - i]
+    for (int t = tid; t < n; t += NT) {
+        const int p = t_begin + t;
+        int lo = max(0, p - krem), hi = min(p, above);
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (ds.sure[mid] < ds.kept[p - 1 - mid]) lo = mid + 1;
+            else hi = mid;
+        }
+        const int j = p - lo;
+        ds.dsel[t] = (j >= krem || (lo < above && ds.sure[lo] < ds.kept[j])) ? ds.sure[lo] : ds.kept[j];
+    }
+    __syncthreads();
+    for (int t = tid; t < n; t += NT) idx_b[t_begin + t] = ds.dsel[t];
+    if (first && tid == 0) a.count[b] = top_k;
+    __syncthreads();
+    t_end -= t_begin;
+    t_begin = 0;
+    return ds.dsel;
+}
+
 template <int NH, int DL, int DR>
 __global__ __launch_bounds__((AttnShape<NH, DL, DR>::NT)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_split_kernel(AttnSplitArgs a, SeqMeta m) {
     using C = AttnShape<NH, DL, DR>;
     using A = Attend<NH, DL, DR, false>;
     __shared__ __attribute__((aligned(16))) typename A::Smem sm;
+    __shared__ DecSelSmem ds;
     const int item = blockIdx.x;
     const int b = seq_of_block(m, item);
     const int ctx = m.ctx[b];
     const int cnt = min(ctx, a.top_k);
-    const int t_begin = (item - m.blk0[b]) * a.chunk;
-    const int t_end = min(t_begin + a.chunk, cnt);
-    const auto c = A::setup(a.kv + m.key_off[b] * C::DQK, a.idx + (int64_t)b * a.top_k, t_begin, t_end, ctx, sm);
+    int t_begin = (item - m.blk0[b]) * a.chunk;
+    int t_end = min(t_begin + a.chunk, cnt);
+    const int32_t* sel = decode_selection<C::NT>(a, m, b, item == m.blk0[b], t_begin, t_end, ds);
+    const auto c = A::setup(a.kv + m.key_off[b] * C::DQK, sel, t_begin, t_end, ctx, sm);
     if (c.w < C::NHB) {
         A::produce(c, a.q + (int64_t)b * NH * C::DQK, a.scale_log2);
         if (c.w == 0 && c.l < 16) {

@@ -223,7 +223,9 @@ dsa_status decode_run(const dsa_shape* shape, const uint16_t* q, const uint16_t*
     if ((st = launched(dsa::launch_indexer_decode(sid, qI, kI, w, S, d.idx_meta, d.idx_blocks, s)))) return st;
     if ((st = launched(dsa::launch_topk_decode(S, d.topk_meta, shape->top_k, idx, cnt, base + d.cand_off, s))))
         return st;
-    dsa::AttnSplitArgs aa{q, kv, idx, shape->top_k, d.chunk, scale_log2(shape),
+    const dsa::DecWork dw = dsa::topk_decode_work(base + d.cand_off, d.topk_meta.B, d.topk_meta.blk0[d.topk_meta.B],
+                                                  shape->top_k);
+    dsa::AttnSplitArgs aa{q, kv, idx, cnt, dw, shape->top_k, d.chunk, scale_log2(shape),
                           reinterpret_cast<float*>(base + d.po_off), reinterpret_cast<float*>(base + d.pml_off),
                           out};
     return launched(dsa::launch_attention_split(sid, aa, d.attn_meta, d.attn_items, s));

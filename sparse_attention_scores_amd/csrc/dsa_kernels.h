@@ -74,6 +74,29 @@ __device__ inline uint32_t pack_f16_rne(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
 
+// ---- wave primitives on DPP (every lane of the wave active) ----
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each 16-lane row
+
+// A permutation inside each 16-lane row: every lane has a source.
+template <int CTRL>
+__device__ inline int dpp_perm(int x) {
+    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
+}
+
+// Sum over aligned groups of P lanes (P a power of two up to 16, uniform):
+// after the two quad exchanges every lane holds its quad's sum, and each
+// mirror adds the group it is paired with.
+__device__ inline int group_sum(int x, int P) {
+    if (P >= 2) x += dpp_perm<kDppXor1>(x);
+    if (P >= 4) x += dpp_perm<kDppXor2>(x);
+    if (P >= 8) x += dpp_perm<kDppHalfMirror>(x);
+    if (P >= 16) x += dpp_perm<kDppMirror>(x);
+    return x;
+}
+
 #define DSA_LDS __attribute__((address_space(3)))
 
 __device__ inline uint32_t lds_addr(const void* p) {
@@ -135,8 +158,32 @@ hipError_t launch_topk_prefill(const TopkArgs& a, int n_max, hipStream_t s);
 // Decode top-k: m.blk0 numbers the segment blocks of each sequence
 // (topk_decode_segments(ctx, top_k) each: none for a sequence of at most
 // top_k keys); `work` holds topk_decode_work_bytes(B, blocks, top_k) bytes.
+// The two launches leave, per sequence of more than top_k keys, either its
+// selection in idx/count (the fallback: info.degenerate or info.fallback
+// set) or the lists the decode attention merges: `above` sure keys and
+// `inbin` candidates, of which the top_k - above best (score, then lower
+// key) are kept.
+constexpr int kDecCap = 1024;                 // boundary-bin keys a sequence may leave as candidates
+struct DecCand {        // a boundary-bin key of a sequence and its score (NaN as -inf)
+    int32_t key;
+    float score;
+};
+struct DecSeqInfo {     // per sequence
+    float scale, off;   // the shared map: bin(v) = clamp(trunc(v * scale + off), 0, kDecBins - 1)
+    int degenerate;     // the sample gave no usable range
+    int fallback;       // the boundary bin holds more than kDecCap keys
+    int above, inbin;   // keys in bins above the boundary bin; keys in it
+    int pad_[2];
+};
+struct DecWork {
+    int* hist;          // [segment block][kDecBins]
+    DecSeqInfo* info;   // [B]
+    int32_t* sure;      // [B][top_k]: keys above the boundary bin, ascending
+    DecCand* cand;      // [B][kDecCap]: keys in it, ascending
+};
 int topk_decode_segments(int ctx, int top_k);
 size_t topk_decode_work_bytes(int B, int blocks, int top_k);
+DecWork topk_decode_work(void* work, int B, int blocks, int top_k);
 hipError_t launch_topk_decode(const float* S, const SeqMeta& m, int top_k, int32_t* idx,
                               int32_t* count, void* work, hipStream_t s);
 
@@ -153,11 +200,17 @@ struct AttnArgs {
     float* lse;            // [rows, H] or null
 };
 // Split (decode) variant: block -> (sequence, chunk of `chunk` selected keys);
-// writes unnormalised partial outputs, then a combine kernel finishes.
+// writes unnormalised partial outputs, then a combine kernel finishes.  The
+// blocks also finish the selection: each takes its chunk of the ascending
+// selection (merging the top-k lists in `dec`, or every key of a sequence of
+// at most top_k keys, or the fallback's idx) and writes it to idx; the first
+// chunk of a sequence writes its count and padding.
 struct AttnSplitArgs {
     const uint16_t* q;
     const uint16_t* kv;
-    const int32_t* idx;
+    int32_t* idx;          // [B, top_k]
+    int32_t* count;        // [B]
+    DecWork dec;
     int32_t top_k;
     int32_t chunk;
     float scale_log2;

@@ -64,16 +64,7 @@ __device__ inline int count_below(uint64_t m) {
 
 // ---- wave primitives on DPP (every lane of the wave active) ----
 
-constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]: lane ^ 1
-constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]: lane ^ 2
-constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
-constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each 16-lane row
-
-// A permutation inside each 16-lane row: every lane has a source.
-template <int CTRL>
-__device__ inline int dpp_perm(int x) {
-    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
-}
+// (kDpp* controls, dpp_perm on ints and group_sum are in dsa_kernels.h)
 template <int CTRL>
 __device__ inline float dpp_perm(float x) {
     return __builtin_bit_cast(float, dpp_perm<CTRL>(__builtin_bit_cast(int, x)));
@@ -96,14 +87,6 @@ __device__ inline float wave_reduce(float x, Op op) {
     return op(op(readlane_f(x, 0), readlane_f(x, 16)), op(readlane_f(x, 32), readlane_f(x, 48)));
 }
 
-// Sum over aligned groups of P lanes (P a power of two up to 16, uniform).
-__device__ inline int group_sum(int x, int P) {
-    if (P >= 2) x += dpp_perm<kDppXor1>(x);
-    if (P >= 4) x += dpp_perm<kDppXor2>(x);
-    if (P >= 8) x += dpp_perm<kDppHalfMirror>(x);
-    if (P >= 16) x += dpp_perm<kDppMirror>(x);
-    return x;
-}
 
 // Inclusive sum over the lanes at or below this one: row shifts inside each
 // 16-lane row (zeros shifted in), then the totals of earlier rows broadcast.
@@ -549,45 +532,26 @@ __global__ __launch_bounds__(1024) void topk_long_kernel(TopkArgs a) {
 // value-linear map: kDecBins bins between the minimum and maximum of a fixed
 // sample of the sequence's scores.  Keys outside that range fall into the
 // end bins, so the map stays monotone and every key is counted, and the
-// segments' histograms add up to the sequence's.  Three launches:
+// segments' histograms add up to the sequence's.  Two launches:
 //   A. each segment block stores its histogram;
 //   B. each segment block sums its sequence's histograms and finds the bin
 //      holding the top_k-th key; its keys above that bin go to the
 //      sequence's list of sure keys and its keys in that bin (with scores)
 //      to the candidate list, at offsets the histograms give, so both lists
-//      are in key order;
-//   C. one block per sequence ranks the candidates (score, then lower key),
-//      keeps as many as the count still allows, and merges them into the
-//      sure keys by binary search.
-// A sequence whose sample gives no usable range, or whose boundary bin holds
-// more than kDecCap keys, is selected by its final block in one pass over
-// all of its keys instead: slower, same result.
+//      are in key order.
+// The decode attention blocks finish the selection: each ranks the
+// candidates (score, then lower key), keeps as many as the count still
+// allows, and merges them into the sure keys by binary search, keeping the
+// slots of its own chunk.  A sequence whose sample gives no usable range, or
+// whose boundary bin holds more than kDecCap keys, is selected in launch B
+// by its first segment block over all of its keys instead (slower, same
+// result), straight into idx and count.
 constexpr int kDecSeg = 8192;                 // keys per segment block
 constexpr int kDecT = 512;                    // threads of a segment block (one sample key each)
 constexpr int kDecEPT = kDecSeg / kDecT;
 constexpr int kDecBins = 1024;                // bins of the shared map
-constexpr int kDecCap = 1024;                 // boundary-bin keys the final block ranks
-constexpr int kDecFinT = 1024;                // threads of the final block
 static_assert(kDecBins == 16 * 64 && kDecBins == 2 * kDecT, "one wave scans the bins, sixteen per lane");
-static_assert(kDecSeg / 32 <= kDecT && kDecCap <= kDecFinT, "decode block shapes");
-
-struct DecCand {        // a boundary-bin key of a sequence and its score (NaN as -inf)
-    int32_t key;
-    float score;
-};
-struct DecSeqInfo {     // per sequence
-    float scale, off;   // the shared map: bin(v) = clamp(trunc(v * scale + off), 0, kDecBins - 1)
-    int degenerate;     // the sample gave no usable range
-    int fallback;       // the boundary bin holds more than kDecCap keys
-    int above, inbin;   // keys in bins above the boundary bin; keys in it
-    int pad_[2];
-};
-struct DecWork {
-    int* hist;          // [segment block][kDecBins]
-    DecSeqInfo* info;   // [B]
-    int32_t* sure;      // [B][top_k]: keys above the boundary bin, ascending
-    DecCand* cand;      // [B][kDecCap]: keys in it, ascending
-};
+static_assert(kDecSeg / 32 <= kDecT, "decode block shape");
 
 // The shared bin of a (NaN-free) score: clamped in float, so +-inf and
 // values outside the sample range land in the end bins.
@@ -606,16 +570,6 @@ __device__ inline void dec_sample_range(const float* srow, int ctx, float& lo, f
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kDecT / 64; ++w) { lo = fminf(lo, red[0][w]); hi = fmaxf(hi, red[1][w]); }
-}
-
-__device__ inline int lower_bound_lds(const int* a, int n, int x) {   // first index with a[i] >= x
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] < x) lo = mid + 1;
-        else hi = mid;
-    }
-    return lo;
 }
 
 // Pass A: block -> (sequence b, segment g).
@@ -652,18 +606,28 @@ __global__ __launch_bounds__(kDecT) __attribute__((amdgpu_waves_per_eu(2, 8))) v
 
 // Pass B: block -> (sequence b, segment g), for sequences of two or more.
 __global__ __launch_bounds__(kDecT) __attribute__((amdgpu_waves_per_eu(2, 8))) void topk_dec_split_kernel(
-        const float* S, SeqMeta m, int top_k, DecWork w) {
+        const float* S, SeqMeta m, int top_k, DecWork w, int32_t* idx, int32_t* count) {
     __shared__ int htot[kDecBins] __attribute__((aligned(16)));
     __shared__ int hbef[kDecBins] __attribute__((aligned(16)));
     __shared__ uint64_t bm_sure[kDecSeg / 64], bm_cand[kDecSeg / 64];
     __shared__ float cval[kDecSeg];
     __shared__ int wsum[kDecT / 64];
     __shared__ int s_bstar, s_above, s_inbin, s_bef_above, s_bef_in;
+    __shared__ TopkSmem<kDecT, 32> fsm;   // the fallback selection
+    __shared__ int32_t carry[kMaxTopK];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = seq_of_block(m, blockIdx.x), g = blockIdx.x - m.blk0[b];
     const int ctx = m.ctx[b], G = m.blk0[b + 1] - m.blk0[b];
     const DecSeqInfo info = w.info[b];
-    if (info.degenerate) return;
+    // the whole sequence by its first segment block, straight into idx/count
+    auto fallback = [&]() {
+        if (g == 0)
+            topk_row_long<kDecT, 32>(S + m.s_off[b], ctx, top_k, idx + (int64_t)b * top_k, count + b, fsm, carry);
+    };
+    if (info.degenerate) {
+        fallback();
+        return;
+    }
     const int k0 = g * kDecSeg, n = min(ctx - k0, kDecSeg);
     float f[kDecEPT];
     {
@@ -726,6 +690,7 @@ __global__ __launch_bounds__(kDecT) __attribute__((amdgpu_waves_per_eu(2, 8))) v
     const int bef_in = __builtin_amdgcn_readfirstlane(s_bef_in);
     if (inbin > kDecCap) {
         if (g == 0 && tid == 0) w.info[b].fallback = 1;
+        fallback();
         return;
     }
     if (g == 0 && tid == 0) { w.info[b].above = above; w.info[b].inbin = inbin; }
@@ -777,70 +742,6 @@ __global__ __launch_bounds__(kDecT) __attribute__((amdgpu_waves_per_eu(2, 8))) v
         if (pc < inbin) cand[pc] = DecCand{k0 + k, cval[k]};
         ++pc;
     }
-}
-
-// Pass C: block b finishes sequence b.
-__global__ __launch_bounds__(kDecFinT) void topk_dec_final_kernel(const float* S, SeqMeta m, int top_k, int32_t* idx,
-                                                                 int32_t* count, DecWork w) {
-    __shared__ TopkSmem<kDecFinT, 64> sm;   // the fallback's passes over a whole sequence
-    __shared__ int sure_l[kMaxTopK], kept_l[kMaxTopK];
-    __shared__ float cv[kDecCap];
-    __shared__ int ck[kDecCap];
-    __shared__ int wsum[kDecFinT / 64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = blockIdx.x;
-    const int ctx = m.ctx[b];
-    int32_t* out = idx + (int64_t)b * top_k;
-    if (ctx <= top_k) {   // every earlier key
-        for (int t = tid; t < top_k; t += kDecFinT) out[t] = t < ctx ? t : -1;
-        if (tid == 0 && count) count[b] = ctx;
-        return;
-    }
-    const DecSeqInfo info = w.info[b];
-    if (info.degenerate || info.fallback) {
-        topk_row_long<kDecFinT, 64>(S + m.s_off[b], ctx, top_k, out, count ? count + b : nullptr, sm,
-                                    kept_l);   // kept_l is free on this path: it carries the long row's keys
-        return;
-    }
-    const int above = info.above, inbin = info.inbin, krem = top_k - above;   // 1 <= krem <= inbin
-    const DecCand* cand = w.cand + (int64_t)b * kDecCap;
-    if (tid < inbin) { const DecCand c = cand[tid]; cv[tid] = c.score; ck[tid] = c.key; }
-    for (int i = tid; i < above; i += kDecFinT) sure_l[i] = w.sure[(int64_t)b * top_k + i];
-    __syncthreads();
-    // rank of candidate c: candidates with a higher score, or the same score
-    // and a lower key (a strict order: ranks 0 .. inbin-1), split over P lanes
-    int lg = 0;
-    while (lg < 4 && (inbin << (lg + 1)) <= kDecFinT) ++lg;
-    const int P = 1 << lg, c = tid >> lg, part = tid & (P - 1);
-    const float v = cv[min(c, inbin - 1)];
-    const int kc = ck[min(c, inbin - 1)];
-    int r = 0;
-    if (c < inbin)
-        for (int i = part; i < inbin; i += P) {
-            const float x = cv[i];
-            r += (x > v || (x == v && ck[i] < kc)) ? 1 : 0;
-        }
-    r = group_sum(r, P);
-    // the kept candidates in list (= key) order
-    const int flag = (c < inbin && part == 0 && r < krem) ? 1 : 0;
-    const int incl = wave_inclusive_sum(flag);
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int pos = incl - flag;
-#pragma unroll
-    for (int q = 0; q < kDecFinT / 64; ++q) pos += q < wave ? wsum[q] : 0;
-    if (flag) kept_l[pos] = kc;
-    __syncthreads();
-    // merge the two ascending lists
-    for (int i = tid; i < above; i += kDecFinT) {
-        const int d = sure_l[i];
-        out[i + lower_bound_lds(kept_l, krem, d)] = d;
-    }
-    for (int j = tid; j < krem; j += kDecFinT) {
-        const int x = kept_l[j];
-        out[j + lower_bound_lds(sure_l, above, x)] = x;
-    }
-    if (tid == 0 && count) count[b] = top_k;
 }
 
 // Block shape by row length: up to 32 keys per thread in 256-, then 512-,
@@ -895,6 +796,8 @@ DecWork carve(void* base, int B, int blocks, int top_k) {
 }
 }  // namespace
 
+DecWork topk_decode_work(void* work, int B, int blocks, int top_k) { return carve(work, B, blocks, top_k); }
+
 size_t topk_decode_work_bytes(int B, int blocks, int top_k) {
     return align256((size_t)blocks * kDecBins * sizeof(int)) + align256((size_t)B * sizeof(DecSeqInfo)) +
            align256((size_t)B * top_k * sizeof(int32_t)) + align256((size_t)B * kDecCap * sizeof(DecCand));
@@ -907,9 +810,8 @@ hipError_t launch_topk_decode(const float* S, const SeqMeta& m, int top_k, int32
     const DecWork w = carve(work, m.B, blocks, top_k);
     if (blocks > 0) {
         hipLaunchKernelGGL(topk_dec_hist_kernel, dim3(blocks), dim3(kDecT), 0, s, S, m, w);
-        hipLaunchKernelGGL(topk_dec_split_kernel, dim3(blocks), dim3(kDecT), 0, s, S, m, top_k, w);
+        hipLaunchKernelGGL(topk_dec_split_kernel, dim3(blocks), dim3(kDecT), 0, s, S, m, top_k, w, idx, count);
     }
-    hipLaunchKernelGGL(topk_dec_final_kernel, dim3(m.B), dim3(kDecFinT), 0, s, S, m, top_k, idx, count, w);
     return hipGetLastError();
 }
 
