@@ -484,7 +484,7 @@ def test_decode_step_large_batch(name, B):
     assert err <= ATTN_TOL, err
 
 
-@pytest.mark.parametrize("case", ["all_ties", "one_segment", "ties_in_bin", "long", "all_ties_long"])
+@pytest.mark.parametrize("case", ["all_ties", "one_segment", "ties_in_bin", "wide_bin", "long", "all_ties_long"])
 def test_decode_segmented_topk(case):
     """Decode selection over sequences longer than one segment block (8192
     keys): ties spanning every segment (all scores equal: the first top_k
@@ -492,10 +492,13 @@ def test_decode_segmented_topk(case):
     must all lose; its top_k equal scores fill one bin), and scores from
     1999 values repeated across the sequence, so the bin holding the top_k-th
     key has a few dozen keys with ties inside it, ranked by the final block
-    (lower key first).  Contexts past 65536 keys: normal scores over 32
+    (lower key first); 251 repeated values, whose boundary bins hold 35 to
+    260 equal keys (ranked by several waves past 64).  Contexts past 65536
+    keys: normal scores over 32
     segments (the histogram counts summed eight segments at a time), and all
     ties, where the final block selects the whole sequence in pieces."""
-    ctx = {"ties_in_bin": (65536, 40000, 16385, 8193, 18000), "long": (262144, 70001, 131072),
+    ctx = {"ties_in_bin": (65536, 40000, 16385, 8193, 18000), "wide_bin": (65536, 30000, 9000),
+           "long": (262144, 70001, 131072),
            "all_ties_long": (262144, 70000)}.get(case, (40000, 16385, 18000))
     cfg = W.Decode("seg_" + case, W.GLM, ctx, 31, 8, 0.05, 0.05)
     d = W.make_decode(cfg)
@@ -506,10 +509,11 @@ def test_decode_segmented_topk(case):
         want0 = np.arange(top_k)
     elif case == "long":
         pass
-    elif case == "ties_in_bin":
+    elif case in ("ties_in_bin", "wide_bin"):
         d["qI"][:] = W.to_bf16_bits(np.float32(1.0))   # every q.k is the sum of k
         rows = np.arange(d["kI"].shape[0])
-        vals = W.to_bf16_bits(((rows % 1999) / 128.0).astype(np.float32))
+        period = 1999 if case == "ties_in_bin" else 251   # 251 values: boundary bins of 35-260 equal keys
+        vals = W.to_bf16_bits(((rows % period) / 128.0).astype(np.float32))
         d["kI"][:] = vals[:, None]
     else:
         one, eight = W.to_bf16_bits(np.float32(1.0)), W.to_bf16_bits(np.float32(8.0))
