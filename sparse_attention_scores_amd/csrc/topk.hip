@@ -64,10 +64,12 @@ __device__ inline int count_below(uint64_t m) {
 
 // ---- wave primitives on DPP (every lane of the wave active) ----
 
-// (kDpp* controls, dpp_perm on ints and group_sum are in dsa_kernels.h)
+// (kDpp* controls, dpp_perm on ints and group_sum are in dsa_kernels.h.
+// The float form has a name of its own: a dpp_perm declared in this
+// namespace would hide the int one, and its call would become a recursion.)
 template <int CTRL>
-__device__ inline float dpp_perm(float x) {
-    return __builtin_bit_cast(float, dpp_perm<CTRL>(__builtin_bit_cast(int, x)));
+__device__ inline float dpp_perm_f(float x) {
+    return __builtin_bit_cast(float, dsa::dpp_perm<CTRL>(__builtin_bit_cast(int, x)));
 }
 __device__ inline float readlane_f(float x, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
@@ -80,10 +82,10 @@ struct MaxOp { __device__ float operator()(float a, float b) const { return fmax
 // through four in-row exchanges, then the four rows are read out.
 template <typename Op>
 __device__ inline float wave_reduce(float x, Op op) {
-    x = op(x, dpp_perm<kDppXor1>(x));
-    x = op(x, dpp_perm<kDppXor2>(x));
-    x = op(x, dpp_perm<kDppHalfMirror>(x));
-    x = op(x, dpp_perm<kDppMirror>(x));
+    x = op(x, dpp_perm_f<kDppXor1>(x));
+    x = op(x, dpp_perm_f<kDppXor2>(x));
+    x = op(x, dpp_perm_f<kDppHalfMirror>(x));
+    x = op(x, dpp_perm_f<kDppMirror>(x));
     return op(op(readlane_f(x, 0), readlane_f(x, 16)), op(readlane_f(x, 32), readlane_f(x, 48)));
 }
 
