@@ -51,12 +51,14 @@ def _configure(lib):
     lib.oracle_o_proj.argtypes = [P, P, i64, i32, i32, P, i64, P]
     lib.oracle_selection_mask.argtypes = [P, P, i64, i32, i64, i64, i64, P]
     lib.oracle_kv_b_proj.argtypes = [P, i32, P, i64, i32, i32, i32, i32, i32, P]
+    lib.oracle_q_absorb.argtypes = [P, P, i64, i32, i32, i32, i32, i32, P]
     lib.oracle_dense_masked_attn.argtypes = [P, P, P, P, i64, i64, i32, i32, i32, i32, i32, i32, i64,
                                              dbl, P, i64, P, i32]
     for f in (lib.oracle_indexer_scores, lib.oracle_topk_select, lib.oracle_sparse_mla_attn,
               lib.oracle_prefill_chunk, lib.oracle_decode_step, lib.oracle_cache_write,
               lib.oracle_router_topk, lib.oracle_value_up_proj, lib.oracle_o_proj,
-              lib.oracle_selection_mask, lib.oracle_dense_masked_attn, lib.oracle_kv_b_proj):
+              lib.oracle_selection_mask, lib.oracle_dense_masked_attn, lib.oracle_kv_b_proj,
+              lib.oracle_q_absorb):
         f.restype = ctypes.c_int
     return lib
 
@@ -264,6 +266,19 @@ def dense_masked_attn(q, kvb, kv, mask, d_nope: int, d_rope: int, d_v: int, rope
     _check(_load().oracle_dense_masked_attn(_p(q), _p(kvb), _p(kv), _p(mask), L, N, H, d_nope, d_rope, d_v,
                                             Dc, rope_col, mask.shape[1], scale, _p(rows), rows.size, _p(out),
                                             nthreads or default_threads()), "dense attention")
+    return out
+
+
+def q_absorb(q, w, d_latent: int, d_nope: int, d_v: int) -> np.ndarray:
+    """The absorbed query [T, H, d_latent + d_rope] as bf16 bits: each head's
+    no-rope query times the key block of the kv_b weight w [H * (d_nope +
+    d_v), d_latent], the rope part copied (pipeline trace, section 6)."""
+    q, w = _c(q, np.uint16), _c(w, np.uint16)
+    T, H, qc = q.shape
+    Dr = qc - d_nope
+    assert Dr >= 0 and w.shape == (H * (d_nope + d_v), d_latent)
+    out = np.empty((T, H, d_latent + Dr), dtype=np.uint16)
+    _check(_load().oracle_q_absorb(_p(q), _p(w), T, H, d_nope, Dr, d_latent, d_v, _p(out)), "q_absorb")
     return out
 
 

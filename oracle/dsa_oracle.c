@@ -721,3 +721,35 @@ int oracle_kv_b_proj(const uint16_t* kv, int32_t kv_cols, const uint16_t* w, int
     free(x);
     return 0;
 }
+
+/* Query absorption, "GLM-5.2-Vision: llama.cpp vs vLLM line-by-line pipeline
+ * trace", section 6: each head's no-rope query is carried into the latent
+ * space through the key block of the kv_b weight, so that it can score the
+ * shared latent rows directly.  With C = Dn + Dv:
+ *   out[t, h, d]      = round( sum_c q[t, h, c] * w[h*C + c, d] ),  c < Dn, d < Dl
+ *   out[t, h, Dl + r] = q[t, h, Dn + r]                            (the rope part, copied)
+ * q [T, H, Dn + Dr] bf16, w [H*C, Dl] bf16 (the kv_b weight), out
+ * [T, H, Dl + Dr] bf16 (nearest even).  For every latent row kv,
+ * <out[t, h, :Dl], kv> equals <q[t, h, :Dn], kvb key> before the rounding. */
+int oracle_q_absorb(const uint16_t* q, const uint16_t* w, int64_t T, int32_t H, int32_t Dn, int32_t Dr,
+                    int32_t Dl, int32_t Dv, uint16_t* out) {
+    if (!q || !w || !out || T < 0 || H <= 0 || Dn <= 0 || Dr < 0 || Dl <= 0 || Dv < 0) return -1;
+    const int32_t C = Dn + Dv;
+    double* qn = (double*)malloc((size_t)Dn * sizeof(double));
+    if (!qn) return -8;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < H; ++h) {
+            const uint16_t* qrow = q + (t * H + h) * (int64_t)(Dn + Dr);
+            uint16_t* orow = out + (t * H + h) * (int64_t)(Dl + Dr);
+            for (int32_t c = 0; c < Dn; ++c) qn[c] = bf16_to_double(qrow[c]);
+            for (int32_t d = 0; d < Dl; ++d) {
+                double acc = 0.0;
+                for (int32_t c = 0; c < Dn; ++c) acc += qn[c] * bf16_to_double(w[((int64_t)h * C + c) * Dl + d]);
+                orow[d] = double_to_bf16(acc);
+            }
+            for (int32_t r = 0; r < Dr; ++r) orow[Dl + r] = qrow[Dn + r];
+        }
+    }
+    free(qn);
+    return 0;
+}

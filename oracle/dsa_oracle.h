@@ -140,6 +140,12 @@ int oracle_dense_masked_attn(const uint16_t* q, const uint16_t* kvb, const uint1
 int oracle_kv_b_proj(const uint16_t* kv, int32_t kv_cols, const uint16_t* w, int64_t N, int32_t H,
                      int32_t Dl, int32_t Dn, int32_t Dv, int32_t values_f16, uint16_t* kvb);
 
+/* Query absorption: out[t, h, d] = round(sum_c q[t, h, c] * w[h*(Dn+Dv) + c, d])
+ * for c < Dn, d < Dl (bf16, nearest even), and out[t, h, Dl + r] = q[t, h,
+ * Dn + r] (the rope part). */
+int oracle_q_absorb(const uint16_t* q, const uint16_t* w, int64_t T, int32_t H, int32_t Dn, int32_t Dr,
+                    int32_t Dl, int32_t Dv, uint16_t* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -849,4 +849,51 @@ def pin_kv_b_matches_numpy():
     assert np.array_equal(_f16_bits_to_f64(got[..., Dn:]), exact[..., Dn:])
 
 
+def pin_q_absorb_one_hot():
+    """Key rows of the kv_b weight that copy no-rope query column c to latent
+    column perm[c]: the absorbed query holds q[..., c] at perm[c] exactly and
+    zero elsewhere, whatever the value rows hold; the rope part is copied."""
+    T, H, Dn, Dr, Dl, Dv = 3, 2, 8, 4, 32, 8
+    rng = np.random.default_rng(41)
+    q = _bf(rng.standard_normal((T, H, Dn + Dr)).astype(np.float32))
+    w = _bf(rng.standard_normal((H * (Dn + Dv), Dl)).astype(np.float32))   # value rows: noise
+    perm = np.stack([rng.permutation(Dl)[:Dn] for _ in range(H)])
+    for h in range(H):
+        w[h * (Dn + Dv):h * (Dn + Dv) + Dn] = 0
+        w[h * (Dn + Dv) + np.arange(Dn), perm[h]] = 0x3F80
+    out = oracle.q_absorb(q, w, Dl, Dn, Dv)
+    assert out.shape == (T, H, Dl + Dr)
+    for h in range(H):
+        want = np.zeros((T, Dl), np.uint16)
+        want[:, perm[h]] = q[:, h, :Dn]
+        assert np.array_equal(out[:, h, :Dl], want)
+    assert np.array_equal(out[..., Dl:], q[..., Dn:])
+
+
+def pin_q_absorb_score_invariant():
+    """The absorbed query scores a latent row as the no-rope query scores
+    that row's up-projected key: <absorb(q), kv> = <q, W_UK kv>, up to the
+    bf16 rounding of the absorbed query (half a unit per element).  Against
+    numpy's float64 products, with integer data exactly."""
+    T, H, Dn, Dr, Dl, Dv, N = 4, 3, 16, 8, 64, 24, 5
+    rng = np.random.default_rng(42)
+    q = _bf(rng.standard_normal((T, H, Dn + Dr)).astype(np.float32))
+    w = _bf((rng.standard_normal((H * (Dn + Dv), Dl)) / 8).astype(np.float32))
+    kv = _f(_bf(rng.standard_normal((N, Dl)).astype(np.float32)))
+    out = _f(oracle.q_absorb(q, w, Dl, Dn, Dv)[..., :Dl])
+    wk = _f(w).reshape(H, Dn + Dv, Dl)[:, :Dn]                 # [H, Dn, Dl]
+    exact = np.einsum("thc,hcd->thd", _f(q[..., :Dn]), wk)     # float64
+    assert np.all(np.abs(out - exact) <= _half_ulp_bf16(exact) * 1.0000001 + 1e-30)
+    kvb_key = np.einsum("hcd,nd->nhc", wk, kv)                 # the up-projected keys
+    lhs = np.einsum("thd,nd->thn", out, kv)
+    rhs = np.einsum("thc,nhc->thn", _f(q[..., :Dn]), kvb_key)
+    bound = np.einsum("thd,nd->thn", np.abs(out), np.abs(kv)) * 2.0 ** -8
+    assert np.all(np.abs(lhs - rhs) <= bound + 1e-12)
+    qi = rng.integers(-2, 3, size=(T, H, Dn + Dr))
+    wi = rng.integers(-1, 2, size=(H * (Dn + Dv), Dl))
+    got = _f(oracle.q_absorb(_bf(qi), _bf(wi), Dl, Dn, Dv))
+    ex = np.einsum("thc,hcd->thd", qi[..., :Dn], wi.reshape(H, Dn + Dv, Dl)[:, :Dn])
+    assert np.array_equal(got[..., :Dl], ex) and np.array_equal(got[..., Dl:], qi[..., Dn:])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -100,6 +100,14 @@ MUTATIONS = [
     ("fp16 rounding truncates", "double n = nearbyint(ldexp(m, 11));", "double n = floor(ldexp(m, 11));"),
     ("fp16 subnormals flushed", "const double n = nearbyint(ldexp(a, 24));   /* 1024 lands on the smallest normal */",
      "const double n = 0.0;"),
+    ("absorption reads the value rows", "acc += qn[c] * bf16_to_double(w[((int64_t)h * C + c) * Dl + d]);",
+     "acc += qn[c] * bf16_to_double(w[((int64_t)h * C + Dn + c % (Dv > 0 ? Dv : 1)) * Dl + d]);"),
+    ("absorption weight transposed", "acc += qn[c] * bf16_to_double(w[((int64_t)h * C + c) * Dl + d]);",
+     "acc += qn[c] * bf16_to_double(w[((int64_t)h * C + (d % C)) * Dl + (c % Dl)]);"),
+    ("absorption head stride dropped", "acc += qn[c] * bf16_to_double(w[((int64_t)h * C + c) * Dl + d]);",
+     "acc += qn[c] * bf16_to_double(w[((int64_t)c) * Dl + d]);"),
+    ("absorption rope not copied", "for (int32_t r = 0; r < Dr; ++r) orow[Dl + r] = qrow[Dn + r];",
+     "for (int32_t r = 0; r < Dr; ++r) orow[Dl + r] = 0;"),
 ]
 
 _RUNNER = r"""
