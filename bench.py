@@ -110,6 +110,9 @@ def dense_setup(np, torch, dsa, W, cfg):
     mask = torch.empty((cfg.L, dsa.mask_words(cfg.N)), dtype=torch.int32, device="cuda")
     vt = torch.empty((cfg.H, cfg.Dv, dsa.vt_keys(cfg.N)), dtype=torch.int16, device="cuda")
     wkvb = torch.from_numpy(W.make_kvb_weight(cfg).view(np.int16)).cuda()
+    wk_t = torch.empty((cfg.H, cfg.Dl, cfg.Dn), dtype=torch.int16, device="cuda")
+    dsa.dsa_absorb_weight(wkvb, cfg.H, cfg.Dn, cfg.Dv, cfg.Dl, wk_t)   # once per weight, not timed
+    q_abs = torch.empty((cfg.L, cfg.H, cfg.Dl + cfg.Dr), dtype=torch.int16, device="cuda")
     kvb_out = torch.empty_like(t["kvb"])
     vt_out = torch.empty_like(vt)
     out = torch.empty((cfg.L, cfg.H, cfg.Dv), dtype=torch.float32, device="cuda")
@@ -118,14 +121,19 @@ def dense_setup(np, torch, dsa, W, cfg):
     f = {"mask": lambda: dsa.dsa_selection_mask(idx, cnt, cfg.L, cfg.top_k, cfg.N, cfg.q_start, mask),
          "convert": lambda: dsa.dsa_values_to_f16(t["kvb"], cfg.N, cfg.H, cfg.Dn, cfg.Dv, vt),
          "kv_b": lambda: dsa.dsa_kv_b_proj(t["kv"], kc, wkvb, cfg.N, cfg.H, cfg.Dl, cfg.Dn, cfg.Dv, kvb_out, vt_out),
+         "q_absorb": lambda: dsa.dsa_q_absorb(t["q"], wk_t, cfg.L, cfg.H, cfg.Dn, cfg.Dr, cfg.Dl, q_abs),
          "attn_f16": lambda: dsa.dsa_dense_masked_attn_f16(t["q"], t["kvb"], vt, *tail),
          "attn_bf16": lambda: dsa.dsa_dense_masked_attn(t["q"], t["kvb"], *tail)}
     visible = sum(min(p + 1, cfg.N) for p in range(cfg.q_start, cfg.q_start + cfg.L))
     work = {"flop": 2.0 * cfg.H * (cfg.Dn + cfg.Dr + cfg.Dv) * visible,
             "mask_bytes": 4 * cfg.L * cfg.top_k + 4 * cfg.L + 4 * cfg.L * mask.shape[1],
             "convert_bytes": 2 * 2 * cfg.N * cfg.H * cfg.Dv,   # bf16 value columns in, fp16 vt out
-            "kv_b_flop": 2.0 * cfg.N * cfg.Dl * cfg.H * (cfg.Dn + cfg.Dv)}
-    return f, work, (t, idx, cnt, mask, vt, out, wkvb, kvb_out, vt_out)
+            "kv_b_flop": 2.0 * cfg.N * cfg.Dl * cfg.H * (cfg.Dn + cfg.Dv),
+            "q_absorb_flop": 2.0 * cfg.L * cfg.H * cfg.Dn * cfg.Dl,
+            # no-rope query read, weight read once, latent query written, rope part read and written
+            "q_absorb_bytes": 2 * cfg.L * cfg.H * cfg.Dn + 2 * cfg.H * cfg.Dl * cfg.Dn + 2 * cfg.L * cfg.H * cfg.Dl
+                              + 4 * cfg.L * cfg.H * cfg.Dr}
+    return f, work, (t, idx, cnt, mask, vt, out, wkvb, kvb_out, vt_out, wk_t, q_abs)
 
 
 def crossover(np, torch, dsa, W, reps: int) -> int:
@@ -134,8 +142,8 @@ def crossover(np, torch, dsa, W, reps: int) -> int:
     sparse: indexer, top-k, latent -> fp16, gathered attention, value
     up-projection; dense: the same indexer and top-k, the selection mask,
     the kv_b up-projection of every key (values written as fp16), dense
-    attention.  Not timed: the sparse side's query absorption, for which
-    this library has no entry point; its flops are given."""
+    attention.  The sparse side also carries the query absorption
+    (dsa_q_absorb; its weight is prepared once, untimed)."""
     base = W.PREFILL["glm_8k"]
     pc = W.PROJ["glm_16k_chunk"]
     wv = torch.from_numpy(W.make_proj(pc)["wv"].view(np.int16)).cuda()
@@ -167,12 +175,13 @@ def crossover(np, torch, dsa, W, reps: int) -> int:
         dc = W.Dense("crossover", L, N, N - L, 0)
         fd, work, keep = dense_setup(np, torch, dsa, W, dc)
         td = {}
-        for k in ("mask", "kv_b", "attn_f16"):
+        for k in ("mask", "kv_b", "attn_f16", "q_absorb"):
             fd[k]()
             torch.cuda.synchronize()
             td[k] = timed_events(fd[k], reps, torch) * 1e6
         del keep, fd, S, idx, cnt, kv
         torch.cuda.empty_cache()
+        ts["q_absorb"] = td.pop("q_absorb")
         sparse_us = sum(ts.values())
         dense_us = ts["indexer"] + ts["topk"] + td["mask"] + td["kv_b"] + td["attn_f16"]
         print(json.dumps({"crossover_keys": N, "queries": L, "sparse_us": round(sparse_us, 1),
@@ -180,7 +189,7 @@ def crossover(np, torch, dsa, W, reps: int) -> int:
                           "dense": {k: round(v, 1) for k, v in td.items()},
                           "dense_attn_tflops": round(work["flop"] / td["attn_f16"] / 1e6, 1),
                           "kv_b_tflops": round(work["kv_b_flop"] / td["kv_b"] / 1e6, 1),
-                          "untimed_gflop": {"q_absorption": round(2.0 * L * 64 * 192 * 512 / 1e9, 1)}}),
+                          "q_absorb_tflops": round(work["q_absorb_flop"] / ts["q_absorb"] / 1e6, 1)}),
               flush=True)
     return 0
 
@@ -610,7 +619,7 @@ def main() -> int:
         dcfg = W.DENSE[DENSE]
         fd, dwork, keep = dense_setup(np, torch, dsa, W, dcfg)
         td = {}
-        for k in ("mask", "convert", "kv_b", "attn_f16", "attn_bf16"):
+        for k in ("mask", "convert", "kv_b", "attn_f16", "attn_bf16", "q_absorb"):
             fd[k]()
             torch.cuda.synchronize()
             td[k] = timed_events(fd[k], max(n // 2, 3), torch)
@@ -628,6 +637,13 @@ def main() -> int:
                                "frac": tk / PEAK_MFMA_TFLOPS,
                                "workload": "%d latent rows [%d] -> %d heads x [%d key bf16 | %d value fp16]" % (
                                    dcfg.N, dcfg.Dl, dcfg.H, dcfg.Dn, dcfg.Dv)}
+        tq = dwork["q_absorb_flop"] / td["q_absorb"] / 1e12
+        gq = dwork["q_absorb_bytes"] / td["q_absorb"] / 1e9
+        # about 110 flop per byte, below the ridge: bound by HBM
+        stages["q_absorb"] = {"kernel": "gemm_nt_kernel<false,false,256> + copy_cols_kernel", "us": td["q_absorb"] * 1e6,
+                              "bound": "hbm", "gbps": gq, "frac": gq / PEAK_HBM_GBPS, "tflops": tq,
+                              "workload": "%d tokens x %d heads: [%d] no-rope bf16 -> [%d] latent bf16, rope [%d] copied" % (
+                                  dcfg.L, dcfg.H, dcfg.Dn, dcfg.Dl, dcfg.Dr)}
         for k, kern in (("attn_f16", "dense_attn_kernel<192,64,256,true>"),
                         ("attn_bf16", "dense_attn_kernel<192,64,256,false>")):
             tf = dwork["flop"] / td[k] / 1e12

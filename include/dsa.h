@@ -362,6 +362,33 @@ dsa_status dsa_kv_b_proj(const uint16_t* kv, int32_t kv_cols, const uint16_t* wk
                          int32_t d_latent, int32_t d_nope, int32_t d_v, uint16_t* kvb, uint16_t* vt,
                          void* stream);
 
+/* Query absorption ("GLM-5.2-Vision: llama.cpp vs vLLM line-by-line
+ * pipeline trace", section 6: q_nope_absorbed, the query the absorbed-MLA
+ * attention scores the shared latent rows with):
+ *   q_abs[t, h, d]      = sum_c q[t, h, c] * wkvb[h * (d_nope + d_v) + c, d],  c < d_nope, d < d_latent
+ *   q_abs[t, h, d_latent + r] = q[t, h, d_nope + r],  r < d_rope (the rope part, copied)
+ * so that <q_abs[t, h, :d_latent], kv row> equals the no-rope query's score
+ * against that row's up-projected key (dsa_kv_b_proj) before rounding.
+ * q [dev] [T, H, d_nope + d_rope] bf16; wk_t [dev] [H, d_latent, d_nope]
+ * bf16, the key block of the kv_b weight transposed per head (wk_t[h, d, c]
+ * = wkvb[h * (d_nope + d_v) + c, d]; dsa_absorb_weight writes it once per
+ * weight); q_abs [dev] [T, H, d_latent + d_rope] bf16, the query layout of
+ * dsa_sparse_mla_attn.  bf16 products, fp32 sums, each result rounded once
+ * (nearest even).  Requires pointers 16-byte aligned, T >= 0 (0: nothing is
+ * enqueued), H >= 1; d_nope a multiple of 64, d_latent a multiple of 256,
+ * d_rope a multiple of 8 and T * H * (d_nope + d_rope) * 2 < 2^32
+ * (DSA_ERR_UNSUPPORTED otherwise). */
+dsa_status dsa_q_absorb(const uint16_t* q, const uint16_t* wk_t, int32_t T, int32_t H, int32_t d_nope,
+                        int32_t d_rope, int32_t d_latent, uint16_t* q_abs, void* stream);
+
+/* The weight dsa_q_absorb reads: wk_t [dev] [H, d_latent, d_nope] bf16,
+ * wk_t[h, d, c] = wkvb[h * (d_nope + d_v) + c, d], from the kv_b weight
+ * wkvb [dev] [H * (d_nope + d_v), d_latent] bf16 (stored [out, in], as
+ * dsa_kv_b_proj reads it).  Not overlapping; H, d_nope, d_latent >= 1,
+ * d_v >= 0. */
+dsa_status dsa_absorb_weight(const uint16_t* wkvb, int32_t H, int32_t d_nope, int32_t d_v, int32_t d_latent,
+                             uint16_t* wk_t, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,8 @@ __all__ = [
     "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
     "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_decode_step_noalloc", "dsa_cache_write",
     "dsa_router_topk", "dsa_value_up_proj", "dsa_o_proj", "dsa_selection_mask", "dsa_dense_masked_attn",
-    "dsa_dense_masked_attn_f16", "dsa_values_to_f16", "dsa_kv_b_proj", "dsa_status_string",
+    "dsa_dense_masked_attn_f16", "dsa_values_to_f16", "dsa_kv_b_proj", "dsa_q_absorb", "dsa_absorb_weight",
+    "dsa_status_string",
     "EXPORTED_SYMBOLS", "DECODE_STATIC_SCRATCH_BYTES",
 ]
 
@@ -31,7 +32,7 @@ EXPORTED_SYMBOLS = (
     "dsa_latent_to_f16", "dsa_sparse_mla_attn_f16", "dsa_prefill_workspace_bytes", "dsa_prefill_chunk",
     "dsa_decode_workspace_bytes", "dsa_decode_step", "dsa_decode_step_noalloc", "dsa_cache_write",
     "dsa_router_topk", "dsa_value_up_proj", "dsa_o_proj", "dsa_selection_mask", "dsa_dense_masked_attn",
-    "dsa_dense_masked_attn_f16", "dsa_values_to_f16", "dsa_kv_b_proj",
+    "dsa_dense_masked_attn_f16", "dsa_values_to_f16", "dsa_kv_b_proj", "dsa_q_absorb", "dsa_absorb_weight",
 )
 
 DECODE_STATIC_SCRATCH_BYTES = 32 << 20   # DSA_DECODE_STATIC_SCRATCH_BYTES in include/dsa.h
@@ -95,6 +96,8 @@ def _load() -> ctypes.CDLL:
                                                      i32, ctypes.c_float, P, P]),
         "dsa_values_to_f16": (ctypes.c_int, [P, i32, i32, i32, i32, P, P]),
         "dsa_kv_b_proj": (ctypes.c_int, [P, i32, P, i32, i32, i32, i32, i32, P, P, P]),
+        "dsa_q_absorb": (ctypes.c_int, [P, P, i32, i32, i32, i32, i32, P, P]),
+        "dsa_absorb_weight": (ctypes.c_int, [P, i32, i32, i32, i32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -291,6 +294,16 @@ def dsa_dense_masked_attn_f16(q, kvb, vt, kv, kv_cols: int, rope_col: int, mask,
 def dsa_values_to_f16(kvb, N: int, H: int, d_nope: int, d_v: int, vt, stream=None) -> None:
     _check("dsa_values_to_f16", lib.dsa_values_to_f16(_bits(kvb, "kvb"), N, H, d_nope, d_v, _bits(vt, "vt"),
                                                       _stream(stream)))
+
+
+def dsa_absorb_weight(wkvb, H: int, d_nope: int, d_v: int, d_latent: int, wk_t, stream=None) -> None:
+    _check("dsa_absorb_weight", lib.dsa_absorb_weight(_bits(wkvb, "wkvb"), H, d_nope, d_v, d_latent,
+                                                      _bits(wk_t, "wk_t"), _stream(stream)))
+
+
+def dsa_q_absorb(q, wk_t, T: int, H: int, d_nope: int, d_rope: int, d_latent: int, q_abs, stream=None) -> None:
+    _check("dsa_q_absorb", lib.dsa_q_absorb(_bits(q, "q"), _bits(wk_t, "wk_t"), T, H, d_nope, d_rope, d_latent,
+                                            _bits(q_abs, "q_abs"), _stream(stream)))
 
 
 def dsa_kv_b_proj(kv, kv_cols: int, wkvb, N: int, H: int, d_latent: int, d_nope: int, d_v: int, kvb, vt=None,

@@ -508,6 +508,34 @@ dsa_status dsa_kv_b_proj(const uint16_t* kv, int32_t kv_cols, const uint16_t* wk
     return launched(dsa::launch_kv_b_proj(g, (hipStream_t)stream));
 }
 
+dsa_status dsa_absorb_weight(const uint16_t* wkvb, int32_t H, int32_t d_nope, int32_t d_v, int32_t d_latent,
+                             uint16_t* wk_t, void* stream) {
+    if (!wkvb || !wk_t || H <= 0 || d_nope <= 0 || d_v < 0 || d_latent <= 0) return DSA_ERR_INVALID_ARG;
+    if ((int64_t)H * (d_nope + d_v) * d_latent >= ((int64_t)1 << 40)) return DSA_ERR_UNSUPPORTED;
+    dsa_status st = check_device();
+    if (st) return st;
+    return launched(dsa::launch_absorb_weight(wkvb, H, d_nope, d_v, d_latent, wk_t, (hipStream_t)stream));
+}
+
+dsa_status dsa_q_absorb(const uint16_t* q, const uint16_t* wk_t, int32_t T, int32_t H, int32_t d_nope,
+                        int32_t d_rope, int32_t d_latent, uint16_t* q_abs, void* stream) {
+    if (!q || !wk_t || !q_abs || !aligned16(q) || !aligned16(wk_t) || !aligned16(q_abs) || T < 0 || H <= 0 ||
+        d_nope <= 0 || d_rope < 0 || d_latent <= 0)
+        return DSA_ERR_INVALID_ARG;
+    const int64_t qc = (int64_t)d_nope + d_rope, oc = (int64_t)d_latent + d_rope;
+    if (d_nope % 64 != 0 || d_latent % 256 != 0 || d_rope % 8 != 0 || (int64_t)T * H * qc * 2 >= (1ll << 32) ||
+        (int64_t)d_latent * d_nope * 2 >= (1ll << 32))
+        return DSA_ERR_UNSUPPORTED;
+    if (T == 0) return DSA_OK;
+    dsa_status st = check_device();
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    dsa::GemmArgs g{q, H * qc, qc, wk_t, d_nope, (int64_t)d_latent * d_nope, q_abs, H * oc, oc,
+                    T, d_latent, d_nope};
+    if ((st = launched(dsa::launch_q_absorb(g, H, s)))) return st;
+    return launched(dsa::launch_copy_cols(q, qc, d_nope, q_abs, oc, d_latent, (int64_t)T * H, d_rope, s));
+}
+
 dsa_status dsa_sparse_mla_attn_f16(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv16,
                                    const int32_t* idx, const int32_t* count, int32_t L, int32_t N,
                                    float* out, float* lse, void* stream) {

@@ -270,6 +270,14 @@ hipError_t launch_value_up_proj(const GemmArgs& g, int batch, hipStream_t s);
 hipError_t launch_o_proj(const GemmArgs& g, hipStream_t s);
 // kv_b up-projection: A bf16 (latent rows), C bf16 / fp16 columns, N % 256 == 0, K % 64 == 0
 hipError_t launch_kv_b_proj(const GemmArgs& g, hipStream_t s);
+// query absorption: A = q no-rope columns (bf16), B = transposed key block,
+// C bf16, batch = heads (grid z); N % 256 == 0, K % 64 == 0
+hipError_t launch_q_absorb(const GemmArgs& g, int batch, hipStream_t s);
+// dst[r, dst_col0 + c] = src[r, src_col0 + c], c < ncols (bf16, 16-byte chunks)
+hipError_t launch_copy_cols(const uint16_t* src, int64_t src_ld, int src_col0, uint16_t* dst, int64_t dst_ld,
+                            int dst_col0, int64_t rows, int ncols, hipStream_t s);
+// wkT[h, d, c] = w[h*(Dn+Dv) + c, d]
+hipError_t launch_absorb_weight(const uint16_t* w, int H, int Dn, int Dv, int Dl, uint16_t* wkT, hipStream_t s);
 
 // Selection mask: row i of mask [L, W] has bit j set iff key j is among
 // idx[i, :count[i]], 0 <= j < N and j <= q_start + i.

@@ -293,7 +293,58 @@ void gemm_nt_kernel(GemmArgs g) {
     }
 }
 
+// dst[r, dst_col0 + c] = src[r, src_col0 + c] for c < ncols, rows r < rows,
+// in 16-byte chunks (ncols, the column offsets and the row strides are
+// multiples of 8 bf16).  One thread per chunk.
+__global__ __launch_bounds__(256) void copy_cols_kernel(const uint16_t* __restrict__ src, int64_t src_ld, int src_col0,
+                                                        uint16_t* __restrict__ dst, int64_t dst_ld, int dst_col0,
+                                                        int64_t rows, int ncols) {
+    const int cpr = ncols / 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= rows * cpr) return;
+    const int64_t r = gid / cpr;
+    const int c = (int)(gid - r * cpr) * 8;
+    *reinterpret_cast<u32x4*>(dst + r * dst_ld + dst_col0 + c) = ldg16(src + r * src_ld + src_col0 + c);
+}
+
+// wkT[h, d, c] = w[h*(Dn+Dv) + c, d] for c < Dn, d < Dl: the key block of
+// each head transposed, through a 64 x 64 LDS tile (rows padded by one
+// element so the column reads do not conflict).  Block (d tile, c tile, h).
+__global__ __launch_bounds__(256) void absorb_weight_kernel(const uint16_t* __restrict__ w, int Dn, int Dv, int Dl,
+                                                            uint16_t* __restrict__ wkT) {
+    __shared__ uint16_t tile[64][65];
+    const int d0 = blockIdx.x * 64, c0 = blockIdx.y * 64, h = blockIdx.z;
+    const int64_t C = Dn + Dv;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int r = ty; r < 64; r += 4) {   // tile row r: key row c0 + r, columns d0..d0+63
+        const int c = c0 + r, d = d0 + tx;
+        tile[r][tx] = (c < Dn && d < Dl) ? w[((int64_t)h * C + c) * Dl + d] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int r = ty; r < 64; r += 4) {   // output row d0 + r, columns c0..c0+63
+        const int d = d0 + r, c = c0 + tx;
+        if (d < Dl && c < Dn) wkT[((int64_t)h * Dl + d) * Dn + c] = tile[tx][r];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_copy_cols(const uint16_t* src, int64_t src_ld, int src_col0, uint16_t* dst, int64_t dst_ld,
+                            int dst_col0, int64_t rows, int ncols, hipStream_t s) {
+    if (rows <= 0 || ncols <= 0) return hipSuccess;
+    if (ncols % 8 || src_ld % 8 || dst_ld % 8 || src_col0 % 8 || dst_col0 % 8) return hipErrorInvalidValue;
+    const int64_t n = rows * (ncols / 8);
+    hipLaunchKernelGGL(copy_cols_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, src_ld, src_col0,
+                       dst, dst_ld, dst_col0, rows, ncols);
+    return hipGetLastError();
+}
+
+hipError_t launch_absorb_weight(const uint16_t* w, int H, int Dn, int Dv, int Dl, uint16_t* wkT, hipStream_t s) {
+    if (H <= 0 || Dn <= 0 || Dl <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((Dl + 63) / 64), (unsigned)((Dn + 63) / 64), (unsigned)H);
+    hipLaunchKernelGGL(absorb_weight_kernel, grid, dim3(256), 0, s, w, Dn, Dv, Dl, wkT);
+    return hipGetLastError();
+}
 
 hipError_t launch_value_up_proj(const GemmArgs& g, int batch, hipStream_t s) {
     if (g.M <= 0 || batch <= 0) return hipSuccess;
@@ -311,6 +362,20 @@ hipError_t launch_o_proj(const GemmArgs& g, hipStream_t s) {
     const int tiles = (g.M + kBM - 1) / kBM * (g.N / 192);
     const dim3 grid((unsigned)(8 * ((tiles + 7) / 8)), 1, 1);
     hipLaunchKernelGGL((gemm_nt_kernel<false, true, 192>), grid, dim3(kGemmThreads), 0, s, g);
+    return hipGetLastError();
+}
+
+// Query absorption: per head z, C = q_nope (rows of A) times the head's
+// transposed key block (B, Dl rows of Dn), written into the first Dl columns
+// of the head's absorbed query; the rope columns are copied by
+// copy_cols_kernel.
+hipError_t launch_q_absorb(const GemmArgs& g, int batch, hipStream_t s) {
+    if (g.M <= 0 || batch <= 0) return hipSuccess;
+    if (g.N % 256 != 0 || g.K % kBK != 0) return hipErrorInvalidValue;
+    if ((int64_t)g.M * g.lda * 2 >= (1ll << 32) || (int64_t)g.N * g.ldb * 2 >= (1ll << 32)) return hipErrorInvalidValue;
+    const int tiles = (g.M + kBM - 1) / kBM * (g.N / 256);
+    const dim3 grid((unsigned)(8 * ((tiles + 7) / 8)), 1, (unsigned)batch);
+    hipLaunchKernelGGL((gemm_nt_kernel<false, false, 256>), grid, dim3(kGemmThreads), 0, s, g);
     return hipGetLastError();
 }
 

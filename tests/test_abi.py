@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     assert sorted(dsa.EXPORTED_SYMBOLS) == names
     raw = ctypes.CDLL(dsa._build.LIB)
     for n in names:
@@ -211,3 +211,15 @@ def test_dense_validation():
     assert k(fake(), 572, fake(), 8, 64, 512, 192, 256, fake(), fake(), None) == INVALID
     assert k(fake(), 576, fake(), 8, 64, 480, 192, 256, fake(), fake(), None) == UNSUPPORTED
     assert k(fake(), 576, fake(), 8, 3, 512, 192, 256, fake(), fake(), None) == UNSUPPORTED
+    a = L.dsa_q_absorb
+    assert a(fake(), fake(), 0, 64, 192, 64, 512, fake(), None) == OK            # T = 0: nothing enqueued
+    assert a(None, fake(), 8, 64, 192, 64, 512, fake(), None) == INVALID
+    assert a(fake(), fake(), 8, 64, 192, 64, 512, fake(0x1008), None) == INVALID
+    assert a(fake(), fake(), 8, 0, 192, 64, 512, fake(), None) == INVALID
+    assert a(fake(), fake(), 8, 64, 160, 64, 512, fake(), None) == UNSUPPORTED   # d_nope % 64
+    assert a(fake(), fake(), 8, 64, 192, 64, 384, fake(), None) == UNSUPPORTED   # d_latent % 256
+    assert a(fake(), fake(), 8, 64, 192, 60, 512, fake(), None) == UNSUPPORTED   # d_rope % 8
+    assert a(fake(), fake(), 1 << 20, 64, 192, 64, 512, fake(), None) == UNSUPPORTED   # 32-bit row offsets
+    aw = L.dsa_absorb_weight
+    assert aw(None, 64, 192, 256, 512, fake(), None) == INVALID
+    assert aw(fake(), 0, 192, 256, 512, fake(), None) == INVALID

@@ -161,3 +161,56 @@ def test_kv_b_proj_matches_oracle(name, f16):
         unit = np.ldexp(1.0, (np.floor(np.log2(np.maximum(np.abs(rv), 2.0 ** -14))) - mant).astype(int))
         excess = np.abs(gv - rv) - (unit + 2.0 ** -20 * terms[sl])
         assert excess.max() <= 0, float(excess.max())
+
+
+# ---------------------------------------------------------------- query absorption
+@pytest.mark.parametrize("name", ["glm_8k_chunk", "glm_small"])
+def test_q_absorb_matches_oracle(name):
+    """The absorbed query (no-rope query times each head's key block of the
+    kv_b weight, rope part copied) against the oracle, which sums exactly from
+    the untransposed weight and rounds once.  dsa_absorb_weight's transposed
+    key block must equal numpy's transpose bit for bit; the rope columns are
+    copies.  Latent columns: same bf16 operands, fp32 against exact sums, so
+    one bf16 unit + 2^-20 * sum |terms| per output, under 1% of outputs
+    differing.  glm_8k_chunk: 4096 tokens (the benchmark's launch) on a
+    seeded sample of 24 rows; glm_small: 160 tokens (a partial row tile)."""
+    import torch
+    import sparse_attention_scores_amd as dsa
+    cfg = W.DENSE[name]
+    d = W.make_dense(cfg)
+    w = W.make_kvb_weight(cfg)
+    H, Dn, Dr, Dl, Dv = cfg.H, cfg.Dn, cfg.Dr, cfg.Dl, cfg.Dv
+    say("q_absorb", name, "T=%d" % cfg.L)
+    wk_t = torch.empty((H, Dl, Dn), dtype=torch.int16, device="cuda")
+    dsa.dsa_absorb_weight(dev(w), H, Dn, Dv, Dl, wk_t)
+    want_t = np.ascontiguousarray(np.transpose(w.reshape(H, Dn + Dv, Dl)[:, :Dn], (0, 2, 1)))
+    assert np.array_equal(host(wk_t).view(np.uint16), want_t)
+    q_abs = torch.full((cfg.L, H, Dl + Dr), -1, dtype=torch.int16, device="cuda")
+    dsa.dsa_q_absorb(dev(d["q"]), wk_t, cfg.L, H, Dn, Dr, Dl, q_abs)
+    got = host(q_abs).view(np.uint16)
+    rows = np.arange(cfg.L) if cfg.L <= 256 else W.sample_rows(cfg.L, 24, seed=13, must=[0, cfg.L - 1])
+    want = oracle.q_absorb(d["q"][rows], w, Dl, Dn, Dv)
+    g = got[rows]
+    assert np.array_equal(g[..., Dl:], want[..., Dl:])
+    gl, rl = g[..., :Dl], want[..., :Dl]
+    assert (gl != rl).mean() < 0.01, float((gl != rl).mean())
+    qa = np.abs(W.bf16_bits_to_f32(d["q"][rows, :, :Dn]).astype(np.float64))
+    wa = np.abs(W.bf16_bits_to_f32(want_t).astype(np.float64))
+    terms = np.einsum("thc,hdc->thd", qa, wa)
+    gv = W.bf16_bits_to_f32(gl).astype(np.float64)
+    rv = W.bf16_bits_to_f32(rl).astype(np.float64)
+    unit = np.ldexp(1.0, (np.floor(np.log2(np.maximum(np.abs(rv), 1e-38))) - 7).astype(int))
+    excess = np.abs(gv - rv) - (unit + 2.0 ** -20 * terms)
+    assert excess.max() <= 0, float(excess.max())
+
+
+def test_q_absorb_rejects_unsupported_shapes():
+    import torch
+    import sparse_attention_scores_amd as dsa
+    q = torch.zeros((4, 2, 128), dtype=torch.int16, device="cuda")
+    wk_t = torch.zeros((2, 256, 64), dtype=torch.int16, device="cuda")
+    out = torch.zeros((4, 2, 320), dtype=torch.int16, device="cuda")
+    with pytest.raises(dsa.DsaError):
+        dsa.dsa_q_absorb(q, wk_t, 4, 2, 48, 80, 256, out)    # d_nope not a multiple of 64
+    with pytest.raises(dsa.DsaError):
+        dsa.dsa_q_absorb(q, wk_t, 4, 2, 64, 64, 192, out)    # d_latent not a multiple of 256
