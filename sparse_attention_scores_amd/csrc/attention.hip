@@ -610,7 +610,7 @@ struct DecSelSmem {
 // the candidates are ranked (higher score, then lower key: a strict order),
 // the best top_k - above are kept, and each slot of the block takes its
 // element of the merge of the sure and kept lists.  Every thread calls it;
-// ends with a barrier where it wrote LDS.
+// the slots it built in LDS are complete (behind a barrier) when it returns.
 template <int NT>
 __device__ __forceinline__ const int32_t* decode_selection(const AttnSplitArgs& a, const SeqMeta& m, int b,
                                                            bool first, int& t_begin, int& t_end,
@@ -707,7 +707,6 @@ __device__ __forceinline__ const int32_t* decode_selection(const AttnSplitArgs& 
     __syncthreads();
     for (int t = tid; t < n; t += NT) idx_b[t_begin + t] = ds.dsel[t];
     if (first && tid == 0) a.count[b] = top_k;
-    __syncthreads();
     t_end -= t_begin;
     t_begin = 0;
     return ds.dsel;
