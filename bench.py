@@ -712,6 +712,13 @@ def main() -> int:
                             "steps": nd, "hbm_floor_us": moved / (PEAK_HBM_GBPS * 1e9) * 1e6,
                             "hbm_floor_bytes": moved,
                             "kernels_us": kernel_breakdown(dstep, nd, torch)}
+        # the indexer streams every cached indexer key once (Di bf16) and writes one score per key
+        ikern = [k for k in (result["decode"]["kernels_us"] or {}) if k.startswith("indexer_decode")]
+        if ikern:
+            ib = (2 * sh.d_idx + 4) * sum_ctx
+            ius = result["decode"]["kernels_us"][ikern[0]]
+            result["decode"]["indexer"] = {"kernel": ikern[0], "bytes": ib, "us": ius, "gbps": ib / ius / 1e3,
+                                           "frac": ib / ius / 1e3 / PEAK_HBM_GBPS}
 
     # ---------------- CPU oracle on a bounded sample ----------------
     if args.cpu_rows > 0:
