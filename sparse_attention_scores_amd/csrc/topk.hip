@@ -16,17 +16,21 @@
 //      bins below are dropped.  Bins that follow the value (not the float's
 //      exponent bits) spread a bell-shaped score row over many LDS counters,
 //      so the atomics rarely collide.
-//   2. Once at most NT keys are alive they are gathered (each wave into its
-//      own LDS slice) and ranked directly, which yields T exactly.
+//   2. Once at most NT keys are alive, one pass over the keys writes the
+//      LDS bitmap of the keys above the boundary bin (bit k is element k:
+//      each wave stores its 64-lane ballot masks) and gathers the bin's keys
+//      (each wave into its own LDS slice).  The gathered keys are ranked
+//      directly: each sets its bit when it is among the krem best, and the
+//      keys equal to T, when only some of them fit, go to a tie bitmap.
 //   3. Degenerate rows (non-finite values, a value range too wide or too
 //      narrow for fp32 binning, too many levels) finish with an exact
-//      32-step bisection over the live keys.  Every loop is bounded.
-// Finally the kept keys go to an LDS bitmap (bit k is element k: each wave
-// stores its 64-lane ballot masks), and each thread walks a few consecutive
-// words of it after one block-wide scan of their counts, so the output is in
-// ascending key order with no sort.  Every decision is an exact float
-// comparison (-0 and +0 compare equal; NaN scores count as -inf): the
-// result is exact.
+//      32-step bisection over the live keys, then one pass writes the
+//      bitmaps of the keys above T and equal to T.  Every loop is bounded.
+// Finally each thread walks a few consecutive words of the bitmaps after one
+// block-wide scan of their counts (keeping the lowest of the ties that
+// fit), so the output is in ascending key order with no sort.  Every
+// decision is an exact float comparison (-0 and +0 compare equal; NaN scores
+// count as -inf): the result is exact.
 // A row longer than one block holds in registers (1024 x 64 keys) is taken
 // in pieces in key order, carrying the top_k kept so far into the next
 // piece (topk_row_long).
@@ -108,26 +112,37 @@ struct TopkSmem {
     static constexpr int NE = NT * EPT;                           // elements of a row
     static constexpr int NB = NE / 32;                            // bitmap words, bit k is element k
     static constexpr int kSlice = NT < 64 * EPT ? NT : 64 * EPT;  // a wave's most boundary-bin keys
+    static_assert(NE <= 65536, "element indices are stored in 16 bits");
     float red[2][2][NW] __attribute__((aligned(16)));   // min / max partials, double buffered
     int cnt[2][NW];                                     // bisection counts, double buffered
     int wsum[NW];                                       // block-scan partials
     int hist[kBins] __attribute__((aligned(16)));
     float cand[NT + 64] __attribute__((aligned(16)));   // the boundary bin's values, NaN past them
+    int candk[NT] __attribute__((aligned(16)));         // and their elements
+    uint32_t keep[NB];                                  // kept elements
+    uint32_t tie[NB];                                   // elements equal to T, where only some stay
     union {
         struct {                                        // gathering the boundary bin
             float slice[NW][kSlice];                    // each wave's boundary-bin values
+            uint16_t slicek[NW][kSlice];                // and elements
             int wcnt[NW];                               // and their number
         } g;
         struct {                                        // writing the selection
-            uint64_t keep[NB / 2];                      // kept elements (above T, or at T when all ties stay)
-            uint64_t tie[NB / 2];                       // elements equal to T, where only some stay
             int outk[kMaxTopK];                         // kept keys in output order
         } c;
     } u;
     int bstar, above, inbin;                            // the level's boundary bin
-    float T;
-    int keep, neq;
+    int ties;                                           // the ties at T kept, when only some are
 };
+
+// Compare predicates of the lane-mask builtins (LLVM's numbering).
+constexpr int kCmpOgt = 2, kCmpOge = 3, kCmpOle = 5, kCmpOrd = 7;   // float
+constexpr int kCmpEq = 32, kCmpUgt = 34;                            // integer
+
+// Lane l (wave-uniform) of x takes the wave-uniform value u (v_writelane).
+__device__ __forceinline__ void write_lane(uint32_t& x, uint32_t u, int l) {
+    asm("v_writelane_b32 %0, %1, %2" : "+v"(x) : "s"(u), "i"(l));
+}
 
 // Block-wide minimum and maximum (every thread gets both).
 template <typename Sm>
@@ -226,7 +241,6 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
     const int lim = n - tid;   // element e is in the row when e * NT < lim
 #pragma unroll
     for (int e = 0; e < EPT; ++e) f[e] = e * NT < lim ? fmaxf(f[e], -INFINITY) : kNone;
-    if (tid == 0) { sm.T = INFINITY; sm.keep = 0; sm.neq = -1; }
     if (tid < kBins) sm.hist[tid] = 0;
 
     // the live set is every key with lo <= value <= hi; krem of them are kept
@@ -236,7 +250,7 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
     int par = 0;
     block_minmax(lo, hi, par, sm);
     int krem = top_k;
-    bool found = false;
+    bool found = false, direct = false;
     float T = 0.f;
 
     for (int lev = 0; lev < kMaxLevels; ++lev) {
@@ -281,21 +295,60 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
         const int inbin = __builtin_amdgcn_readfirstlane(sm.inbin);
         krem -= __builtin_amdgcn_readfirstlane(sm.above);
         if (inbin <= NT) {
-            // rank the keys of the bin directly: each wave gathers its own
-            // into its slice of LDS (a running count, no atomics), the
-            // slices are packed into one list, then each key counts the
-            // gathered values above and at its own
-            int wc = 0;
+            // Direct ranking.  One pass over the keys writes the bitmap of
+            // the keys above the bin (a 64-lane mask per element group, kept
+            // in lanes 2e and 2e+1 of mw until one store per lane) and
+            // gathers the bin's keys with their elements: each wave into its
+            // own slice of LDS with a running count, no atomics.  The slices
+            // are packed into one list and each key of the bin is ranked
+            // against the others: a key kept together with all its ties sets
+            // its bit; when only some of the keys equal to T fit, those set
+            // tie bits instead (the walk keeps the lowest).
+            constexpr int NMW = (EPT + 31) / 32;
+            uint32_t mw[NMW];
 #pragma unroll
-            for (int e = 0; e < EPT; ++e) {
-                const bool a = f[e] >= lo && f[e] <= hi && value_bin(f[e], scale, off) == bstar;
-                const uint64_t m = __ballot(a);
-                if (m) {
-                    if (a) sm.u.g.slice[wave][wc + count_below(m)] = f[e];
-                    wc += (int)__popcll(m);
+            for (int i = 0; i < NMW; ++i) mw[i] = 0u;
+            // Lane masks straight from the compares (combined in scalar
+            // registers).  At the first level every value lies in [lo, hi]:
+            // a key is live unless it is padding, and none lies above hi.
+            int wc = 0;
+            int me = tid;
+            asm volatile("" : "+v"(me));   // elements computed where stored, not kept per element
+            auto gather = [&](auto first) {
+                constexpr bool kFirst = decltype(first)::value;
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) {
+                    const uint32_t b = (uint32_t)value_bin(f[e], scale, off);
+                    const uint64_t live = kFirst ? __builtin_amdgcn_fcmpf(f[e], f[e], kCmpOrd)
+                                                 : __builtin_amdgcn_fcmpf(f[e], lo, kCmpOge) &
+                                                       __builtin_amdgcn_fcmpf(f[e], hi, kCmpOle);
+                    uint64_t up = live & __builtin_amdgcn_uicmp(b, (uint32_t)bstar, kCmpUgt);
+                    if (!kFirst) up |= __builtin_amdgcn_fcmpf(f[e], hi, kCmpOgt);
+                    write_lane(mw[e / 32], (uint32_t)up, 2 * (e % 32));
+                    write_lane(mw[e / 32], (uint32_t)(up >> 32), 2 * (e % 32) + 1);
+                    const uint64_t m = live & __builtin_amdgcn_uicmp(b, (uint32_t)bstar, kCmpEq);
+                    if (m) {
+                        if ((m >> lane) & 1) {
+                            const int p = wc + count_below(m);
+                            sm.u.g.slice[wave][p] = f[e];
+                            sm.u.g.slicek[wave][p] = (uint16_t)(e * NT + me);
+                        }
+                        wc += (int)__popcll(m);
+                    }
+                }
+            };
+            if (lev == 0) gather(std::true_type{});
+            else gather(std::false_type{});
+#pragma unroll
+            for (int i = 0; i < NMW; ++i) {
+                const int e = 32 * i + (lane >> 1);
+                if (e < EPT) {
+                    sm.keep[(e * NT + 64 * wave) / 32 + (lane & 1)] = mw[i];
+                    sm.tie[(e * NT + 64 * wave) / 32 + (lane & 1)] = 0u;
                 }
             }
             if (lane == 0) sm.u.g.wcnt[wave] = wc;
+            if (tid == 0) sm.ties = 0;
             __syncthreads();
             if (tid < inbin) {
                 // key tid sits in the first slice whose running total exceeds it
@@ -308,6 +361,7 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
                     base = past ? cum : base;
                 }
                 sm.cand[tid] = sm.u.g.slice[w][tid - base];
+                sm.candk[tid] = sm.u.g.slicek[w][tid - base];
             }
             if (tid < 64) sm.cand[inbin + tid] = kNone;   // whole groups of four past the bin
             __syncthreads();
@@ -333,11 +387,21 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
             }
             gt = group_sum(gt, P);
             ge = group_sum(ge, P);
-            if (c < inbin && part == 0 && gt < krem && krem <= ge) { sm.T = v; sm.keep = krem - gt; sm.neq = ge - gt; }
+            // kept when every key at or above its score fits; when only some
+            // of its ties fit (gt < krem < ge: its score is T), it is marked
+            // as a tie, and the lowest krem - gt of them stay
+            if (c < inbin && part == 0 && gt < krem) {
+                const int k = sm.candk[c];
+                if (ge <= krem) {
+                    atomicOr(&sm.keep[k >> 5], 1u << (k & 31));
+                } else {
+                    atomicOr(&sm.tie[k >> 5], 1u << (k & 31));
+                    sm.ties = krem - gt;   // the same for every tie
+                }
+            }
             __syncthreads();
-            T = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sm.T)));
-            krem = __builtin_amdgcn_readfirstlane(sm.keep);
-            found = true;
+            krem = __builtin_amdgcn_readfirstlane(sm.ties);
+            direct = true;
             break;
         }
         // narrow the live range to the bin's values
@@ -354,69 +418,61 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
         block_minmax(lo, hi, par, sm);
     }
 
-    if (!found) {
-        // exact bisection on order-preserving keys: the largest key t with
-        // #(live keys >= t) >= krem, then the live keys above t are kept
-        uint32_t t = 0;
-#pragma unroll 1
-        for (int bit = 31; bit >= -1; --bit) {
-            const uint32_t c = bit >= 0 ? (t | (1u << bit)) : t + 1u;
-            int w = 0;
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) {
-                asm volatile("" : "+v"(f[e]));   // recompute per step: no hoisted masks or keys
-                w += (f[e] >= lo && f[e] <= hi && order_key(f[e]) >= c) ? 1 : 0;
-            }
-#pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) w += __shfl_xor(w, d);
-            if (lane == 0) sm.cnt[par][wave] = w;
-            __syncthreads();
-            int tot = 0;
-#pragma unroll
-            for (int v = 0; v < NW; ++v) tot += sm.cnt[par][v];
-            tot = __builtin_amdgcn_readfirstlane(tot);
-            par ^= 1;
-            if (bit >= 0) {
-                if (tot >= krem) t = c;
-            } else {
-                krem -= (t == 0xFFFFFFFFu) ? 0 : tot;
-            }
-        }
-        T = key_value(t);
-    }
-    // Keep every key > T and the first krem keys == T in key order (NaN
-    // padding is neither).  When the kept ties are all the ties (always, for
-    // distinct scores) that is every key >= T.
-    const int keep = krem;
-    const bool all_ties = keep == __builtin_amdgcn_readfirstlane(sm.neq);
+    // Without direct ranking (a bin of equal values, the bisection), keep
+    // every key > T and the first krem keys == T in key order (NaN padding
+    // is neither): lane 0 of each wave stores its group's 64-lane masks,
+    // bits e*NT + 64w .. +63 of the kept and tie bitmaps.
     constexpr int NB = Sm::NB;
-
-    // Pass 1: lane 0 of each wave stores its group's 64-lane masks, which
-    // are bits e*NT + 64w .. +63 of the element bitmaps; kept lanes stage
-    // their scores where the output carries them.
-    if (all_ties) {
+    int keep = krem;   // the ties kept
+    if (!direct) {
+        if (!found) {
+            // exact bisection on order-preserving keys: the largest key t with
+            // #(live keys >= t) >= krem, then the live keys above t are kept
+            uint32_t t = 0;
+#pragma unroll 1
+            for (int bit = 31; bit >= -1; --bit) {
+                const uint32_t c = bit >= 0 ? (t | (1u << bit)) : t + 1u;
+                int w = 0;
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) {
+                    asm volatile("" : "+v"(f[e]));   // recompute per step: no hoisted masks or keys
+                    w += (f[e] >= lo && f[e] <= hi && order_key(f[e]) >= c) ? 1 : 0;
+                }
+#pragma unroll
+                for (int d = 32; d >= 1; d >>= 1) w += __shfl_xor(w, d);
+                if (lane == 0) sm.cnt[par][wave] = w;
+                __syncthreads();
+                int tot = 0;
+#pragma unroll
+                for (int v = 0; v < NW; ++v) tot += sm.cnt[par][v];
+                tot = __builtin_amdgcn_readfirstlane(tot);
+                par ^= 1;
+                if (bit >= 0) {
+                    if (tot >= krem) t = c;
+                } else {
+                    krem -= (t == 0xFFFFFFFFu) ? 0 : tot;
+                }
+            }
+            T = key_value(t);
+        }
+        keep = krem;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             asm volatile("" : "+v"(f[e]));   // one element at a time: no hoisted masks
-            const bool k = f[e] >= T;
-            const uint64_t m = __ballot(k);
-            if (lane == 0) sm.u.c.keep[(e * NT + 64 * wave) / 64] = m;
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            asm volatile("" : "+v"(f[e]));
             const uint64_t m = __ballot(f[e] > T);
             const uint64_t q = __ballot(f[e] == T);
             if (lane == 0) {
-                sm.u.c.keep[(e * NT + 64 * wave) / 64] = m;
-                sm.u.c.tie[(e * NT + 64 * wave) / 64] = q;
+                const int w = (e * NT + 64 * wave) / 32;
+                sm.keep[w] = (uint32_t)m;
+                sm.keep[w + 1] = (uint32_t)(m >> 32);
+                sm.tie[w] = (uint32_t)q;
+                sm.tie[w + 1] = (uint32_t)(q >> 32);
             }
         }
+        __syncthreads();
     }
-    __syncthreads();
 
-    // Pass 2: thread t owns bitmap words t*WPT .. t*WPT+WPT-1 (consecutive
+    // The walk: thread t owns bitmap words t*WPT .. t*WPT+WPT-1 (consecutive
     // keys).  One block scan of its (kept, tie) counts, packed as
     // kept + (tie << kEqShift), places its keys; the ties it keeps are the
     // first (keep - ties before it) of its own.  Sums never carry between
@@ -424,15 +480,16 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
     constexpr int kEqShift = 13;
     static_assert(kMaxTopK < (1 << kEqShift) && (int64_t)Sm::NE << kEqShift <= 0x7FFFFFFF, "count packing");
     constexpr int WPT = (NB + NT - 1) / NT;
-    const uint32_t* kwords = reinterpret_cast<const uint32_t*>(sm.u.c.keep);
-    const uint32_t* twords = reinterpret_cast<const uint32_t*>(sm.u.c.tie);
+    const uint32_t* kwords = sm.keep;
+    const uint32_t* twords = sm.tie;
+    const bool ties = !direct || keep > 0;
     uint32_t kw[WPT], tw[WPT];
     int ck = 0, ct = 0;
 #pragma unroll
     for (int j = 0; j < WPT; ++j) {
         const int w = tid * WPT + j;
         kw[j] = w < NB ? kwords[w] : 0u;
-        tw[j] = (!all_ties && w < NB) ? twords[w] : 0u;
+        tw[j] = (ties && w < NB) ? twords[w] : 0u;
         ck += __popc(kw[j]);
         ct += __popc(tw[j]);
     }
@@ -449,7 +506,7 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
 #pragma unroll
     for (int j = 0; j < WPT; ++j) {
         uint32_t m = kw[j];
-        if (!all_ties) {
+        if (ties) {
             uint32_t t = tw[j];
             const int c = __popc(t);
             if (c <= q) {
@@ -472,8 +529,10 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
     if (tid == 0 && count) *count = top_k;
 }
 
+// Three 512-thread blocks per CU need at most 80 VGPRs (six waves per SIMD).
 template <int NT, int EPT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void topk_prefill_kernel(TopkArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 512 ? 6 : 4, 8))) void topk_prefill_kernel(
+    TopkArgs a) {
     __shared__ TopkSmem<NT, EPT> sm;
     const int r = blockIdx.x;
     const int64_t p = a.pos0 + r;
