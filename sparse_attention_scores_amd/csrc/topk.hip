@@ -136,12 +136,17 @@ struct TopkSmem {
 };
 
 // Compare predicates of the lane-mask builtins (LLVM's numbering).
-constexpr int kCmpOgt = 2, kCmpOge = 3, kCmpOle = 5, kCmpOrd = 7;   // float
-constexpr int kCmpEq = 32, kCmpUgt = 34;                            // integer
+constexpr int kCmpOge = 3;   // float, ordered >=
 
-// Lane l (wave-uniform) of x takes the wave-uniform value u (v_writelane).
-__device__ __forceinline__ void write_lane(uint32_t& x, uint32_t u, int l) {
-    asm("v_writelane_b32 %0, %1, %2" : "+v"(x) : "s"(u), "i"(l));
+// Lanes l and l + 1 of x take the low and high halves of the wave-uniform
+// mask m (v_writelane).  The mask usually comes straight from a compare;
+// the compiler does not see the lane writes inside the asm, so the asm
+// itself leaves the wait states a VALU-written SGPR needs before a lane
+// access reads it.
+__device__ __forceinline__ void write_mask(uint32_t& x, uint64_t m, int l) {
+    asm("s_nop 4\n\tv_writelane_b32 %0, %1, %3\n\tv_writelane_b32 %0, %2, %4"
+        : "+v"(x)
+        : "s"((uint32_t)m), "s"((uint32_t)(m >> 32)), "i"(l), "i"(l + 1));
 }
 
 // Block-wide minimum and maximum (every thread gets both).
@@ -167,6 +172,75 @@ __device__ inline void block_minmax(float& lo, float& hi, int& par, Sm& sm) {
 __device__ inline int value_bin(float v, float scale, float off) {
     const int b = (int)__builtin_fmaf(v, scale, off);
     return min(max(b, 0), kBins - 1);
+}
+
+// The first float f of [a, b] at which fma(f, scale, off) >= n (a predicate
+// that only grows with f), or b itself when no earlier float reaches n;
+// every lane of the wave gets it.  A search over the order-preserving keys
+// that tests 64 keys per round: the first round a window of 64 consecutive
+// floats at the estimate (n - off) / scale, which usually brackets the
+// answer, then 64 evenly spaced keys, each round keeping the stretch that
+// ends at the first key that passes.  A span of 2^32 keys takes six rounds.
+__device__ inline float first_reaching(float n, float a, float b, float scale, float off) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t kend = order_key(b);
+    uint32_t ka = order_key(a), kb = kend;
+    const uint32_t kg = order_key(fminf(fmaxf((n - off) / scale, a), b));
+    for (int round = 0; round < 16 && ka != kb; ++round) {
+        uint32_t t;
+        if (round == 0) {
+            // kg - 32 + lane within [ka, kb] (unsigned compares throughout)
+            const uint32_t w0 = kg >= ka + 32u ? kg - 32u : ka;
+            t = w0 + (uint32_t)lane;
+            t = t < kb ? t : kb;
+        } else {
+            t = ka + (uint32_t)(((uint64_t)(kb - ka) * (uint32_t)(lane + 1)) >> 6);   // lane 63 tests kb
+        }
+        const bool pass = t == kend || __builtin_fmaf(key_value(t), scale, off) >= n;
+        const uint64_t m = __ballot(pass);
+        if (m == 0) {   // only in the window round: everything up to its last key fails
+            ka = (uint32_t)__builtin_amdgcn_readlane((int)t, 63) + 1u;
+            continue;
+        }
+        const int j = __builtin_ctzll(m);
+        const uint32_t tj = (uint32_t)__builtin_amdgcn_readlane((int)t, j);
+        const uint32_t below = j > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)t, j - 1) + 1u : ka;
+        ka = below;
+        kb = tj;
+    }
+    return key_value(ka);
+}
+
+// Both edges of bin b at once: L, the first float of [lo, hiup] whose bin
+// reaches b, and U, the first whose bin reaches b + 1 (lo for b = 0 and hiup
+// for the last bin).  Lanes 0-31 test a window of 32 consecutive floats at
+// L's estimate and lanes 32-63 one at U's; an edge whose window does not
+// bracket it is searched in full (first_reaching).
+__device__ inline void bin_edges(int b, float lo, float hiup, float scale, float off, float& L, float& U) {
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    const float n = (float)(b + h);
+    const uint32_t ka = order_key(lo), kend = order_key(hiup);
+    const uint32_t kg = order_key(fminf(fmaxf((n - off) / scale, lo), hiup));
+    const uint32_t w0 = kg >= ka + 16u ? kg - 16u : ka;
+    uint32_t t = w0 + (uint32_t)(lane & 31);
+    t = t < kend ? t : kend;
+    const bool pass = t == kend || __builtin_fmaf(key_value(t), scale, off) >= n;
+    const uint64_t m = __ballot(pass);
+    float e[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t mk = (uint32_t)(m >> (32 * k));
+        const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)t, 32 * k);
+        // bracketed: some key passes, and the first that does is the window's
+        // first key only when that is lo itself
+        if (mk != 0u && ((mk & 1u) == 0u || t0 == ka)) {
+            e[k] = key_value((uint32_t)__builtin_amdgcn_readlane((int)t, 32 * k + __builtin_ctz(mk)));
+        } else {
+            e[k] = first_reaching((float)(b + k), lo, hiup, scale, off);
+        }
+    }
+    L = b > 0 ? e[0] : lo;
+    U = b < kBins - 1 ? e[1] : hiup;
 }
 
 // Element k of a row: its score and the key index written for it.
@@ -308,37 +382,33 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
             uint32_t mw[NMW];
 #pragma unroll
             for (int i = 0; i < NMW; ++i) mw[i] = 0u;
-            // Lane masks straight from the compares (combined in scalar
-            // registers).  At the first level every value lies in [lo, hi]:
-            // a key is live unless it is padding, and none lies above hi.
+            // Bin membership as two compares per key.  Uf and L are the
+            // first floats (at or above lo) whose bin reaches bstar + 1 and
+            // bstar, found exactly by searching the fused multiply-add, and
+            // Uf is capped just above hi: a key is above the bin when
+            // f >= Uf and in it when L <= f < Uf.  Keys below lo fail both,
+            // keys above hi (kept at an earlier level) pass the first, and
+            // NaN padding fails both.
+            const float hiup = key_value(order_key(hi) + 1u);
+            float L, Uf;
+            bin_edges(bstar, lo, hiup, scale, off, L, Uf);
             int wc = 0;
             int me = tid;
             asm volatile("" : "+v"(me));   // elements computed where stored, not kept per element
-            auto gather = [&](auto first) {
-                constexpr bool kFirst = decltype(first)::value;
 #pragma unroll
-                for (int e = 0; e < EPT; ++e) {
-                    const uint32_t b = (uint32_t)value_bin(f[e], scale, off);
-                    const uint64_t live = kFirst ? __builtin_amdgcn_fcmpf(f[e], f[e], kCmpOrd)
-                                                 : __builtin_amdgcn_fcmpf(f[e], lo, kCmpOge) &
-                                                       __builtin_amdgcn_fcmpf(f[e], hi, kCmpOle);
-                    uint64_t up = live & __builtin_amdgcn_uicmp(b, (uint32_t)bstar, kCmpUgt);
-                    if (!kFirst) up |= __builtin_amdgcn_fcmpf(f[e], hi, kCmpOgt);
-                    write_lane(mw[e / 32], (uint32_t)up, 2 * (e % 32));
-                    write_lane(mw[e / 32], (uint32_t)(up >> 32), 2 * (e % 32) + 1);
-                    const uint64_t m = live & __builtin_amdgcn_uicmp(b, (uint32_t)bstar, kCmpEq);
-                    if (m) {
-                        if ((m >> lane) & 1) {
-                            const int p = wc + count_below(m);
-                            sm.u.g.slice[wave][p] = f[e];
-                            sm.u.g.slicek[wave][p] = (uint16_t)(e * NT + me);
-                        }
-                        wc += (int)__popcll(m);
+            for (int e = 0; e < EPT; ++e) {
+                const uint64_t up = __builtin_amdgcn_fcmpf(f[e], Uf, kCmpOge);
+                write_mask(mw[e / 32], up, 2 * (e % 32));
+                const uint64_t m = __builtin_amdgcn_fcmpf(f[e], L, kCmpOge) & ~up;
+                if (m) {
+                    if ((m >> lane) & 1) {
+                        const int p = wc + count_below(m);
+                        sm.u.g.slice[wave][p] = f[e];
+                        sm.u.g.slicek[wave][p] = (uint16_t)(e * NT + me);
                     }
+                    wc += (int)__popcll(m);
                 }
-            };
-            if (lev == 0) gather(std::true_type{});
-            else gather(std::false_type{});
+            }
 #pragma unroll
             for (int i = 0; i < NMW; ++i) {
                 const int e = 32 * i + (lane >> 1);
@@ -529,9 +599,10 @@ __device__ __forceinline__ void topk_row(const Row& row, int n, int top_k, const
     if (tid == 0 && count) *count = top_k;
 }
 
-// Three 512-thread blocks per CU need at most 80 VGPRs (six waves per SIMD).
+// Six waves per SIMD (three 512-thread or six 256-thread blocks per CU) need
+// at most 80 VGPRs.
 template <int NT, int EPT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 512 ? 6 : 4, 8))) void topk_prefill_kernel(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT <= 512 && EPT == 32 ? 6 : 4, 8))) void topk_prefill_kernel(
     TopkArgs a) {
     __shared__ TopkSmem<NT, EPT> sm;
     const int r = blockIdx.x;

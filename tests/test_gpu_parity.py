@@ -226,6 +226,41 @@ def test_topk_extreme_values(case):
     assert np.array_equal(host(idx), ref_idx)
 
 
+@pytest.mark.parametrize("case", ["near_zero", "on_edges", "on_edges_scaled"])
+def test_topk_bin_edges(case):
+    """Keys whose scores sit exactly on the edges of the value bins, and a
+    boundary bin around zero (scores of both signs; the selection's last
+    level bins a range of a few thousandths across zero, where the floats
+    are dense and the bin edges have to be found by a full search): the
+    kernel's membership tests must match the bins exactly."""
+    import dataclasses
+    import torch
+    rng = np.random.default_rng({"near_zero": 11, "on_edges": 12, "on_edges_scaled": 13}[case])
+    L = 4
+    if case == "near_zero":
+        N, top_k = 6000, 600
+        S = np.concatenate([rng.uniform(-550, -1, (L, 5000)), rng.uniform(-2e-3, 3e-3, (L, 1000))], axis=1)
+        S = rng.permuted(S, axis=1).astype(np.float32)
+    elif case == "on_edges":   # range [0, 256]: bin edges at the integers
+        N, top_k = 12000, 2048
+        S = rng.integers(0, 257, size=(L, N)).astype(np.float32)
+        S[:, 0], S[:, 1] = 0.0, 256.0
+    else:                      # range [-3, 5]: bin edges at multiples of 1/32
+        N, top_k = 12000, 2048
+        S = (rng.integers(0, 257, size=(L, N)) / 32.0 - 3.0).astype(np.float32)
+        S[:, 0], S[:, 1] = -3.0, 5.0
+    q_start = N - L
+    pos = q_start + np.arange(L)
+    ref_idx, ref_cnt = oracle.topk_select(S, pos, top_k)
+    shape = dataclasses.replace(W.GLM, top_k=top_k)
+    idx = torch.empty((L, top_k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((L,), dtype=torch.int32, device="cuda")
+    say("topk-edges", case)
+    lib().dsa_topk_select(shape, dev(S), L, N, q_start, idx, cnt)
+    assert np.array_equal(host(cnt), ref_cnt)
+    assert np.array_equal(host(idx), ref_idx)
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_topk_full_every_row_bit_exact(name):
     """The standalone top-k on the GPU's scores: every row's selection equals
