@@ -48,7 +48,9 @@ constexpr int kIdxChunks = kIdxSub / 32; // 32-key MFMA chunks per stage
 constexpr int kIdxCUs = 256;              // compute units the grid should cover
 
 constexpr int kIdxdWaves = 4;
-constexpr int kIdxdKeysPerWave = 64;
+constexpr int kIdxdSlab = 64;                                // keys per LDS slab
+constexpr int kIdxdSlabs = 2;                                // slabs per wave, one after the other
+constexpr int kIdxdKeysPerWave = kIdxdSlab * kIdxdSlabs;
 constexpr int kIdxdKeysPerBlock = kIdxdWaves * kIdxdKeysPerWave;
 
 // Head held by accumulator register r of lane-half `half` in the 32x32 layout.
@@ -248,8 +250,8 @@ __global__ __launch_bounds__(kIdxdWaves * 64)
 void indexer_decode_kernel(const uint16_t* __restrict__ qI, const uint16_t* __restrict__ kI,
                            const float* __restrict__ w, float* __restrict__ S, SeqMeta m) {
     using C = IdxShape<HI, DI>;
-    static_assert(kIdxdKeysPerWave == 64, "one 64-key LDS slab per wave");
-    constexpr int SLOTS = 64 * C::CPR;          // 16-byte slots per key slab
+    static_assert(kIdxdSlab == 64, "a slab is two 32-key MFMA tiles");
+    constexpr int SLOTS = kIdxdSlab * C::CPR;   // 16-byte slots of a key slab
     constexpr int QS = HI * C::CPR;             // 16-byte slots of the query
     constexpr int QRUNS = (QS + 63) / 64;       // 64-slot copies of the query
     __shared__ u32x4 lds[kIdxdWaves][SLOTS];
@@ -259,20 +261,23 @@ void indexer_decode_kernel(const uint16_t* __restrict__ qI, const uint16_t* __re
     const int half = lane >> 5, col = lane & 31;
     const int b = seq_of_block(m, blockIdx.x);
     const int ctx = m.ctx[b];
-    const int kb = (blockIdx.x - m.blk0[b]) * kIdxdKeysPerBlock + wave * kIdxdKeysPerWave;
-    const bool live = kb < ctx;   // wave-uniform; idle waves still help with the query
-
-    if (live) {
+    const int kw = (blockIdx.x - m.blk0[b]) * kIdxdKeysPerBlock + wave * kIdxdKeysPerWave;
+    const uint32_t slab = lds_addr(&lds[wave][0]);
+    // whole key rows of the slab at key kb to this wave's LDS slab (rows past
+    // the sequence repeat its last key, never stored); piece p of row r sits
+    // at slot p ^ (r mod CPR)
+    auto copy_slab = [&](int kb) {
         const void* kbase = uniform_ptr(kI + (m.key_off[b] + kb) * DI);
-        const int last = min(63, ctx - 1 - kb);
-        const uint32_t slab = lds_addr(&lds[wave][0]);
+        const int last = min(kIdxdSlab - 1, ctx - 1 - kb);
 #pragma unroll
         for (int i = 0; i < C::CPR; ++i) {
             const int slot = i * 64 + lane, r = slot / C::CPR, p = slot % C::CPR;
             const int piece = p ^ (r % C::CPR);
             gather16_to_lds(kbase, (uint32_t)(min(r, last) * DI * 2 + piece * 16), slab + i * 1024);
         }
-    }
+    };
+    const bool live = kw < ctx;   // wave-uniform; idle waves still help with the query
+    if (live) copy_slab(kw);
     {
         const void* qbase = uniform_ptr(qI + (int64_t)b * HI * DI);
         for (int i = wave; i < QRUNS; i += kIdxdWaves) {
@@ -295,23 +300,41 @@ void indexer_decode_kernel(const uint16_t* __restrict__ qI, const uint16_t* __re
     if (!live) return;
 
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 qf[C::KS], b0[C::KS], b1[C::KS];
+    u32x4 qf[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-        const int pos = (ks * 2 + half) ^ (col % C::CPR);   // rows col and col + 32 share the swizzle
+        const int pos = (ks * 2 + half) ^ (col % C::CPR);
         qf[ks] = col < HI ? ldq[col * C::CPR + pos] : zero;
-        b0[ks] = lds[wave][col * C::CPR + pos];
-        b1[ks] = lds[wave][(col + 32) * C::CPR + pos];
     }
-    f32x16 acc0 = {}, acc1 = {};
+    for (int j = 0; j < kIdxdSlabs; ++j) {
+        const int kb = kw + j * kIdxdSlab;
+        u32x4 b0[C::KS], b1[C::KS];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-        acc0 = mfma32_bf16(qf[ks], b0[ks], acc0);
-        acc1 = mfma32_bf16(qf[ks], b1[ks], acc1);
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const int pos = (ks * 2 + half) ^ (col % C::CPR);   // rows col and col + 32 share the swizzle
+            b0[ks] = lds[wave][col * C::CPR + pos];
+            b1[ks] = lds[wave][(col + 32) * C::CPR + pos];
+        }
+        // the next slab reuses this one's LDS once its reads have returned;
+        // its copy then runs under this slab's MFMAs and store
+        const bool next = j + 1 < kIdxdSlabs && kb + kIdxdSlab < ctx;
+        if (next) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            copy_slab(kb + kIdxdSlab);
+        }
+        f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            acc0 = mfma32_bf16(qf[ks], b0[ks], acc0);
+            acc1 = mfma32_bf16(qf[ks], b1[ks], acc1);
+        }
+        const float tot = combine_halves(weighted_relu(acc0, wr), weighted_relu(acc1, wr));
+        const int key = kb + 32 * half + col;
+        if (key < ctx) S[m.s_off[b] + key] = tot;   // the query sits at ctx-1: every cached key is visible
+        if (!next) break;
+        // the copy's loads precede this store: all but the newest access done
+        wait_vmcnt<1>();
     }
-    const float tot = combine_halves(weighted_relu(acc0, wr), weighted_relu(acc1, wr));
-    const int key = kb + 32 * half + col;
-    if (key < ctx) S[m.s_off[b] + key] = tot;   // the query sits at ctx-1: every cached key is visible
 }
 
 }  // namespace
