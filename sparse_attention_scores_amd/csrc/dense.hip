@@ -336,9 +336,22 @@ __global__ __launch_bounds__(256) void selection_mask_kernel(MaskArgs a) {
     const int c = min(max(a.count[i], 0), a.top_k);
     const int p = a.q_start + i;
     const int32_t* sel = a.idx + (int64_t)i * a.top_k;
-    for (int t = threadIdx.x; t < c; t += 256) {
-        const int j = sel[t];
-        if (j >= 0 && j < a.N && j <= p) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    auto mark = [&](int t, int j) {
+        if (t < c && j >= 0 && j < a.N && j <= p) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    };
+    if ((a.top_k & 3) == 0) {
+        // four ids per 16-byte load (rows start 16-byte aligned), two loads
+        // in flight per thread before any atomic; ids past c are read (they
+        // lie in the row) and ignored
+        for (int t0 = 4 * (int)threadIdx.x; t0 < c; t0 += 2 * 4 * 256) {
+            const int t1 = t0 + 4 * 256;
+            const int4 x = *reinterpret_cast<const int4*>(sel + t0);
+            const int4 y = t1 < c ? *reinterpret_cast<const int4*>(sel + t1) : int4{-1, -1, -1, -1};
+            mark(t0, x.x); mark(t0 + 1, x.y); mark(t0 + 2, x.z); mark(t0 + 3, x.w);
+            mark(t1, y.x); mark(t1 + 1, y.y); mark(t1 + 2, y.z); mark(t1 + 3, y.w);
+        }
+    } else {
+        for (int t = threadIdx.x; t < c; t += 256) mark(t, sel[t]);
     }
     __syncthreads();
     uint32_t* row = a.mask + (int64_t)i * a.W;
