@@ -746,7 +746,9 @@ void attention_split_kernel(AttnSplitArgs a, SeqMeta m) {
             float* orow = a.part_o + ((int64_t)item * NH + head) * DL;
 #pragma unroll
             for (int f = 0; f < C::FBW; ++f)
-                *reinterpret_cast<f32x4*>(orow + 16 * (C::FBW * cw + f) + 4 * c.g) = o[f][hb];
+                // streamed past the L2 (the combine reads them on other XCDs):
+                // less to write back when the launch ends
+                __builtin_nontemporal_store(o[f][hb], reinterpret_cast<f32x4*>(orow + 16 * (C::FBW * cw + f) + 4 * c.g));
         }
     }
 }
