@@ -147,7 +147,9 @@ def test_topk_small_bit_exact(name):
 @pytest.mark.parametrize("N,top_k,levels", [(300, 32, 3), (5000, 2048, 5), (16384, 2048, 40),
                                             (16384, 2048, 2), (65536, 2048, 7), (3000, 1, 4),
                                             (2049, 2048, 2), (65537, 2048, 2), (131072, 2048, 7),
-                                            (200001, 100, 3), (262144, 2048, 40)])
+                                            (200001, 100, 3), (262144, 2048, 40), (1000, 100, 7),
+                                            (2000, 500, 9), (4000, 1000, 50), (8000, 2048, 1000),
+                                            (30000, 2048, 40)])
 def test_topk_ties_and_sizes(N, top_k, levels):
     """Scores drawn from a few values (many ties at the boundary), negative
     values and -0.0/+0.0 included; every row at a different length."""
@@ -164,6 +166,33 @@ def test_topk_ties_and_sizes(N, top_k, levels):
     idx = torch.empty((L, top_k), dtype=torch.int32, device="cuda")
     cnt = torch.empty((L,), dtype=torch.int32, device="cuda")
     say("topk-ties", N, top_k, levels)
+    lib().dsa_topk_select(shape, dev(S), L, N, q_start, idx, cnt)
+    assert np.array_equal(host(cnt), ref_cnt)
+    assert np.array_equal(host(idx), ref_idx)
+
+
+@pytest.mark.parametrize("N,top_k", [(700, 100), (1500, 512), (3500, 2048), (7000, 2048), (12000, 2048),
+                                     (30000, 2048), (60000, 2048), (100000, 2048)])
+def test_topk_distinct_every_block_shape(N, top_k):
+    """Distinct scores (normal, some rows shifted far from zero, one row of
+    both signs around a tiny spread) at lengths that reach every block shape
+    of the selection: 256 threads with 4 to 32 keys each, 512 x 32,
+    1024 x 32, 1024 x 64, and rows taken in pieces."""
+    import dataclasses
+    import torch
+    rng = np.random.default_rng(N + top_k)
+    L = 5
+    S = rng.standard_normal((L, N)).astype(np.float32)
+    S[1] = (S[1] * 0.001 + 1000.0).astype(np.float32)   # narrow range far from zero
+    S[2] = (S[2] * 1e-6).astype(np.float32)             # tiny values of both signs
+    S[3] = (S[3] * 1e4).astype(np.float32)
+    q_start = N - L
+    pos = q_start + np.arange(L)
+    ref_idx, ref_cnt = oracle.topk_select(S, pos, top_k)
+    shape = dataclasses.replace(W.GLM, top_k=top_k)
+    idx = torch.empty((L, top_k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((L,), dtype=torch.int32, device="cuda")
+    say("topk-distinct", N, top_k)
     lib().dsa_topk_select(shape, dev(S), L, N, q_start, idx, cnt)
     assert np.array_equal(host(cnt), ref_cnt)
     assert np.array_equal(host(idx), ref_idx)
