@@ -272,6 +272,11 @@ void gemm_nt_kernel(GemmArgs g) {
             return;
         }
     }
+    // Non-temporal stores: the output is not read again by this launch, and
+    // streaming it past the L2 let the stores overlap the MFMAs far better
+    // (o_proj 806 -> 706 us, q absorption 151 -> 113 us, up-projection
+    // 173 -> 150 us).  The kv_b value form above keeps ordinary stores: its
+    // scattered 8-byte pieces took twice as long when streamed.
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -283,10 +288,11 @@ void gemm_nt_kernel(GemmArgs g) {
                 const int n = n0 + (BN / 2) * wn + 32 * j + (l & 31);
                 const int64_t off = z * g.c_batch + (int64_t)m * g.ldc + n;
                 if constexpr (C_F32) {
-                    static_cast<float*>(g.C)[off] = acc[i][j][r];
+                    __builtin_nontemporal_store(acc[i][j][r], static_cast<float*>(g.C) + off);
                 } else {
                     const uint32_t u = __float_as_uint(acc[i][j][r]);
-                    static_cast<uint16_t*>(g.C)[off] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+                    __builtin_nontemporal_store((uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16),
+                                                static_cast<uint16_t*>(g.C) + off);
                 }
             }
         }
